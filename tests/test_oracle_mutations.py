@@ -1,0 +1,65 @@
+"""Planted mistakes: each mutant is a copy of an oracle step with one plausible error (a
+dropped term, a wrong index, a flipped tie rule), and each must fail the pin that guards
+that step.  The mistakes live here, on the CPU, never in the product path."""
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from oracle.verify import PAD
+from weight_bound_verify_amd import synth
+
+
+def _exact_row(q, s, h):
+    return [float(sum(Fraction(float(s[v, k // 32])) * int(q[v, k]) * Fraction(float(h[k]))
+                      for k in range(q.shape[1]))) for v in range(q.shape[0])]
+
+
+def test_dequant_with_wrong_block_scale_is_caught():
+    def mutant(q, scale):                           # scale index off by one block
+        sh = np.roll(scale.astype(np.float64), 1, axis=1)
+        return q.astype(np.float64) * np.repeat(sh, 32, axis=1)
+    rng = np.random.default_rng(0)
+    q, s = synth.quantize_q8b32(rng.standard_normal((8, 64), dtype=np.float32) * np.float32(0.02))
+    h = synth.fp16_normal(rng, 64)
+    ex = _exact_row(q, s, h)
+    good = oracle.dequantize(q, s) @ h.astype(np.float64)
+    bad = mutant(q, s) @ h.astype(np.float64)
+    assert np.allclose(good, ex, rtol=0, atol=1e-12)
+    assert not np.allclose(bad, ex, rtol=0, atol=1e-6)
+
+
+def test_highest_index_tie_rule_is_caught():
+    L = np.array([[0.0, 2.0, 1.0, 2.0]])
+    mutant = lambda L: L.shape[1] - 1 - np.argmax(L[:, ::-1], axis=1)
+    assert oracle.argmax_lowest(L)[0] == 1 and mutant(L)[0] == 3
+
+
+def test_accept_off_by_one_is_caught():
+    def mutant(a, d):                               # compares d_i with the row of d_i itself
+        j = 0
+        while j < len(d) and d[j] == a[j + 1]:
+            j += 1
+        return j
+    a = [3, 4, 5, 6]
+    d = [3, 4, 5]
+    assert oracle.accept_length(a, d) == 3 and mutant(a, d) != 3
+
+
+def test_oldest_occurrence_drafter_is_caught():
+    def mutant(tokens, n_max, K):                   # scans from the oldest match
+        L = len(tokens)
+        for n in range(min(n_max, L - 1), 0, -1):
+            for e in range(n - 1, L - 1):
+                if tokens[e - n + 1:e + 1] == tokens[L - n:]:
+                    c = tokens[e + 1:min(e + K, L - 1) + 1]
+                    return c + [PAD] * (K - len(c))
+        return [PAD] * K
+    toks = [1, 2, 10, 1, 2, 20, 1, 2]
+    assert oracle.propose_scan(toks, 2, 1)[0] == [20] and mutant(toks, 2, 1) == [10]
+
+
+def test_rmsnorm_without_mean_is_caught():
+    x = np.full((1, 64), 3.0, dtype=np.float16)
+    mutant = lambda x: (x / np.sqrt(np.sum(x.astype(np.float64) ** 2) + 1e-6)).astype(np.float16)
+    assert (oracle.rmsnorm_fp16(x, 0.0) == 1).all() and not (mutant(x) == 1).all()
