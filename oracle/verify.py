@@ -74,8 +74,11 @@ def argmax_lowest(L: np.ndarray) -> np.ndarray:
 
 
 def top2_gap(L: np.ndarray) -> np.ndarray:
-    """top1 - top2 logit per row (0 when the maximum is attained twice)."""
+    """top1 - top2 logit per row (0 when the maximum is attained twice; +inf for a single
+    candidate, which has no runner-up to tie with)."""
     L = np.atleast_2d(L)
+    if L.shape[1] < 2:
+        return np.full(L.shape[0], np.inf)
     part = np.partition(L, L.shape[1] - 2, axis=1)
     return part[:, -1] - part[:, -2]
 

@@ -152,3 +152,4 @@ def test_top2_gap_and_admissible_set():
     assert gap[0] == pytest.approx(0.0005) and gap[1] == 0.0
     adm = oracle.admissible_sets(L, 1e-3)
     assert list(adm[0]) == [1, 2] and list(adm[1]) == [0, 1]
+    assert oracle.top2_gap(np.array([[0.5], [-2.0]])).tolist() == [np.inf, np.inf]
