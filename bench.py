@@ -1,0 +1,321 @@
+"""Verify-round throughput on one MI355X: rounds/s and achieved HBM GB/s of the q8b32 head.
+
+A step is one device-resident verify round through the C ABI:
+  specverify_propose (n-gram drafter over the committed stream)
+  -> specverify_verify (int8 per-block-32 head matmul of the S = K+1 window + fused argmax)
+  -> specverify_accept (greedy accept, commits 1 + j tokens)
+(the dense-stack workload adds 36 x [rmsnorm, gate/up + SiLU*mul, down + residual] and a
+final rmsnorm in front of the head).  Inputs are seeded synthetic data resident in HBM before
+the timed region; hidden rows rotate over 64 sets and, for heads that could sit in the
+256 MB Infinity Cache, over several copies of the weights.
+
+Prints one JSON line.  --gpus N with N > 1 is not supported (one GPU per box).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "verify rounds/s and achieved HBM GB/s (% of peak), int8 lm_head S=K+1"
+
+# workloads: (config id for seeds, V, H, K, drafts, context length, copy rate, layers)
+WORKLOADS = {
+    "c1": dict(cid=0, V=8192, H=512, K=8, drafts="ngram", ctx=512, copy=None, layers=0,
+               name="tiny head H=512 V=8192 K=8 S=9, n-gram drafts over a 512-id context with a planted span"),
+    "c2": dict(cid=1, V=151936, H=2560, K=8, drafts="ngram", ctx=4096, copy=0.30, layers=0,
+               name="Qwen3-4B-shaped head H=2560 V=151936 K=8 S=9, n-gram drafts over 4096 Zipf(1.1) ids with 30% copied spans"),
+    "c3": dict(cid=2, V=248320, H=2048, K=8, drafts="forced", ctx=4096, copy=0.30, layers=0,
+               name="35B-A3B-shaped head H=2048 V=248320 K=8 S=9, drafts forced to match the first j~U{0..K} argmaxes"),
+    "c3s17": dict(cid=2, V=248320, H=2048, K=16, drafts="forced", ctx=4096, copy=0.30, layers=0,
+                  name="35B-A3B-shaped head H=2048 V=248320 K=16 S=17, forced drafts"),
+    "c4s2": dict(cid=3, V=248320, H=5120, K=1, drafts="ngram", ctx=16384, copy=0.20, layers=0,
+                 name="large-hidden head H=5120 V=248320 K=1 S=2, n-gram drafts over 16384 Zipf(1.1) ids with 20% copied spans"),
+    "c4s9": dict(cid=3, V=248320, H=5120, K=8, drafts="ngram", ctx=16384, copy=0.20, layers=0,
+                 name="large-hidden head H=5120 V=248320 K=8 S=9, n-gram drafts"),
+    "c4s17": dict(cid=3, V=248320, H=5120, K=16, drafts="ngram", ctx=16384, copy=0.20, layers=0,
+                  name="large-hidden head H=5120 V=248320 K=16 S=17, n-gram drafts"),
+    "c5": dict(cid=4, V=151936, H=4096, K=8, drafts="ngram", ctx=4096, copy=0.30, layers=36, F=12288,
+               name="dense stack 36 x [4096->12288 gate/up, 12288->4096 down] + 4096x151936 head, K=8 S=9"),
+}
+R_SETS = 64
+
+
+def head_bytes(V, H, S):
+    """Algorithmic HBM bytes of one head launch: int8 codes, fp16 block scales, fp16 window."""
+    return V * H + 2 * V * (H // 32) + 2 * S * H
+
+
+def stack_bytes(layers, H, F, S):
+    per = 3 * (F * H + 2 * F * (H // 32))
+    return layers * (per + 2 * S * (H + 2 * F + H))
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in ("sv_gemm.hip", "sv_device.h"):
+        with open(os.path.join(ROOT, "weight_bound_verify_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM traffic per launch of the head kernel from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"verify_q8b32_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def build_inputs(wl, args, torch, sv, synth):
+    dev = torch.device("cuda:0")
+    V, H, K = wl["V"], wl["H"], wl["K"]
+    S = K + 1
+    st = synth.streams(wl["cid"])
+    t0 = time.time()
+    q, s = synth.quantized_head(st.weights, V, H)
+    copies = args.rotate if args.rotate else (2 if V * H < 2 ** 31 else 1)
+    wq = [torch.from_numpy(q).to(dev)]
+    ws = [torch.from_numpy(s).to(dev)]
+    for _ in range(copies - 1):
+        wq.append(wq[0].clone())
+        ws.append(ws[0].clone())
+    rng_h = np.random.default_rng(st.hidden)
+    hidden = torch.from_numpy(synth.fp16_normal(rng_h, (R_SETS, S, wl["H"]))).to(dev)
+    rng_c = np.random.default_rng(st.context)
+    if wl["copy"] is None:
+        ctx, _, _ = synth.uniform_context_with_span(rng_c, wl["ctx"], V, 12, 16)
+        frac = None
+    else:
+        ctx, frac = synth.zipf_context_with_copies(rng_c, wl["ctx"], V, wl["copy"])
+    layers = []
+    if wl["layers"]:
+        F = wl["F"]
+        kids = st.weights.spawn(1)[0].spawn(3 * wl["layers"])
+        for li in range(wl["layers"]):
+            mats = []
+            for m, (r, c) in enumerate([(F, H), (F, H), (H, F)]):
+                qq, ss = synth.quantized_head(kids[3 * li + m], r, c)
+                mats.append((torch.from_numpy(qq).to(dev), torch.from_numpy(ss).to(dev)))
+            layers.append(mats)
+    print(f"# inputs ready in {time.time() - t0:.1f} s (weight copies: {copies})", file=sys.stderr, flush=True)
+    return dict(q=q, s=s, wq=wq, ws=ws, hidden=hidden, ctx=ctx, copy_frac=frac, layers=layers, copies=copies)
+
+
+def cpu_baseline(wl, inp, seconds_budget=20.0):
+    """The oracle as it stands, timed on the host on a bounded sample of whole rounds."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    from weight_bound_verify_amd import synth
+
+    V, H, K = wl["V"], wl["H"], wl["K"]
+    S = K + 1
+    rng = np.random.default_rng(12345)
+    hid = inp["hidden"][:4].cpu().numpy()
+    tokens = list(inp["ctx"])
+    rounds = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            x = hid[rounds % len(hid)]
+            if wl["layers"]:
+                return None           # the fp64 oracle stack takes minutes per round
+            drafts, _, _ = oracle.propose_scan(tokens, 3, K)
+            L = oracle.head_logits(inp["q"], inp["s"], x)
+            a = oracle.argmax_lowest(L)
+            if wl["drafts"] == "forced":
+                drafts, _ = synth.forced_drafts(rng, a, K, V)
+            _, app = oracle.accept(a, drafts)
+            tokens += app
+            rounds += 1
+            el = time.perf_counter() - t0
+            if el > seconds_budget or rounds >= 8:
+                break
+    return {"value": rounds / el, "unit": "rounds/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rounds} whole rounds of this workload (fp64 dequantize in 8192-row chunks, "
+                      f"fp64 logits for S={S}, argmax, accept, n-gram propose over the {len(inp['ctx'])}-id "
+                      f"context), single thread, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--rotate", type=int, default=0, help="weight copies to rotate (0 = automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=50, help="isolated head launches timed for the roofline")
+    ap.add_argument("--calib-copy", action="store_true", help="run a 1 GiB device copy (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(each box has one MI355X); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from weight_bound_verify_amd import specverify as sv
+    from weight_bound_verify_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.calib_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "launches": 3}))
+        return
+
+    wl = WORKLOADS[args.config]
+    V, H, K = wl["V"], wl["H"], wl["K"]
+    S = K + 1
+    inp = build_inputs(wl, args, torch, sv, synth)
+    wq, ws, hidden = inp["wq"], inp["ws"], inp["hidden"]
+    copies = inp["copies"]
+
+    # device-resident round state
+    total_rounds = args.warmup + args.steps + 8
+    cap = len(inp["ctx"]) + total_rounds * S + 2 * S
+    tokens = torch.zeros(cap, dtype=torch.int32, device=dev)
+    tokens[:len(inp["ctx"])] = torch.from_numpy(inp["ctx"]).to(dev)
+    state = sv.new_state(dev)
+    state[sv.STATE_LEN] = len(inp["ctx"])
+    drafts = torch.empty(K, dtype=torch.int32, device=dev)
+    argmax = torch.empty(S, dtype=torch.int32, device=dev)
+    work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev)
+
+    # anchor bootstrap: S = 1 verify of an extra row, then accept with K = 0 commits a0
+    h_last = torch.from_numpy(synth.fp16_normal(synth.streams(wl["cid"]).h_last, (1, H))).to(dev)
+    a0 = torch.empty(1, dtype=torch.int32, device=dev)
+    sv.verify(wq[0], ws[0], h_last, a0, sv.workspace(sv.verify_workspace_bytes(V, H, 1), dev))
+    sv.accept(a0, None, tokens, state)
+
+    forced = None
+    if wl["drafts"] == "forced":
+        # drafts that match the first j ~ U{0..K} greedy ids of each hidden set (setup, untimed)
+        rng_d = np.random.default_rng(synth.streams(wl["cid"]).drafts)
+        fd = np.empty((R_SETS, K), dtype=np.int32)
+        for r in range(R_SETS):
+            sv.verify(wq[0], ws[0], hidden[r], argmax, work)
+            torch.cuda.synchronize()
+            fd[r], _ = synth.forced_drafts(rng_d, argmax.cpu().numpy(), K, V)
+        forced = torch.from_numpy(fd).to(dev)
+
+    F = wl.get("F", 0)
+    if wl["layers"]:
+        xbuf = torch.empty((S, H), dtype=torch.float16, device=dev)
+        nbuf = torch.empty((S, H), dtype=torch.float16, device=dev)
+        mbuf = torch.empty((S, F), dtype=torch.float16, device=dev)
+        sw = sv.stack_workspace_bytes(H, F, S, False)
+        swork = sv.workspace(sw, dev) if sw else None
+        gw = sv.stack_workspace_bytes(F, H, S, True)
+        gwork = sv.workspace(gw, dev) if gw else None
+
+    def round_(r):
+        c = r % copies
+        sv.propose(tokens, state, drafts, 3)
+        if wl["layers"]:
+            xbuf.copy_(hidden[r % R_SETS])
+            for (wg, sg), (wu, su), (wd, sd) in inp["layers"]:
+                sv.rmsnorm(xbuf, nbuf)
+                sv.gateup_silu(wg, sg, wu, su, nbuf, mbuf, gwork)
+                sv.linear(wd, sd, mbuf, xbuf, xbuf, swork)
+            sv.rmsnorm(xbuf, nbuf)
+            sv.verify(wq[c], ws[c], nbuf, argmax, work)
+        else:
+            sv.verify(wq[c], ws[c], hidden[r % R_SETS], argmax, work)
+        sv.accept(argmax, forced[r % R_SETS] if forced is not None else drafts, tokens, state)
+
+    for r in range(args.warmup):
+        round_(r)
+    torch.cuda.synchronize()
+    st0 = state.cpu().numpy().copy()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for r in range(args.steps):
+        round_(args.warmup + r)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    st1 = state.cpu().numpy()
+    if st1[sv.STATE_FLAGS]:
+        raise RuntimeError(f"device state flags {st1[sv.STATE_FLAGS]}")
+    rounds = int(st1[sv.STATE_ROUNDS] - st0[sv.STATE_ROUNDS])
+    assert rounds == args.steps
+    hist = (st1[sv.STATE_HIST:sv.STATE_HIST + K + 1] - st0[sv.STATE_HIST:sv.STATE_HIST + K + 1]).tolist()
+    sum_j = int(st1[sv.STATE_SUMJ] - st0[sv.STATE_SUMJ])
+
+    # roofline of the dominant kernel: isolated head launches, HIP events on the launch stream
+    stream = torch.cuda.current_stream()
+    durs = []
+    x_head = nbuf if wl["layers"] else None
+    for i in range(args.kernel_reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        sv.verify(wq[i % copies], ws[i % copies], x_head if x_head is not None else hidden[i % R_SETS], argmax, work,
+                  stream=stream)
+        e1.record(stream)
+        durs.append((e0, e1))
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in durs]))
+    hb = head_bytes(V, H, S)
+    achieved = hb / (kern_ms * 1e-3) / 1e9
+
+    round_bytes = hb + (stack_bytes(wl["layers"], H, F, S) if wl["layers"] else 0)
+    rps = 1000.0 / ms
+    gbps = round_bytes * rps / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(rps, 2),
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8xf16->f32",
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "V": V, "H": H, "S": S, "K": K, "layers": wl["layers"],
+                   "drafts": wl["drafts"], "weight_copies": copies, "hidden_sets": R_SETS},
+        "achieved_GBps": round(gbps, 1),
+        "pct_of_peak_hbm": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "bytes_per_round": round_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": load_traffic(args.config),
+                     "kernel": "q8b32_kernel (head matmul + fused argmax) + argmax_final",
+                     "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": hb},
+        "accept_hist": hist,
+        "tokens_per_round": round((args.steps + sum_j) / args.steps, 3),
+    }
+    if inp["copy_frac"] is not None:
+        out["config"]["context_copy_fraction"] = round(inp["copy_frac"], 3)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

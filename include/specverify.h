@@ -1,0 +1,198 @@
+/*
+ * specverify.h - C ABI of the MI355X (gfx950) greedy speculative-decoding verify path.
+ *
+ * One verify round, all on the device, no host synchronisation inside it:
+ *   specverify_propose  n-gram prompt-lookup drafter over the committed token stream
+ *   specverify_verify   int8 per-block-32 head matmul of the S = K+1 window + per-row argmax
+ *   specverify_accept   greedy longest-prefix acceptance, commits 1 + j tokens
+ * plus the dense weight-bound stack in front of the head (rmsnorm, gate/up + SiLU*mul,
+ * down + residual) built on the same int8 matmul core.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers (hipMalloc'd, or torch CUDA tensors), owned by the caller
+ *     and valid until the work enqueued on `stream` has completed.  `stream` is a
+ *     hipStream_t; NULL means the default stream.
+ *   - A call validates its arguments, then enqueues kernels on `stream` and returns.  It
+ *     never allocates, frees, synchronises, prints, aborts or throws.
+ *   - The return value is an sv_status.  Argument errors are detected on the host before any
+ *     HIP call is made and nothing is enqueued.  SV_ERR_HIP reports a launch failure; the
+ *     detail is in specverify_last_error() (thread-local).
+ *   - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
+ *   - Calls on one stream are ordered; calls that share output buffers on different streams
+ *     race unless the caller orders them.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SV_OK = 0,
+    SV_ERR_NULL = 1,       /* a required pointer is NULL                                  */
+    SV_ERR_SHAPE = 2,      /* a size is out of range or inconsistent                      */
+    SV_ERR_ALIGN = 3,      /* a pointer is not aligned as documented                      */
+    SV_ERR_WORKSPACE = 4,  /* workspace smaller than the *_workspace_bytes() answer       */
+    SV_ERR_CAPACITY = 5,   /* token buffer capacity too small for the call                */
+    SV_ERR_HIP = 6,        /* a HIP call failed (see specverify_last_error)               */
+    SV_ERR_DEVICE = 7      /* the current device is not gfx950                            */
+} sv_status;
+
+/* Limits. */
+#define SV_MAX_S 64        /* rows of one verify window (K <= 63)                          */
+#define SV_MAX_NGRAM 8     /* largest n-gram order of the drafter                          */
+#define SV_BLOCK 32        /* quantization block length along the hidden axis             */
+
+/*
+ * Round state: int32_t[SV_STATE_WORDS] on the device, zero-filled by the caller before the
+ * first call, then owned by the library's kernels.
+ *   [0] len      committed tokens in `tokens`; tokens[len-1] is the pending anchor a0
+ *   [1] j        drafts accepted by the last specverify_accept
+ *   [2] n_valid  non-pad drafts written by the last specverify_propose
+ *   [3] n_used   n-gram order that matched in the last propose (0 = no match)
+ *   [4] flags    sticky error bits: bit 0 = a call would have overflowed `cap` or found
+ *                len outside [0, cap] (that call wrote no token)
+ *   [5] rounds   number of accept calls that committed tokens
+ *   [6] sum_j    sum of j over those calls
+ *   [7] reserved
+ *   [8 + j]      histogram of j, j = 0 .. SV_MAX_S-1
+ */
+#define SV_STATE_WORDS 80
+#define SV_STATE_LEN 0
+#define SV_STATE_J 1
+#define SV_STATE_NVALID 2
+#define SV_STATE_NUSED 3
+#define SV_STATE_FLAGS 4
+#define SV_STATE_ROUNDS 5
+#define SV_STATE_SUMJ 6
+#define SV_STATE_HIST 8
+#define SV_FLAG_CAPACITY 1
+
+/*
+ * specverify_propose - n-gram prompt-lookup drafter.
+ * Page: "Stream C - Speculative decoding: feasibility verdict + implementation plan",
+ * section "The delta" (a hashtable over the prompt+generated stream maps the last m tokens
+ * to their most recent continuation; draft cost is nil) and the handoff's n-gram order /
+ * draft length knobs; "Spec-decode on GDN hybrids - static-S verify design", harness
+ * lessons (the stream ends in the pending anchor, drafts continue past it).
+ *
+ * Reads tokens[0 .. len) with len = state[0].  For n = ngram_max, ..., 1 the first n whose
+ * last-n suffix occurs earlier wins; among its occurrences the one ending latest (end
+ * position e <= len-2, overlap with the suffix allowed) is used, and
+ *   drafts[i] = tokens[e+1+i]  for e+1+i <= len-1,  else -1,   i = 0 .. K-1.
+ * No match: all K drafts are -1.  Writes state[2] (non-pad drafts) and state[3] (n used).
+ *   tokens    int32 [cap], 4-byte aligned; ids are compared, never range-checked
+ *   cap       capacity of `tokens`; a state with len outside [0, cap] sets bit 0 of
+ *             state[4] and is treated as an empty stream (all pads)
+ *   ngram_max 1 .. SV_MAX_NGRAM (3 in the reference workloads)
+ *   K         1 .. SV_MAX_S-1
+ *   drafts    int32 [K] output
+ */
+int specverify_propose(const int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max,
+                       int32_t K, int32_t* drafts, hipStream_t stream);
+
+/*
+ * specverify_verify - q8b32 head matmul of the verify window with a fused per-row argmax.
+ * Pages: "Riding Apple's pipelined GPU engine", section "Quantization on the GPU delegate"
+ * (linear per-block-32 int8 head with absmax symmetric scales) and section "Why hand-rolled
+ * per-token loops lose" (sample on the GPU, only the sampled ids leave it);
+ * "Stream C - Speculative decoding", sections "C1 - Engine substrate map" and "The delta"
+ * (one verify forward gives logits for every window position; a batched [K, vocab] -> [K]
+ * argmax replaces the full-logits readback); "Spec-decode on GDN hybrids", verify graph
+ * (static S = K+1 window, all-position logits).
+ *
+ *   L[s, v]   = sum_b f32(wscale[v, b]) * sum_{k in block b} f32(wq[v, k]) * f32(hidden[s, k])
+ *   argmax[s] = min { v : L[s, v] = max_v' L[s, v'] }   (largest logit, lowest id on ties)
+ * Products are exact, accumulation is fp32.
+ *   wq        int8 [V][H] row-major (vocab row contiguous), 16-byte aligned
+ *   wscale    fp16 [V][H/32] row-major (block b of row v at v*H/32 + b), 2-byte aligned
+ *   V         1 .. 2^30;   H: multiple of 32, 32 .. 65536
+ *   hidden    fp16 [S][H] row-major, 16-byte aligned;   S: 1 .. SV_MAX_S
+ *   argmax    int32 [S] output
+ *   logits    fp32 [S][V] output, or NULL (the timed path writes no logits)
+ *   workspace device scratch of at least specverify_verify_workspace_bytes(V, H, S) bytes,
+ *             16-byte aligned; its contents need no initialisation and are clobbered
+ * Errors: SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_ALIGN, SV_ERR_WORKSPACE, SV_ERR_DEVICE, SV_ERR_HIP.
+ */
+size_t specverify_verify_workspace_bytes(int32_t V, int32_t H, int32_t S);
+int specverify_verify(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
+                      const uint16_t* hidden, int32_t S, int32_t* argmax, float* logits,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * specverify_accept - greedy longest-prefix acceptance with the fused anchor.
+ * Pages: "Stream C - Speculative decoding", sections "The delta" and "Control-logic proof"
+ * (draft i is accepted iff it equals the greedy id of its position and every earlier draft
+ * was accepted; the first miss emits the correction, all-accept emits the bonus) and
+ * "Implementation status" (fused scheme: the anchor a0 is always correct; a round commits
+ * what was accepted); "Spec-decode on GDN hybrids", hybrid state discipline (the row after
+ * the last accepted token is the next anchor: correction and bonus are one rule).
+ *
+ * argmax[0..K] are the greedy ids of the window [a0, d_1 .. d_K]; drafts[0..K-1] = d_1..d_K.
+ *   j = max { i in [0, K] : drafts[m-1] == argmax[m-1] for all 1 <= m <= i }
+ * Writes tokens[len .. len+j] = d_1 .. d_j, argmax[j] and sets len += 1 + j (state[0]);
+ * records j in state[1], state[5], state[6] and the histogram.  K = 0 appends argmax[0]:
+ * the anchor bootstrap of a fresh stream.
+ * If len + K + 1 > cap the call writes no token and sets bit 0 of state[4] (sticky).
+ *   argmax    int32 [K+1];  drafts int32 [K] (may be NULL when K = 0); -1 = pad
+ *   K         0 .. SV_MAX_S-1;  tokens int32 [cap]
+ */
+int specverify_accept(const int32_t* argmax, const int32_t* drafts, int32_t K, int32_t* tokens,
+                      int32_t cap, int32_t* state, hipStream_t stream);
+
+/*
+ * Weight-bound dense stack in front of the head (all projections q8b32, same layout and
+ * matmul core as specverify_verify).  Page: "Flagship dramatic-speedup plan - the full
+ * stackable tuning set", sections "Baseline byte model" (decode reads every weight byte
+ * once per forward) and "Axis 4" (fused RMSNorm and SwiGLU).  The pages do not fix the
+ * block; the library implements the weightless pre-norm residual MLP block:
+ *
+ * specverify_rmsnorm: y[s, :] = fp16(x[s, :] / sqrt(mean_k x[s, k]^2 + eps)), fp32 math.
+ *   x, y fp16 [S][H] (may alias), S 1 .. SV_MAX_S, H multiple of 32, 16-byte aligned.
+ *
+ * specverify_gateup_silu_q8b32: m[s, n] = fp16(silu(g) * u) with
+ *   g = sum_k x[s, k] Wg[n, k] and u = sum_k x[s, k] Wu[n, k] (fp32), silu(g) = g/(1+e^-g).
+ *   wg, wu int8 [N][Kin]; sg, su fp16 [N][Kin/32]; x fp16 [S][Kin]; m fp16 [S][N].
+ *
+ * specverify_linear_q8b32: y[s, n] = fp16(sum_k x[s, k] W[n, k] + residual[s, n]) with
+ *   residual fp16 [S][N] or NULL (then no add).  y may alias residual, never x.
+ *   w int8 [N][Kin]; scale fp16 [N][Kin/32]; x fp16 [S][Kin]; y fp16 [S][N].
+ *
+ * Both matmuls take S = 1 .. 16 and the alignment rules of specverify_verify (N plays V,
+ * Kin plays H).  Very long Kin splits the hidden axis across workgroups and then needs a
+ * scratch `workspace` of specverify_stack_workspace_bytes(N, Kin, S, gateup) bytes
+ * (16-byte aligned, no initialisation); when that is 0, workspace may be NULL.
+ */
+int specverify_rmsnorm(const uint16_t* x, int32_t S, int32_t H, float eps, uint16_t* y,
+                       hipStream_t stream);
+size_t specverify_stack_workspace_bytes(int32_t N, int32_t Kin, int32_t S, int32_t gateup);
+int specverify_gateup_silu_q8b32(const int8_t* wg, const uint16_t* sg, const int8_t* wu,
+                                 const uint16_t* su, int32_t N, int32_t Kin,
+                                 const uint16_t* x, int32_t S, uint16_t* m,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+int specverify_linear_q8b32(const int8_t* w, const uint16_t* scale, int32_t N, int32_t Kin,
+                            const uint16_t* x, int32_t S, const uint16_t* residual, uint16_t* y,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Launch-shape override of the q8b32 matmuls, for tuning sweeps: waves per workgroup
+ * (4, 8 or 16; 0 = automatic) and an upper bound on workgroups per launch (1 .. 4096;
+ * 0 = automatic).  Process-wide; affects the *_workspace_bytes answers, so query them
+ * after changing it.  Not thread-safe against concurrent calls.
+ */
+void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups);
+
+/* Static description of a status code. */
+const char* specverify_status_string(int status);
+/* Detail of the last failure on this thread ("" if none). */
+const char* specverify_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECVERIFY_H */

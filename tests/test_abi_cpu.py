@@ -1,0 +1,95 @@
+"""The C-ABI library loads, exports every function include/specverify.h declares, and rejects
+bad arguments on the host before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from weight_bound_verify_amd import specverify as sv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "specverify.h")
+
+P = ctypes.c_void_p
+NULL = None
+A16 = P(0x10000)          # aligned fake addresses: never dereferenced on the host
+A2 = P(0x10002)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(specverify_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sv.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(sv.EXPORTS)
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for macro, val in [("SV_MAX_S", sv.SV_MAX_S), ("SV_MAX_NGRAM", sv.SV_MAX_NGRAM), ("SV_BLOCK", sv.SV_BLOCK),
+                       ("SV_STATE_WORDS", sv.STATE_WORDS), ("SV_STATE_LEN", sv.STATE_LEN),
+                       ("SV_STATE_FLAGS", sv.STATE_FLAGS), ("SV_STATE_HIST", sv.STATE_HIST)]:
+        assert re.search(rf"#define {macro} {val}\b", text), macro
+
+
+def test_status_strings(lib):
+    assert lib.specverify_status_string(0) == b"ok"
+    assert lib.specverify_status_string(4) == b"workspace too small"
+    assert lib.specverify_status_string(99) == b"unknown status"
+
+
+def test_verify_argument_errors(lib):
+    ws = sv.load().specverify_verify_workspace_bytes(1000, 256, 9)
+    assert ws > 0
+    call = lib.specverify_verify
+    assert call(NULL, A16, 1000, 256, A16, 9, A16, NULL, A16, ws, NULL) == 1
+    assert call(A16, A16, 1000, 250, A16, 9, A16, NULL, A16, ws, NULL) == 2     # H % 32
+    assert call(A16, A16, 0, 256, A16, 9, A16, NULL, A16, ws, NULL) == 2        # V
+    assert call(A16, A16, 1000, 256, A16, 65, A16, NULL, A16, ws, NULL) == 2    # S > 64
+    assert call(A16, A16, 1000, 256, A16, 0, A16, NULL, A16, ws, NULL) == 2     # S = 0
+    assert call(A2, A16, 1000, 256, A16, 9, A16, NULL, A16, ws, NULL) == 3      # wq alignment
+    assert call(A16, A16, 1000, 256, A2, 9, A16, NULL, A16, ws, NULL) == 3      # hidden alignment
+    assert call(A16, A16, 1000, 256, A16, 9, A16, NULL, A16, ws - 1, NULL) == 4
+    assert b"workspace" in lib.specverify_last_error()
+    assert lib.specverify_verify_workspace_bytes(1000, 250, 9) == 0
+
+
+def test_accept_and_propose_argument_errors(lib):
+    assert lib.specverify_accept(NULL, A16, 8, A16, 100, A16, NULL) == 1
+    assert lib.specverify_accept(A16, NULL, 8, A16, 100, A16, NULL) == 1        # drafts needed for K > 0
+    assert lib.specverify_accept(A16, A16, 64, A16, 100, A16, NULL) == 2
+    assert lib.specverify_accept(A16, A16, -1, A16, 100, A16, NULL) == 2
+    assert lib.specverify_accept(A16, A16, 8, A16, 0, A16, NULL) == 5
+    assert lib.specverify_accept(A2, A16, 8, A16, 100, A16, NULL) == 3
+    assert lib.specverify_propose(A16, 100, A16, 0, 8, A16, NULL) == 2          # ngram order
+    assert lib.specverify_propose(A16, 100, A16, 9, 8, A16, NULL) == 2
+    assert lib.specverify_propose(A16, 100, A16, 3, 0, A16, NULL) == 2          # K
+    assert lib.specverify_propose(NULL, 100, A16, 3, 8, A16, NULL) == 1
+
+
+def test_stack_argument_errors(lib):
+    assert lib.specverify_rmsnorm(A16, 9, 100, ctypes.c_float(1e-6), A16, NULL) == 2
+    assert lib.specverify_rmsnorm(A16, 9, 256, ctypes.c_float(-1.0), A16, NULL) == 2
+    assert lib.specverify_linear_q8b32(A16, A16, 64, 256, A16, 17, NULL, A16, NULL, 0, NULL) == 2  # S <= 16
+    assert lib.specverify_gateup_silu_q8b32(A16, A16, NULL, A16, 64, 256, A16, 9, A16, NULL, 0, NULL) == 1
+    need = lib.specverify_stack_workspace_bytes(64, 65536, 9, 1)
+    assert need > 0                                     # very long inputs split the hidden axis
+    assert lib.specverify_gateup_silu_q8b32(A16, A16, A16, A16, 64, 65536, A16, 9, A16, NULL, 0, NULL) == 4
+
+
+def test_missing_library_raises(monkeypatch, tmp_path):
+    monkeypatch.setattr(sv, "_lib", None)
+    monkeypatch.setattr(sv, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        sv.load()

@@ -1,0 +1,132 @@
+"""GPU parity of specverify_verify (q8b32 head matmul + fused argmax) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from weight_bound_verify_amd import specverify as sv
+from weight_bound_verify_amd import synth
+
+from gpu_util import check_argmax, check_logits, dev, gpu_verify, head, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("V,H,S", [
+    (1, 32, 1), (15, 32, 2), (17, 64, 9), (1000, 256, 9), (1000, 256, 16), (1000, 256, 17),
+    (333, 2048, 33), (100, 96, 64), (8192, 512, 9), (4099, 320, 5), (70000, 64, 3), (777, 5120, 2),
+])
+def test_verify_matches_oracle(V, H, S):
+    say(f"verify V={V} H={H} S={S}")
+    q, s = head(V * 7 + H + S, V, H)
+    hidden = synth.fp16_normal(np.random.default_rng(S), (S, H))
+    a, lg = gpu_verify(q, s, hidden)
+    L = oracle.head_logits(q, s, hidden)
+    worst = check_logits(lg, L)
+    check_argmax(a, L)
+    say(f"  max rel err {worst:.2e}")
+
+
+def test_verify_exact_on_integer_inputs():
+    # unit scales and small integer hidden values: every partial sum is an exact fp32 integer
+    rng = np.random.default_rng(0)
+    V, H, S = 3000, 512, 9
+    q = rng.integers(-127, 128, size=(V, H)).astype(np.int8)
+    s = np.ones((V, H // 32), dtype=np.float16)
+    hidden = rng.integers(-3, 4, size=(S, H)).astype(np.float16)
+    a, lg = gpu_verify(q, s, hidden)
+    L = oracle.head_logits(q, s, hidden)
+    assert np.array_equal(lg, L)
+    assert np.array_equal(a, oracle.argmax_lowest(L))
+
+
+def test_verify_ties_take_lowest_index():
+    rng = np.random.default_rng(1)
+    V, H, S = 2000, 256, 9
+    q, s = head(5, V, H)
+    q[1500] = q[123]          # duplicated rows: exact ties
+    s[1500] = s[123]
+    hidden = synth.fp16_normal(rng, (S, H))
+    hidden[3] = 0             # all-zero row: every logit is 0 -> id 0
+    hidden[0] = np.sign(q[123]).astype(np.float16)     # rows 123 and 1500 tie for the maximum
+    L = oracle.head_logits(q, s, hidden)
+    assert L[0].argmax() == 123 and L[0, 1500] == L[0, 123]
+    a, _ = gpu_verify(q, s, hidden)
+    assert a[0] == 123 and a[3] == 0
+    check_argmax(a, L)
+
+
+def test_verify_without_logits_same_argmax():
+    q, s = head(9, 5000, 1024)
+    hidden = synth.fp16_normal(np.random.default_rng(2), (9, 1024))
+    a1, _ = gpu_verify(q, s, hidden, want_logits=True)
+    a2, _ = gpu_verify(q, s, hidden, want_logits=False)
+    assert np.array_equal(a1, a2)
+
+
+def test_verify_deterministic_and_window_size_invariant():
+    V, H = 20000, 2048
+    q, s = head(11, V, H)
+    hidden = synth.fp16_normal(np.random.default_rng(3), (16, H))
+    wq, ws = to_dev(q), to_dev(s)
+    a16, l16 = gpu_verify(q, s, hidden, wq=wq, ws=ws)
+    a16b, l16b = gpu_verify(q, s, hidden, wq=wq, ws=ws)
+    assert np.array_equal(l16, l16b) and np.array_equal(a16, a16b)
+    for S in (1, 9):
+        aS, lS = gpu_verify(q, s, hidden[:S], wq=wq, ws=ws)
+        assert np.array_equal(lS, l16[:S]), f"S={S} rows differ bitwise from S=16"
+        assert np.array_equal(aS, a16[:S])
+
+
+@pytest.mark.parametrize("nw,grid", [(4, 0), (8, 1), (16, 7), (0, 4096), (8, 300)])
+def test_verify_launch_shapes_agree(nw, grid):
+    V, H, S = 6000, 2560, 9
+    q, s = head(13, V, H)
+    hidden = synth.fp16_normal(np.random.default_rng(4), (S, H))
+    L = oracle.head_logits(q, s, hidden)
+    try:
+        sv.set_tuning(nw, grid)
+        a, lg = gpu_verify(q, s, hidden)
+    finally:
+        sv.set_tuning(0, 0)
+    check_logits(lg, L)
+    check_argmax(a, L)
+
+
+def test_verify_split_hidden_axis_path():
+    # S = 40 (three M tiles of 16) with H = 16384: the hidden axis is split across workgroups
+    V, H, S = 900, 16384, 40
+    assert sv.verify_workspace_bytes(V, H, S) > 8 * S * 4096
+    q, s = head(17, V, H)
+    hidden = synth.fp16_normal(np.random.default_rng(5), (S, H))
+    a, lg = gpu_verify(q, s, hidden)
+    L = oracle.head_logits(q, s, hidden)
+    check_logits(lg, L)
+    check_argmax(a, L)
+
+
+@pytest.mark.parametrize("S", [9, 17])
+def test_verify_full_35b_head_shape(S):
+    V, H = 248320, 2048
+    say(f"full head V={V} H={H} S={S}")
+    st = synth.streams(2)
+    q, s = synth.quantized_head(st.weights, V, H)
+    hidden = synth.fp16_normal(st.hidden, (S, H))
+    a, lg = gpu_verify(q, s, hidden)
+    L = oracle.head_logits(q, s, hidden)
+    check_logits(lg, L)
+    ex = check_argmax(a, L)
+    say(f"  argmax rows exempt by the 1e-3 gap rule: {ex}")
+
+
+def test_verify_full_large_hidden_shape_sampled_rows():
+    # 248320 x 5120 at S = 2; the oracle computes every row (fp64), the argmax is compared exactly
+    V, H, S = 248320, 5120, 2
+    say(f"full head V={V} H={H} S={S}")
+    st = synth.streams(3)
+    q, s = synth.quantized_head(st.weights, V, H)
+    hidden = synth.fp16_normal(st.hidden, (S, H))
+    a, lg = gpu_verify(q, s, hidden)
+    L = oracle.head_logits(q, s, hidden)
+    check_logits(lg, L)
+    check_argmax(a, L)

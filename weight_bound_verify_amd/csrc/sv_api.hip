@@ -1,0 +1,212 @@
+// C ABI of libspecverify: argument validation on the host, then kernel launches on the
+// caller's stream.  Every argument error is reported before the first HIP call.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/specverify.h"
+#include "sv_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(SV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// 0 = unknown, 1 = gfx950, 2 = other.  Devices are queried once.
+std::atomic<int> g_arch[64];
+
+int check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(SV_ERR_DEVICE, "device index %d out of range", dev);
+    int known = g_arch[dev].load(std::memory_order_relaxed);
+    if (known == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+        known = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch[dev].store(known, std::memory_order_relaxed);
+    }
+    if (known != 1) return fail(SV_ERR_DEVICE, "device %d is not gfx950", dev);
+    return SV_OK;
+}
+
+int check_q8b32(const int8_t* w, const uint16_t* s, int32_t rows, int32_t H, const uint16_t* x, int32_t S,
+                int32_t max_s) {
+    if (!w || !s || !x) return fail(SV_ERR_NULL, "weights, scales and activations are required");
+    if (rows < 1 || rows > (1 << 30)) return fail(SV_ERR_SHAPE, "rows=%d outside [1, 2^30]", rows);
+    if (H < SV_BLOCK || H > 65536 || H % SV_BLOCK) return fail(SV_ERR_SHAPE, "H=%d must be a multiple of 32 in [32, 65536]", H);
+    if (S < 1 || S > max_s) return fail(SV_ERR_SHAPE, "S=%d outside [1, %d]", S, max_s);
+    if (!aligned(w, 16)) return fail(SV_ERR_ALIGN, "int8 weights must be 16-byte aligned");
+    if (!aligned(x, 16)) return fail(SV_ERR_ALIGN, "activation rows must be 16-byte aligned");
+    if (!aligned(s, 2)) return fail(SV_ERR_ALIGN, "scales must be 2-byte aligned");
+    return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* specverify_status_string(int status) {
+    switch (status) {
+        case SV_OK: return "ok";
+        case SV_ERR_NULL: return "null pointer";
+        case SV_ERR_SHAPE: return "size out of range";
+        case SV_ERR_ALIGN: return "misaligned pointer";
+        case SV_ERR_WORKSPACE: return "workspace too small";
+        case SV_ERR_CAPACITY: return "token capacity too small";
+        case SV_ERR_HIP: return "HIP error";
+        case SV_ERR_DEVICE: return "device is not gfx950";
+        default: return "unknown status";
+    }
+}
+
+const char* specverify_last_error(void) { return g_last_error; }
+
+void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups) {
+    if (waves_per_group != 0 && waves_per_group != 4 && waves_per_group != 8 && waves_per_group != 16)
+        waves_per_group = 0;
+    if (max_groups < 0 || max_groups > sv::kGridMax) max_groups = 0;
+    sv::set_tuning(waves_per_group, max_groups);
+}
+
+int specverify_propose(const int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max, int32_t K,
+                       int32_t* drafts, hipStream_t stream) {
+    if (!tokens || !state || !drafts) return fail(SV_ERR_NULL, "tokens, state and drafts are required");
+    if (ngram_max < 1 || ngram_max > SV_MAX_NGRAM) return fail(SV_ERR_SHAPE, "ngram_max=%d outside [1, %d]", ngram_max, SV_MAX_NGRAM);
+    if (K < 1 || K > SV_MAX_S - 1) return fail(SV_ERR_SHAPE, "K=%d outside [1, %d]", K, SV_MAX_S - 1);
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(tokens, 4) || !aligned(state, 4) || !aligned(drafts, 4)) return fail(SV_ERR_ALIGN, "int32 buffers must be 4-byte aligned");
+    if (int st = check_device()) return st;
+    hipError_t e = sv::launch_propose(tokens, cap, state, ngram_max, K, drafts, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "propose launch");
+}
+
+size_t specverify_verify_workspace_bytes(int32_t V, int32_t H, int32_t S) {
+    if (V < 1 || V > (1 << 30) || H < SV_BLOCK || H > 65536 || H % SV_BLOCK || S < 1 || S > SV_MAX_S) return 0;
+    return sv::head_workspace_bytes(V, H, S);
+}
+
+int specverify_verify(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
+                      int32_t S, int32_t* argmax, float* logits, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    if (int st = check_q8b32(wq, wscale, V, H, hidden, S, SV_MAX_S)) return st;
+    if (!argmax || !workspace) return fail(SV_ERR_NULL, "argmax and workspace are required");
+    if (!aligned(argmax, 4) || (logits && !aligned(logits, 4)) || !aligned(workspace, 16))
+        return fail(SV_ERR_ALIGN, "argmax/logits 4-byte, workspace 16-byte alignment required");
+    const size_t need = sv::head_workspace_bytes(V, H, S);
+    if (workspace_bytes < need) return fail(SV_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+    if (int st = check_device()) return st;
+
+    const sv::GemmCfg cfg = sv::gemm_config(V, H, S);
+    sv::GemmArgs a{};
+    a.w0 = wq;
+    a.s0 = wscale;
+    a.x = hidden;
+    a.V = V;
+    a.H = H;
+    a.S = S;
+    a.nb = H / SV_BLOCK;
+    a.nitems = (V + 15) / 16;
+    a.ksplit = cfg.ksplit;
+    a.part_val = static_cast<float*>(workspace);
+    a.part_idx = reinterpret_cast<int*>(static_cast<char*>(workspace) + (size_t)4 * S * sv::kGridMax);
+    a.logits = logits;
+    if (cfg.ksplit > 1) a.kpart0 = reinterpret_cast<float*>(static_cast<char*>(workspace) + (size_t)8 * S * sv::kGridMax);
+    hipError_t e = sv::launch_q8b32(sv::EPI_HEAD, cfg, a, stream);
+    if (e != hipSuccess) return hip_fail(e, "verify matmul launch");
+    const int nparts = cfg.ksplit > 1 ? ((V + 255) / 256 < 256 ? (V + 255) / 256 : 256) : cfg.grid;
+    e = sv::launch_argmax_final(a.part_val, a.part_idx, nparts, S, argmax, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "argmax launch");
+}
+
+int specverify_accept(const int32_t* argmax, const int32_t* drafts, int32_t K, int32_t* tokens, int32_t cap,
+                      int32_t* state, hipStream_t stream) {
+    if (!argmax || !tokens || !state || (K > 0 && !drafts)) return fail(SV_ERR_NULL, "argmax, drafts, tokens and state are required");
+    if (K < 0 || K > SV_MAX_S - 1) return fail(SV_ERR_SHAPE, "K=%d outside [0, %d]", K, SV_MAX_S - 1);
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(argmax, 4) || !aligned(tokens, 4) || !aligned(state, 4) || (drafts && !aligned(drafts, 4)))
+        return fail(SV_ERR_ALIGN, "int32 buffers must be 4-byte aligned");
+    if (int st = check_device()) return st;
+    hipError_t e = sv::launch_accept(argmax, drafts, K, tokens, cap, state, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "accept launch");
+}
+
+int specverify_rmsnorm(const uint16_t* x, int32_t S, int32_t H, float eps, uint16_t* y, hipStream_t stream) {
+    if (!x || !y) return fail(SV_ERR_NULL, "x and y are required");
+    if (S < 1 || S > SV_MAX_S || H < SV_BLOCK || H > 65536 || H % SV_BLOCK) return fail(SV_ERR_SHAPE, "S=%d H=%d", S, H);
+    if (!(eps >= 0.0f)) return fail(SV_ERR_SHAPE, "eps must be >= 0");
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(SV_ERR_ALIGN, "x and y must be 16-byte aligned");
+    if (int st = check_device()) return st;
+    hipError_t e = sv::launch_rmsnorm(x, S, H, eps, y, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "rmsnorm launch");
+}
+
+size_t specverify_stack_workspace_bytes(int32_t N, int32_t Kin, int32_t S, int32_t gateup) {
+    if (N < 1 || N > (1 << 30) || Kin < SV_BLOCK || Kin > 65536 || Kin % SV_BLOCK || S < 1 || S > 16) return 0;
+    return sv::stack_workspace_bytes(N, Kin, S, gateup != 0);
+}
+
+int specverify_gateup_silu_q8b32(const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su,
+                                 int32_t N, int32_t Kin, const uint16_t* x, int32_t S, uint16_t* m,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (int st = check_q8b32(wg, sg, N, Kin, x, S, 16)) return st;
+    if (!wu || !su || !m) return fail(SV_ERR_NULL, "up weights, scales and output are required");
+    if (!aligned(wu, 16) || !aligned(su, 2) || !aligned(m, 2)) return fail(SV_ERR_ALIGN, "alignment");
+    const size_t need = sv::stack_workspace_bytes(N, Kin, S, true);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+        return fail(SV_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+    if (int st = check_device()) return st;
+    const sv::GemmCfg cfg = sv::gemm_config(N, Kin, S);
+    sv::GemmArgs a{};
+    a.w0 = wg; a.s0 = sg; a.w1 = wu; a.s1 = su; a.x = x;
+    a.V = N; a.H = Kin; a.S = S; a.nb = Kin / SV_BLOCK; a.nitems = (N + 15) / 16; a.ksplit = cfg.ksplit;
+    a.y = m;
+    if (cfg.ksplit > 1) {
+        a.kpart0 = static_cast<float*>(workspace);
+        a.kpart1 = a.kpart0 + (size_t)cfg.ksplit * S * N;
+    }
+    hipError_t e = sv::launch_q8b32(sv::EPI_GATEUP, cfg, a, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "gate/up launch");
+}
+
+int specverify_linear_q8b32(const int8_t* w, const uint16_t* scale, int32_t N, int32_t Kin, const uint16_t* x,
+                            int32_t S, const uint16_t* residual, uint16_t* y, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    if (int st = check_q8b32(w, scale, N, Kin, x, S, 16)) return st;
+    if (!y) return fail(SV_ERR_NULL, "output is required");
+    if (!aligned(y, 2) || (residual && !aligned(residual, 2))) return fail(SV_ERR_ALIGN, "alignment");
+    const size_t need = sv::stack_workspace_bytes(N, Kin, S, false);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+        return fail(SV_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+    if (int st = check_device()) return st;
+    const sv::GemmCfg cfg = sv::gemm_config(N, Kin, S);
+    sv::GemmArgs a{};
+    a.w0 = w; a.s0 = scale; a.x = x;
+    a.V = N; a.H = Kin; a.S = S; a.nb = Kin / SV_BLOCK; a.nitems = (N + 15) / 16; a.ksplit = cfg.ksplit;
+    a.y = y; a.residual = residual;
+    if (cfg.ksplit > 1) a.kpart0 = static_cast<float*>(workspace);
+    hipError_t e = sv::launch_q8b32(sv::EPI_STORE, cfg, a, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "linear launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Device-side helpers shared by the gfx950 kernels of libspecverify.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 32;       // quantization block length (hidden axis)
+constexpr int kTileRows = 16;    // vocab rows per MFMA tile (N of the 16x16x32 MFMA)
+
+// Four int8 codes packed in a dword -> four exact fp16 values.
+// Each byte is biased to u = q + 128 (xor 0x80), placed under the fp16 exponent of 1024
+// (bit pattern 0x64uu = 1024 + u, exact since the ulp at 1024 is 1), and 1152 = 1024 + 128
+// is subtracted; the result q is an integer in [-128, 127], exact in fp16.
+__device__ __forceinline__ void i8x4_to_f16(uint32_t w, f16x2& lo, f16x2& hi) {
+    const uint32_t u = w ^ 0x80808080u;
+    const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);  // [u0,64,u1,64]
+    const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);  // [u2,64,u3,64]
+    const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    lo = __builtin_bit_cast(f16x2, a) - bias;
+    hi = __builtin_bit_cast(f16x2, b) - bias;
+}
+
+// Eight int8 codes (two dwords, k order preserved) -> f16x8 MFMA operand.
+__device__ __forceinline__ f16x8 i8x8_to_f16x8(u32x2 w) {
+    f16x2 p0, p1, p2, p3;
+    i8x4_to_f16(w.x, p0, p1);
+    i8x4_to_f16(w.y, p2, p3);
+    f16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ uint16_t f2h(float f) {            // round to nearest even
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Argmax order: larger value first, then lower index.  -0.0 == +0.0.
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+// Reduce (value, index) over each aligned group of `width` lanes; every lane of the
+// group ends with the group's best.
+template <int WIDTH>
+__device__ __forceinline__ void argmax_group(float& v, int& i) {
+#pragma unroll
+    for (int off = WIDTH / 2; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(v, off, WIDTH);
+        const int oi = __shfl_xor(i, off, WIDTH);
+        if (better(ov, oi, v, i)) { v = ov; i = oi; }
+    }
+}
+
+}  // namespace sv

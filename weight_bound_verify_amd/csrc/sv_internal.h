@@ -1,0 +1,57 @@
+// Host-side internal interface between the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+enum Epi { EPI_HEAD = 0, EPI_STORE = 1, EPI_GATEUP = 2 };
+
+constexpr int kGridMax = 4096;     // upper bound on workgroups of one q8b32 launch
+
+// Launch shape of one q8b32 matmul, a pure function of (rows, H, S, tuning).
+struct GemmCfg {
+    int mt;       // 16-row M tiles of the window: 1, 2 or 4
+    int nbw;      // hidden blocks held per wave (register budget bucket)
+    int nw;       // waves per workgroup (in-workgroup split of the hidden axis)
+    int ksplit;   // split of the hidden axis across workgroups (>1 only for very long H)
+    int grid;     // workgroups along the row axis
+};
+
+GemmCfg gemm_config(int rows, int H, int S);
+void set_tuning(int waves_per_group, int max_groups);
+
+struct GemmArgs {
+    const int8_t* w0;
+    const uint16_t* s0;
+    const int8_t* w1;          // EPI_GATEUP: up projection
+    const uint16_t* s1;
+    const uint16_t* x;         // [S][H] fp16
+    int V, H, S, nb, nitems, ksplit;
+    float* part_val;           // EPI_HEAD: per-workgroup argmax partials [S][kGridMax]
+    int* part_idx;
+    float* logits;             // EPI_HEAD: [S][V] or null
+    uint16_t* y;               // EPI_STORE / EPI_GATEUP: [S][V] fp16
+    const uint16_t* residual;  // EPI_STORE: [S][V] fp16 or null
+    float* kpart0;             // ksplit > 1: fp32 partial sums [ksplit][S][V]
+    float* kpart1;             // ksplit > 1, EPI_GATEUP: partial sums of the up projection
+};
+
+// Workspace bytes a head matmul of this shape needs.
+size_t head_workspace_bytes(int V, int H, int S);
+// Workspace bytes a store / gate-up matmul needs (non-zero only when ksplit > 1).
+size_t stack_workspace_bytes(int N, int K, int S, bool gateup);
+
+hipError_t launch_q8b32(int epi, const GemmCfg& cfg, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_argmax_final(const float* pv, const int* pi, int nparts, int S, int* argmax,
+                               hipStream_t stream);
+hipError_t launch_propose(const int32_t* tokens, int cap, int32_t* state, int nmax, int K, int32_t* drafts,
+                          hipStream_t stream);
+hipError_t launch_accept(const int32_t* argmax, const int32_t* drafts, int K, int32_t* tokens,
+                         int cap, int32_t* state, hipStream_t stream);
+hipError_t launch_rmsnorm(const uint16_t* x, int S, int H, float eps, uint16_t* y,
+                          hipStream_t stream);
+
+}  // namespace sv

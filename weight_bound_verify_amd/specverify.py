@@ -1,0 +1,174 @@
+"""ctypes binding of libspecverify.so (declared in include/specverify.h).
+
+Argument marshalling only: tensors are checked for device, dtype, contiguity and shape,
+their device pointers and torch's current HIP stream are handed to the C ABI, and a non-OK
+status becomes ``SpecVerifyError``.  Every step of the verify path runs in the library's
+HIP kernels; there is no fallback, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+# mirrors include/specverify.h
+SV_MAX_S = 64
+SV_MAX_NGRAM = 8
+SV_BLOCK = 32
+STATE_WORDS = 80
+STATE_LEN, STATE_J, STATE_NVALID, STATE_NUSED, STATE_FLAGS, STATE_ROUNDS, STATE_SUMJ, STATE_HIST = 0, 1, 2, 3, 4, 5, 6, 8
+FLAG_CAPACITY = 1
+STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_ALIGN", 4: "SV_ERR_WORKSPACE",
+          5: "SV_ERR_CAPACITY", 6: "SV_ERR_HIP", 7: "SV_ERR_DEVICE"}
+
+EXPORTS = (
+    "specverify_propose", "specverify_verify_workspace_bytes", "specverify_verify", "specverify_accept",
+    "specverify_rmsnorm", "specverify_stack_workspace_bytes", "specverify_gateup_silu_q8b32",
+    "specverify_linear_q8b32", "specverify_set_tuning", "specverify_status_string", "specverify_last_error",
+)
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def load():
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with `python -m weight_bound_verify_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "specverify_propose": (_I, [_P, _I, _P, _I, _I, _P, _P]),
+        "specverify_verify_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+        "specverify_verify": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+        "specverify_accept": (_I, [_P, _P, _I, _P, _I, _P, _P]),
+        "specverify_rmsnorm": (_I, [_P, _I, _I, ctypes.c_float, _P, _P]),
+        "specverify_stack_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+        "specverify_gateup_silu_q8b32": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _P, _P, ctypes.c_size_t, _P]),
+        "specverify_linear_q8b32": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+        "specverify_set_tuning": (None, [_I, _I]),
+        "specverify_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "specverify_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        detail = load().specverify_last_error().decode(errors="replace")
+        raise SpecVerifyError(status, detail)
+
+
+def _ptr(t, dtype, name, numel=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def new_state(device="cuda") -> torch.Tensor:
+    return torch.zeros(STATE_WORDS, dtype=torch.int32, device=device)
+
+
+def verify_workspace_bytes(V: int, H: int, S: int) -> int:
+    return int(load().specverify_verify_workspace_bytes(V, H, S))
+
+
+def stack_workspace_bytes(N: int, K: int, S: int, gateup: bool) -> int:
+    return int(load().specverify_stack_workspace_bytes(N, K, S, int(gateup)))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
+
+
+def set_tuning(waves_per_group: int = 0, max_groups: int = 0) -> None:
+    load().specverify_set_tuning(int(waves_per_group), int(max_groups))
+
+
+def propose(tokens, state, drafts, ngram_max: int = 3, stream=None) -> None:
+    """n-gram drafts of ``tokens[:state[0]]`` into ``drafts`` (int32 [K])."""
+    _check(load().specverify_propose(_ptr(tokens, torch.int32, "tokens"), tokens.numel(),
+                                     _ptr(state, torch.int32, "state", STATE_WORDS), int(ngram_max),
+                                     drafts.numel(), _ptr(drafts, torch.int32, "drafts"), _stream(stream)))
+
+
+def verify(wq, wscale, hidden, argmax, ws, logits=None, stream=None) -> None:
+    """argmax[s] of the q8b32 head over ``hidden`` rows; optional fp32 logits [S, V]."""
+    V, H = wq.shape
+    S = hidden.shape[0]
+    if hidden.shape[1] != H or tuple(wscale.shape) != (V, H // SV_BLOCK):
+        raise ValueError("shape mismatch between wq, wscale and hidden")
+    _check(load().specverify_verify(
+        _ptr(wq, torch.int8, "wq"), _ptr(wscale, torch.float16, "wscale"), V, H,
+        _ptr(hidden, torch.float16, "hidden"), S, _ptr(argmax, torch.int32, "argmax", S),
+        _ptr(logits, torch.float32, "logits", S * V), _ptr(ws, torch.uint8, "workspace"), ws.numel(),
+        _stream(stream)))
+
+
+def accept(argmax, drafts, tokens, state, stream=None) -> None:
+    """Commit the accepted drafts and the next anchor; ``argmax`` holds K+1 ids."""
+    K = argmax.numel() - 1
+    _check(load().specverify_accept(_ptr(argmax, torch.int32, "argmax"),
+                                    _ptr(drafts, torch.int32, "drafts", K) if K > 0 else None, K,
+                                    _ptr(tokens, torch.int32, "tokens"), tokens.numel(),
+                                    _ptr(state, torch.int32, "state", STATE_WORDS), _stream(stream)))
+
+
+def rmsnorm(x, y, eps: float = 1e-6, stream=None) -> None:
+    S, H = x.shape
+    _check(load().specverify_rmsnorm(_ptr(x, torch.float16, "x"), S, H, float(eps),
+                                     _ptr(y, torch.float16, "y", S * H), _stream(stream)))
+
+
+def gateup_silu(wg, sg, wu, su, x, m, ws=None, stream=None) -> None:
+    N, K = wg.shape
+    S = x.shape[0]
+    if tuple(wu.shape) != (N, K) or x.shape[1] != K:
+        raise ValueError("shape mismatch")
+    _check(load().specverify_gateup_silu_q8b32(
+        _ptr(wg, torch.int8, "wg"), _ptr(sg, torch.float16, "sg"), _ptr(wu, torch.int8, "wu"),
+        _ptr(su, torch.float16, "su"), N, K, _ptr(x, torch.float16, "x"), S, _ptr(m, torch.float16, "m", S * N),
+        _ptr(ws, torch.uint8, "workspace"), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def linear(w, scale, x, y, residual=None, ws=None, stream=None) -> None:
+    N, K = w.shape
+    S = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("shape mismatch")
+    _check(load().specverify_linear_q8b32(
+        _ptr(w, torch.int8, "w"), _ptr(scale, torch.float16, "scale"), N, K, _ptr(x, torch.float16, "x"), S,
+        _ptr(residual, torch.float16, "residual", S * N), _ptr(y, torch.float16, "y", S * N),
+        _ptr(ws, torch.uint8, "workspace"), 0 if ws is None else ws.numel(), _stream(stream)))
