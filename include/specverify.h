@@ -110,7 +110,7 @@ int specverify_propose(const int32_t* tokens, int32_t cap, int32_t* state, int32
  *   argmax[s] = min { v : L[s, v] = max_v' L[s, v'] }   (largest logit, lowest id on ties)
  * Products are exact, accumulation is fp32.
  *   wq        int8 [V][H] row-major (vocab row contiguous), 16-byte aligned
- *   wscale    fp16 [V][H/32] row-major (block b of row v at v*H/32 + b), 2-byte aligned
+ *   wscale    fp16 [V][H/32] row-major (block b of row v at v*H/32 + b), 16-byte aligned
  *   V         1 .. 2^30;   H: multiple of 32, 32 .. 65536
  *   hidden    fp16 [S][H] row-major, 16-byte aligned;   S: 1 .. SV_MAX_S
  *   argmax    int32 [S] output

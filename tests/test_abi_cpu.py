@@ -60,6 +60,7 @@ def test_verify_argument_errors(lib):
     assert call(A16, A16, 1000, 256, A16, 0, A16, NULL, A16, ws, NULL) == 2     # S = 0
     assert call(A2, A16, 1000, 256, A16, 9, A16, NULL, A16, ws, NULL) == 3      # wq alignment
     assert call(A16, A16, 1000, 256, A2, 9, A16, NULL, A16, ws, NULL) == 3      # hidden alignment
+    assert call(A16, A2, 1000, 256, A16, 9, A16, NULL, A16, ws, NULL) == 3      # scale alignment
     assert call(A16, A16, 1000, 256, A16, 9, A16, NULL, A16, ws - 1, NULL) == 4
     assert b"workspace" in lib.specverify_last_error()
     assert lib.specverify_verify_workspace_bytes(1000, 250, 9) == 0

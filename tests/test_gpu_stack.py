@@ -109,11 +109,13 @@ def test_small_stack_end_to_end_teacher_forced():
     xd = to_dev(x)
     n = torch.empty_like(xd)
     m = torch.empty((S, F), dtype=torch.float16, device=dev())
+    gw = sv.workspace(sv.stack_workspace_bytes(F, H, S, True), dev())
+    dw = sv.workspace(sv.stack_workspace_bytes(H, F, S, False), dev())
     for li, (g, u, d) in enumerate(layers):
         x_in = xd.cpu().numpy()
         sv.rmsnorm(xd, n)
-        sv.gateup_silu(to_dev(g[0]), to_dev(g[1]), to_dev(u[0]), to_dev(u[1]), n, m)
-        sv.linear(to_dev(d[0]), to_dev(d[1]), m, xd, xd)
+        sv.gateup_silu(to_dev(g[0]), to_dev(g[1]), to_dev(u[0]), to_dev(u[1]), n, m, gw)
+        sv.linear(to_dev(d[0]), to_dev(d[1]), m, xd, xd, dw)
         torch.cuda.synchronize()
         # oracle block on the GPU's own layer input
         ref_x, parts = oracle.mlp_block(x_in, (g, u, d), return_parts=True)

@@ -58,7 +58,7 @@ int check_q8b32(const int8_t* w, const uint16_t* s, int32_t rows, int32_t H, con
     if (S < 1 || S > max_s) return fail(SV_ERR_SHAPE, "S=%d outside [1, %d]", S, max_s);
     if (!aligned(w, 16)) return fail(SV_ERR_ALIGN, "int8 weights must be 16-byte aligned");
     if (!aligned(x, 16)) return fail(SV_ERR_ALIGN, "activation rows must be 16-byte aligned");
-    if (!aligned(s, 2)) return fail(SV_ERR_ALIGN, "scales must be 2-byte aligned");
+    if (!aligned(s, 16)) return fail(SV_ERR_ALIGN, "scales must be 16-byte aligned");
     return SV_OK;
 }
 
@@ -117,7 +117,7 @@ int specverify_verify(const int8_t* wq, const uint16_t* wscale, int32_t V, int32
     if (workspace_bytes < need) return fail(SV_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
     if (int st = check_device()) return st;
 
-    const sv::GemmCfg cfg = sv::gemm_config(V, H, S);
+    const sv::GemmCfg cfg = sv::gemm_config(V, H, S, sv::EPI_HEAD);
     sv::GemmArgs a{};
     a.w0 = wq;
     a.s0 = wscale;
@@ -134,7 +134,7 @@ int specverify_verify(const int8_t* wq, const uint16_t* wscale, int32_t V, int32
     if (cfg.ksplit > 1) a.kpart0 = reinterpret_cast<float*>(static_cast<char*>(workspace) + (size_t)8 * S * sv::kGridMax);
     hipError_t e = sv::launch_q8b32(sv::EPI_HEAD, cfg, a, stream);
     if (e != hipSuccess) return hip_fail(e, "verify matmul launch");
-    const int nparts = cfg.ksplit > 1 ? ((V + 255) / 256 < 256 ? (V + 255) / 256 : 256) : cfg.grid;
+    const int nparts = cfg.ksplit > 1 ? sv::combine_groups(V) : cfg.grid;
     e = sv::launch_argmax_final(a.part_val, a.part_idx, nparts, S, argmax, stream);
     return e == hipSuccess ? SV_OK : hip_fail(e, "argmax launch");
 }
@@ -171,12 +171,12 @@ int specverify_gateup_silu_q8b32(const int8_t* wg, const uint16_t* sg, const int
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (int st = check_q8b32(wg, sg, N, Kin, x, S, 16)) return st;
     if (!wu || !su || !m) return fail(SV_ERR_NULL, "up weights, scales and output are required");
-    if (!aligned(wu, 16) || !aligned(su, 2) || !aligned(m, 2)) return fail(SV_ERR_ALIGN, "alignment");
+    if (!aligned(wu, 16) || !aligned(su, 16) || !aligned(m, 2)) return fail(SV_ERR_ALIGN, "alignment");
     const size_t need = sv::stack_workspace_bytes(N, Kin, S, true);
     if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
         return fail(SV_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
     if (int st = check_device()) return st;
-    const sv::GemmCfg cfg = sv::gemm_config(N, Kin, S);
+    const sv::GemmCfg cfg = sv::gemm_config(N, Kin, S, sv::EPI_GATEUP);
     sv::GemmArgs a{};
     a.w0 = wg; a.s0 = sg; a.w1 = wu; a.s1 = su; a.x = x;
     a.V = N; a.H = Kin; a.S = S; a.nb = Kin / SV_BLOCK; a.nitems = (N + 15) / 16; a.ksplit = cfg.ksplit;
@@ -199,7 +199,7 @@ int specverify_linear_q8b32(const int8_t* w, const uint16_t* scale, int32_t N, i
     if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
         return fail(SV_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
     if (int st = check_device()) return st;
-    const sv::GemmCfg cfg = sv::gemm_config(N, Kin, S);
+    const sv::GemmCfg cfg = sv::gemm_config(N, Kin, S, sv::EPI_STORE);
     sv::GemmArgs a{};
     a.w0 = w; a.s0 = scale; a.x = x;
     a.V = N; a.H = Kin; a.S = S; a.nb = Kin / SV_BLOCK; a.nitems = (N + 15) / 16; a.ksplit = cfg.ksplit;

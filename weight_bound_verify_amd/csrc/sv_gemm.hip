@@ -15,10 +15,21 @@
 //                         block scale of that weight row multiplies all four in fp32:
 //                         acc += scale * D.  The sum over one block is exact (integer codes
 //                         times fp16 values); only the cross-block accumulation rounds.
-// A workgroup owns 16 weight rows at a time; its NW waves split the hidden axis, each
-// holding its share of the window rows in registers, and reduce through LDS in a fixed
+// A workgroup owns 16 weight rows at a time ("item"); its NW waves split the hidden axis,
+// each holding its share of the window rows in registers, and reduce through LDS in a fixed
 // order (deterministic).  The head epilogue keeps a running (value, lowest index) argmax
-// per window row; only 8 bytes per (row, workgroup) leave the kernel.
+// per window row; only 8 bytes per (window row, workgroup) leave the kernel.  The next
+// item's loads are issued before the current item's math (two alternating register sets).
+//
+// Two kernels share this structure:
+//   q8b32_fast     each load instruction reads 8 rows x 128 contiguous bytes (the access
+//                  pattern that streams HBM near its peak; 16 rows x 8 bytes per
+//                  instruction, the MFMA operand layout, streams at about half of it).  Each
+//                  wave exchanges the bytes into the MFMA layout through two 2 KB LDS slots
+//                  of its own, XOR-swizzled by row so both the 16-byte writes and the 8-byte
+//                  reads are free of bank conflicts.  Every wave's share of the hidden axis
+//                  must be a whole number of 128-byte segments.
+//   q8b32_generic  any shape: each lane loads its 8 MFMA bytes directly.
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -32,26 +43,17 @@ namespace {
 int g_nw_override = 0;       // 0 = choose
 int g_grid_override = 0;     // 0 = choose
 
-template <int MT, int NBW, int NW, int EPI>
-__global__ __launch_bounds__(NW * 64) void q8b32_kernel(GemmArgs a) {
-    constexpr int NACC = (EPI == EPI_GATEUP) ? 2 : 1;
-    __shared__ f32x4 red[2][NW][NACC * MT][kWave];
+// Workgroup barrier that orders LDS only, so prefetched global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int n = lane & 15;       // weight row within the tile / window row within A
-    const int g = lane >> 4;       // 8-code group within the block
-
-    // hidden-axis range of this workgroup (ksplit) and of this wave
-    const int ks = blockIdx.y;
-    const int kb0 = (int)((long long)a.nb * ks / a.ksplit);
-    const int kb1 = (int)((long long)a.nb * (ks + 1) / a.ksplit);
-    const int nbk = kb1 - kb0;
-    const int bw0 = kb0 + (int)((long long)nbk * wave / NW);
-    const int nbw = kb0 + (int)((long long)nbk * (wave + 1) / NW) - bw0;
-
-    // window rows for this wave's blocks, kept in registers
-    f16x8 hid[NBW][MT];
+// Window rows for blocks [bw0, bw0 + nbw) in this lane's A-operand slots.
+template <int MT, int NBW>
+__device__ __forceinline__ void load_hidden(f16x8 (&hid)[NBW][MT], const GemmArgs& a, int bw0, int nbw, int n,
+                                            int g) {
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
 #pragma unroll
@@ -63,131 +65,305 @@ __global__ __launch_bounds__(NW * 64) void q8b32_kernel(GemmArgs a) {
             hid[i][mt] = h;
         }
     }
+}
 
+// Cross-wave reduction of one item through LDS, then the epilogue in wave 0.
+template <int MT, int NW, int EPI, int NACC>
+struct Reducer {
+    f32x4 (*red)[NW][NACC * MT][kWave];
     float best_v[MT][4];
     int best_i[MT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) { best_v[mt][r] = -INFINITY; best_i[mt][r] = INT_MAX; }
 
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    int buf = 0;
-    for (int it = blockIdx.x; it < a.nitems; it += gridDim.x) {
-        const int row0 = it * kTileRows;
-        const int row = min(row0 + n, a.V - 1);        // tail rows re-read the last row; masked below
-
-        u32x2 wv[NACC][NBW];
-        uint16_t sv[NACC][NBW];
-        {
-            const int8_t* wp = a.w0 + (size_t)row * a.H + (size_t)bw0 * kBlock + g * 8;
-            const uint16_t* sp = a.s0 + (size_t)row * a.nb + bw0;
+    __device__ __forceinline__ void init() {
 #pragma unroll
-            for (int i = 0; i < NBW; ++i)
-                if (i < nbw) {
-                    wv[0][i] = *reinterpret_cast<const u32x2*>(wp + i * kBlock);
-                    sv[0][i] = sp[i];
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) { best_v[mt][r] = -INFINITY; best_i[mt][r] = INT_MAX; }
+    }
+
+    __device__ __forceinline__ void run(const GemmArgs& a, const f32x4 (&acc)[NACC][MT], int it, int buf, int wave,
+                                        int lane, int ks) {
+#pragma unroll
+        for (int c = 0; c < NACC; ++c)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) red[buf][wave][c * MT + mt][lane] = acc[c][mt];
+        lds_barrier();
+        if (wave != 0) return;
+
+        f32x4 tot[NACC][MT];
+#pragma unroll
+        for (int c = 0; c < NACC; ++c)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                f32x4 t = red[buf][0][c * MT + mt][lane];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) t += red[buf][w][c * MT + mt][lane];
+                tot[c][mt] = t;
+            }
+        const int n = lane & 15, g = lane >> 4;
+        const int v = it * kTileRows + n;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = mt * 16 + g * 4 + r;
+                if (s < a.S && v < a.V) {
+                    const size_t o = (size_t)s * a.V + v;
+                    if (a.ksplit > 1) {
+                        const size_t po = (size_t)ks * a.S * a.V + o;
+                        a.kpart0[po] = tot[0][mt][r];
+                        if constexpr (NACC == 2) a.kpart1[po] = tot[NACC - 1][mt][r];
+                    } else if constexpr (EPI == EPI_HEAD) {
+                        const float val = tot[0][mt][r];
+                        if (a.logits) a.logits[o] = val;
+                        if (val > best_v[mt][r]) { best_v[mt][r] = val; best_i[mt][r] = v; }
+                    } else if constexpr (EPI == EPI_STORE) {
+                        float val = tot[0][mt][r];
+                        if (a.residual) val += h2f(a.residual[o]);
+                        a.y[o] = f2h(val);
+                    } else {
+                        const float gg = tot[0][mt][r];
+                        const float uu = tot[NACC - 1][mt][r];
+                        a.y[o] = f2h(gg / (1.0f + expf(-gg)) * uu);
+                    }
                 }
-        }
-        if constexpr (NACC == 2) {
-            const int8_t* wp = a.w1 + (size_t)row * a.H + (size_t)bw0 * kBlock + g * 8;
-            const uint16_t* sp = a.s1 + (size_t)row * a.nb + bw0;
-#pragma unroll
-            for (int i = 0; i < NBW; ++i)
-                if (i < nbw) {
-                    wv[NACC - 1][i] = *reinterpret_cast<const u32x2*>(wp + i * kBlock);
-                    sv[NACC - 1][i] = sp[i];
-                }
-        }
+            }
+    }
 
+    // Per-workgroup argmax partials of the head (wave 0).
+    __device__ __forceinline__ void finish(const GemmArgs& a, int lane) {
+        const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float bv = best_v[mt][r];
+                int bi = best_i[mt][r];
+                argmax_group<16>(bv, bi);
+                const int s = mt * 16 + g * 4 + r;
+                if (n == 0 && s < a.S) {
+                    a.part_val[(size_t)s * kGridMax + blockIdx.x] = bv;
+                    a.part_idx[(size_t)s * kGridMax + blockIdx.x] = bi;
+                }
+            }
+    }
+};
+
+// ------------------------------------------------------------------------------------------
+// fast kernel
+// ------------------------------------------------------------------------------------------
+template <int NBW, int NACC>
+struct FastRegs {
+    static constexpr int NSEG = NBW / 4;          // 128-byte segments per row per wave
+    u32x4 w[NACC][NSEG][2];                        // [matrix][segment][row half]
+    uint32_t sc[NACC][NBW / 2];                    // fp16 scales of the lane's row, in pairs
+};
+
+template <int MT, int NBW, int NW, int EPI>
+__global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
+    constexpr int NACC = (EPI == EPI_GATEUP) ? 2 : 1;
+    constexpr int NSEG = NBW / 4;
+    static_assert(NBW % 4 == 0, "whole 128-byte segments");
+    __shared__ f32x4 red[2][NW][NACC * MT][kWave];
+    __shared__ __attribute__((aligned(16))) uint8_t xch[NW][NACC][2][2048];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15, g = lane >> 4;
+    const int ks = blockIdx.y;
+    const int bw0 = (a.nb / a.ksplit) * ks + NBW * wave;     // every wave owns exactly NBW blocks
+
+    f16x8 hid[NBW][MT];
+    load_hidden<MT, NBW>(hid, a, bw0, NBW, n, g);
+
+    Reducer<MT, NW, EPI, NACC> red_{red};
+    red_.init();
+
+    // loads: row half h covers rows 8h .. 8h+7; lane l reads row 8h + l/8, bytes
+    // 16*(l%8) .. +15 of each 128-byte segment of the wave's range
+    const int lrow = lane >> 3, lchunk = lane & 7;
+    auto load = [&](FastRegs<NBW, NACC>& r, int item) {
+#pragma unroll
+        for (int m = 0; m < NACC; ++m) {
+            const int8_t* w = m == 0 ? a.w0 : a.w1;
+            const uint16_t* s = m == 0 ? a.s0 : a.s1;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int row = min(item * kTileRows + 8 * h + lrow, a.V - 1);   // tail rows: masked later
+                const int8_t* p = w + (size_t)row * a.H + (size_t)bw0 * kBlock + 16 * lchunk;
+#pragma unroll
+                for (int t = 0; t < NSEG; ++t)
+                    r.w[m][t][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 128 * t));
+            }
+            const int srow = min(item * kTileRows + n, a.V - 1);
+            const uint16_t* sp = s + (size_t)srow * a.nb + bw0;
+            if constexpr (NBW % 8 == 0) {
+#pragma unroll
+                for (int v = 0; v < NBW / 8; ++v) {
+                    const u32x4 q = *reinterpret_cast<const u32x4*>(sp + 8 * v);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) r.sc[m][4 * v + e] = q[e];
+                }
+            } else {
+                const u32x2 q = *reinterpret_cast<const u32x2*>(sp);
+                r.sc[m][0] = q.x;
+                r.sc[m][1] = q.y;
+            }
+        }
+    };
+
+    auto process = [&](const FastRegs<NBW, NACC>& cur, int it, int buf) {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         f32x4 acc[NACC][MT];
 #pragma unroll
         for (int c = 0; c < NACC; ++c)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[c][mt] = zero;
+#pragma unroll
+        for (int t = 0; t < NSEG; ++t) {
+            // exchange one segment: row r lands at r*128, 16-byte chunks XOR-swizzled by row
+#pragma unroll
+            for (int m = 0; m < NACC; ++m)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = 8 * h + lrow;
+                    *reinterpret_cast<u32x4*>(&xch[wave][m][t & 1][row * 128 + 16 * (lchunk ^ (row & 7))]) =
+                        cur.w[m][t][h];
+                }
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const int i = 4 * t + bb;
+                const int chunk = 2 * bb + (g >> 1);
+                const int off = n * 128 + 16 * (chunk ^ (n & 7)) + 8 * (g & 1);
+#pragma unroll
+                for (int c = 0; c < NACC; ++c) {
+                    const u32x2 q8 = *reinterpret_cast<const u32x2*>(&xch[wave][c][t & 1][off]);
+                    const f16x8 b = i8x8_to_f16x8(q8);
+                    const float sc = h2f((uint16_t)(cur.sc[c][i >> 1] >> (16 * (i & 1))));
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(hid[i][mt], b, zero, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[c][mt][r] = __builtin_fmaf(sc, d[r], acc[c][mt][r]);
+                    }
+                }
+            }
+        }
+        red_.run(a, acc, it, buf, wave, lane, ks);
+    };
 
+    const int step = gridDim.x;
+    const int last = a.nitems - 1;
+    FastRegs<NBW, NACC> ra, rb;
+    int it = blockIdx.x;
+    load(ra, it);
+    while (true) {
+        if (it >= a.nitems) break;
+        load(rb, min(it + step, last));
+        process(ra, it, 0);
+        it += step;
+        if (it >= a.nitems) break;
+        load(ra, min(it + step, last));
+        process(rb, it, 1);
+        it += step;
+    }
+    if constexpr (EPI == EPI_HEAD)
+        if (a.ksplit == 1 && wave == 0) red_.finish(a, lane);
+}
+
+// ------------------------------------------------------------------------------------------
+// generic kernel (any H; per-wave block counts may differ by one)
+// ------------------------------------------------------------------------------------------
+template <int NBW>
+struct GenRegs {
+    u32x2 w[NBW];
+    uint16_t sc[NBW];
+};
+
+// Branch-free loads: blocks past the wave's share re-read its last block (cache hit) and
+// are never used.
+template <int NBW>
+__device__ __forceinline__ void load_generic(GenRegs<NBW>& r, const int8_t* __restrict__ w,
+                                             const uint16_t* __restrict__ sc, int row, int H, int nb, int bw0,
+                                             int nbw, int g) {
+    const int8_t* wp = w + (size_t)row * H + (size_t)bw0 * kBlock + g * 8;
+    const uint16_t* sp = sc + (size_t)row * nb + bw0;
+    const int last = nbw > 0 ? nbw - 1 : 0;
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+        const int b = i < last ? i : last;
+        r.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wp + b * kBlock));
+        r.sc[i] = sp[b];
+    }
+}
+
+template <int MT, int NBW, int NW, int EPI>
+__global__ __launch_bounds__(NW * 64) void q8b32_generic(GemmArgs a) {
+    constexpr int NACC = (EPI == EPI_GATEUP) ? 2 : 1;
+    __shared__ f32x4 red[2][NW][NACC * MT][kWave];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15, g = lane >> 4;
+    const int ks = blockIdx.y;
+    const int kb0 = (int)((long long)a.nb * ks / a.ksplit);
+    const int nbk = (int)((long long)a.nb * (ks + 1) / a.ksplit) - kb0;
+    const int bw0 = kb0 + (int)((long long)nbk * wave / NW);
+    const int nbw = kb0 + (int)((long long)nbk * (wave + 1) / NW) - bw0;
+
+    f16x8 hid[NBW][MT];
+    load_hidden<MT, NBW>(hid, a, bw0, nbw, n, g);
+    Reducer<MT, NW, EPI, NACC> red_{red};
+    red_.init();
+
+    auto load = [&](GenRegs<NBW> (&r)[NACC], int item) {
+        const int row = min(item * kTileRows + n, a.V - 1);     // tail rows re-read the last row; masked
+        load_generic<NBW>(r[0], a.w0, a.s0, row, a.H, a.nb, bw0, nbw, g);
+        if constexpr (NACC == 2) load_generic<NBW>(r[NACC - 1], a.w1, a.s1, row, a.H, a.nb, bw0, nbw, g);
+    };
+    auto process = [&](const GenRegs<NBW> (&cur)[NACC], int it, int buf) {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[NACC][MT];
+#pragma unroll
+        for (int c = 0; c < NACC; ++c)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[c][mt] = zero;
 #pragma unroll
         for (int i = 0; i < NBW; ++i) {
             if (i < nbw) {
 #pragma unroll
                 for (int c = 0; c < NACC; ++c) {
-                    const f16x8 b = i8x8_to_f16x8(wv[c][i]);
-                    const float sc = h2f(sv[c][i]);
+                    const f16x8 b = i8x8_to_f16x8(cur[c].w[i]);
+                    const float sc = h2f(cur[c].sc[i]);
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
-                        const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(hid[i][mt], b, zero, 0, 0, 0);
+                        const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(hid[i][mt], b, zero, 0, 0, 0);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[c][mt][r] = __builtin_fmaf(sc, t[r], acc[c][mt][r]);
+                        for (int r = 0; r < 4; ++r) acc[c][mt][r] = __builtin_fmaf(sc, d[r], acc[c][mt][r]);
                     }
                 }
             }
         }
+        red_.run(a, acc, it, buf, wave, lane, ks);
+    };
 
-#pragma unroll
-        for (int c = 0; c < NACC; ++c)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) red[buf][wave][c * MT + mt][lane] = acc[c][mt];
-        __syncthreads();
-
-        if (wave == 0) {
-            f32x4 tot[NACC][MT];
-#pragma unroll
-            for (int c = 0; c < NACC; ++c)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    f32x4 t = red[buf][0][c * MT + mt][lane];
-#pragma unroll
-                    for (int w = 1; w < NW; ++w) t += red[buf][w][c * MT + mt][lane];
-                    tot[c][mt] = t;
-                }
-            const int v = row0 + n;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int s = mt * 16 + g * 4 + r;
-                    if (s < a.S && v < a.V) {
-                        const size_t o = (size_t)s * a.V + v;
-                        if (a.ksplit > 1) {
-                            const size_t po = (size_t)ks * a.S * a.V + o;
-                            a.kpart0[po] = tot[0][mt][r];
-                            if constexpr (NACC == 2) a.kpart1[po] = tot[NACC - 1][mt][r];
-                        } else if constexpr (EPI == EPI_HEAD) {
-                            const float val = tot[0][mt][r];
-                            if (a.logits) a.logits[o] = val;
-                            if (val > best_v[mt][r]) { best_v[mt][r] = val; best_i[mt][r] = v; }
-                        } else if constexpr (EPI == EPI_STORE) {
-                            float val = tot[0][mt][r];
-                            if (a.residual) val += h2f(a.residual[o]);
-                            a.y[o] = f2h(val);
-                        } else {
-                            const float gg = tot[0][mt][r];
-                            const float uu = tot[NACC - 1][mt][r];
-                            a.y[o] = f2h(gg / (1.0f + expf(-gg)) * uu);
-                        }
-                    }
-                }
-        }
-        buf ^= 1;
+    const int step = gridDim.x;
+    const int last = a.nitems - 1;
+    GenRegs<NBW> ra[NACC], rb[NACC];
+    int it = blockIdx.x;
+    load(ra, it);
+    while (true) {
+        if (it >= a.nitems) break;
+        load(rb, min(it + step, last));
+        process(ra, it, 0);
+        it += step;
+        if (it >= a.nitems) break;
+        load(ra, min(it + step, last));
+        process(rb, it, 1);
+        it += step;
     }
-
-    if constexpr (EPI == EPI_HEAD) {
-        if (a.ksplit == 1 && wave == 0) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float bv = best_v[mt][r];
-                    int bi = best_i[mt][r];
-                    argmax_group<16>(bv, bi);
-                    const int s = mt * 16 + g * 4 + r;
-                    if (n == 0 && s < a.S) {
-                        a.part_val[(size_t)s * kGridMax + blockIdx.x] = bv;
-                        a.part_idx[(size_t)s * kGridMax + blockIdx.x] = bi;
-                    }
-                }
-        }
-    }
+    if constexpr (EPI == EPI_HEAD)
+        if (a.ksplit == 1 && wave == 0) red_.finish(a, lane);
 }
 
 // ksplit > 1: sum the partial sums in split order, then apply the epilogue.
@@ -250,23 +426,49 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const float* pv, cons
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// shape tables (every instantiation compiles without register spills on gfx950)
+// ------------------------------------------------------------------------------------------
 typedef void (*KernelFn)(GemmArgs);
+struct Shape { int mt, nbw, nw, epis; };
+constexpr int kH = 1 << EPI_HEAD, kS = 1 << EPI_STORE, kG = 1 << EPI_GATEUP;
 
-// Instantiated (MT, NBW, NW) shapes: all compile without register spills on gfx950
-// (1024-thread workgroups are limited to 128 VGPRs, so NW = 16 only with small NBW).
-struct Shape { int mt, nbw, nw; };
-constexpr Shape kShapes[] = {
-    {1, 4, 4}, {1, 8, 4}, {1, 16, 4}, {1, 4, 8}, {1, 8, 8}, {1, 16, 8}, {1, 4, 16}, {1, 8, 16},
-    {2, 4, 4}, {2, 8, 4}, {2, 4, 8}, {2, 8, 8},
-    {4, 2, 4}, {4, 4, 4}, {4, 2, 8},
+// fast kernel: every wave owns exactly nbw blocks (a multiple of 4); listed in order of
+// preference within each MT; epis = the epilogues that compile for it without spills
+// within the LDS limit
+constexpr Shape kFast[] = {
+    {1, 4, 16, kH | kS}, {1, 16, 5, kH | kS | kG}, {1, 8, 8, kH | kS | kG}, {1, 8, 10, kH | kS | kG},
+    {1, 16, 8, kH | kS | kG}, {1, 8, 16, kH | kS}, {1, 16, 4, kH | kS | kG}, {1, 8, 4, kH | kS | kG},
+    {1, 4, 4, kH | kS | kG}, {1, 8, 2, kH | kS | kG},
+    {2, 8, 8, kH}, {2, 8, 4, kH}, {2, 4, 4, kH},
+    {4, 4, 4, kH},
+};
+// generic kernel
+constexpr Shape kGeneric[] = {
+    {1, 4, 4, kH | kS | kG}, {1, 8, 4, kH | kS | kG}, {1, 16, 4, kH | kS | kG}, {1, 4, 8, kH | kS | kG},
+    {1, 8, 8, kH | kS | kG}, {1, 16, 8, kH | kS}, {1, 4, 16, kH | kS | kG}, {1, 8, 16, kH | kS},
+    {2, 4, 4, kH}, {2, 8, 4, kH}, {2, 4, 8, kH}, {2, 8, 8, kH},
+    {4, 2, 4, kH}, {4, 4, 4, kH}, {4, 2, 8, kH},
 };
 
 template <int EPI>
-KernelFn pick(const GemmCfg& c) {
+KernelFn pick_fast(const GemmCfg& c) {
 #define SV_SHAPE(MT, NBW, NW) \
-    if (c.mt == MT && c.nbw == NBW && c.nw == NW) return q8b32_kernel<MT, NBW, NW, EPI>;
-    SV_SHAPE(1, 4, 4) SV_SHAPE(1, 8, 4) SV_SHAPE(1, 16, 4) SV_SHAPE(1, 4, 8) SV_SHAPE(1, 8, 8)
-    SV_SHAPE(1, 16, 8) SV_SHAPE(1, 4, 16) SV_SHAPE(1, 8, 16)
+    if (c.mt == MT && c.nbw == NBW && c.nw == NW) return q8b32_fast<MT, NBW, NW, EPI>;
+    SV_SHAPE(1, 8, 8) SV_SHAPE(1, 8, 10) SV_SHAPE(1, 16, 8) SV_SHAPE(1, 16, 5) SV_SHAPE(1, 16, 4)
+    SV_SHAPE(1, 8, 4) SV_SHAPE(1, 4, 4) SV_SHAPE(1, 8, 2)
+    if constexpr (EPI != EPI_GATEUP) { SV_SHAPE(1, 8, 16) SV_SHAPE(1, 4, 16) }
+    if constexpr (EPI == EPI_HEAD) { SV_SHAPE(2, 8, 8) SV_SHAPE(2, 8, 4) SV_SHAPE(2, 4, 4) SV_SHAPE(4, 4, 4) }
+#undef SV_SHAPE
+    return nullptr;
+}
+
+template <int EPI>
+KernelFn pick_generic(const GemmCfg& c) {
+#define SV_SHAPE(MT, NBW, NW) \
+    if (c.mt == MT && c.nbw == NBW && c.nw == NW) return q8b32_generic<MT, NBW, NW, EPI>;
+    SV_SHAPE(1, 4, 4) SV_SHAPE(1, 8, 4) SV_SHAPE(1, 16, 4) SV_SHAPE(1, 4, 8) SV_SHAPE(1, 8, 8) SV_SHAPE(1, 4, 16)
+    if constexpr (EPI != EPI_GATEUP) { SV_SHAPE(1, 16, 8) SV_SHAPE(1, 8, 16) }
     if constexpr (EPI == EPI_HEAD) {
         SV_SHAPE(2, 4, 4) SV_SHAPE(2, 8, 4) SV_SHAPE(2, 4, 8) SV_SHAPE(2, 8, 8)
         SV_SHAPE(4, 2, 4) SV_SHAPE(4, 4, 4) SV_SHAPE(4, 2, 8)
@@ -275,41 +477,38 @@ KernelFn pick(const GemmCfg& c) {
     return nullptr;
 }
 
-// Smallest instantiated NBW >= need for (mt, nw); 0 if none.
-int bucket(int need, int mt, int nw) {
-    int best = 0;
-    for (const Shape& sh : kShapes)
-        if (sh.mt == mt && sh.nw == nw && sh.nbw >= need && (best == 0 || sh.nbw < best)) best = sh.nbw;
-    return best;
+// Fast shape: the hidden axis splits into ks equal parts, each into nw waves of exactly
+// nbw blocks.
+bool try_fast(int nb, int mt, int epi, GemmCfg& c) {
+    for (int ks = 1; ks <= 4; ++ks) {
+        if (nb % ks) continue;
+        const int nbk = nb / ks;
+        for (const Shape& sh : kFast) {
+            if (sh.mt != mt || !(sh.epis & (1 << epi))) continue;
+            if (g_nw_override && sh.nw != g_nw_override) continue;
+            if (sh.nbw * sh.nw == nbk) {
+                c.mt = mt; c.nbw = sh.nbw; c.nw = sh.nw; c.ksplit = ks; c.fast = 1;
+                return true;
+            }
+        }
+    }
+    return false;
 }
 
-}  // namespace
-
-void set_tuning(int waves_per_group, int max_groups) {
-    g_nw_override = waves_per_group;
-    g_grid_override = max_groups;
-}
-
-namespace {
-
-bool try_config(int rows, int H, int S, int nw_fixed, GemmCfg& c) {
-    c.mt = S <= 16 ? 1 : (S <= 32 ? 2 : 4);
-    const int nb = H / kBlock;
+bool try_generic(int nb, int mt, int epi, int nw_fixed, GemmCfg& c) {
     const int pref[3] = {8, 16, 4};
     for (int ks = 1; ks <= nb; ++ks) {
         const int nbk = (nb + ks - 1) / ks;
         for (int t = 0; t < 3; ++t) {
             const int nw = nw_fixed ? nw_fixed : (nb < 32 ? 4 : pref[t]);
-            const int b = bucket((nbk + nw - 1) / nw, c.mt, nw);
-            if (b) {
-                c.nw = nw;
-                c.nbw = b;
-                c.ksplit = ks;
-                const int items = (rows + kTileRows - 1) / kTileRows;
-                const int cap = g_grid_override ? g_grid_override : 1024;
-                c.grid = items < cap ? items : cap;
-                if (c.grid > kGridMax) c.grid = kGridMax;
-                if (c.grid < 1) c.grid = 1;
+            const int need = (nbk + nw - 1) / nw;
+            int best = 0;
+            for (const Shape& sh : kGeneric)
+                if (sh.mt == mt && (sh.epis & (1 << epi)) && sh.nw == nw && sh.nbw >= need &&
+                    (best == 0 || sh.nbw < best))
+                    best = sh.nbw;
+            if (best) {
+                c.mt = mt; c.nbw = best; c.nw = nw; c.ksplit = ks; c.fast = 0;
                 return true;
             }
             if (nw_fixed || nb < 32) break;
@@ -320,36 +519,64 @@ bool try_config(int rows, int H, int S, int nw_fixed, GemmCfg& c) {
 
 }  // namespace
 
-GemmCfg gemm_config(int rows, int H, int S) {
+void set_tuning(int waves_per_group, int max_groups) {
+    g_nw_override = waves_per_group;
+    g_grid_override = max_groups;
+}
+
+GemmCfg gemm_config(int rows, int H, int S, int epi) {
     GemmCfg c{};
-    if (g_nw_override && try_config(rows, H, S, g_nw_override, c)) return c;
-    try_config(rows, H, S, 0, c);       // always succeeds: (mt, smallest nbw, 4 waves) exists
+    const int mt = S <= 16 ? 1 : (S <= 32 ? 2 : 4);
+    const int nb = H / kBlock;
+    // fewest workgroup splits of the hidden axis first (a split costs a combine pass), then
+    // the fast loads
+    GemmCfg f{}, gen{};
+    const bool have_fast = try_fast(nb, mt, epi, f);
+    if (!(g_nw_override && try_generic(nb, mt, epi, g_nw_override, gen)))
+        try_generic(nb, mt, epi, 0, gen);     // always succeeds: (mt, smallest nbw, 4 waves) exists
+    c = (have_fast && f.ksplit <= gen.ksplit) ? f : gen;
+    // measured on MI355X: 16-wave groups stream best one per CU, smaller groups two per CU
+    const int items = (rows + kTileRows - 1) / kTileRows;
+    int cap = g_grid_override ? g_grid_override : (c.nw >= 16 ? 256 : 512);
+    if (cap > kGridMax) cap = kGridMax;
+    c.grid = items < cap ? (items > 0 ? items : 1) : cap;
     return c;
 }
 
+int combine_groups(int V) {
+    const int g = (V + 255) / 256;
+    return g < 256 ? g : 256;
+}
+
 size_t head_workspace_bytes(int V, int H, int S) {
-    const GemmCfg c = gemm_config(V, H, S);
+    const GemmCfg c = gemm_config(V, H, S, EPI_HEAD);
     size_t b = (size_t)8 * S * kGridMax;
     if (c.ksplit > 1) b += (size_t)4 * c.ksplit * S * V;
     return b;
 }
 
 size_t stack_workspace_bytes(int N, int K, int S, bool gateup) {
-    const GemmCfg c = gemm_config(N, K, S);
+    const GemmCfg c = gemm_config(N, K, S, gateup ? EPI_GATEUP : EPI_STORE);
     if (c.ksplit == 1) return 0;
     return (size_t)4 * c.ksplit * S * N * (gateup ? 2 : 1);
 }
 
 hipError_t launch_q8b32(int epi, const GemmCfg& cfg, const GemmArgs& a, hipStream_t stream) {
     KernelFn fn = nullptr;
-    if (epi == EPI_HEAD) fn = pick<EPI_HEAD>(cfg);
-    else if (epi == EPI_STORE) fn = pick<EPI_STORE>(cfg);
-    else fn = pick<EPI_GATEUP>(cfg);
+    if (cfg.fast) {
+        if (epi == EPI_HEAD) fn = pick_fast<EPI_HEAD>(cfg);
+        else if (epi == EPI_STORE) fn = pick_fast<EPI_STORE>(cfg);
+        else fn = pick_fast<EPI_GATEUP>(cfg);
+    } else {
+        if (epi == EPI_HEAD) fn = pick_generic<EPI_HEAD>(cfg);
+        else if (epi == EPI_STORE) fn = pick_generic<EPI_STORE>(cfg);
+        else fn = pick_generic<EPI_GATEUP>(cfg);
+    }
     if (!fn) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(fn, dim3(cfg.grid, cfg.ksplit), dim3(cfg.nw * 64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || cfg.ksplit == 1) return e;
-    const int cg = (a.V + 255) / 256 < 256 ? (a.V + 255) / 256 : 256;
+    const int cg = combine_groups(a.V);
     if (epi == EPI_HEAD)
         hipLaunchKernelGGL(combine_kernel<EPI_HEAD>, dim3(cg, a.S), dim3(256), 0, stream, a);
     else if (epi == EPI_STORE)

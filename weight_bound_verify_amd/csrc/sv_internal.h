@@ -18,9 +18,13 @@ struct GemmCfg {
     int nw;       // waves per workgroup (in-workgroup split of the hidden axis)
     int ksplit;   // split of the hidden axis across workgroups (>1 only for very long H)
     int grid;     // workgroups along the row axis
+    int fast;     // 1: 128-byte-segment loads with an LDS exchange; 0: generic loads
 };
 
-GemmCfg gemm_config(int rows, int H, int S);
+// epi = the epilogue kind (Epi); the stack epilogues take S <= 16.
+GemmCfg gemm_config(int rows, int H, int S, int epi);
+// Workgroups of the split-combine pass (also the number of argmax partials it writes).
+int combine_groups(int V);
 void set_tuning(int waves_per_group, int max_groups);
 
 struct GemmArgs {

@@ -153,6 +153,7 @@ def rmsnorm(x, y, eps: float = 1e-6, stream=None) -> None:
 
 
 def gateup_silu(wg, sg, wu, su, x, m, ws=None, stream=None) -> None:
+    """m = fp16(silu(x Wg^T) * (x Wu^T)); ``ws`` is needed when stack_workspace_bytes(...) > 0."""
     N, K = wg.shape
     S = x.shape[0]
     if tuple(wu.shape) != (N, K) or x.shape[1] != K:
@@ -164,6 +165,7 @@ def gateup_silu(wg, sg, wu, su, x, m, ws=None, stream=None) -> None:
 
 
 def linear(w, scale, x, y, residual=None, ws=None, stream=None) -> None:
+    """y = fp16(x W^T [+ residual]); ``ws`` is needed when stack_workspace_bytes(...) > 0."""
     N, K = w.shape
     S = x.shape[0]
     if x.shape[1] != K:
