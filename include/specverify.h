@@ -116,13 +116,33 @@ int specverify_propose(const int32_t* tokens, int32_t cap, int32_t* state, int32
  *   argmax    int32 [S] output
  *   logits    fp32 [S][V] output, or NULL (the timed path writes no logits)
  *   workspace device scratch of at least specverify_verify_workspace_bytes(V, H, S) bytes,
- *             16-byte aligned; its contents need no initialisation and are clobbered
+ *             16-byte aligned; its contents need no initialisation and are clobbered, so
+ *             calls that share a workspace must be ordered (one stream)
  * Errors: SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_ALIGN, SV_ERR_WORKSPACE, SV_ERR_DEVICE, SV_ERR_HIP.
  */
 size_t specverify_verify_workspace_bytes(int32_t V, int32_t H, int32_t S);
 int specverify_verify(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
                       const uint16_t* hidden, int32_t S, int32_t* argmax, float* logits,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * specverify_round - one whole verify round in as few launches as the shape allows:
+ *   specverify_verify(hidden, S = K+1) -> specverify_accept(argmax, drafts_in)
+ *   -> specverify_propose(next drafts into drafts_out)
+ * with the same results as the three calls in that order, in two launches: the matmul, then
+ * one workgroup that reduces the argmax, accepts and drafts from LDS ("Riding Apple's
+ * pipelined GPU engine", section "Why hand-rolled per-token loops lose": per-step
+ * dispatches and host round trips are what a pipelined engine removes).
+ *   hidden     fp16 [K+1][H], the rows of the window [a0, d_1 .. d_K]
+ *   drafts_in  int32 [K] drafts being verified; drafts_out int32 [K] the next round's drafts
+ *              (may alias drafts_in: the accept reads them before the drafter writes)
+ *   other arguments as for specverify_verify / _accept / _propose; K in 1 .. SV_MAX_S-1.
+ */
+int specverify_round(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
+                     const uint16_t* hidden, int32_t K, const int32_t* drafts_in, int32_t* tokens,
+                     int32_t cap, int32_t* state, int32_t ngram_max, int32_t* drafts_out,
+                     int32_t* argmax, float* logits, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
 
 /*
  * specverify_accept - greedy longest-prefix acceptance with the fused anchor.

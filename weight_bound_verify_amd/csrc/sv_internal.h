@@ -43,14 +43,21 @@ struct GemmArgs {
     float* kpart1;             // ksplit > 1, EPI_GATEUP: partial sums of the up projection
 };
 
+// Head workspace layout: per-workgroup argmax partials [S][kGridMax] (values, then indices),
+// then the split sums when the hidden axis is split across workgroups.
+constexpr size_t head_partials_bytes(int S) { return (size_t)8 * S * kGridMax; }
+
 // Workspace bytes a head matmul of this shape needs.
 size_t head_workspace_bytes(int V, int H, int S);
 // Workspace bytes a store / gate-up matmul needs (non-zero only when ksplit > 1).
 size_t stack_workspace_bytes(int N, int K, int S, bool gateup);
 
 hipError_t launch_q8b32(int epi, const GemmCfg& cfg, const GemmArgs& a, hipStream_t stream);
-hipError_t launch_argmax_final(const float* pv, const int* pi, int nparts, int S, int* argmax,
-                               hipStream_t stream);
+// Argmax stage 2 of a head launch and, when drafts_out != null, the rest of the round
+// (accept, then the next drafts): one workgroup.
+hipError_t launch_round_tail(const float* pv, const int* pi, int nparts, int S, int32_t* argmax,
+                             const int32_t* drafts_in, int32_t* tokens, int cap, int32_t* state, int nmax,
+                             int32_t* drafts_out, hipStream_t stream);
 hipError_t launch_propose(const int32_t* tokens, int cap, int32_t* state, int nmax, int K, int32_t* drafts,
                           hipStream_t stream);
 hipError_t launch_accept(const int32_t* argmax, const int32_t* drafts, int K, int32_t* tokens,

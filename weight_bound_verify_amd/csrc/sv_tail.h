@@ -1,0 +1,188 @@
+// Round-tail device functions shared by the standalone accept / propose kernels and by the
+// last workgroup of a fused round (argmax -> accept -> next drafts in one launch).
+#pragma once
+
+#include "sv_device.h"
+#include "../../include/specverify.h"
+
+namespace sv {
+
+constexpr int kHalo = SV_MAX_NGRAM;   // ids before an LDS chunk that a match may reach back to
+
+// Copy src[0 .. n) to LDS dst[0 .. n) with the whole workgroup, several 16-byte loads in
+// flight per thread (a strided one-id-per-iteration loop would wait on every load).  Ids
+// src[i] with i outside [0, n) are never read.  `src` must be 16-byte aligned for the
+// vector part; otherwise single ids are copied.
+__device__ __forceinline__ void stage_ids(const int32_t* __restrict__ src, int n, int32_t* dst) {
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    const int tid = threadIdx.x, nt = blockDim.x;
+    int done = 0;
+    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+        const int n4 = n >> 2;
+        const i32x4* s4 = reinterpret_cast<const i32x4*>(src);
+        i32x4* d4 = reinterpret_cast<i32x4*>(dst);
+        constexpr int U = 4;
+        for (int base = 0; base < n4; base += nt * U) {
+            i32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = base + u * nt + tid;
+                if (i < n4) v[u] = s4[i];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = base + u * nt + tid;
+                if (i < n4) d4[i] = v[u];
+            }
+        }
+        done = n4 << 2;
+    }
+    for (int i = done + tid; i < n; i += nt) dst[i] = src[i];
+}
+
+// Greedy accept by one wave ("Stream C - Speculative decoding", the delta and control-logic
+// proof; "Spec-decode on GDN hybrids", hybrid state discipline): lane i compares d_{i+1}
+// with the greedy id of window row i, a ballot finds the first miss j, the accepted drafts
+// and argmax[j] (correction or bonus) are appended and len advances by 1 + j.  A call that
+// could overflow `cap` writes no token and sets the sticky capacity flag.
+__device__ __forceinline__ void accept_wave(const int32_t* argmax, const int32_t* drafts, int K, int32_t* tokens,
+                                            int cap, int32_t* state, int lane) {
+    const int len = state[SV_STATE_LEN];
+    if (len + K + 1 > cap || len < 0) {
+        if (lane == 0) state[SV_STATE_FLAGS] |= SV_FLAG_CAPACITY;
+        return;
+    }
+    int d = -1, a = -2;
+    if (lane < K) { d = drafts[lane]; a = argmax[lane]; }
+    const unsigned long long hit = __ballot(lane < K && d >= 0 && d == a);
+    const int j = __builtin_ctzll(~hit);                 // <= K: bit K is never set
+    if (lane < j) tokens[len + lane] = d;
+    if (lane == j) tokens[len + j] = argmax[j];
+    if (lane == 0) {
+        state[SV_STATE_LEN] = len + 1 + j;
+        state[SV_STATE_J] = j;
+        state[SV_STATE_ROUNDS] += 1;
+        state[SV_STATE_SUMJ] += j;
+        state[SV_STATE_HIST + j] += 1;
+    }
+}
+
+// n-gram prompt lookup by a whole workgroup ("Stream C - Speculative decoding", the delta:
+// the last m ids of the stream index their most recent continuation; "Spec-decode on GDN
+// hybrids", harness lessons: the stream ends in the pending anchor, so drafts continue past
+// it).  For every end position e <= len-2 a thread computes the match length l(e) of the
+// stream's suffix ending at e (capped at nmax).  "First n from nmax down with a match, latest
+// occurrence" is the lexicographic maximum of (l(e), e): one 64-bit max-reduction.  The
+// stream is staged through LDS (`tk`, chunk + kHalo ids) so the scan reads HBM once.
+// `wbest` holds one slot per wave.  Every thread of the workgroup must call it.
+__device__ __forceinline__ void propose_block(const int32_t* tokens, int cap, int32_t* state, int nmax, int K,
+                                              int32_t* drafts, int32_t* tk, int chunk,
+                                              unsigned long long* wbest) {
+    const int tid = threadIdx.x;
+    const int nthreads = blockDim.x;
+    int len = state[SV_STATE_LEN];
+    if (len < 0 || len > cap) {              // corrupt state: never read past the buffer
+        if (tid == 0) state[SV_STATE_FLAGS] |= SV_FLAG_CAPACITY;
+        len = 0;
+    }
+
+    int32_t suf[SV_MAX_NGRAM];
+#pragma unroll
+    for (int i = 0; i < SV_MAX_NGRAM; ++i) suf[i] = (i < nmax && len - 1 - i >= 0) ? tokens[len - 1 - i] : -1;
+
+    unsigned long long best = 0;
+    for (int base = 0; base < len - 1; base += chunk) {
+        __syncthreads();
+        // tk[t] holds stream id base - kHalo + t; ids before the stream start are never compared
+        const int lo = base - kHalo < 0 ? 0 : base - kHalo;
+        const int hi = base + chunk < len ? base + chunk : len;
+        stage_ids(tokens + lo, hi - lo, tk + (lo - (base - kHalo)));
+        __syncthreads();
+        const int end = min(base + chunk, len - 1);     // e in [base, end)
+        for (int e = base + tid; e < end; e += nthreads) {
+            int l = 0;
+#pragma unroll
+            for (int i = 0; i < SV_MAX_NGRAM; ++i) {
+                if (l == i && i < nmax && e - i >= 0 && tk[e - i - base + kHalo] == suf[i]) l = i + 1;
+            }
+            if (l > 0) {
+                const unsigned long long key = ((unsigned long long)l << 32) | (unsigned)e;
+                best = key > best ? key : best;
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const unsigned long long o = __shfl_xor(best, off, 64);
+        best = o > best ? o : best;
+    }
+    if ((tid & 63) == 0) wbest[tid >> 6] = best;
+    __syncthreads();
+    if (tid < kWave) {
+        unsigned long long b = tid < nthreads / kWave ? wbest[tid] : 0ull;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const unsigned long long o = __shfl_xor(b, off, 64);
+            b = o > b ? o : b;
+        }
+        const int nused = (int)(b >> 32);
+        const int e = (int)(b & 0xffffffffu);
+        if (tid < K) {
+            const int p = e + 1 + tid;
+            drafts[tid] = (nused > 0 && p <= len - 1) ? tokens[p] : -1;
+        }
+        if (tid == 0) {
+            state[SV_STATE_NVALID] = nused > 0 ? min(K, len - 1 - e) : 0;
+            state[SV_STATE_NUSED] = nused;
+        }
+    }
+}
+
+// Drafter over a stream held whole in LDS (`tk[0 .. len)`): the same rule as propose_block,
+// with no global reads.  Every thread of the workgroup must call it.
+__device__ __forceinline__ void propose_lds(const int32_t* tk, int len, int nmax, int K, int32_t* drafts,
+                                            int32_t* state, unsigned long long* wbest) {
+    const int tid = threadIdx.x;
+    const int nthreads = blockDim.x;
+    int32_t suf[SV_MAX_NGRAM];
+#pragma unroll
+    for (int i = 0; i < SV_MAX_NGRAM; ++i) suf[i] = (i < nmax && len - 1 - i >= 0) ? tk[len - 1 - i] : -1;
+    unsigned long long best = 0;
+    for (int e = tid; e < len - 1; e += nthreads) {
+        int l = 0;
+#pragma unroll
+        for (int i = 0; i < SV_MAX_NGRAM; ++i)
+            if (l == i && i < nmax && e - i >= 0 && tk[e - i] == suf[i]) l = i + 1;
+        if (l > 0) {
+            const unsigned long long key = ((unsigned long long)l << 32) | (unsigned)e;
+            best = key > best ? key : best;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const unsigned long long o = __shfl_xor(best, off, 64);
+        best = o > best ? o : best;
+    }
+    if ((tid & 63) == 0) wbest[tid >> 6] = best;
+    __syncthreads();
+    if (tid < kWave) {
+        unsigned long long b = tid < nthreads / kWave ? wbest[tid] : 0ull;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const unsigned long long o = __shfl_xor(b, off, 64);
+            b = o > b ? o : b;
+        }
+        const int nused = (int)(b >> 32);
+        const int e = (int)(b & 0xffffffffu);
+        if (tid < K) {
+            const int p = e + 1 + tid;
+            drafts[tid] = (nused > 0 && p <= len - 1) ? tk[p] : -1;
+        }
+        if (tid == 0) {
+            state[SV_STATE_NVALID] = nused > 0 ? min(K, len - 1 - e) : 0;
+            state[SV_STATE_NUSED] = nused;
+        }
+    }
+}
+
+}  // namespace sv

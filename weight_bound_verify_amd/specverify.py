@@ -26,7 +26,8 @@ STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_ALIGN", 4:
           5: "SV_ERR_CAPACITY", 6: "SV_ERR_HIP", 7: "SV_ERR_DEVICE"}
 
 EXPORTS = (
-    "specverify_propose", "specverify_verify_workspace_bytes", "specverify_verify", "specverify_accept",
+    "specverify_propose", "specverify_verify_workspace_bytes", "specverify_verify", "specverify_round",
+    "specverify_accept",
     "specverify_rmsnorm", "specverify_stack_workspace_bytes", "specverify_gateup_silu_q8b32",
     "specverify_linear_q8b32", "specverify_set_tuning", "specverify_status_string", "specverify_last_error",
 )
@@ -54,6 +55,7 @@ def load():
         "specverify_propose": (_I, [_P, _I, _P, _I, _I, _P, _P]),
         "specverify_verify_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
         "specverify_verify": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+        "specverify_round": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
         "specverify_accept": (_I, [_P, _P, _I, _P, _I, _P, _P]),
         "specverify_rmsnorm": (_I, [_P, _I, _I, ctypes.c_float, _P, _P]),
         "specverify_stack_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
@@ -110,6 +112,7 @@ def stack_workspace_bytes(N: int, K: int, S: int, gateup: bool) -> int:
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """Device scratch of at least ``nbytes`` (no initialisation needed)."""
     return torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
 
 
@@ -133,6 +136,23 @@ def verify(wq, wscale, hidden, argmax, ws, logits=None, stream=None) -> None:
     _check(load().specverify_verify(
         _ptr(wq, torch.int8, "wq"), _ptr(wscale, torch.float16, "wscale"), V, H,
         _ptr(hidden, torch.float16, "hidden"), S, _ptr(argmax, torch.int32, "argmax", S),
+        _ptr(logits, torch.float32, "logits", S * V), _ptr(ws, torch.uint8, "workspace"), ws.numel(),
+        _stream(stream)))
+
+
+def round(wq, wscale, hidden, drafts_in, tokens, state, drafts_out, argmax, ws, ngram_max: int = 3, logits=None,
+          stream=None) -> None:
+    """verify(hidden) -> accept(argmax, drafts_in) -> propose(next drafts into drafts_out), fused."""
+    V, H = wq.shape
+    S = hidden.shape[0]
+    K = S - 1
+    if hidden.shape[1] != H or tuple(wscale.shape) != (V, H // SV_BLOCK) or drafts_in.numel() < K:
+        raise ValueError("shape mismatch")
+    _check(load().specverify_round(
+        _ptr(wq, torch.int8, "wq"), _ptr(wscale, torch.float16, "wscale"), V, H,
+        _ptr(hidden, torch.float16, "hidden"), K, _ptr(drafts_in, torch.int32, "drafts_in", K),
+        _ptr(tokens, torch.int32, "tokens"), tokens.numel(), _ptr(state, torch.int32, "state", STATE_WORDS),
+        int(ngram_max), _ptr(drafts_out, torch.int32, "drafts_out", K), _ptr(argmax, torch.int32, "argmax", S),
         _ptr(logits, torch.float32, "logits", S * V), _ptr(ws, torch.uint8, "workspace"), ws.numel(),
         _stream(stream)))
 
