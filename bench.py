@@ -153,8 +153,8 @@ def cpu_baseline(wl, inp, seconds_budget=20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=0, help="weight copies to rotate (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -217,7 +217,7 @@ int specverify_gateup_silu_q8b32(const int8_t* wg, const uint16_t* sg, const int
     const sv::GemmCfg cfg = sv::gemm_config(N, Kin, S, sv::EPI_GATEUP);
     sv::GemmArgs a{};
     a.w0 = wg; a.s0 = sg; a.w1 = wu; a.s1 = su; a.x = x;
-    a.V = N; a.H = Kin; a.S = S; a.nb = Kin / SV_BLOCK; a.nitems = (N + 15) / 16; a.ksplit = cfg.ksplit;
+    a.V = N; a.H = Kin; a.S = S; a.nb = Kin / SV_BLOCK; a.nitems = (N + 7) / 8; a.ksplit = cfg.ksplit;
     a.y = m;
     if (cfg.ksplit > 1) {
         a.kpart0 = static_cast<float*>(workspace);

@@ -68,10 +68,21 @@ __device__ __forceinline__ void load_hidden(f16x8 (&hid)[NBW][MT], const GemmArg
     }
 }
 
+// Weight row feeding MFMA tile row n (0..15) of item `it`.  Head and plain projections: 16
+// rows of one matrix.  Gate/up: tile rows 0..7 are 8 rows of the gate matrix and 8..15 the
+// same 8 rows of the up matrix, so one tile yields both operands of silu(g) * u and the two
+// 8-row halves of a tile map onto the two 8-row load instructions of the fast kernel.
+template <int EPI>
+__device__ __forceinline__ int tile_row(int it, int n) {
+    return EPI == EPI_GATEUP ? it * 8 + (n & 7) : it * kTileRows + n;
+}
+template <int EPI>
+__device__ __forceinline__ bool tile_up(int n) { return EPI == EPI_GATEUP && n >= 8; }
+
 // Cross-wave reduction of one item through LDS, then the epilogue in wave 0.
-template <int MT, int NW, int EPI, int NACC>
+template <int MT, int NW, int EPI>
 struct Reducer {
-    f32x4 (*red)[NW][NACC * MT][kWave];
+    f32x4 (*red)[NW][MT][kWave];
     float best_v[MT][4];
     int best_i[MT][4];
 
@@ -82,27 +93,44 @@ struct Reducer {
             for (int r = 0; r < 4; ++r) { best_v[mt][r] = -INFINITY; best_i[mt][r] = INT_MAX; }
     }
 
-    __device__ __forceinline__ void run(const GemmArgs& a, const f32x4 (&acc)[NACC][MT], int it, int buf, int wave,
-                                        int lane, int ks) {
+    __device__ __forceinline__ void run(const GemmArgs& a, const f32x4 (&acc)[MT], int it, int buf, int wave, int lane,
+                                        int ks) {
 #pragma unroll
-        for (int c = 0; c < NACC; ++c)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) red[buf][wave][c * MT + mt][lane] = acc[c][mt];
+        for (int mt = 0; mt < MT; ++mt) red[buf][wave][mt][lane] = acc[mt];
         lds_barrier();
         if (wave != 0) return;
 
-        f32x4 tot[NACC][MT];
+        f32x4 tot[MT];
 #pragma unroll
-        for (int c = 0; c < NACC; ++c)
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x4 t = red[buf][0][mt][lane];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                f32x4 t = red[buf][0][c * MT + mt][lane];
-#pragma unroll
-                for (int w = 1; w < NW; ++w) t += red[buf][w][c * MT + mt][lane];
-                tot[c][mt] = t;
-            }
+            for (int w = 1; w < NW; ++w) t += red[buf][w][mt][lane];
+            tot[mt] = t;
+        }
         const int n = lane & 15, g = lane >> 4;
-        const int v = it * kTileRows + n;
+        const int v = tile_row<EPI>(it, n);
+        if constexpr (EPI == EPI_GATEUP) {
+            // lanes n < 8 hold the gate sums, lanes n + 8 the up sums of the same output rows
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float other = __shfl_xor(tot[mt][r], 8, 16);
+                    const int s = mt * 16 + g * 4 + r;
+                    if (s < a.S && v < a.V) {
+                        const size_t o = (size_t)s * a.V + v;
+                        if (a.ksplit > 1) {
+                            float* part = n < 8 ? a.kpart0 : a.kpart1;
+                            part[(size_t)ks * a.S * a.V + o] = tot[mt][r];
+                        } else if (n < 8) {
+                            const float gg = tot[mt][r];
+                            a.y[o] = f2h(gg / (1.0f + expf(-gg)) * other);
+                        }
+                    }
+                }
+            return;
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -111,21 +139,15 @@ struct Reducer {
                 if (s < a.S && v < a.V) {
                     const size_t o = (size_t)s * a.V + v;
                     if (a.ksplit > 1) {
-                        const size_t po = (size_t)ks * a.S * a.V + o;
-                        a.kpart0[po] = tot[0][mt][r];
-                        if constexpr (NACC == 2) a.kpart1[po] = tot[NACC - 1][mt][r];
+                        a.kpart0[(size_t)ks * a.S * a.V + o] = tot[mt][r];
                     } else if constexpr (EPI == EPI_HEAD) {
-                        const float val = tot[0][mt][r];
+                        const float val = tot[mt][r];
                         if (a.logits) a.logits[o] = val;
                         if (val > best_v[mt][r]) { best_v[mt][r] = val; best_i[mt][r] = v; }
-                    } else if constexpr (EPI == EPI_STORE) {
-                        float val = tot[0][mt][r];
+                    } else {
+                        float val = tot[mt][r];
                         if (a.residual) val += h2f(a.residual[o]);
                         a.y[o] = f2h(val);
-                    } else {
-                        const float gg = tot[0][mt][r];
-                        const float uu = tot[NACC - 1][mt][r];
-                        a.y[o] = f2h(gg / (1.0f + expf(-gg)) * uu);
                     }
                 }
             }
@@ -153,20 +175,19 @@ struct Reducer {
 // ------------------------------------------------------------------------------------------
 // fast kernel
 // ------------------------------------------------------------------------------------------
-template <int NBW, int NACC>
+template <int NBW>
 struct FastRegs {
     static constexpr int NSEG = NBW / 4;          // 128-byte segments per row per wave
-    u32x4 w[NACC][NSEG][2];                        // [matrix][segment][row half]
-    uint32_t sc[NACC][NBW / 2];                    // fp16 scales of the lane's row, in pairs
+    u32x4 w[NSEG][2];                              // [segment][row half]
+    uint32_t sc[NBW / 2];                          // fp16 scales of the lane's row, in pairs
 };
 
 template <int MT, int NBW, int NW, int EPI>
 __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
-    constexpr int NACC = (EPI == EPI_GATEUP) ? 2 : 1;
     constexpr int NSEG = NBW / 4;
     static_assert(NBW % 4 == 0, "whole 128-byte segments");
-    __shared__ f32x4 red[2][NW][NACC * MT][kWave];
-    __shared__ __attribute__((aligned(16))) uint8_t xch[NW][NACC][2][2048];
+    __shared__ f32x4 red[2][NW][MT][kWave];
+    __shared__ __attribute__((aligned(16))) uint8_t xch[NW][2][2048];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -177,76 +198,68 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
     f16x8 hid[NBW][MT];
     load_hidden<MT, NBW>(hid, a, bw0, NBW, n, g);
 
-    Reducer<MT, NW, EPI, NACC> red_{red};
+    Reducer<MT, NW, EPI> red_{red};
     red_.init();
 
-    // loads: row half h covers rows 8h .. 8h+7; lane l reads row 8h + l/8, bytes
+    // loads: row half h feeds tile rows 8h .. 8h+7; lane l reads the tile row 8h + l/8, bytes
     // 16*(l%8) .. +15 of each 128-byte segment of the wave's range
     const int lrow = lane >> 3, lchunk = lane & 7;
-    auto load = [&](FastRegs<NBW, NACC>& r, int item) {
+    auto load = [&](FastRegs<NBW>& r, int item) {
 #pragma unroll
-        for (int m = 0; m < NACC; ++m) {
-            const int8_t* w = m == 0 ? a.w0 : a.w1;
-            const uint16_t* s = m == 0 ? a.s0 : a.s1;
+        for (int h = 0; h < 2; ++h) {
+            const int8_t* w = tile_up<EPI>(8 * h) ? a.w1 : a.w0;
+            const int row = min(tile_row<EPI>(item, 8 * h + lrow), a.V - 1);      // tail rows: masked later
+            const int8_t* p = w + (size_t)row * a.H + (size_t)bw0 * kBlock + 16 * lchunk;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int row = min(item * kTileRows + 8 * h + lrow, a.V - 1);   // tail rows: masked later
-                const int8_t* p = w + (size_t)row * a.H + (size_t)bw0 * kBlock + 16 * lchunk;
+            for (int t = 0; t < NSEG; ++t)
+                r.w[t][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 128 * t));
+        }
+        const uint16_t* s = tile_up<EPI>(n) ? a.s1 : a.s0;
+        const int srow = min(tile_row<EPI>(item, n), a.V - 1);
+        const uint16_t* sp = s + (size_t)srow * a.nb + bw0;
+        if constexpr (NBW % 8 == 0) {
 #pragma unroll
-                for (int t = 0; t < NSEG; ++t)
-                    r.w[m][t][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 128 * t));
+            for (int v = 0; v < NBW / 8; ++v) {
+                const u32x4 q = *reinterpret_cast<const u32x4*>(sp + 8 * v);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r.sc[4 * v + e] = q[e];
             }
-            const int srow = min(item * kTileRows + n, a.V - 1);
-            const uint16_t* sp = s + (size_t)srow * a.nb + bw0;
-            if constexpr (NBW % 8 == 0) {
+        } else {
 #pragma unroll
-                for (int v = 0; v < NBW / 8; ++v) {
-                    const u32x4 q = *reinterpret_cast<const u32x4*>(sp + 8 * v);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) r.sc[m][4 * v + e] = q[e];
-                }
-            } else {
-                const u32x2 q = *reinterpret_cast<const u32x2*>(sp);
-                r.sc[m][0] = q.x;
-                r.sc[m][1] = q.y;
+            for (int v = 0; v < NBW / 4; ++v) {
+                const u32x2 q = *reinterpret_cast<const u32x2*>(sp + 4 * v);
+                r.sc[2 * v] = q.x;
+                r.sc[2 * v + 1] = q.y;
             }
         }
     };
 
-    auto process = [&](const FastRegs<NBW, NACC>& cur, int it, int buf) {
+    auto process = [&](const FastRegs<NBW>& cur, int it, int buf) {
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        f32x4 acc[NACC][MT];
+        f32x4 acc[MT];
 #pragma unroll
-        for (int c = 0; c < NACC; ++c)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[c][mt] = zero;
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = zero;
 #pragma unroll
         for (int t = 0; t < NSEG; ++t) {
-            // exchange one segment: row r lands at r*128, 16-byte chunks XOR-swizzled by row
+            // exchange one segment: tile row r lands at r*128, 16-byte chunks XOR-swizzled by row
 #pragma unroll
-            for (int m = 0; m < NACC; ++m)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int row = 8 * h + lrow;
-                    *reinterpret_cast<u32x4*>(&xch[wave][m][t & 1][row * 128 + 16 * (lchunk ^ (row & 7))]) =
-                        cur.w[m][t][h];
-                }
+            for (int h = 0; h < 2; ++h) {
+                const int row = 8 * h + lrow;
+                *reinterpret_cast<u32x4*>(&xch[wave][t & 1][row * 128 + 16 * (lchunk ^ (row & 7))]) = cur.w[t][h];
+            }
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
                 const int i = 4 * t + bb;
                 const int chunk = 2 * bb + (g >> 1);
                 const int off = n * 128 + 16 * (chunk ^ (n & 7)) + 8 * (g & 1);
+                const u32x2 q8 = *reinterpret_cast<const u32x2*>(&xch[wave][t & 1][off]);
+                const f16x8 b = i8x8_to_f16x8(q8);
+                const float sc = h2f((uint16_t)(cur.sc[i >> 1] >> (16 * (i & 1))));
 #pragma unroll
-                for (int c = 0; c < NACC; ++c) {
-                    const u32x2 q8 = *reinterpret_cast<const u32x2*>(&xch[wave][c][t & 1][off]);
-                    const f16x8 b = i8x8_to_f16x8(q8);
-                    const float sc = h2f((uint16_t)(cur.sc[c][i >> 1] >> (16 * (i & 1))));
+                for (int mt = 0; mt < MT; ++mt) {
+                    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(hid[i][mt], b, zero, 0, 0, 0);
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(hid[i][mt], b, zero, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[c][mt][r] = __builtin_fmaf(sc, d[r], acc[c][mt][r]);
-                    }
+                    for (int r = 0; r < 4; ++r) acc[mt][r] = __builtin_fmaf(sc, d[r], acc[mt][r]);
                 }
             }
         }
@@ -255,7 +268,7 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
 
     const int step = gridDim.x;
     const int last = a.nitems - 1;
-    FastRegs<NBW, NACC> ra, rb;
+    FastRegs<NBW> ra, rb;
     int it = blockIdx.x;
     load(ra, it);
     while (true) {
@@ -300,8 +313,7 @@ __device__ __forceinline__ void load_generic(GenRegs<NBW>& r, const int8_t* __re
 
 template <int MT, int NBW, int NW, int EPI>
 __global__ __launch_bounds__(NW * 64) void q8b32_generic(GemmArgs a) {
-    constexpr int NACC = (EPI == EPI_GATEUP) ? 2 : 1;
-    __shared__ f32x4 red[2][NW][NACC * MT][kWave];
+    __shared__ f32x4 red[2][NW][MT][kWave];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -314,34 +326,30 @@ __global__ __launch_bounds__(NW * 64) void q8b32_generic(GemmArgs a) {
 
     f16x8 hid[NBW][MT];
     load_hidden<MT, NBW>(hid, a, bw0, nbw, n, g);
-    Reducer<MT, NW, EPI, NACC> red_{red};
+    Reducer<MT, NW, EPI> red_{red};
     red_.init();
 
-    auto load = [&](GenRegs<NBW> (&r)[NACC], int item) {
-        const int row = min(item * kTileRows + n, a.V - 1);     // tail rows re-read the last row; masked
-        load_generic<NBW>(r[0], a.w0, a.s0, row, a.H, a.nb, bw0, nbw, g);
-        if constexpr (NACC == 2) load_generic<NBW>(r[NACC - 1], a.w1, a.s1, row, a.H, a.nb, bw0, nbw, g);
+    const int8_t* w = tile_up<EPI>(n) ? a.w1 : a.w0;
+    const uint16_t* sc = tile_up<EPI>(n) ? a.s1 : a.s0;
+    auto load = [&](GenRegs<NBW>& r, int item) {
+        const int row = min(tile_row<EPI>(item, n), a.V - 1);     // tail rows re-read the last row; masked
+        load_generic<NBW>(r, w, sc, row, a.H, a.nb, bw0, nbw, g);
     };
-    auto process = [&](const GenRegs<NBW> (&cur)[NACC], int it, int buf) {
+    auto process = [&](const GenRegs<NBW>& cur, int it, int buf) {
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        f32x4 acc[NACC][MT];
+        f32x4 acc[MT];
 #pragma unroll
-        for (int c = 0; c < NACC; ++c)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[c][mt] = zero;
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = zero;
 #pragma unroll
         for (int i = 0; i < NBW; ++i) {
             if (i < nbw) {
+                const f16x8 b = i8x8_to_f16x8(cur.w[i]);
+                const float s = h2f(cur.sc[i]);
 #pragma unroll
-                for (int c = 0; c < NACC; ++c) {
-                    const f16x8 b = i8x8_to_f16x8(cur[c].w[i]);
-                    const float sc = h2f(cur[c].sc[i]);
+                for (int mt = 0; mt < MT; ++mt) {
+                    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(hid[i][mt], b, zero, 0, 0, 0);
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(hid[i][mt], b, zero, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[c][mt][r] = __builtin_fmaf(sc, d[r], acc[c][mt][r]);
-                    }
+                    for (int r = 0; r < 4; ++r) acc[mt][r] = __builtin_fmaf(s, d[r], acc[mt][r]);
                 }
             }
         }
@@ -350,7 +358,7 @@ __global__ __launch_bounds__(NW * 64) void q8b32_generic(GemmArgs a) {
 
     const int step = gridDim.x;
     const int last = a.nitems - 1;
-    GenRegs<NBW> ra[NACC], rb[NACC];
+    GenRegs<NBW> ra, rb;
     int it = blockIdx.x;
     load(ra, it);
     while (true) {
@@ -494,16 +502,16 @@ constexpr int kH = 1 << EPI_HEAD, kS = 1 << EPI_STORE, kG = 1 << EPI_GATEUP;
 // preference within each MT; epis = the epilogues that compile for it without spills
 // within the LDS limit
 constexpr Shape kFast[] = {
-    {1, 4, 16, kH | kS}, {1, 16, 5, kH | kS | kG}, {1, 8, 8, kH | kS | kG}, {1, 8, 10, kH | kS | kG},
-    {1, 16, 8, kH | kS | kG}, {1, 8, 16, kH | kS}, {1, 16, 4, kH | kS | kG}, {1, 8, 4, kH | kS | kG},
-    {1, 4, 4, kH | kS | kG}, {1, 8, 2, kH | kS | kG},
-    {2, 8, 8, kH}, {2, 8, 4, kH}, {2, 4, 4, kH},
+    {1, 4, 16, kH | kS | kG}, {1, 16, 5, kH | kS | kG}, {1, 8, 8, kH | kS | kG}, {1, 8, 10, kH | kS | kG},
+    {1, 16, 8, kH | kS | kG}, {1, 20, 8, kH | kS | kG}, {1, 8, 16, kH | kS}, {1, 16, 4, kH | kS | kG},
+    {1, 8, 4, kH | kS | kG}, {1, 4, 4, kH | kS | kG}, {1, 8, 2, kH | kS | kG},
+    {2, 8, 8, kH}, {2, 8, 5, kH}, {2, 8, 4, kH}, {2, 4, 4, kH},
     {4, 4, 4, kH},
 };
 // generic kernel
 constexpr Shape kGeneric[] = {
     {1, 4, 4, kH | kS | kG}, {1, 8, 4, kH | kS | kG}, {1, 16, 4, kH | kS | kG}, {1, 4, 8, kH | kS | kG},
-    {1, 8, 8, kH | kS | kG}, {1, 16, 8, kH | kS}, {1, 4, 16, kH | kS | kG}, {1, 8, 16, kH | kS},
+    {1, 8, 8, kH | kS | kG}, {1, 16, 8, kH | kS | kG}, {1, 4, 16, kH | kS}, {1, 8, 16, kH | kS},
     {2, 4, 4, kH}, {2, 8, 4, kH}, {2, 4, 8, kH}, {2, 8, 8, kH},
     {4, 2, 4, kH}, {4, 4, 4, kH}, {4, 2, 8, kH},
 };
@@ -513,9 +521,11 @@ KernelFn pick_fast(const GemmCfg& c) {
 #define SV_SHAPE(MT, NBW, NW) \
     if (c.mt == MT && c.nbw == NBW && c.nw == NW) return q8b32_fast<MT, NBW, NW, EPI>;
     SV_SHAPE(1, 8, 8) SV_SHAPE(1, 8, 10) SV_SHAPE(1, 16, 8) SV_SHAPE(1, 16, 5) SV_SHAPE(1, 16, 4)
-    SV_SHAPE(1, 8, 4) SV_SHAPE(1, 4, 4) SV_SHAPE(1, 8, 2)
-    if constexpr (EPI != EPI_GATEUP) { SV_SHAPE(1, 8, 16) SV_SHAPE(1, 4, 16) }
-    if constexpr (EPI == EPI_HEAD) { SV_SHAPE(2, 8, 8) SV_SHAPE(2, 8, 4) SV_SHAPE(2, 4, 4) SV_SHAPE(4, 4, 4) }
+    SV_SHAPE(1, 8, 4) SV_SHAPE(1, 4, 4) SV_SHAPE(1, 8, 2) SV_SHAPE(1, 4, 16) SV_SHAPE(1, 20, 8)
+    if constexpr (EPI != EPI_GATEUP) { SV_SHAPE(1, 8, 16) }
+    if constexpr (EPI == EPI_HEAD) {
+        SV_SHAPE(2, 8, 8) SV_SHAPE(2, 8, 5) SV_SHAPE(2, 8, 4) SV_SHAPE(2, 4, 4) SV_SHAPE(4, 4, 4)
+    }
 #undef SV_SHAPE
     return nullptr;
 }
@@ -524,8 +534,8 @@ template <int EPI>
 KernelFn pick_generic(const GemmCfg& c) {
 #define SV_SHAPE(MT, NBW, NW) \
     if (c.mt == MT && c.nbw == NBW && c.nw == NW) return q8b32_generic<MT, NBW, NW, EPI>;
-    SV_SHAPE(1, 4, 4) SV_SHAPE(1, 8, 4) SV_SHAPE(1, 16, 4) SV_SHAPE(1, 4, 8) SV_SHAPE(1, 8, 8) SV_SHAPE(1, 4, 16)
-    if constexpr (EPI != EPI_GATEUP) { SV_SHAPE(1, 16, 8) SV_SHAPE(1, 8, 16) }
+    SV_SHAPE(1, 4, 4) SV_SHAPE(1, 8, 4) SV_SHAPE(1, 16, 4) SV_SHAPE(1, 4, 8) SV_SHAPE(1, 8, 8) SV_SHAPE(1, 16, 8)
+    if constexpr (EPI != EPI_GATEUP) { SV_SHAPE(1, 4, 16) SV_SHAPE(1, 8, 16) }
     if constexpr (EPI == EPI_HEAD) {
         SV_SHAPE(2, 4, 4) SV_SHAPE(2, 8, 4) SV_SHAPE(2, 4, 8) SV_SHAPE(2, 8, 8)
         SV_SHAPE(4, 2, 4) SV_SHAPE(4, 4, 4) SV_SHAPE(4, 2, 8)
@@ -537,7 +547,7 @@ KernelFn pick_generic(const GemmCfg& c) {
 // Fast shape: the hidden axis splits into ks equal parts, each into nw waves of exactly
 // nbw blocks.
 bool try_fast(int nb, int mt, int epi, GemmCfg& c) {
-    for (int ks = 1; ks <= 4; ++ks) {
+    for (int ks = 1; ks <= 8; ++ks) {
         if (nb % ks) continue;
         const int nbk = nb / ks;
         for (const Shape& sh : kFast) {
@@ -585,15 +595,17 @@ GemmCfg gemm_config(int rows, int H, int S, int epi) {
     GemmCfg c{};
     const int mt = S <= 16 ? 1 : (S <= 32 ? 2 : 4);
     const int nb = H / kBlock;
-    // fewest workgroup splits of the hidden axis first (a split costs a combine pass), then
-    // the fast loads
+    // The fast loads stream at about twice the generic ones, so the fast kernel wins unless it
+    // needs more than one extra workgroup split of the hidden axis (each split adds partial
+    // sums and a combine pass); an unsplit generic launch beats any split one.
     GemmCfg f{}, gen{};
     const bool have_fast = try_fast(nb, mt, epi, f);
     if (!(g_nw_override && try_generic(nb, mt, epi, g_nw_override, gen)))
         try_generic(nb, mt, epi, 0, gen);     // always succeeds: (mt, smallest nbw, 4 waves) exists
-    c = (have_fast && f.ksplit <= gen.ksplit) ? f : gen;
+    const bool take_fast = have_fast && (f.ksplit == 1 || (gen.ksplit > 1 && f.ksplit <= gen.ksplit + 1));
+    c = take_fast ? f : gen;
     // measured on MI355X: 16-wave groups stream best one per CU, smaller groups two per CU
-    const int items = (rows + kTileRows - 1) / kTileRows;
+    const int items = epi == EPI_GATEUP ? (rows + 7) / 8 : (rows + kTileRows - 1) / kTileRows;
     int cap = g_grid_override ? g_grid_override : (c.nw >= 16 ? 256 : 512);
     if (cap > kGridMax) cap = kGridMax;
     c.grid = items < cap ? (items > 0 ? items : 1) : cap;
