@@ -183,6 +183,12 @@ int specverify_accept(const int32_t* argmax, const int32_t* drafts, int32_t K, i
  *   residual fp16 [S][N] or NULL (then no add).  y may alias residual, never x.
  *   w int8 [N][Kin]; scale fp16 [N][Kin/32]; x fp16 [S][Kin]; y fp16 [S][N].
  *
+ * specverify_linear_residual_rmsnorm_q8b32: specverify_linear_q8b32, then
+ *   norm_out = specverify_rmsnorm(y, eps): the end of one block and the input norm of the
+ *   next ("Axis 4": the norm fused into the neighbouring kernel).  When the hidden axis is
+ *   split, one row pass sums the split partials, adds the residual, writes y and the norm.
+ *   norm_out fp16 [S][N] must not alias x, y or residual (SV_ERR_SHAPE); eps >= 0.
+ *
  * Both matmuls take S = 1 .. 16 and the alignment rules of specverify_verify (N plays V,
  * Kin plays H).  Very long Kin splits the hidden axis across workgroups and then needs a
  * scratch `workspace` of specverify_stack_workspace_bytes(N, Kin, S, gateup) bytes
@@ -198,6 +204,11 @@ int specverify_gateup_silu_q8b32(const int8_t* wg, const uint16_t* sg, const int
 int specverify_linear_q8b32(const int8_t* w, const uint16_t* scale, int32_t N, int32_t Kin,
                             const uint16_t* x, int32_t S, const uint16_t* residual, uint16_t* y,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+int specverify_linear_residual_rmsnorm_q8b32(const int8_t* w, const uint16_t* scale, int32_t N,
+                                             int32_t Kin, const uint16_t* x, int32_t S,
+                                             const uint16_t* residual, uint16_t* y, float eps,
+                                             uint16_t* norm_out, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Launch-shape override of the q8b32 matmuls, for tuning sweeps: waves per workgroup

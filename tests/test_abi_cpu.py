@@ -87,6 +87,17 @@ def test_stack_argument_errors(lib):
     need = lib.specverify_stack_workspace_bytes(64, 65536, 9, 1)
     assert need > 0                                     # very long inputs split the hidden axis
     assert lib.specverify_gateup_silu_q8b32(A16, A16, A16, A16, 64, 65536, A16, 9, A16, NULL, 0, NULL) == 4
+    fused = lib.specverify_linear_residual_rmsnorm_q8b32
+    fused.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P, ctypes.c_float, P, P,
+                      ctypes.c_size_t, P]
+    A16b, A16c = P(0x20000), P(0x30000)
+    assert fused(A16, A16, 64, 256, A16, 9, A16b, A16b, 1e-6, NULL, NULL, 0, NULL) == 1        # norm_out
+    assert fused(A16, A16, 64, 256, A16, 9, A16b, A16b, 1e-6, A16b, NULL, 0, NULL) == 2        # aliases y
+    assert fused(A16, A16, 64, 256, A16, 9, A16b, A16b, -1.0, A16c, NULL, 0, NULL) == 2        # eps
+    assert fused(A16, A16, 64, 256, A16, 17, A16b, A16b, 1e-6, A16c, NULL, 0, NULL) == 2       # S <= 16
+    need = lib.specverify_stack_workspace_bytes(64, 65536, 9, 0)
+    assert need > 0
+    assert fused(A16, A16, 64, 65536, A16, 9, A16b, A16b, 1e-6, A16c, NULL, 0, NULL) == 4
 
 
 def test_missing_library_raises(monkeypatch, tmp_path):

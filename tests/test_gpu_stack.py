@@ -50,7 +50,7 @@ def _gpu_linear(w, x, residual):
     return y.cpu().numpy()
 
 
-@pytest.mark.parametrize("S,H", [(9, 4096), (1, 32), (16, 5120), (3, 96)])
+@pytest.mark.parametrize("S,H", [(9, 4096), (1, 32), (16, 5120), (3, 96), (2, 12288), (1, 65536)])
 def test_rmsnorm(S, H):
     x = (synth.fp16_normal(np.random.default_rng(H), (S, H)).astype(np.float32) * 7).astype(np.float16)
     y = torch.empty((S, H), dtype=torch.float16, device=dev())
@@ -89,6 +89,41 @@ def test_linear_residual(N, K, S, res):
     _check_f16(y, ref)
 
 
+def test_rmsnorm_in_place():
+    x = (synth.fp16_normal(np.random.default_rng(8), (5, 9216)).astype(np.float32) * 3).astype(np.float16)
+    buf = to_dev(x)
+    sv.rmsnorm(buf, buf, 1e-6)
+    torch.cuda.synchronize()
+    xx = x.astype(np.float64)
+    _check_f16(buf.cpu().numpy(), xx / np.sqrt(np.mean(xx * xx, axis=1, keepdims=True) + 1e-6), slack=1e-5)
+
+
+@pytest.mark.parametrize("N,K,S,res", [(4096, 12288, 9, True), (4096, 12288, 16, True), (77, 96, 5, True),
+                                       (300, 65536, 2, True), (5000, 1024, 3, True), (9000, 12288, 4, False),
+                                       (1, 32, 1, True)])
+def test_linear_residual_rmsnorm(N, K, S, res):
+    """End of one block plus the next block's input norm, in one call."""
+    say(f"linear+residual+rmsnorm N={N} K={K} S={S} residual={res}")
+    rng = np.random.default_rng(N * 7 + K + S)
+    w = _w(rng, N, K)
+    x = synth.fp16_normal(rng, (S, K))
+    r = (synth.fp16_normal(rng, (S, N)).astype(np.float32) * 4).astype(np.float16) if res else None
+    y = torch.empty((S, N), dtype=torch.float16, device=dev())
+    n = torch.empty((S, N), dtype=torch.float16, device=dev())
+    nb = sv.stack_workspace_bytes(N, K, S, False)
+    sv.linear_residual_rmsnorm(to_dev(w[0]), to_dev(w[1]), to_dev(x), y, n, None if r is None else to_dev(r),
+                               1e-6, sv.workspace(nb, dev()) if nb else None)
+    torch.cuda.synchronize()
+    ref = oracle.linear_q8b32(*w, x)
+    if res:
+        ref = ref + r.astype(np.float64)
+    y16 = y.cpu().numpy()
+    _check_f16(y16, ref)
+    # the norm of the library's own fp16 y (teacher-forced)
+    yy = y16.astype(np.float64)
+    _check_f16(n.cpu().numpy(), yy / np.sqrt(np.mean(yy * yy, axis=1, keepdims=True) + 1e-6), slack=1e-5)
+
+
 def test_linear_output_may_alias_residual():
     rng = np.random.default_rng(3)
     w = _w(rng, 512, 256)
@@ -111,17 +146,23 @@ def test_small_stack_end_to_end_teacher_forced():
     m = torch.empty((S, F), dtype=torch.float16, device=dev())
     gw = sv.workspace(sv.stack_workspace_bytes(F, H, S, True), dev())
     dw = sv.workspace(sv.stack_workspace_bytes(H, F, S, False), dev())
+    sv.rmsnorm(xd, n)
     for li, (g, u, d) in enumerate(layers):
         x_in = xd.cpu().numpy()
-        sv.rmsnorm(xd, n)
+        n_in = n.cpu().numpy()
+        xx = x_in.astype(np.float64)
+        _check_f16(n_in, xx / np.sqrt(np.mean(xx * xx, axis=1, keepdims=True) + 1e-6), slack=1e-5)
         sv.gateup_silu(to_dev(g[0]), to_dev(g[1]), to_dev(u[0]), to_dev(u[1]), n, m, gw)
-        sv.linear(to_dev(d[0]), to_dev(d[1]), m, xd, xd, dw)
+        if li % 2:
+            sv.linear(to_dev(d[0]), to_dev(d[1]), m, xd, xd, dw)
+            sv.rmsnorm(xd, n)
+        else:       # the fused end-of-block call; y aliases the residual stream
+            sv.linear_residual_rmsnorm(to_dev(d[0]), to_dev(d[1]), m, xd, n, xd, 1e-6, dw)
         torch.cuda.synchronize()
         # oracle block on the GPU's own layer input
         ref_x, parts = oracle.mlp_block(x_in, (g, u, d), return_parts=True)
         ref_full = x_in.astype(np.float64) + oracle.linear_q8b32(*d, m.cpu().numpy())
         _check_f16(xd.cpu().numpy(), ref_full)
-    sv.rmsnorm(xd, n)
     am = torch.empty(S, dtype=torch.int32, device=dev())
     lg = torch.empty((S, V), dtype=torch.float32, device=dev())
     sv.verify(to_dev(hq), to_dev(hs), n, am, sv.workspace(sv.verify_workspace_bytes(V, H, S), dev()), lg)

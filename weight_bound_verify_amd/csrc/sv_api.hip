@@ -195,7 +195,7 @@ int specverify_rmsnorm(const uint16_t* x, int32_t S, int32_t H, float eps, uint1
     if (!(eps >= 0.0f)) return fail(SV_ERR_SHAPE, "eps must be >= 0");
     if (!aligned(x, 16) || !aligned(y, 16)) return fail(SV_ERR_ALIGN, "x and y must be 16-byte aligned");
     if (int st = check_device()) return st;
-    hipError_t e = sv::launch_rmsnorm(x, S, H, eps, y, stream);
+    hipError_t e = sv::launch_row_norm(nullptr, 0, S, H, x, nullptr, eps, y, stream);
     return e == hipSuccess ? SV_OK : hip_fail(e, "rmsnorm launch");
 }
 
@@ -245,6 +245,37 @@ int specverify_linear_q8b32(const int8_t* w, const uint16_t* scale, int32_t N, i
     if (cfg.ksplit > 1) a.kpart0 = static_cast<float*>(workspace);
     hipError_t e = sv::launch_q8b32(sv::EPI_STORE, cfg, a, stream);
     return e == hipSuccess ? SV_OK : hip_fail(e, "linear launch");
+}
+
+int specverify_linear_residual_rmsnorm_q8b32(const int8_t* w, const uint16_t* scale, int32_t N, int32_t Kin,
+                                             const uint16_t* x, int32_t S, const uint16_t* residual, uint16_t* y,
+                                             float eps, uint16_t* norm_out, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
+    if (int st = check_q8b32(w, scale, N, Kin, x, S, 16)) return st;
+    if (!y || !norm_out) return fail(SV_ERR_NULL, "y and norm_out are required");
+    if (!(eps >= 0.0f)) return fail(SV_ERR_SHAPE, "eps must be >= 0");
+    if (!aligned(y, 2) || !aligned(norm_out, 2) || (residual && !aligned(residual, 2)))
+        return fail(SV_ERR_ALIGN, "alignment");
+    if (norm_out == y || norm_out == residual || norm_out == x)
+        return fail(SV_ERR_SHAPE, "norm_out must not alias x, y or residual");
+    const size_t need = sv::stack_workspace_bytes(N, Kin, S, false);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+        return fail(SV_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+    if (int st = check_device()) return st;
+    const sv::GemmCfg cfg = sv::gemm_config(N, Kin, S, sv::EPI_STORE);
+    sv::GemmArgs a{};
+    a.w0 = w; a.s0 = scale; a.x = x;
+    a.V = N; a.H = Kin; a.S = S; a.nb = Kin / SV_BLOCK; a.nitems = (N + 15) / 16; a.ksplit = cfg.ksplit;
+    a.y = y; a.residual = residual;
+    if (cfg.ksplit > 1) a.kpart0 = static_cast<float*>(workspace);
+    // split: the row pass sums the partials, adds the residual and normalises in one launch;
+    // unsplit: the matmul epilogue adds the residual and the row pass only normalises y
+    const bool fused = cfg.ksplit > 1 && cfg.ksplit <= sv::kRowNormMaxSplit;
+    hipError_t e = sv::launch_q8b32(sv::EPI_STORE, cfg, a, stream, /*combine=*/!fused);
+    if (e != hipSuccess) return hip_fail(e, "linear launch");
+    e = fused ? sv::launch_row_norm(a.kpart0, cfg.ksplit, S, N, residual, y, eps, norm_out, stream)
+                       : sv::launch_row_norm(nullptr, 0, S, N, y, nullptr, eps, norm_out, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "row norm launch");
 }
 
 }  // extern "C"

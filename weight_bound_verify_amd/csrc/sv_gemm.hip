@@ -36,6 +36,7 @@
 
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 namespace sv {
 
@@ -584,6 +585,45 @@ bool try_generic(int nb, int mt, int epi, int nw_fixed, GemmCfg& c) {
     return false;
 }
 
+KernelFn kernel_for(int epi, const GemmCfg& c) {
+    if (c.fast) {
+        if (epi == EPI_HEAD) return pick_fast<EPI_HEAD>(c);
+        if (epi == EPI_STORE) return pick_fast<EPI_STORE>(c);
+        return pick_fast<EPI_GATEUP>(c);
+    }
+    if (epi == EPI_HEAD) return pick_generic<EPI_HEAD>(c);
+    if (epi == EPI_STORE) return pick_generic<EPI_STORE>(c);
+    return pick_generic<EPI_GATEUP>(c);
+}
+
+// Workgroups of this kernel resident on the whole device at once.  Without a device to ask
+// (no GPU, or a failed query) the answer is one 16-wave group or two smaller groups per
+// compute unit of a 256-CU part; it only sizes the grid, never a buffer.
+int resident_groups(int epi, const GemmCfg& c) {
+    struct Entry { KernelFn fn; int dev; int groups; };
+    static Entry cache[64];
+    static int used = 0;
+    static std::mutex mu;
+    KernelFn fn = kernel_for(epi, c);
+    int dev = -1;
+    const int fallback = c.nw >= 16 ? 256 : 512;
+    if (!fn || hipGetDevice(&dev) != hipSuccess) return fallback;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].fn == fn && cache[i].dev == dev) return cache[i].groups;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), c.nw * 64, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 ||
+        cus < 1) {
+        (void)hipGetLastError();
+        return fallback;
+    }
+    const int groups = per_cu * cus;
+    if (used < 64) cache[used++] = Entry{fn, dev, groups};
+    return groups;
+}
+
 }  // namespace
 
 void set_tuning(int waves_per_group, int max_groups) {
@@ -604,9 +644,12 @@ GemmCfg gemm_config(int rows, int H, int S, int epi) {
         try_generic(nb, mt, epi, 0, gen);     // always succeeds: (mt, smallest nbw, 4 waves) exists
     const bool take_fast = have_fast && (f.ksplit == 1 || (gen.ksplit > 1 && f.ksplit <= gen.ksplit + 1));
     c = take_fast ? f : gen;
-    // measured on MI355X: 16-wave groups stream best one per CU, smaller groups two per CU
+    // Persistent grid: as many workgroups as the chip holds at once (the register and LDS
+    // footprint of the chosen kernel decide how many fit on a compute unit), so no
+    // workgroup waits for another to retire and every one keeps its loads in flight.
     const int items = epi == EPI_GATEUP ? (rows + 7) / 8 : (rows + kTileRows - 1) / kTileRows;
-    int cap = g_grid_override ? g_grid_override : (c.nw >= 16 ? 256 : 512);
+    int cap = g_grid_override ? g_grid_override : resident_groups(epi, c) / c.ksplit;
+    if (cap < 1) cap = 1;
     if (cap > kGridMax) cap = kGridMax;
     c.grid = items < cap ? (items > 0 ? items : 1) : cap;
     return c;
@@ -630,21 +673,12 @@ size_t stack_workspace_bytes(int N, int K, int S, bool gateup) {
     return (size_t)4 * c.ksplit * S * N * (gateup ? 2 : 1);
 }
 
-hipError_t launch_q8b32(int epi, const GemmCfg& cfg, const GemmArgs& a, hipStream_t stream) {
-    KernelFn fn = nullptr;
-    if (cfg.fast) {
-        if (epi == EPI_HEAD) fn = pick_fast<EPI_HEAD>(cfg);
-        else if (epi == EPI_STORE) fn = pick_fast<EPI_STORE>(cfg);
-        else fn = pick_fast<EPI_GATEUP>(cfg);
-    } else {
-        if (epi == EPI_HEAD) fn = pick_generic<EPI_HEAD>(cfg);
-        else if (epi == EPI_STORE) fn = pick_generic<EPI_STORE>(cfg);
-        else fn = pick_generic<EPI_GATEUP>(cfg);
-    }
+hipError_t launch_q8b32(int epi, const GemmCfg& cfg, const GemmArgs& a, hipStream_t stream, bool combine) {
+    KernelFn fn = kernel_for(epi, cfg);
     if (!fn) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(fn, dim3(cfg.grid, cfg.ksplit), dim3(cfg.nw * 64), 0, stream, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || cfg.ksplit == 1) return e;
+    if (e != hipSuccess || cfg.ksplit == 1 || !combine) return e;
     const int cg = combine_groups(a.V);
     if (epi == EPI_HEAD)
         hipLaunchKernelGGL(combine_kernel<EPI_HEAD>, dim3(cg, a.S), dim3(256), 0, stream, a);

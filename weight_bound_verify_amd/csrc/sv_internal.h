@@ -52,7 +52,9 @@ size_t head_workspace_bytes(int V, int H, int S);
 // Workspace bytes a store / gate-up matmul needs (non-zero only when ksplit > 1).
 size_t stack_workspace_bytes(int N, int K, int S, bool gateup);
 
-hipError_t launch_q8b32(int epi, const GemmCfg& cfg, const GemmArgs& a, hipStream_t stream);
+// The matmul and, when cfg.ksplit > 1 and `combine` is set, the pass that sums the split
+// partial sums into the epilogue's output.
+hipError_t launch_q8b32(int epi, const GemmCfg& cfg, const GemmArgs& a, hipStream_t stream, bool combine = true);
 // Argmax stage 2 of a head launch and, when drafts_out != null, the rest of the round
 // (accept, then the next drafts): one workgroup.
 hipError_t launch_round_tail(const float* pv, const int* pi, int nparts, int S, int32_t* argmax,
@@ -62,7 +64,10 @@ hipError_t launch_propose(const int32_t* tokens, int cap, int32_t* state, int nm
                           hipStream_t stream);
 hipError_t launch_accept(const int32_t* argmax, const int32_t* drafts, int K, int32_t* tokens,
                          int cap, int32_t* state, hipStream_t stream);
-hipError_t launch_rmsnorm(const uint16_t* x, int S, int H, float eps, uint16_t* y,
-                          hipStream_t stream);
+// Per window row: t = sum of `ks` split partial sums [ks][S][N] (+ residual), y = fp16(t)
+// (y may be null), norm_out = fp16(RMSNorm(fp16(t))).  ks = 0 is a plain RMSNorm of residual.
+constexpr int kRowNormMaxSplit = 8;
+hipError_t launch_row_norm(const float* part, int ks, int S, int N, const uint16_t* residual, uint16_t* y,
+                           float eps, uint16_t* norm_out, hipStream_t stream);
 
 }  // namespace sv

@@ -29,7 +29,7 @@ EXPORTS = (
     "specverify_propose", "specverify_verify_workspace_bytes", "specverify_verify", "specverify_round",
     "specverify_accept",
     "specverify_rmsnorm", "specverify_stack_workspace_bytes", "specverify_gateup_silu_q8b32",
-    "specverify_linear_q8b32", "specverify_set_tuning", "specverify_status_string", "specverify_last_error",
+    "specverify_linear_q8b32", "specverify_linear_residual_rmsnorm_q8b32", "specverify_set_tuning", "specverify_status_string", "specverify_last_error",
 )
 
 _lib = None
@@ -61,6 +61,8 @@ def load():
         "specverify_stack_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
         "specverify_gateup_silu_q8b32": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _P, _P, ctypes.c_size_t, _P]),
         "specverify_linear_q8b32": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+        "specverify_linear_residual_rmsnorm_q8b32": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, ctypes.c_float, _P, _P,
+                                                          ctypes.c_size_t, _P]),
         "specverify_set_tuning": (None, [_I, _I]),
         "specverify_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "specverify_last_error": (ctypes.c_char_p, []),
@@ -194,3 +196,17 @@ def linear(w, scale, x, y, residual=None, ws=None, stream=None) -> None:
         _ptr(w, torch.int8, "w"), _ptr(scale, torch.float16, "scale"), N, K, _ptr(x, torch.float16, "x"), S,
         _ptr(residual, torch.float16, "residual", S * N), _ptr(y, torch.float16, "y", S * N),
         _ptr(ws, torch.uint8, "workspace"), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def linear_residual_rmsnorm(w, scale, x, y, norm_out, residual=None, eps: float = 1e-6, ws=None,
+                            stream=None) -> None:
+    """y = fp16(x W^T [+ residual]) and norm_out = fp16(rmsnorm(y)) in one call."""
+    N, K = w.shape
+    S = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("shape mismatch")
+    _check(load().specverify_linear_residual_rmsnorm_q8b32(
+        _ptr(w, torch.int8, "w"), _ptr(scale, torch.float16, "scale"), N, K, _ptr(x, torch.float16, "x"), S,
+        _ptr(residual, torch.float16, "residual", S * N), _ptr(y, torch.float16, "y", S * N), float(eps),
+        _ptr(norm_out, torch.float16, "norm_out", S * N), _ptr(ws, torch.uint8, "workspace"),
+        0 if ws is None else ws.numel(), _stream(stream)))
