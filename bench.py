@@ -270,11 +270,11 @@ def main():
     hist = (st1[sv.STATE_HIST:sv.STATE_HIST + K + 1] - st0[sv.STATE_HIST:sv.STATE_HIST + K + 1]).tolist()
     sum_j = int(st1[sv.STATE_SUMJ] - st0[sv.STATE_SUMJ])
 
-    # roofline of the dominant kernel: the round launch itself (head matmul + fused argmax,
-    # accept and next drafts), timed in isolation with HIP events on the launch stream
+    # roofline of the dominant kernel, the q8b32 head matmul with its fused argmax stage 1:
+    # whole rounds launched one by one, HIP events recorded by the library on the launch
+    # stream right before and after the matmul kernel
     stream = torch.cuda.current_stream()
     durs = []
-    len_mid = int(st1[sv.STATE_LEN])
     for i in range(args.kernel_reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         if wl["layers"]:
@@ -282,15 +282,13 @@ def main():
         else:
             x, c = hidden[i % R_SETS], i % copies
         d_in = forced[i % R_SETS] if forced is not None else drafts
-        e0.record(stream)
+        sv.profile_next_matmul(e0, e1, stream=stream)
         sv.round(wq[c], ws[c], x, d_in, tokens, state, drafts, argmax, work, stream=stream)
-        e1.record(stream)
         durs.append((e0, e1))
     torch.cuda.synchronize()
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in durs]))
     hb = head_bytes(V, H, S)
-    launch_bytes = hb + 4 * len_mid + 4 * (3 * K + 1)       # + drafter stream read, drafts, accept
-    achieved = launch_bytes / (kern_ms * 1e-3) / 1e9
+    achieved = hb / (kern_ms * 1e-3) / 1e9
 
     round_bytes = hb + (stack_bytes(wl["layers"], H, F, S) if wl["layers"] else 0)
     rps = 1000.0 / ms
@@ -315,8 +313,8 @@ def main():
         "bytes_per_round": round_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": load_traffic(args.config),
-                     "kernel": "specverify_round launch: q8b32 head matmul, fused argmax, accept, next drafts",
-                     "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": launch_bytes},
+                     "kernel": "q8b32 head matmul with the fused argmax stage 1 (one launch per round)",
+                     "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": hb},
         "accept_hist": hist,
         "tokens_per_round": round((args.steps + sum_j) / args.steps, 3),
     }

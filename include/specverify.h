@@ -218,6 +218,16 @@ int specverify_linear_residual_rmsnorm_q8b32(const int8_t* w, const uint16_t* sc
  */
 void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups);
 
+/*
+ * Timing hook for the dominant kernel.  The next int8 matmul that this thread enqueues through
+ * any entry point (the head matmul of specverify_verify / _round, or a stack projection)
+ * records `before` on its stream right before the matmul kernel and `after` right after it
+ * (after its split-combine pass when the hidden axis is split across workgroups); the hook
+ * is then cleared.  The events are the caller's (created on the current device, timing
+ * enabled).  (NULL, NULL) clears a pending hook; one NULL alone is SV_ERR_NULL.
+ */
+int specverify_profile_next_matmul(hipEvent_t before, hipEvent_t after);
+
 /* Static description of a status code. */
 const char* specverify_status_string(int status);
 /* Detail of the last failure on this thread ("" if none). */

@@ -14,6 +14,9 @@
 namespace {
 
 thread_local char g_last_error[256] = "";
+// Timing hook: events recorded around the next matmul launch of this thread, then cleared.
+thread_local hipEvent_t g_prof_before = nullptr;
+thread_local hipEvent_t g_prof_after = nullptr;
 
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char* fmt, ...) {
@@ -62,6 +65,20 @@ int check_q8b32(const int8_t* w, const uint16_t* s, int32_t rows, int32_t H, con
     return SV_OK;
 }
 
+// The matmul (and its split combine), bracketed by the pending timing hook if one is set.
+hipError_t launch_matmul(int epi, const sv::GemmCfg& cfg, const sv::GemmArgs& a, hipStream_t stream,
+                         bool combine = true) {
+    hipEvent_t before = g_prof_before, after = g_prof_after;
+    g_prof_before = g_prof_after = nullptr;
+    if (before) {
+        hipError_t e = hipEventRecord(before, stream);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e = sv::launch_q8b32(epi, cfg, a, stream, combine);
+    if (e == hipSuccess && after) e = hipEventRecord(after, stream);
+    return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,6 +98,13 @@ const char* specverify_status_string(int status) {
 }
 
 const char* specverify_last_error(void) { return g_last_error; }
+
+int specverify_profile_next_matmul(hipEvent_t before, hipEvent_t after) {
+    if ((before == nullptr) != (after == nullptr)) return fail(SV_ERR_NULL, "give both events or neither");
+    g_prof_before = before;
+    g_prof_after = after;
+    return SV_OK;
+}
 
 void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups) {
     if (waves_per_group != 0 && waves_per_group != 4 && waves_per_group != 8 && waves_per_group != 16)
@@ -131,7 +155,7 @@ int launch_head(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, 
     a.part_idx = reinterpret_cast<int*>(ws + (size_t)4 * S * sv::kGridMax);
     a.logits = logits;
     if (cfg.ksplit > 1) a.kpart0 = reinterpret_cast<float*>(ws + sv::head_partials_bytes(S));
-    hipError_t e = sv::launch_q8b32(sv::EPI_HEAD, cfg, a, stream);
+    hipError_t e = launch_matmul(sv::EPI_HEAD, cfg, a, stream);
     if (e != hipSuccess) return hip_fail(e, "verify matmul launch");
     const int nparts = cfg.ksplit > 1 ? sv::combine_groups(V) : cfg.grid;
     e = sv::launch_round_tail(a.part_val, a.part_idx, nparts, S, argmax, round ? drafts_in : nullptr, tokens, cap,
@@ -223,7 +247,7 @@ int specverify_gateup_silu_q8b32(const int8_t* wg, const uint16_t* sg, const int
         a.kpart0 = static_cast<float*>(workspace);
         a.kpart1 = a.kpart0 + (size_t)cfg.ksplit * S * N;
     }
-    hipError_t e = sv::launch_q8b32(sv::EPI_GATEUP, cfg, a, stream);
+    hipError_t e = launch_matmul(sv::EPI_GATEUP, cfg, a, stream);
     return e == hipSuccess ? SV_OK : hip_fail(e, "gate/up launch");
 }
 
@@ -243,7 +267,7 @@ int specverify_linear_q8b32(const int8_t* w, const uint16_t* scale, int32_t N, i
     a.V = N; a.H = Kin; a.S = S; a.nb = Kin / SV_BLOCK; a.nitems = (N + 15) / 16; a.ksplit = cfg.ksplit;
     a.y = y; a.residual = residual;
     if (cfg.ksplit > 1) a.kpart0 = static_cast<float*>(workspace);
-    hipError_t e = sv::launch_q8b32(sv::EPI_STORE, cfg, a, stream);
+    hipError_t e = launch_matmul(sv::EPI_STORE, cfg, a, stream);
     return e == hipSuccess ? SV_OK : hip_fail(e, "linear launch");
 }
 
@@ -271,7 +295,7 @@ int specverify_linear_residual_rmsnorm_q8b32(const int8_t* w, const uint16_t* sc
     // split: the row pass sums the partials, adds the residual and normalises in one launch;
     // unsplit: the matmul epilogue adds the residual and the row pass only normalises y
     const bool fused = cfg.ksplit > 1 && cfg.ksplit <= sv::kRowNormMaxSplit;
-    hipError_t e = sv::launch_q8b32(sv::EPI_STORE, cfg, a, stream, /*combine=*/!fused);
+    hipError_t e = launch_matmul(sv::EPI_STORE, cfg, a, stream, /*combine=*/!fused);
     if (e != hipSuccess) return hip_fail(e, "linear launch");
     e = fused ? sv::launch_row_norm(a.kpart0, cfg.ksplit, S, N, residual, y, eps, norm_out, stream)
                        : sv::launch_row_norm(nullptr, 0, S, N, y, nullptr, eps, norm_out, stream);

@@ -29,7 +29,7 @@ EXPORTS = (
     "specverify_propose", "specverify_verify_workspace_bytes", "specverify_verify", "specverify_round",
     "specverify_accept",
     "specverify_rmsnorm", "specverify_stack_workspace_bytes", "specverify_gateup_silu_q8b32",
-    "specverify_linear_q8b32", "specverify_linear_residual_rmsnorm_q8b32", "specverify_set_tuning", "specverify_status_string", "specverify_last_error",
+    "specverify_linear_q8b32", "specverify_linear_residual_rmsnorm_q8b32", "specverify_set_tuning", "specverify_profile_next_matmul", "specverify_status_string", "specverify_last_error",
 )
 
 _lib = None
@@ -64,6 +64,7 @@ def load():
         "specverify_linear_residual_rmsnorm_q8b32": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, ctypes.c_float, _P, _P,
                                                           ctypes.c_size_t, _P]),
         "specverify_set_tuning": (None, [_I, _I]),
+        "specverify_profile_next_matmul": (_I, [_P, _P]),
         "specverify_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "specverify_last_error": (ctypes.c_char_p, []),
     }
@@ -120,6 +121,17 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 def set_tuning(waves_per_group: int = 0, max_groups: int = 0) -> None:
     load().specverify_set_tuning(int(waves_per_group), int(max_groups))
+
+
+def profile_next_matmul(before, after, stream=None) -> None:
+    """Record two torch.cuda.Events around the next matmul kernel this thread launches."""
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    for ev in (before, after):
+        if not ev.cuda_event:           # torch creates its events on first record
+            ev.record(stream)
+    _check(load().specverify_profile_next_matmul(ctypes.c_void_p(before.cuda_event),
+                                                 ctypes.c_void_p(after.cuda_event)))
 
 
 def propose(tokens, state, drafts, ngram_max: int = 3, stream=None) -> None:
