@@ -211,12 +211,45 @@ int specverify_linear_residual_rmsnorm_q8b32(const int8_t* w, const uint16_t* sc
                                              size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Launch-shape override of the q8b32 matmuls, for tuning sweeps: waves per workgroup
- * (4, 8 or 16; 0 = automatic) and an upper bound on workgroups per launch (1 .. 4096;
- * 0 = automatic).  Process-wide; affects the *_workspace_bytes answers, so query them
- * after changing it.  Not thread-safe against concurrent calls.
+ * specverify_stack - the whole weight-bound dense stack in front of the head, one call:
+ * L blocks of [n = rmsnorm(x); m = fp16(silu(n Wg^T) * (n Wu^T)); x = fp16(x + m Wd^T)],
+ * then norm_out = rmsnorm(x) (the head's input).  Pages: "Flagship dramatic-speedup plan -
+ * the full stackable tuning set", "Baseline byte model" (every weight byte read once per
+ * forward) and "Axis 4" (RMSNorm fused into the neighbouring kernels; SwiGLU in the
+ * projection's epilogue).  Block as for the per-op calls above; rmsnorm(x) =
+ * fp16(x / sqrt(mean(x^2) + eps)) with the sum of squares in fp32 over the fp16 values.
+ *
+ * Two launches per block: gate/up (normalising its window rows on the fly) and down (adding
+ * the residual, storing x and the per-tile sums of squares the next norm needs).
+ *   wg, wu  int8 [L][F][H] (layer l at l*F*H);  sg, su fp16 [L][F][H/32]
+ *   wd      int8 [L][H][F];                      sd     fp16 [L][H][F/32]
+ *   H, F    multiples of 512 in [512, 65536];   S 1 .. 16;   L 1 .. 4096;   eps >= 0
+ *   x       fp16 [S][H]: the stack's input; overwritten with the output of block L-1 when
+ *           x_layers is NULL, else left unchanged
+ *   x_layers fp16 [L][S][H] or NULL: the output of every block (for per-block checks)
+ *   norm_out fp16 [S][H]: rmsnorm of the last block's output; must not overlap x or x_layers
+ *   workspace  at least specverify_stack_forward_workspace_bytes(H, F, S) bytes, no
+ *           initialisation; calls that share it must be ordered (one stream)
+ * All pointers 16-byte aligned.  Errors: SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_ALIGN,
+ * SV_ERR_WORKSPACE, SV_ERR_DEVICE, SV_ERR_HIP.  Returns 0 bytes for unsupported shapes.
  */
-void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups);
+size_t specverify_stack_forward_workspace_bytes(int32_t H, int32_t F, int32_t S);
+int specverify_stack(const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su,
+                     const int8_t* wd, const uint16_t* sd, int32_t L, int32_t H, int32_t F,
+                     uint16_t* x, int32_t S, float eps, uint16_t* x_layers, uint16_t* norm_out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Launch-shape override of the q8b32 matmuls, for tuning sweeps: waves per workgroup
+ * (4, 8 or 16; 0 = automatic), an upper bound on workgroups per launch (1 .. 4096;
+ * 0 = automatic) and, for the chunked stack kernels, load units in flight per wave (2 .. 4;
+ * 0 = automatic; a depth that has no kernel for a shape falls back to the automatic one).
+ * Waves that do not divide a chunked shape make specverify_stack fail with SV_ERR_SHAPE.
+ * Process-wide;
+ * affects the *_workspace_bytes answers, so query them after changing it.  Not thread-safe
+ * against concurrent calls.
+ */
+void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups, int32_t depth);
 
 /*
  * Timing hook for the dominant kernel.  The next int8 matmul that this thread enqueues through

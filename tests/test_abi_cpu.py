@@ -100,6 +100,31 @@ def test_stack_argument_errors(lib):
     assert fused(A16, A16, 64, 65536, A16, 9, A16b, A16b, 1e-6, A16c, NULL, 0, NULL) == 4
 
 
+def test_whole_stack_argument_errors(lib):
+    f = lib.specverify_stack
+    ws = lib.specverify_stack_forward_workspace_bytes(4096, 12288, 9)
+    assert ws == 2 * 9 * 12288 + 4 * 9 * 256          # m [S][F] fp16 + sum-of-squares partials [S][H/16]
+    assert lib.specverify_stack_forward_workspace_bytes(4096, 12288, 17) == 0
+    assert lib.specverify_stack_forward_workspace_bytes(4000, 12288, 9) == 0
+    B, C, D = P(0x20000), P(0x40000), P(0x60000)
+    ok = [A16, A16, A16, A16, A16, A16, 2, 4096, 12288, B, 9, ctypes.c_float(1e-6), NULL, C, D, ws, NULL]
+    def call(**kw):
+        args = list(ok)
+        for k, v in kw.items():
+            args[int(k[1:])] = v
+        return f(*args)
+    assert call(a0=NULL) == 1                           # weights
+    assert call(a13=NULL) == 1                          # norm_out
+    assert call(a6=0) == 2                              # L
+    assert call(a10=17) == 2                            # S
+    assert call(a7=4000) == 2                           # H not a multiple of 512
+    assert call(a11=ctypes.c_float(-1.0)) == 2          # eps
+    assert call(a13=B) == 2                             # norm_out overlaps x
+    assert call(a9=A2) == 3                             # x alignment
+    assert call(a15=ws - 1) == 4                        # workspace
+    assert b"workspace" in lib.specverify_last_error()
+
+
 def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(sv, "_lib", None)
     monkeypatch.setattr(sv, "LIB_PATH", str(tmp_path / "nope.so"))

@@ -1,0 +1,116 @@
+"""GPU parity of specverify_stack (the whole dense stack in two chunked launches per block, its
+RMSNorm carried as per-tile sum-of-squares partials) against the CPU oracle, teacher-forced
+block by block: every block output the library writes to x_layers is compared with the oracle
+block applied to the library's own input of that block."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from weight_bound_verify_amd import specverify as sv
+from weight_bound_verify_amd import synth
+
+from gpu_util import dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_f16(got16, ref64, slack=1e-4):
+    """fp16 outputs: within one fp16 rounding step of the fp64 value plus slack * row rms."""
+    got = got16.astype(np.float64)
+    ulp = np.spacing(np.abs(ref64.astype(np.float16))).astype(np.float64)
+    rms = np.sqrt(np.mean(ref64 * ref64, axis=-1, keepdims=True))
+    err = np.abs(got - ref64)
+    bad = np.argwhere(~(err <= ulp + slack * rms))
+    assert bad.size == 0, f"{len(bad)} outputs outside, first {bad[:3].tolist()} err {err[tuple(bad[0])]}"
+
+
+def _stacked(rng, L, H, F):
+    def w(r, c):
+        return synth.quantize_q8b32(rng.standard_normal((r, c), dtype=np.float32) * np.float32(synth.W_STD))
+    layers = [(w(F, H), w(F, H), w(H, F)) for _ in range(L)]
+    cat = lambda i, j: np.stack([lay[i][j] for lay in layers])
+    return layers, [cat(0, 0), cat(0, 1), cat(1, 0), cat(1, 1), cat(2, 0), cat(2, 1)]
+
+
+def _run(mats, x, L, eps=1e-6, layers_out=True):
+    S, H = x.shape
+    F = mats[0].shape[1]
+    dm = [to_dev(m) for m in mats]
+    xd = to_dev(x)
+    xl = torch.full((L, S, H), float("nan"), dtype=torch.float16, device=dev()) if layers_out else None
+    nrm = torch.full((S, H), float("nan"), dtype=torch.float16, device=dev())
+    ws = sv.workspace(sv.stack_forward_workspace_bytes(H, F, S), dev())
+    sv.stack(*dm, xd, nrm, ws, eps, x_layers=xl)
+    torch.cuda.synchronize()
+    return xd.cpu().numpy(), (xl.cpu().numpy() if layers_out else None), nrm.cpu().numpy()
+
+
+@pytest.mark.parametrize("H,F,S,L", [
+    (512, 1024, 9, 3),      # 4 waves, one chunk (held window rows)
+    (1024, 1536, 16, 2),    # gate/up 8 waves x 1 chunk; down 4 waves x 3 chunks (streamed rows)
+    (2048, 512, 1, 2),
+    (512, 2048, 5, 2),
+    (4096, 12288, 9, 1),    # the dense-stack workload's block shape
+])
+def test_stack_matches_oracle_per_block(H, F, S, L):
+    say(f"stack H={H} F={F} S={S} L={L}")
+    rng = np.random.default_rng(H + 3 * F + S + L)
+    layers, mats = _stacked(rng, L, H, F)
+    x = (synth.fp16_normal(rng, (S, H)).astype(np.float32) * 3).astype(np.float16)
+    x_out, xl, nrm = _run(mats, x, L)
+    assert np.array_equal(x_out, x), "x must be left unchanged when x_layers is given"
+    prev = x
+    for li in range(L):
+        _, parts = oracle.mlp_block(prev, layers[li], return_parts=True)
+        _check_f16(xl[li], prev.astype(np.float64) + parts["y"])
+        assert np.isfinite(xl[li]).all()
+        prev = xl[li]
+    last = xl[L - 1].astype(np.float64)
+    _check_f16(nrm, last / np.sqrt(np.mean(last * last, axis=1, keepdims=True) + 1e-6), slack=1e-5)
+
+
+def test_stack_in_place_is_bit_identical_to_layer_outputs():
+    rng = np.random.default_rng(5)
+    H, F, S, L = 1024, 2048, 9, 4
+    _, mats = _stacked(rng, L, H, F)
+    x = synth.fp16_normal(rng, (S, H))
+    _, xl, n1 = _run(mats, x, L)
+    x_in_place, _, n2 = _run(mats, x, L, layers_out=False)
+    assert np.array_equal(x_in_place, xl[L - 1])
+    assert np.array_equal(n1, n2)
+
+
+def test_stack_depth_variants_bit_identical():
+    """The pipeline depth changes only when loads are issued, never the arithmetic order."""
+    rng = np.random.default_rng(6)
+    H, F, S, L = 2048, 4096, 9, 2
+    _, mats = _stacked(rng, L, H, F)
+    x = synth.fp16_normal(rng, (S, H))
+    try:
+        outs = []
+        for nw, depth in [(8, 2), (8, 4), (4, 2), (4, 4)]:
+            sv.set_tuning(nw, 0, depth)
+            _, xl, nrm = _run(mats, x, L)
+            outs.append((nw, xl, nrm))
+    finally:
+        sv.set_tuning(0, 0, 0)
+    for (nw0, a, na), (nw1, b, nb) in zip(outs, outs[1:]):
+        if nw0 == nw1:
+            assert np.array_equal(a, b) and np.array_equal(na, nb)
+
+
+def test_stack_eps_and_zero_rows():
+    """An all-zero window row stays zero through the blocks (rmsnorm of 0 is 0 with eps > 0)."""
+    rng = np.random.default_rng(8)
+    H, F, S, L = 512, 1024, 4, 2
+    layers, mats = _stacked(rng, L, H, F)
+    x = synth.fp16_normal(rng, (S, H))
+    x[2] = 0
+    _, xl, nrm = _run(mats, x, L, eps=1e-3)
+    assert (xl[:, 2] == 0).all() and (nrm[2] == 0).all()
+    prev = x
+    for li in range(L):
+        m = oracle.mlp_block(prev, layers[li], eps=1e-3, return_parts=True)[1]["m"]
+        _check_f16(xl[li], prev.astype(np.float64) + oracle.linear_q8b32(*layers[li][2], m))
+        prev = xl[li]

@@ -106,11 +106,13 @@ int specverify_profile_next_matmul(hipEvent_t before, hipEvent_t after) {
     return SV_OK;
 }
 
-void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups) {
+void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups, int32_t depth) {
     if (waves_per_group != 0 && waves_per_group != 4 && waves_per_group != 8 && waves_per_group != 16)
         waves_per_group = 0;
     if (max_groups < 0 || max_groups > sv::kGridMax) max_groups = 0;
+    if (depth < 0 || depth > 4) depth = 0;
     sv::set_tuning(waves_per_group, max_groups);
+    sv::set_chunk_tuning(waves_per_group, depth, max_groups);
 }
 
 int specverify_propose(const int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max, int32_t K,
@@ -300,6 +302,95 @@ int specverify_linear_residual_rmsnorm_q8b32(const int8_t* w, const uint16_t* sc
     e = fused ? sv::launch_row_norm(a.kpart0, cfg.ksplit, S, N, residual, y, eps, norm_out, stream)
                        : sv::launch_row_norm(nullptr, 0, S, N, y, nullptr, eps, norm_out, stream);
     return e == hipSuccess ? SV_OK : hip_fail(e, "row norm launch");
+}
+
+namespace {
+
+// Workspace of specverify_stack: m = silu(g) * u [S][F] fp16, then the sum-of-squares
+// partials [S][H/16] fp32, each part 256-byte aligned.
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+size_t stack_m_bytes(int S, int F) { return align256((size_t)2 * S * F); }
+size_t stack_ss_bytes(int S, int H) { return align256((size_t)4 * S * (H / 16)); }
+
+bool stack_shape_ok(int H, int F) {
+    sv::ChunkCfg c;
+    return H >= 512 && F >= 512 && H <= 65536 && F <= 65536 && H % 512 == 0 && F % 512 == 0 &&
+           sv::chunked_config(F, H, sv::EPI_GATEUP, c) && sv::chunked_config(H, F, sv::EPI_STORE, c);
+}
+
+}  // namespace
+
+size_t specverify_stack_forward_workspace_bytes(int32_t H, int32_t F, int32_t S) {
+    if (S < 1 || S > 16 || !stack_shape_ok(H, F)) return 0;
+    return stack_m_bytes(S, F) + stack_ss_bytes(S, H);
+}
+
+int specverify_stack(const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su,
+                     const int8_t* wd, const uint16_t* sd, int32_t L, int32_t H, int32_t F, uint16_t* x,
+                     int32_t S, float eps, uint16_t* x_layers, uint16_t* norm_out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    if (!wg || !sg || !wu || !su || !wd || !sd || !x || !norm_out || !workspace)
+        return fail(SV_ERR_NULL, "weights, scales, x, norm_out and workspace are required");
+    if (L < 1 || L > 4096) return fail(SV_ERR_SHAPE, "L=%d outside [1, 4096]", L);
+    if (S < 1 || S > 16) return fail(SV_ERR_SHAPE, "S=%d outside [1, 16]", S);
+    if (!stack_shape_ok(H, F)) return fail(SV_ERR_SHAPE, "H=%d and F=%d must be multiples of 512 in [512, 65536]", H, F);
+    if (!(eps >= 0.0f)) return fail(SV_ERR_SHAPE, "eps must be >= 0");
+    const void* ptrs16[] = {wg, sg, wu, su, wd, sd, x, norm_out, workspace};
+    for (const void* p : ptrs16)
+        if (!aligned(p, 16)) return fail(SV_ERR_ALIGN, "all buffers must be 16-byte aligned");
+    if (x_layers && !aligned(x_layers, 16)) return fail(SV_ERR_ALIGN, "x_layers must be 16-byte aligned");
+    const size_t rows_bytes = (size_t)2 * S * H;
+    auto overlaps = [](const void* p, size_t pn, const void* q, size_t qn) {
+        const char* a = static_cast<const char*>(p);
+        const char* b = static_cast<const char*>(q);
+        return a < b + qn && b < a + pn;
+    };
+    if (overlaps(norm_out, rows_bytes, x, rows_bytes) ||
+        (x_layers && (overlaps(norm_out, rows_bytes, x_layers, rows_bytes * L) ||
+                      overlaps(x, rows_bytes, x_layers, rows_bytes * L))))
+        return fail(SV_ERR_SHAPE, "norm_out, x and x_layers must not overlap");
+    const size_t need = specverify_stack_forward_workspace_bytes(H, F, S);
+    if (workspace_bytes < need) return fail(SV_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+    if (int st = check_device()) return st;
+
+    sv::ChunkCfg cg, cd;
+    sv::chunked_config(F, H, sv::EPI_GATEUP, cg);
+    sv::chunked_config(H, F, sv::EPI_STORE, cd);
+    uint16_t* m = static_cast<uint16_t*>(workspace);
+    float* ss = reinterpret_cast<float*>(static_cast<char*>(workspace) + stack_m_bytes(S, F));
+
+    hipError_t e = sv::launch_row_ss(x, S, H, ss, stream);
+    if (e != hipSuccess) return hip_fail(e, "row sum-of-squares launch");
+    const uint16_t* cur = x;
+    for (int l = 0; l < L; ++l) {
+        uint16_t* out = x_layers ? x_layers + (size_t)l * S * H : x;
+        sv::ChunkArgs g{};
+        g.w0 = wg + (size_t)l * F * H;
+        g.s0 = sg + (size_t)l * F * (H / SV_BLOCK);
+        g.w1 = wu + (size_t)l * F * H;
+        g.s1 = su + (size_t)l * F * (H / SV_BLOCK);
+        g.x = cur;
+        g.norm_ss = ss;
+        g.norm_tiles = H / 16;
+        g.eps = eps;
+        g.V = F; g.H = H; g.S = S; g.nb = H / SV_BLOCK; g.nitems = cg.items; g.nkc = cg.nkc;
+        g.y = m;
+        e = sv::launch_chunked(sv::EPI_GATEUP, cg, g, stream);
+        if (e != hipSuccess) return hip_fail(e, "stack gate/up launch");
+        sv::ChunkArgs d{};
+        d.w0 = wd + (size_t)l * H * F;
+        d.s0 = sd + (size_t)l * H * (F / SV_BLOCK);
+        d.x = m;
+        d.V = H; d.H = F; d.S = S; d.nb = F / SV_BLOCK; d.nitems = cd.items; d.nkc = cd.nkc;
+        d.y = out;
+        d.residual = cur;
+        d.ss_out = ss;
+        e = sv::launch_chunked(sv::EPI_STORE, cd, d, stream);
+        if (e != hipSuccess) return hip_fail(e, "stack down launch");
+        cur = out;
+    }
+    e = sv::launch_apply_norm(cur, ss, S, H, eps, norm_out, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "final norm launch");
 }
 
 }  // extern "C"

@@ -1,0 +1,471 @@
+// Chunked streaming q8b32 matmul for the weight-bound dense stack, and the row passes that
+// carry its RMSNorm between layers.
+//
+// Page: "Flagship dramatic-speedup plan - the full stackable tuning set", sections "Baseline
+// byte model" (a decode step reads every weight byte once; its time is bytes / bandwidth) and
+// "Axis 4" (the RMSNorm fused into the neighbouring kernels).  The contraction and its MFMA
+// mapping are those of the head matmul (int8 codes of one 32-block -> exact fp16, one
+// v_mfma_f32_16x16x32_f16 per block and 16 rows, block scale applied in fp32):
+//   out[s, v] = sum_b f32(scale[v, b]) * sum_{k in block b} f32(w[v, k]) * f32(x[s, k])
+//
+// Why another kernel: a stack projection streams only 50-110 MB, so a launch lasts 10-25 us
+// and its ramp-up and drain are a large share of it.  Here a workgroup of NW waves walks a
+// flat sequence of load units, one unit = one 16-row tile x one chunk of the hidden axis in
+// which every wave owns one 128-byte segment (4 blocks) of each of the 16 rows.  Each wave
+// keeps DEPTH units in flight in a ring of registers and issues the next unit as soon as it
+// has consumed one, so loads leave at an even rate from the first to the last unit; the
+// per-tile cross-wave reduction happens after the tile's last chunk.  The window rows are
+// held in registers for the whole launch when the hidden axis has at most two chunks
+// (HOLD), and are otherwise loaded with each unit from L2 (they are a few hundred KB, read
+// by every workgroup).
+//
+// The stack's RMSNorm never gets a launch of its own: the down projection's epilogue adds
+// the residual, stores the fp16 stream and writes, per 16-column tile, the sum of squares
+// of the stored values; the next gate/up launch reduces those partials in a fixed order to
+// 1/sqrt(mean + eps) per row and normalises its window rows as it loads them.
+#include "sv_device.h"
+#include "sv_internal.h"
+
+#include <climits>
+#include <cmath>
+#include <mutex>
+
+namespace sv {
+
+namespace {
+
+constexpr int kUnitBytes = 2048;        // one wave's unit: 16 rows x 128 bytes
+
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Tile row n (0..15) of item `it`: 16 rows of one matrix, or for gate/up 8 gate rows (n < 8)
+// and the same 8 rows of the up matrix (n >= 8).
+template <int EPI>
+__device__ __forceinline__ int crow(int it, int n) {
+    return EPI == EPI_GATEUP ? it * 8 + (n & 7) : it * kTileRows + n;
+}
+
+// 1 / sqrt(sum_t ss[s][t] / H + eps) for the window rows s of this workgroup, summed in a
+// fixed order (per lane sequentially over t = lane, lane+64, ..., then a fixed butterfly),
+// so every workgroup and the final norm pass get the same value.  Written to inv[s].
+template <int NW>
+__device__ __forceinline__ void norm_scales(const float* __restrict__ ss, int nt, int S, int H, float eps, int wave,
+                                            int lane, float* inv) {
+    constexpr int kPer = 8;          // partials per lane per pass, all loads issued before the sums
+    for (int s = wave; s < S; s += NW) {
+        float t = 0.f;
+        for (int base = 0; base < nt; base += kPer * kWave) {
+            float v[kPer];
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = base + j * kWave + lane;
+                v[j] = i < nt ? ss[(size_t)s * nt + i] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) t += v[j];
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, kWave);
+        if (lane == 0) inv[s] = 1.0f / sqrtf(t / (float)H + eps);
+    }
+}
+
+__device__ __forceinline__ f16x8 scale_f16x8(f16x8 h, float f) {
+    f16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (_Float16)((float)h[e] * f);
+    return r;
+}
+
+// Raw buffer view of `bytes` bytes at p: 32-bit offsets from a scalar base, and loads past
+// the end return zeros (tail rows of the last tile need no clamping).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_view(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kAuxNT = 2;        // non-temporal: the weights are read once
+constexpr uint32_t kPastEnd = 0xF0000000u;   // an offset beyond every view (views are < 2^31 bytes)
+
+template <int HOLD>
+struct Unit {
+    u32x4 w[2];                       // [row half]: 16 bytes of rows 8h + lane/8
+    u32x2 sc, sc2;                    // fp16 scales of the lane's row, 4 blocks (gate/up: gate | up, one is zero)
+    f16x8 hid[HOLD ? 1 : 4];          // window rows of the unit's 4 blocks (streamed mode)
+};
+// Nothing is computed from a unit's registers until the unit is consumed: an instruction
+// that used a just-issued load would wait for every older load too.
+
+// Every wave issues the same sequence of memory instructions whatever the data: loads past a
+// workgroup's last unit and stores of rows past S read zeros / are dropped by the buffer
+// bounds check instead of being skipped by a branch.  The compiler's wait counts are then
+// exact, so waiting for the oldest unit of the ring never drains the younger ones.
+//
+// HOLD = 1 or 2: the hidden axis has exactly HOLD chunks, the window rows stay in registers,
+// and one ring cycle of DEPTH units covers DEPTH / HOLD whole tiles.  HOLD = 0: any number of
+// chunks (a multiple of DEPTH), window rows loaded with each unit, one cycle = DEPTH chunks of
+// one tile.
+template <int NW, int DEPTH, int HOLD, int EPI>
+__global__ __launch_bounds__(NW * 64) void q8b32_chunked(ChunkArgs a) {
+    static_assert(HOLD == 0 || DEPTH % HOLD == 0, "a ring cycle must cover whole tiles");
+    static_assert(16 % NW == 0 || NW == 16, "epilogue rows per wave");
+    constexpr int RPW = 16 / NW;                  // window rows each wave finishes per tile
+    __shared__ f32x4 red[2][NW][kWave];
+    __shared__ __attribute__((aligned(16))) uint8_t xch[NW][2][kUnitBytes];
+    __shared__ float inv_s[kTileRows];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15, g = lane >> 4;
+    const int lrow = lane >> 3, lchunk = lane & 7;
+    const int nkc = HOLD ? HOLD : a.nkc;
+    const int step = gridDim.x;
+    const int my_items = (int)blockIdx.x < a.nitems ? (a.nitems - 1 - (int)blockIdx.x) / step + 1 : 0;
+    const bool row_ok = n < a.S;       // lanes whose A-operand row is a real window row
+
+    const uint32_t wbytes = (uint32_t)a.V * (uint32_t)a.H;
+    const uint32_t sbytes = (uint32_t)a.V * (uint32_t)a.nb * 2u;
+    const __amdgpu_buffer_rsrc_t rw0 = buf_view(a.w0, wbytes), rs0 = buf_view(a.s0, sbytes);
+    const __amdgpu_buffer_rsrc_t rw1 = buf_view(EPI == EPI_GATEUP ? a.w1 : a.w0, wbytes);
+    const __amdgpu_buffer_rsrc_t rs1 = buf_view(EPI == EPI_GATEUP ? a.s1 : a.s0, sbytes);
+    const __amdgpu_buffer_rsrc_t rx = buf_view(a.x, (uint32_t)a.S * (uint32_t)a.H * 2u);
+    // per-lane parts of the offsets: weight row within the tile half, window row
+    const uint32_t wlane = (uint32_t)lrow * (uint32_t)a.H + 16u * lchunk;
+    const uint32_t xlane = row_ok ? ((uint32_t)n * (uint32_t)a.H + 8u * g) * 2u : kPastEnd;  // rows >= S read zeros
+    const bool srow_up = EPI == EPI_GATEUP && n >= 8;
+
+    // Unit (k-th tile of this workgroup, chunk c); k >= my_items loads zeros.
+    auto load = [&](Unit<HOLD>& r, int k, int c) {
+        const bool live = k < my_items;
+        const int it = (int)blockIdx.x + k * step;
+        const int blk0 = c * (NW * 4) + wave * 4;
+        // tile half h covers weight rows base_h .. base_h + 7 (gate/up: 8 gate rows, then the same 8 up rows)
+        const uint32_t base0 = (uint32_t)(EPI == EPI_GATEUP ? it * 8 : it * kTileRows);
+        const uint32_t base1 = EPI == EPI_GATEUP ? base0 : base0 + 8u;
+        const uint32_t kofs = (uint32_t)blk0 * kBlock;
+        const uint32_t o0 = live ? base0 * (uint32_t)a.H + kofs + wlane : kPastEnd;
+        const uint32_t o1 = live ? base1 * (uint32_t)a.H + kofs + wlane : kPastEnd;
+        r.w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw0, (int)o0, 0, kAuxNT));
+        r.w[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw1, (int)o1, 0, kAuxNT));
+        const uint32_t srow = (uint32_t)crow<EPI>(it, n);
+        const uint32_t sofs = live ? (srow * (uint32_t)a.nb + (uint32_t)blk0) * 2u : kPastEnd;
+        if constexpr (EPI == EPI_GATEUP) {
+            // both descriptors stay uniform: each lane reads its own matrix and gets zeros
+            // (an offset past the end) from the other
+            r.sc = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                 rs0, (int)(srow_up ? kPastEnd : sofs), 0, 0));
+            r.sc2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                  rs1, (int)(srow_up ? sofs : kPastEnd), 0, 0));
+        } else {
+            r.sc = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs0, (int)sofs, 0, 0));
+        }
+        if constexpr (!HOLD) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                r.hid[b] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rx, (int)(xlane + (uint32_t)(blk0 + b) * kBlock * 2u), 0, 0));
+        }
+    };
+
+    // ---- prologue: ring, held window rows, then the norm (its loads are the youngest) ----
+    Unit<HOLD> ring[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+        if constexpr (HOLD > 0) load(ring[d], d / HOLD, d % HOLD);
+        else load(ring[d], 0, d);
+    }
+    f16x8 hold[HOLD ? HOLD : 1][4];
+    if constexpr (HOLD > 0) {
+#pragma unroll
+        for (int c = 0; c < HOLD; ++c)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                hold[c][b] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           rx, (int)(xlane + (uint32_t)(c * NW * 4 + wave * 4 + b) * kBlock * 2u),
+                                                           0, 0));
+    }
+    float inv = 1.0f;
+    if (a.norm_ss) {
+        norm_scales<NW>(a.norm_ss, a.norm_tiles, a.S, a.H, a.eps, wave, lane, inv_s);
+        lds_sync();
+        if (row_ok) inv = inv_s[n];
+        if constexpr (HOLD > 0) {
+#pragma unroll
+            for (int c = 0; c < HOLD; ++c)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) hold[c][b] = scale_f16x8(hold[c][b], inv);
+        }
+    }
+
+    // ---- distributed epilogue: wave w finishes window rows w, w + NW, ... of every tile --
+    const uint32_t out_elems = (uint32_t)a.S * (uint32_t)a.V;
+    const __amdgpu_buffer_rsrc_t ry = buf_view(a.y, a.y ? out_elems * 2u : 0u);
+    const __amdgpu_buffer_rsrc_t rres = buf_view(a.residual, a.residual ? out_elems * 2u : 0u);
+    const __amdgpu_buffer_rsrc_t rlog = buf_view(a.logits, a.logits ? out_elems * 4u : 0u);
+    const __amdgpu_buffer_rsrc_t rss = buf_view(a.ss_out, a.ss_out ? (uint32_t)a.S * (uint32_t)a.nitems * 4u : 0u);
+    float best_v[RPW];
+    int best_i[RPW];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) { best_v[j] = -INFINITY; best_i[j] = INT_MAX; }
+
+    auto finish_tile = [&](const f32x4& acc, int k, int buf) {
+        red[buf][wave][lane] = acc;
+        lds_sync();
+        const int it = (int)blockIdx.x + k * step;
+        const bool live = k < my_items;
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+            const int s = wave + j * NW;                       // window row (compile-time count)
+            const float* col = reinterpret_cast<const float*>(&red[buf][0][n + 16 * (s >> 2)]) + (s & 3);
+            float val = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) val += col[w * kWave * 4];
+            const int v = crow<EPI>(it, n);
+            const bool ok = live && lane < 16 && s < a.S && v < a.V;
+            if constexpr (EPI == EPI_GATEUP) {
+                const float up = __shfl_xor(val, 8, 16);
+                const float out = val / (1.0f + expf(-val)) * up;
+                const uint32_t off = ok && n < 8 ? ((uint32_t)s * a.V + v) * 2u : kPastEnd;
+                __builtin_amdgcn_raw_buffer_store_b16(f2h(out), ry, (int)off, 0, 0);
+            } else if constexpr (EPI == EPI_HEAD) {
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rlog,
+                                                      (int)(ok ? ((uint32_t)s * a.V + v) * 4u : kPastEnd), 0, 0);
+                if (ok && val > best_v[j]) { best_v[j] = val; best_i[j] = v; }
+            } else {
+                const uint32_t off = ok ? ((uint32_t)s * a.V + v) * 2u : kPastEnd;
+                val += h2f(__builtin_amdgcn_raw_buffer_load_b16(rres, (int)off, 0, 0));    // zero without a residual
+                const uint16_t hv = f2h(val);
+                __builtin_amdgcn_raw_buffer_store_b16(hv, ry, (int)off, 0, 0);
+                const float q = ok ? h2f(hv) : 0.f;
+                float sq = q * q;
+#pragma unroll
+                for (int o = 8; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 16);
+                const bool first = ok && n == 0;
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sq), rss,
+                                                      (int)(first ? ((uint32_t)s * a.nitems + it) * 4u : kPastEnd), 0, 0);
+            }
+        }
+    };
+
+    // ---- consume one unit: LDS exchange into the MFMA layout, 4 blocks -------------------
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    auto consume = [&](const Unit<HOLD>& cur, int slot, const f16x8 (&aops)[4], f32x4& acc) {
+        uint8_t* xs = xch[wave][slot];
+        // exchange: tile row r lands at r*128, 16-byte chunks XOR-swizzled by row
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = 8 * h + lrow;
+            *reinterpret_cast<u32x4*>(xs + row * 128 + 16 * (lchunk ^ (row & 7))) = cur.w[h];
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int chunk = 2 * b + (g >> 1);
+            const u32x2 q8 = *reinterpret_cast<const u32x2*>(xs + n * 128 + 16 * (chunk ^ (n & 7)) + 8 * (g & 1));
+            const f16x8 bop = i8x8_to_f16x8(q8);
+            const u32x2 scw = EPI == EPI_GATEUP ? (cur.sc | cur.sc2) : cur.sc;
+            const float sc = h2f((uint16_t)(scw[b >> 1] >> (16 * (b & 1))));
+            const f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(aops[b], bop, zero, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(sc, dd[r], acc[r]);
+            if constexpr (NW == 16) __builtin_amdgcn_sched_barrier(0);   // bound live temporaries at 16 waves
+        }
+    };
+
+    if constexpr (HOLD > 0) {
+        constexpr int TPC = DEPTH / HOLD;                // tiles per ring cycle
+        const int ncycles = (my_items + TPC - 1) / TPC;
+        for (int cy = 0; cy < ncycles; ++cy) {
+            f32x4 acc = zero;
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int k = cy * TPC + d / HOLD;
+                consume(ring[d], d & 1, hold[d % HOLD], acc);
+                load(ring[d], k + TPC, d % HOLD);        // the same slot, one cycle ahead
+                if (d % HOLD == HOLD - 1) {
+                    finish_tile(acc, k, k & 1);
+                    acc = zero;
+                }
+            }
+        }
+    } else {
+        for (int k = 0; k < my_items; ++k) {
+            f32x4 acc = zero;
+            for (int c0 = 0; c0 < nkc; c0 += DEPTH) {
+#pragma unroll
+                for (int d = 0; d < DEPTH; ++d) {
+                    f16x8 aops[4];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) aops[b] = a.norm_ss ? scale_f16x8(ring[d].hid[b], inv) : ring[d].hid[b];
+                    consume(ring[d], d & 1, aops, acc);
+                    const int c = c0 + d + DEPTH;         // the same slot, DEPTH units ahead
+                    const bool next = c >= nkc;
+                    load(ring[d], next ? k + 1 : k, next ? c - nkc : c);
+                }
+            }
+            finish_tile(acc, k, k & 1);
+        }
+    }
+
+    if constexpr (EPI == EPI_HEAD) {
+        const __amdgpu_buffer_rsrc_t rpv = buf_view(a.part_val, (uint32_t)a.S * kGridMax * 4u);
+        const __amdgpu_buffer_rsrc_t rpi = buf_view(a.part_idx, (uint32_t)a.S * kGridMax * 4u);
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+            float bv = best_v[j];
+            int bi = best_i[j];
+            argmax_group<16>(bv, bi);
+            const int s = wave + j * NW;
+            const uint32_t off = lane == 0 && s < a.S ? ((uint32_t)s * kGridMax + blockIdx.x) * 4u : kPastEnd;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, bv), rpv, (int)off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)bi, rpi, (int)off, 0, 0);
+        }
+    }
+}
+
+// ss[s][t] = sum over the 16 columns of tile t of fp16(x[s, k])^2, in column order: the
+// partials of a stream that did not come out of a down projection (the stack's input).
+__global__ __launch_bounds__(256) void row_ss_kernel(const uint16_t* __restrict__ x, int S, int H,
+                                                     float* __restrict__ ss) {
+    const int nt = H / kTileRows;
+    const int s = blockIdx.y;
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (s >= S || t >= nt) return;
+    const uint16_t* p = x + (size_t)s * H + (size_t)t * kTileRows;
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kTileRows; ++k) {
+        const float q = h2f(p[k]);
+        acc = __builtin_fmaf(q, q, acc);
+    }
+    ss[(size_t)s * nt + t] = acc;
+}
+
+// out[s, k] = fp16(x[s, k] * inv[s]) with inv from the ss partials exactly as the gate/up
+// prologue computes it.  One workgroup per window row.
+__global__ __launch_bounds__(256) void apply_norm_kernel(const uint16_t* __restrict__ x, const float* __restrict__ ss,
+                                                         int S, int H, float eps, uint16_t* __restrict__ out) {
+    __shared__ float inv_s[kTileRows];
+    const int s = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the same fixed summation order as the gate/up prologue (norm_scales), for row s only
+    if (wave == 0) norm_scales<1>(ss + (size_t)s * (H / kTileRows), H / kTileRows, 1, H, eps, 0, lane, inv_s);
+    __syncthreads();
+    const float inv = inv_s[0];
+    for (int k = threadIdx.x; k < H; k += 256) out[(size_t)s * H + k] = f2h(h2f(x[(size_t)s * H + k]) * inv);
+}
+
+typedef void (*ChunkFn)(ChunkArgs);
+
+// (waves, hold, depth) -> kernel; hold = 0 streams the window rows with each unit.  Only
+// shapes that compile without register spills on gfx950 are instantiated.
+template <int EPI>
+ChunkFn pick_chunked(int nw, int hold, int depth) {
+#define SV_CH(NW, HOLD, DEPTH) \
+    if (nw == NW && hold == HOLD && depth == DEPTH) return q8b32_chunked<NW, DEPTH, HOLD, EPI>;
+    SV_CH(16, 0, 2) SV_CH(16, 1, 2) SV_CH(16, 1, 4) SV_CH(16, 2, 2)
+    SV_CH(8, 0, 2) SV_CH(8, 0, 3) SV_CH(8, 0, 4) SV_CH(8, 1, 2) SV_CH(8, 1, 4) SV_CH(8, 2, 2) SV_CH(8, 2, 4)
+    SV_CH(4, 0, 2) SV_CH(4, 0, 3) SV_CH(4, 0, 4) SV_CH(4, 1, 4) SV_CH(4, 2, 4)
+#undef SV_CH
+    return nullptr;
+}
+
+ChunkFn chunked_fn(int epi, int nw, int hold, int depth) {
+    if (epi == EPI_HEAD) return pick_chunked<EPI_HEAD>(nw, hold, depth);
+    if (epi == EPI_STORE) return pick_chunked<EPI_STORE>(nw, hold, depth);
+    return pick_chunked<EPI_GATEUP>(nw, hold, depth);
+}
+
+int chunked_resident(ChunkFn fn, int nw) {
+    struct Entry { ChunkFn fn; int dev; int groups; };
+    static Entry cache[32];
+    static int used = 0;
+    static std::mutex mu;
+    int dev = -1;
+    const int fallback = nw >= 16 ? 256 : 512;
+    if (hipGetDevice(&dev) != hipSuccess) return fallback;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].fn == fn && cache[i].dev == dev) return cache[i].groups;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), nw * 64, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 ||
+        cus < 1) {
+        (void)hipGetLastError();
+        return fallback;
+    }
+    if (used < 32) cache[used++] = Entry{fn, dev, per_cu * cus};
+    return per_cu * cus;
+}
+
+}  // namespace
+
+namespace {
+int g_chunk_nw = 0;       // tuning overrides, 0 = automatic
+int g_chunk_depth = 0;
+int g_grid_override_chunk = 0;
+}  // namespace
+
+void set_chunk_tuning(int waves, int depth, int max_groups) {
+    g_chunk_nw = waves;
+    g_chunk_depth = depth;
+    g_grid_override_chunk = max_groups;
+}
+
+bool chunked_config(int rows, int H, int epi, ChunkCfg& c) {
+    const int nb = H / kBlock;
+    if (H % kBlock || nb % 4) return false;
+    if ((uint64_t)rows * (uint64_t)H >= (1ull << 31)) return false;     // 32-bit buffer offsets
+    const int segs = nb / 4;
+    // measured preference: the streamed-row down projection is fastest at 8 waves, the
+    // held-row shapes at 16
+    const int pref[2][3] = {{16, 8, 4}, {8, 16, 4}};
+    for (int nw : pref[epi == EPI_STORE ? 1 : 0]) {
+        if (segs % nw) continue;
+        if (g_chunk_nw && nw != g_chunk_nw) continue;
+        c.nw = nw;
+        c.nkc = segs / nw;
+        c.hold = c.nkc <= 2 ? c.nkc : 0;
+        // deepest ring that compiles without spills at this width (see pick_chunked)
+        // held rows: 4 units in flight; streamed rows: the deepest ring that divides the chunks
+        auto fits = [&](int d) { return chunked_fn(epi, nw, c.hold, d) && (c.hold || c.nkc % d == 0); };
+        int depth = 0;
+        for (int d : {4, 3, 2})
+            if (!depth && fits(d)) depth = d;
+        if (g_chunk_depth && fits(g_chunk_depth)) depth = g_chunk_depth;       // else automatic
+        if (!depth) continue;
+        c.depth = depth;
+        const int items = epi == EPI_GATEUP ? (rows + 7) / 8 : (rows + kTileRows - 1) / kTileRows;
+        int cap = chunked_resident(chunked_fn(epi, nw, c.hold, depth), nw);
+        if (g_grid_override_chunk > 0) cap = g_grid_override_chunk;
+        if (cap > kGridMax) cap = kGridMax;
+        const int per = (items + cap - 1) / cap;
+        c.grid = (items + per - 1) / per;
+        c.items = items;
+        return true;
+    }
+    return false;
+}
+
+hipError_t launch_chunked(int epi, const ChunkCfg& c, const ChunkArgs& a, hipStream_t stream) {
+    ChunkFn fn = chunked_fn(epi, c.nw, c.hold, c.depth);
+    if (!fn) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(fn, dim3(c.grid), dim3(c.nw * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_ss(const uint16_t* x, int S, int H, float* ss, hipStream_t stream) {
+    const int nt = H / kTileRows;
+    hipLaunchKernelGGL(row_ss_kernel, dim3((nt + 255) / 256, S), dim3(256), 0, stream, x, S, H, ss);
+    return hipGetLastError();
+}
+
+hipError_t launch_apply_norm(const uint16_t* x, const float* ss, int S, int H, float eps, uint16_t* out,
+                             hipStream_t stream) {
+    hipLaunchKernelGGL(apply_norm_kernel, dim3(S), dim3(256), 0, stream, x, ss, S, H, eps, out);
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -651,7 +651,10 @@ GemmCfg gemm_config(int rows, int H, int S, int epi) {
     int cap = g_grid_override ? g_grid_override : resident_groups(epi, c) / c.ksplit;
     if (cap < 1) cap = 1;
     if (cap > kGridMax) cap = kGridMax;
-    c.grid = items < cap ? (items > 0 ? items : 1) : cap;
+    // Balanced: every workgroup gets the same number of items (+-1 only when the items do not
+    // divide), so no single workgroup runs an extra item after the others have finished.
+    const int per = (items + cap - 1) / cap;
+    c.grid = items > 0 ? (items + per - 1) / per : 1;
     return c;
 }
 

@@ -70,4 +70,41 @@ constexpr int kRowNormMaxSplit = 8;
 hipError_t launch_row_norm(const float* part, int ks, int S, int N, const uint16_t* residual, uint16_t* y,
                            float eps, uint16_t* norm_out, hipStream_t stream);
 
+// Chunked streaming matmul (dense stack, and heads whose hidden axis splits into whole 128-byte
+// wave segments): see sv_chunked.hip.  Window rows S <= 16.
+struct ChunkArgs {
+    const int8_t* w0;          // [V][H] (gate rows for EPI_GATEUP)
+    const uint16_t* s0;
+    const int8_t* w1;          // EPI_GATEUP: up projection
+    const uint16_t* s1;
+    const uint16_t* x;         // [S][H] fp16 window rows (before the norm when norm_ss is set)
+    const float* norm_ss;      // [S][norm_tiles] sum-of-squares partials of x, or null (no norm)
+    int norm_tiles;
+    float eps;
+    int V, H, S, nb, nitems, nkc;
+    float* part_val;           // EPI_HEAD: per-workgroup argmax partials [S][kGridMax]
+    int* part_idx;
+    float* logits;             // EPI_HEAD: [S][V] or null
+    uint16_t* y;               // EPI_STORE / EPI_GATEUP: [S][V] fp16
+    const uint16_t* residual;  // EPI_STORE: [S][V] fp16 or null
+    float* ss_out;             // EPI_STORE: [S][nitems] sum of squares of each stored 16-column tile, or null
+};
+struct ChunkCfg {
+    int nw;       // waves per workgroup (16, 8 or 4)
+    int nkc;      // hidden-axis chunks per tile (chunk = nw x 128 bytes)
+    int hold;     // nkc when the window rows stay in registers (nkc <= 2), else 0 (streamed with each unit)
+    int depth;    // load units in flight per wave
+    int grid;     // workgroups
+    int items;    // tiles (16 rows; gate/up: 8 row pairs)
+};
+void set_chunk_tuning(int waves, int depth, int max_groups);
+// False when H is not a whole number of 4-block segments for 4, 8 or 16 waves.
+bool chunked_config(int rows, int H, int epi, ChunkCfg& c);
+hipError_t launch_chunked(int epi, const ChunkCfg& c, const ChunkArgs& a, hipStream_t stream);
+// ss[s][t] = sum of squares of the 16 fp16 values of x[s][16t .. 16t+15]
+hipError_t launch_row_ss(const uint16_t* x, int S, int H, float* ss, hipStream_t stream);
+// out = fp16(x * inv[s]), inv from the ss partials as the chunked gate/up prologue computes it
+hipError_t launch_apply_norm(const uint16_t* x, const float* ss, int S, int H, float eps, uint16_t* out,
+                             hipStream_t stream);
+
 }  // namespace sv

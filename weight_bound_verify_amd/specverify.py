@@ -29,7 +29,8 @@ EXPORTS = (
     "specverify_propose", "specverify_verify_workspace_bytes", "specverify_verify", "specverify_round",
     "specverify_accept",
     "specverify_rmsnorm", "specverify_stack_workspace_bytes", "specverify_gateup_silu_q8b32",
-    "specverify_linear_q8b32", "specverify_linear_residual_rmsnorm_q8b32", "specverify_set_tuning", "specverify_profile_next_matmul", "specverify_status_string", "specverify_last_error",
+    "specverify_linear_q8b32", "specverify_linear_residual_rmsnorm_q8b32",
+    "specverify_stack_forward_workspace_bytes", "specverify_stack", "specverify_set_tuning", "specverify_profile_next_matmul", "specverify_status_string", "specverify_last_error",
 )
 
 _lib = None
@@ -63,7 +64,10 @@ def load():
         "specverify_linear_q8b32": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
         "specverify_linear_residual_rmsnorm_q8b32": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, ctypes.c_float, _P, _P,
                                                           ctypes.c_size_t, _P]),
-        "specverify_set_tuning": (None, [_I, _I]),
+        "specverify_stack_forward_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+        "specverify_stack": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I, ctypes.c_float, _P, _P, _P,
+                                  ctypes.c_size_t, _P]),
+        "specverify_set_tuning": (None, [_I, _I, _I]),
         "specverify_profile_next_matmul": (_I, [_P, _P]),
         "specverify_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "specverify_last_error": (ctypes.c_char_p, []),
@@ -119,8 +123,8 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
 
 
-def set_tuning(waves_per_group: int = 0, max_groups: int = 0) -> None:
-    load().specverify_set_tuning(int(waves_per_group), int(max_groups))
+def set_tuning(waves_per_group: int = 0, max_groups: int = 0, depth: int = 0) -> None:
+    load().specverify_set_tuning(int(waves_per_group), int(max_groups), int(depth))
 
 
 def profile_next_matmul(before, after, stream=None) -> None:
@@ -222,3 +226,26 @@ def linear_residual_rmsnorm(w, scale, x, y, norm_out, residual=None, eps: float 
         _ptr(residual, torch.float16, "residual", S * N), _ptr(y, torch.float16, "y", S * N), float(eps),
         _ptr(norm_out, torch.float16, "norm_out", S * N), _ptr(ws, torch.uint8, "workspace"),
         0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def stack_forward_workspace_bytes(H: int, F: int, S: int) -> int:
+    return int(load().specverify_stack_forward_workspace_bytes(H, F, S))
+
+
+def stack(wg, sg, wu, su, wd, sd, x, norm_out, ws, eps: float = 1e-6, x_layers=None, stream=None) -> None:
+    """The dense stack: L x [rmsnorm -> gate/up SiLU*mul -> down + residual], then
+    norm_out = rmsnorm(x).  wg/wu [L, F, H], wd [L, H, F] int8 with fp16 block scales; x [S, H]
+    is updated in place unless ``x_layers`` [L, S, H] receives every block's output."""
+    L, F, H = wg.shape
+    S = x.shape[0]
+    if (tuple(wu.shape) != (L, F, H) or tuple(wd.shape) != (L, H, F) or tuple(sg.shape) != (L, F, H // SV_BLOCK)
+            or tuple(su.shape) != (L, F, H // SV_BLOCK) or tuple(sd.shape) != (L, H, F // SV_BLOCK)
+            or tuple(x.shape) != (S, H) or tuple(norm_out.shape) != (S, H)):
+        raise ValueError("shape mismatch")
+    if x_layers is not None and tuple(x_layers.shape) != (L, S, H):
+        raise ValueError("x_layers must be [L, S, H]")
+    _check(load().specverify_stack(
+        _ptr(wg, torch.int8, "wg"), _ptr(sg, torch.float16, "sg"), _ptr(wu, torch.int8, "wu"),
+        _ptr(su, torch.float16, "su"), _ptr(wd, torch.int8, "wd"), _ptr(sd, torch.float16, "sd"), L, H, F,
+        _ptr(x, torch.float16, "x"), S, float(eps), _ptr(x_layers, torch.float16, "x_layers"),
+        _ptr(norm_out, torch.float16, "norm_out"), _ptr(ws, torch.uint8, "workspace"), ws.numel(), _stream(stream)))
