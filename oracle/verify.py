@@ -228,7 +228,7 @@ def greedy_decode(context, hidden_fn, argmax_fn, n_new: int) -> list[int]:
 
 
 def spec_decode(context, hidden_fn, argmax_fn, n_new: int, K: int, n_max: int,
-                drafter=None, stats: dict | None = None) -> list[int]:
+                drafter=None, stats: dict | None = None, gate_after: int = 0) -> list[int]:
     """Greedy speculative decoding with the fused S=K+1 window.
 
     a0 bootstrap (hybrid verify-design page, hybrid state discipline and status: one probe
@@ -236,6 +236,11 @@ def spec_decode(context, hidden_fn, argmax_fn, n_new: int, K: int, n_max: int,
     propose past a0, one verify of [a0, d_1..d_K] (pads feed token 0), accept, commit
     1 + j tokens.  ``drafter(tokens, K)`` overrides the n-gram drafter.  Stops once at least
     ``n_new`` tokens beyond the context are committed; returns exactly that many.
+
+    ``gate_after`` > 0: the hit-rate gate of the feasibility page ("SHIPPED" note: the app
+    drops the drafter after a number of zero-accept rounds).  Reading: once ``gate_after``
+    consecutive rounds have accepted no draft, the drafter is dropped for the rest of the
+    sequence and every later window holds only pads.  The committed stream is unchanged.
     """
     toks = [int(t) for t in context]
     target = len(toks) + n_new
@@ -243,8 +248,12 @@ def spec_decode(context, hidden_fn, argmax_fn, n_new: int, K: int, n_max: int,
     forwards = 1
     index = NgramIndex(n_max)
     js = []
+    zero_run = 0
+    gated_at = None
     while len(toks) < target:
-        if drafter is None:
+        if gated_at is not None:
+            drafts = [PAD] * K
+        elif drafter is None:
             drafts, _, _ = index.propose(toks, K)
         else:
             drafts = [int(x) for x in drafter(toks, K)]
@@ -255,7 +264,11 @@ def spec_decode(context, hidden_fn, argmax_fn, n_new: int, K: int, n_max: int,
         j, app = accept(a, drafts)
         js.append(j)
         toks.extend(app)
+        zero_run = zero_run + 1 if j == 0 else 0
+        if gate_after > 0 and gated_at is None and zero_run >= gate_after:
+            gated_at = len(js)
     if stats is not None:
         stats["forwards"] = forwards
         stats["accepted"] = js
+        stats["gated_after_round"] = gated_at
     return toks[:target]

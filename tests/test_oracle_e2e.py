@@ -97,3 +97,50 @@ def test_verify_window_equals_sequential_single_row_argmaxes():
     a = oracle.argmax_lowest(oracle.head_logits(q, s, h))
     seq = [int(oracle.argmax_lowest(oracle.head_logits(q, s, h[i:i + 1]))[0]) for i in range(9)]
     assert list(a) == seq
+
+
+def test_hit_rate_gate_is_lossless_and_drops_the_drafter():
+    """Gating never changes the committed stream (it equals greedy decoding), and once it
+    fires every later round commits exactly one token (feasibility page, SHIPPED note)."""
+    n_gated = 0
+    for c, (ctx, hidden_fn, argmax_fn, n_new, K, n_max) in enumerate(_cases(400, 4321)):
+        g = 1 + c % 4
+        st = {}
+        ref = oracle.greedy_decode(ctx, hidden_fn, argmax_fn, n_new)
+        got = oracle.spec_decode(ctx, hidden_fn, argmax_fn, n_new, K, n_max, stats=st, gate_after=g)
+        assert got == ref
+        js, at = st["accepted"], st["gated_after_round"]
+        if at is not None:
+            n_gated += 1
+            assert js[at - g:at] == [0] * g                 # the g zero-accept rounds that fired it
+            assert all(j == 0 for j in js[at:])             # pads are never accepted
+            # no earlier run of g zero-accept rounds
+            run = 0
+            for j in js[:at - 1]:
+                run = run + 1 if j == 0 else 0
+                assert run < g
+    assert n_gated > 50
+
+
+def test_gate_with_never_hitting_and_always_hitting_drafters():
+    rng = np.random.default_rng(9)
+    V, H, K = 32, 64, 4
+    argmax_fn = _head(rng, V, H)
+    hidden_fn = synth.HashHidden(5, H)
+    ctx = list(rng.integers(0, V, size=12))
+    n_new = 40
+    ref = oracle.greedy_decode(ctx, hidden_fn, argmax_fn, n_new + K + 1)
+    # a drafter that is always wrong (greedy id + 1): the gate fires after exactly g rounds
+    # and every round, gated or not, commits one token
+    st = {}
+    wrong = lambda toks, k: [(ref[len(toks)] + 1) % V] + [0] * (k - 1)
+    got = oracle.spec_decode(ctx, hidden_fn, argmax_fn, n_new, K, 3, drafter=wrong, stats=st, gate_after=3)
+    assert got == ref[:len(ctx) + n_new]
+    # the a0 bootstrap commits the first new token, each round one more
+    assert st["gated_after_round"] == 3 and len(st["accepted"]) == n_new - 1 and sum(st["accepted"]) == 0
+    # a perfect drafter never gates: every round commits K + 1 tokens
+    st = {}
+    perfect = lambda toks, k: ref[len(toks):len(toks) + k]
+    got = oracle.spec_decode(ctx, hidden_fn, argmax_fn, n_new, K, 3, drafter=perfect, stats=st, gate_after=1)
+    assert got == ref[:len(ctx) + n_new]
+    assert st["gated_after_round"] is None and set(st["accepted"]) == {K}
