@@ -43,6 +43,10 @@ WORKLOADS = {
                  name="large-hidden head H=5120 V=248320 K=8 S=9, n-gram drafts"),
     "c4s17": dict(cid=3, V=248320, H=5120, K=16, drafts="ngram", ctx=16384, copy=0.20, layers=0,
                   name="large-hidden head H=5120 V=248320 K=16 S=17, n-gram drafts"),
+    "c3gen": dict(cid=2, V=248320, H=2048, K=8, drafts="ngram", ctx=4096, copy=0.30, layers=0, model="table",
+                  name="generation loop: 35B-A3B-shaped head H=2048 V=248320 K=8 S=9 under a token-indexed stand-in "
+                       "model (window rows gathered from a seeded fp16 N(0,1) table [V, H]), n-gram drafts, "
+                       "device-resident rounds through specverify_generate"),
     "c5": dict(cid=4, V=151936, H=4096, K=8, drafts="ngram", ctx=4096, copy=0.30, layers=36, F=12288,
                name="dense stack 36 x [4096->12288 gate/up, 12288->4096 down] + 4096x151936 head, K=8 S=9"),
 }
@@ -120,7 +124,7 @@ def build_inputs(wl, args, torch, sv, synth):
     return dict(q=q, s=s, wq=wq, ws=ws, hidden=hidden, ctx=ctx, copy_frac=frac, layers=layers, copies=copies)
 
 
-def cpu_baseline(wl, inp, seconds_budget=20.0):
+def cpu_baseline(wl, inp, table=None, seconds_budget=20.0):
     """The oracle as it stands, timed on the host on a bounded sample of whole rounds."""
     import oracle
     from threadpoolctl import threadpool_limits
@@ -139,6 +143,9 @@ def cpu_baseline(wl, inp, seconds_budget=20.0):
             if wl["layers"]:
                 return None           # the fp64 oracle stack takes minutes per round
             drafts, _, _ = oracle.propose_scan(tokens, 3, K)
+            if table is not None:     # the stand-in model: rows of the oracle's own window
+                ids = [tokens[-1]] + [d if d >= 0 else 0 for d in drafts]
+                x = table[ids].cpu().numpy()
             L = oracle.head_logits(inp["q"], inp["s"], x)
             a = oracle.argmax_lowest(L)
             if wl["drafts"] == "forced":
@@ -208,8 +215,18 @@ def main():
     argmax = torch.empty(S, dtype=torch.int32, device=dev)
     work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev)
 
-    # anchor bootstrap: S = 1 verify of an extra row, then accept with K = 0 commits a0
-    h_last = torch.from_numpy(synth.fp16_normal(synth.streams(wl["cid"]).h_last, (1, H))).to(dev)
+    table = window = None
+    if wl.get("model") == "table":
+        # token-indexed stand-in model: hidden row of a window position = table[token]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(20261202 + wl["cid"])
+        table = torch.randn((V, H), generator=gen, device=dev, dtype=torch.float32).half()
+        window = torch.empty((S, H), dtype=torch.float16, device=dev)
+        h_last = torch.empty((1, H), dtype=torch.float16, device=dev)
+        sv.gather_window(tokens, state, drafts[:0], table, h_last)      # the context's last token
+    else:
+        h_last = torch.from_numpy(synth.fp16_normal(synth.streams(wl["cid"]).h_last, (1, H))).to(dev)
+    # anchor bootstrap: S = 1 verify of the last context row, then accept with K = 0 commits a0
     a0 = torch.empty(1, dtype=torch.int32, device=dev)
     sv.verify(wq[0], ws[0], h_last, a0, sv.workspace(sv.verify_workspace_bytes(V, H, 1), dev))
     sv.accept(a0, None, tokens, state)
@@ -238,6 +255,10 @@ def main():
 
     def round_(r):
         c = r % copies
+        if table is not None:
+            # gather the window [a0, drafts] from the stand-in model, verify, accept, draft
+            sv.generate(wq[c], ws[c], table, tokens, state, drafts, window, argmax, work, 1)
+            return
         if wl["layers"]:
             # the whole stack in one call (2 launches per block); the round's input rows stay
             # unchanged, block outputs go to a scratch [L, S, H]
@@ -281,7 +302,10 @@ def main():
             x, c = hidden[i % R_SETS], i % copies
         d_in = forced[i % R_SETS] if forced is not None else drafts
         sv.profile_next_matmul(e0, e1, stream=stream)
-        sv.round(wq[c], ws[c], x, d_in, tokens, state, drafts, argmax, work, stream=stream)
+        if table is not None:
+            sv.generate(wq[c], ws[c], table, tokens, state, drafts, window, argmax, work, 1, stream=stream)
+        else:
+            sv.round(wq[c], ws[c], x, d_in, tokens, state, drafts, argmax, work, stream=stream)
         durs.append((e0, e1))
     torch.cuda.synchronize()
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in durs]))
@@ -318,8 +342,20 @@ def main():
     }
     if inp["copy_frac"] is not None:
         out["config"]["context_copy_fraction"] = round(inp["copy_frac"], 3)
+    if table is not None:
+        # tokens/s accounting against the feasibility page's C-value model: with each draft
+        # accepted independently with probability alpha, a round commits
+        # E(alpha, K) = (1 - alpha^(K+1)) / (1 - alpha) tokens; alpha estimated from the
+        # accept histogram (maximum likelihood: sum j / (sum j + rounds with j < K))
+        stops = sum(hist[:K])
+        alpha = sum_j / (sum_j + stops) if sum_j + stops else 0.0
+        e_model = float(K + 1) if alpha >= 1.0 else (1.0 - alpha ** (K + 1)) / (1.0 - alpha)
+        out["tokens_per_second"] = round(rps * (args.steps + sum_j) / args.steps, 1)
+        out["alpha_hat"] = round(alpha, 4)
+        out["expected_tokens_per_round"] = round(e_model, 3)
+        out["gated_at_round"] = int(st1[sv.STATE_GATED])
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp)
+        out["cpu_baseline"] = cpu_baseline(wl, inp, table)
     print(json.dumps(out), flush=True)
 
 

@@ -61,6 +61,12 @@ typedef enum {
  *   [6] sum_j    sum of j over those calls
  *   [7] reserved
  *   [8 + j]      histogram of j, j = 0 .. SV_MAX_S-1
+ *   [72] gate_after  hit-rate gate, set by the caller (0 = off): once this many consecutive
+ *                    rounds have accepted no draft, the drafter emits only pads for the rest
+ *                    of the stream ("Stream C - Speculative decoding", the shipped app note:
+ *                    the drafter is dropped after gateAfter zero-accept rounds)
+ *   [73] zero_run    consecutive rounds with j = 0, kept by the accept step
+ *   [74] gated       0, or the round count at which the gate fired (sticky)
  */
 #define SV_STATE_WORDS 80
 #define SV_STATE_LEN 0
@@ -71,7 +77,11 @@ typedef enum {
 #define SV_STATE_ROUNDS 5
 #define SV_STATE_SUMJ 6
 #define SV_STATE_HIST 8
+#define SV_STATE_GATE_AFTER 72
+#define SV_STATE_ZERO_RUN 73
+#define SV_STATE_GATED 74
 #define SV_FLAG_CAPACITY 1
+#define SV_FLAG_TOKEN 2    /* a token id outside [0, V) was gathered (its row read as zeros) */
 
 /*
  * specverify_propose - n-gram prompt-lookup drafter.
@@ -81,7 +91,8 @@ typedef enum {
  * draft length knobs; "Spec-decode on GDN hybrids - static-S verify design", harness
  * lessons (the stream ends in the pending anchor, drafts continue past it).
  *
- * Reads tokens[0 .. len) with len = state[0].  For n = ngram_max, ..., 1 the first n whose
+ * Once the hit-rate gate has fired (state[74] != 0) every draft is -1 and nothing is read.
+ * Otherwise reads tokens[0 .. len) with len = state[0].  For n = ngram_max, ..., 1 the first n whose
  * last-n suffix occurs earlier wins; among its occurrences the one ending latest (end
  * position e <= len-2, overlap with the suffix allowed) is used, and
  *   drafts[i] = tokens[e+1+i]  for e+1+i <= len-1,  else -1,   i = 0 .. K-1.
@@ -145,6 +156,43 @@ int specverify_round(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_
                      hipStream_t stream);
 
 /*
+ * specverify_gather_window - the window rows of a token-indexed stand-in model:
+ *   window[0] = table[tokens[len-1]] (the anchor a0, len = state[0]),
+ *   window[i] = table[drafts[i-1]] for i = 1 .. K, a pad (-1) reading token 0's row,
+ * so a whole generation loop stays on the device (the model body is a per-token table, the
+ * "Markov" stand-in of the control-logic proof in "Stream C - Speculative decoding"; pads
+ * feed token 0 as in the static-S window of "Spec-decode on GDN hybrids").
+ *   table   fp16 [V][H], 16-byte aligned;  window fp16 [K+1][H] output, 16-byte aligned
+ *   K       0 .. SV_MAX_S-1 (drafts may be NULL when K = 0)
+ * An id outside [0, V) writes a zero row and sets bit 1 (SV_FLAG_TOKEN) of state[4]; a
+ * length outside [1, cap] writes zero rows and sets bit 0.
+ */
+int specverify_gather_window(const int32_t* tokens, int32_t cap, int32_t* state,
+                             const int32_t* drafts, int32_t K, const uint16_t* table, int32_t V,
+                             int32_t H, uint16_t* window, hipStream_t stream);
+
+/*
+ * specverify_generate - `rounds` speculative-decoding rounds enqueued back to back with no
+ * host synchronisation ("Riding Apple's pipelined GPU engine", "Why hand-rolled per-token
+ * loops lose": encode and return, only sampled ids leave the GPU).  Each round is
+ *   specverify_gather_window(table) -> specverify_round(window, drafts -> drafts)
+ * i.e. verify [a0, d_1 .. d_K], accept, draft the next round, with the hit-rate gate of the
+ * state word.  Before the first call the stream must hold its anchor (the bootstrap:
+ * specverify_verify at S = 1 and specverify_accept with K = 0) and `drafts` the first
+ * drafts (specverify_propose).  A round that would overflow `cap` commits nothing and sets
+ * the capacity flag; later rounds then repeat the same window.  Capturable in a HIP graph
+ * (no allocation, no memset, no synchronisation).
+ *   table   fp16 [V][H] (the stand-in model);  window fp16 [K+1][H] scratch;  argmax int32 [K+1]
+ *   drafts  int32 [K], read and rewritten by every round;  rounds >= 0
+ *   other arguments as for specverify_round; logits are not written.
+ */
+int specverify_generate(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
+                        const uint16_t* table, int32_t K, int32_t rounds, int32_t* tokens,
+                        int32_t cap, int32_t* state, int32_t ngram_max, int32_t* drafts,
+                        uint16_t* window, int32_t* argmax, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
  * specverify_accept - greedy longest-prefix acceptance with the fused anchor.
  * Pages: "Stream C - Speculative decoding", sections "The delta" and "Control-logic proof"
  * (draft i is accepted iff it equals the greedy id of its position and every earlier draft
@@ -156,8 +204,9 @@ int specverify_round(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_
  * argmax[0..K] are the greedy ids of the window [a0, d_1 .. d_K]; drafts[0..K-1] = d_1..d_K.
  *   j = max { i in [0, K] : drafts[m-1] == argmax[m-1] for all 1 <= m <= i }
  * Writes tokens[len .. len+j] = d_1 .. d_j, argmax[j] and sets len += 1 + j (state[0]);
- * records j in state[1], state[5], state[6] and the histogram.  K = 0 appends argmax[0]:
- * the anchor bootstrap of a fresh stream.
+ * records j in state[1], state[5], state[6] and the histogram, and advances the hit-rate
+ * gate (state[73], state[74]).  K = 0 appends argmax[0]: the anchor bootstrap of a fresh
+ * stream (it records nothing else).
  * If len + K + 1 > cap the call writes no token and sets bit 0 of state[4] (sticky).
  *   argmax    int32 [K+1];  drafts int32 [K] (may be NULL when K = 0); -1 = pad
  *   K         0 .. SV_MAX_S-1;  tokens int32 [cap]
@@ -223,7 +272,8 @@ int specverify_linear_residual_rmsnorm_q8b32(const int8_t* w, const uint16_t* sc
  * the residual, storing x and the per-tile sums of squares the next norm needs).
  *   wg, wu  int8 [L][F][H] (layer l at l*F*H);  sg, su fp16 [L][F][H/32]
  *   wd      int8 [L][H][F];                      sd     fp16 [L][H][F/32]
- *   H, F    multiples of 512 in [512, 65536];   S 1 .. 16;   L 1 .. 4096;   eps >= 0
+ *   H, F    multiples of 512 in [512, 65536] with H * F < 2^31;   S 1 .. 16;   L 1 .. 4096;
+ *           eps >= 0
  *   x       fp16 [S][H]: the stack's input; overwritten with the output of block L-1 when
  *           x_layers is NULL, else left unchanged
  *   x_layers fp16 [L][S][H] or NULL: the output of every block (for per-block checks)
@@ -243,13 +293,15 @@ int specverify_stack(const int8_t* wg, const uint16_t* sg, const int8_t* wu, con
  * Launch-shape override of the q8b32 matmuls, for tuning sweeps: waves per workgroup
  * (4, 8 or 16; 0 = automatic), an upper bound on workgroups per launch (1 .. 4096;
  * 0 = automatic) and, for the chunked stack kernels, load units in flight per wave (2 .. 4;
- * 0 = automatic; a depth that has no kernel for a shape falls back to the automatic one).
- * Waves that do not divide a chunked shape make specverify_stack fail with SV_ERR_SHAPE.
- * Process-wide;
+ * 0 = automatic; a depth that has no kernel for a shape falls back to the automatic one),
+ * and the head matmul kernel family (0 = automatic, 1 = one pass per 16-row item, 2 = the
+ * chunked ring kernel where the shape allows it, S <= 16).  Waves that do not divide a
+ * chunked shape make specverify_stack fail with SV_ERR_SHAPE.  Process-wide;
  * affects the *_workspace_bytes answers, so query them after changing it.  Not thread-safe
  * against concurrent calls.
  */
-void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups, int32_t depth);
+void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups, int32_t depth,
+                           int32_t head_kernel);
 
 /*
  * Timing hook for the dominant kernel.  The next int8 matmul that this thread enqueues through

@@ -39,7 +39,9 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     for macro, val in [("SV_MAX_S", sv.SV_MAX_S), ("SV_MAX_NGRAM", sv.SV_MAX_NGRAM), ("SV_BLOCK", sv.SV_BLOCK),
                        ("SV_STATE_WORDS", sv.STATE_WORDS), ("SV_STATE_LEN", sv.STATE_LEN),
-                       ("SV_STATE_FLAGS", sv.STATE_FLAGS), ("SV_STATE_HIST", sv.STATE_HIST)]:
+                       ("SV_STATE_FLAGS", sv.STATE_FLAGS), ("SV_STATE_HIST", sv.STATE_HIST),
+                       ("SV_STATE_GATE_AFTER", sv.STATE_GATE_AFTER), ("SV_STATE_ZERO_RUN", sv.STATE_ZERO_RUN),
+                       ("SV_STATE_GATED", sv.STATE_GATED), ("SV_FLAG_TOKEN", sv.FLAG_TOKEN)]:
         assert re.search(rf"#define {macro} {val}\b", text), macro
 
 
@@ -123,6 +125,40 @@ def test_whole_stack_argument_errors(lib):
     assert call(a9=A2) == 3                             # x alignment
     assert call(a15=ws - 1) == 4                        # workspace
     assert b"workspace" in lib.specverify_last_error()
+
+
+def test_every_documented_stack_shape_has_a_launch_configuration(lib):
+    """H and F multiples of 512 with H*F < 2^31 are documented as supported: each must get a
+    configuration (a non-zero workspace answer) for every S it allows."""
+    sizes = [512, 1024, 1536, 2048, 2560, 3072, 3584, 4096, 5120, 6144, 8192, 12288, 14336, 65536]
+    for H in sizes:
+        for F in sizes:
+            for S in (1, 9, 16):
+                got = lib.specverify_stack_forward_workspace_bytes(H, F, S)
+                assert (got > 0) == (H * F < 2 ** 31), (H, F, S)
+
+
+def test_generate_and_gather_argument_errors(lib):
+    ws = lib.specverify_verify_workspace_bytes(1000, 256, 9)
+    g = lib.specverify_generate
+    ok = [A16, A16, 1000, 256, A16, 8, 5, A16, 100, A16, 3, A16, A16, A16, A16, ws, NULL]
+    def call(**kw):
+        args = list(ok)
+        for k, v in kw.items():
+            args[int(k[1:])] = v
+        return g(*args)
+    assert call(a4=NULL) == 1                           # table
+    assert call(a5=0) == 2                              # K
+    assert call(a6=-1) == 2                             # rounds
+    assert call(a10=0) == 2                             # n-gram order
+    assert call(a4=A2) == 3                             # table alignment
+    assert call(a15=ws - 1) == 4                        # workspace
+    gw = lib.specverify_gather_window
+    assert gw(A16, 100, A16, A16, 8, NULL, 1000, 256, A16, NULL) == 1
+    assert gw(A16, 100, A16, NULL, 0, A16, 1000, 256, A16, NULL) != 1      # drafts optional at K = 0
+    assert gw(A16, 100, A16, A16, 64, A16, 1000, 256, A16, NULL) == 2
+    assert gw(A16, 100, A16, A16, 8, A16, 1000, 250, A16, NULL) == 2
+    assert gw(A16, 100, A16, A16, 8, A16, 1000, 256, A2, NULL) == 3
 
 
 def test_missing_library_raises(monkeypatch, tmp_path):

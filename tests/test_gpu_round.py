@@ -40,7 +40,11 @@ def test_accept_matches_oracle_random():
         assert stv[sv.STATE_LEN] == length + 1 + j and stv[sv.STATE_J] == j, case
         assert list(got[length:length + 1 + j]) == app
         assert np.array_equal(got[:length], toks0[:length]) and np.array_equal(got[length + 1 + j:], toks0[length + 1 + j:])
-        assert stv[sv.STATE_ROUNDS] == 1 and stv[sv.STATE_SUMJ] == j and stv[sv.STATE_HIST + j] == 1
+        if K > 0:
+            assert stv[sv.STATE_ROUNDS] == 1 and stv[sv.STATE_SUMJ] == j and stv[sv.STATE_HIST + j] == 1
+            assert stv[sv.STATE_ZERO_RUN] == (1 if j == 0 else 0) and stv[sv.STATE_GATED] == 0
+        else:                   # the anchor bootstrap commits a0 and is not a round
+            assert stv[sv.STATE_ROUNDS] == 0 and stv[sv.STATE_HIST] == 0 and stv[sv.STATE_ZERO_RUN] == 0
 
 
 def test_accept_capacity_overflow_writes_nothing():

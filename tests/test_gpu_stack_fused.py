@@ -25,6 +25,25 @@ def _check_f16(got16, ref64, slack=1e-4):
     assert bad.size == 0, f"{len(bad)} outputs outside, first {bad[:3].tolist()} err {err[tuple(bad[0])]}"
 
 
+def _m_bound(x16, parts, layer, eps=1e-6):
+    """Largest |m_gpu - m| the rounding of the normalised row can cause: where x / rms lies
+    within fp32 noise (4e-7 relative) of an fp16 rounding midpoint the library may round n to
+    the other neighbour (its 1/rms is fp32); each such element moves g and u by at most one
+    n ulp times the weights, and m = silu(g) u moves by |silu'(g)| |u| dg + |silu(g)| du
+    (|silu'| <= 1.1)."""
+    xx = x16.astype(np.float64)
+    t = xx / np.sqrt(np.mean(xx * xx, axis=-1, keepdims=True) + eps)
+    n16 = t.astype(np.float16).astype(np.float64)
+    ulp_n = np.spacing(np.abs(t.astype(np.float16))).astype(np.float64)
+    amb = np.abs(np.abs(t - n16) - ulp_n / 2) <= 4e-7 * np.abs(t) + 1e-12
+    dn = np.where(amb, ulp_n, 0.0)                                   # [S][H]
+    (qg, sg), (qu, su), _ = layer
+    dg = dn @ np.abs(oracle.dequantize(qg, sg)).T                    # [S][F]
+    du = dn @ np.abs(oracle.dequantize(qu, su)).T
+    g, u = parts["g"], parts["u"]
+    return 1.1 * np.abs(u) * dg + np.abs(oracle.silu(g)) * du
+
+
 def _stacked(rng, L, H, F):
     def w(r, c):
         return synth.quantize_q8b32(rng.standard_normal((r, c), dtype=np.float32) * np.float32(synth.W_STD))
@@ -33,7 +52,7 @@ def _stacked(rng, L, H, F):
     return layers, [cat(0, 0), cat(0, 1), cat(1, 0), cat(1, 1), cat(2, 0), cat(2, 1)]
 
 
-def _run(mats, x, L, eps=1e-6, layers_out=True):
+def _run(mats, x, L, eps=1e-6, layers_out=True, want_ws=False):
     S, H = x.shape
     F = mats[0].shape[1]
     dm = [to_dev(m) for m in mats]
@@ -43,17 +62,65 @@ def _run(mats, x, L, eps=1e-6, layers_out=True):
     ws = sv.workspace(sv.stack_forward_workspace_bytes(H, F, S), dev())
     sv.stack(*dm, xd, nrm, ws, eps, x_layers=xl)
     torch.cuda.synchronize()
-    return xd.cpu().numpy(), (xl.cpu().numpy() if layers_out else None), nrm.cpu().numpy()
+    out = (xd.cpu().numpy(), (xl.cpu().numpy() if layers_out else None), nrm.cpu().numpy())
+    if not want_ws:
+        return out
+    # workspace layout: m = silu(g)*u [S][F] fp16, then the sum-of-squares partials [S][H/16] fp32,
+    # each part 256-byte aligned
+    w = ws.cpu().numpy()
+    m = w[:2 * S * F].view(np.float16).reshape(S, F)
+    off = (2 * S * F + 255) // 256 * 256
+    ss = w[off:off + 4 * S * (H // 16)].view(np.float32).reshape(S, H // 16)
+    return out + (m, ss)
 
 
-@pytest.mark.parametrize("H,F,S,L", [
+SHAPES = [
     (512, 1024, 9, 3),      # 4 waves, one chunk (held window rows)
-    (1024, 1536, 16, 2),    # gate/up 8 waves x 1 chunk; down 4 waves x 3 chunks (streamed rows)
+    (1024, 1536, 16, 2),    # gate/up 8 waves x 1 chunk; down 12 waves x 1 chunk
     (2048, 512, 1, 2),
     (512, 2048, 5, 2),
     (4096, 12288, 9, 1),    # the dense-stack workload's block shape
-])
+    (2560, 1536, 9, 2),     # 10 waves x 2 held chunks (gate/up); 12 waves (down)
+    (3584, 2560, 16, 1),    # 14 waves; down 10 waves
+]
+
+
+@pytest.mark.parametrize("H,F,S,L", SHAPES)
+def test_stack_block_by_block_teacher_forced(H, F, S, L):
+    """Each block on its own (L = 1 per call), teacher-forced at both stages: the GPU's
+    m = silu(g)*u must be within one fp16 rounding of the oracle's m from the same input
+    (the norm and both projections of gate/up), and the block output within one rounding of
+    x + m_gpu Wd^T (the down projection, residual and store)."""
+    say(f"stack block by block H={H} F={F} S={S} L={L}")
+    rng = np.random.default_rng(H + 3 * F + S + L)
+    layers, mats = _stacked(rng, L, H, F)
+    x = (synth.fp16_normal(rng, (S, H)).astype(np.float32) * 3).astype(np.float16)
+    for li in range(L):
+        one = [m[li:li + 1] for m in mats]
+        _, xl, nrm, m_gpu, ss = _run(one, x, 1, want_ws=True)
+        _, parts = oracle.mlp_block(x, layers[li], return_parts=True)
+        ref_m = oracle.silu(parts["g"]) * parts["u"]
+        ulp = np.spacing(np.abs(ref_m.astype(np.float16))).astype(np.float64)
+        rms = np.sqrt(np.mean(ref_m * ref_m, axis=-1, keepdims=True))
+        err = np.abs(m_gpu.astype(np.float64) - ref_m)
+        bad = np.argwhere(~(err <= ulp + 1e-5 * rms + _m_bound(x, parts, layers[li])))
+        assert bad.size == 0, f"m: {len(bad)} outside, first {bad[:3].tolist()} err {err[tuple(bad[0])]}"
+        _check_f16(xl[0], x.astype(np.float64) + oracle.linear_q8b32(*layers[li][2], m_gpu), slack=1e-5)
+        out = xl[0].astype(np.float64)
+        # the down epilogue's per-16-column sums of squares of the stored fp16 outputs
+        ref_ss = (out.reshape(S, H // 16, 16) ** 2).sum(-1)
+        assert np.allclose(ss, ref_ss, rtol=1e-5, atol=0), "sum-of-squares partials"
+        _check_f16(nrm, out / np.sqrt(np.mean(out * out, axis=1, keepdims=True) + 1e-6), slack=1e-5)
+        x = xl[0]
+
+
+@pytest.mark.parametrize("H,F,S,L", [sh for sh in SHAPES if sh[3] > 1])
 def test_stack_matches_oracle_per_block(H, F, S, L):
+    """The multi-block call (each block's norm from the previous down epilogue's partials),
+    every block output against the oracle block on the library's own input of that block.
+    Allowed error: one fp16 rounding of the output, 1e-4 of the row rms, and the effect of
+    m = silu(g)*u rounding to the other fp16 neighbour (fp32 versus fp64 before rounding):
+    at most one m ulp per term of the down projection, bounded by 4 ulps x |Wd| summed."""
     say(f"stack H={H} F={F} S={S} L={L}")
     rng = np.random.default_rng(H + 3 * F + S + L)
     layers, mats = _stacked(rng, L, H, F)
@@ -63,8 +130,16 @@ def test_stack_matches_oracle_per_block(H, F, S, L):
     prev = x
     for li in range(L):
         _, parts = oracle.mlp_block(prev, layers[li], return_parts=True)
-        _check_f16(xl[li], prev.astype(np.float64) + parts["y"])
-        assert np.isfinite(xl[li]).all()
+        ref = prev.astype(np.float64) + parts["y"]
+        wd = np.abs(oracle.dequantize(*layers[li][2]))
+        ulp_m = np.spacing(np.abs(parts["m"])).astype(np.float64)          # [S][F]
+        flip = 4.0 * np.sqrt((ulp_m ** 2) @ (wd.T ** 2))                   # rms-style bound of sparse flips
+        got = xl[li].astype(np.float64)
+        ulp = np.spacing(np.abs(ref.astype(np.float16))).astype(np.float64)
+        rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+        err = np.abs(got - ref)
+        bad = np.argwhere(~(err <= ulp + 1e-4 * rms + flip))
+        assert bad.size == 0, f"block {li}: {len(bad)} outside, first {bad[:3].tolist()} err {err[tuple(bad[0])]}"
         prev = xl[li]
     last = xl[L - 1].astype(np.float64)
     _check_f16(nrm, last / np.sqrt(np.mean(last * last, axis=1, keepdims=True) + 1e-6), slack=1e-5)

@@ -130,3 +130,22 @@ def test_verify_full_large_hidden_shape_sampled_rows():
     L = oracle.head_logits(q, s, hidden)
     check_logits(lg, L)
     check_argmax(a, L)
+
+
+@pytest.mark.parametrize("V,H,S", [(1000, 512, 9), (4099, 2048, 9), (777, 4096, 16), (70000, 2048, 1), (5000, 5120, 9),
+                                   (33, 512, 3)])
+def test_verify_ring_kernel_matches_oracle(V, H, S):
+    """The chunked ring kernel for the head (selected through the tuning switch)."""
+    say(f"verify ring kernel V={V} H={H} S={S}")
+    q, s = head(V * 3 + H + S, V, H)
+    hidden = synth.fp16_normal(np.random.default_rng(S + 1), (S, H))
+    try:
+        sv.set_tuning(0, 0, 0, 2)
+        a, lg = gpu_verify(q, s, hidden)
+        a2, _ = gpu_verify(q, s, hidden, want_logits=False)
+    finally:
+        sv.set_tuning(0, 0, 0, 0)
+    L = oracle.head_logits(q, s, hidden)
+    check_logits(lg, L)
+    check_argmax(a, L)
+    assert np.array_equal(a, a2)

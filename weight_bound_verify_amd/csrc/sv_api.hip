@@ -79,6 +79,19 @@ hipError_t launch_matmul(int epi, const sv::GemmCfg& cfg, const sv::GemmArgs& a,
     return e;
 }
 
+// The chunked head matmul, bracketed by the pending timing hook if one is set.
+hipError_t launch_chunked_matmul(const sv::ChunkCfg& cfg, const sv::ChunkArgs& a, hipStream_t stream) {
+    hipEvent_t before = g_prof_before, after = g_prof_after;
+    g_prof_before = g_prof_after = nullptr;
+    if (before) {
+        hipError_t e = hipEventRecord(before, stream);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e = sv::launch_chunked(sv::EPI_HEAD, cfg, a, stream);
+    if (e == hipSuccess && after) e = hipEventRecord(after, stream);
+    return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,13 +119,14 @@ int specverify_profile_next_matmul(hipEvent_t before, hipEvent_t after) {
     return SV_OK;
 }
 
-void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups, int32_t depth) {
+void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups, int32_t depth, int32_t head_kernel) {
     if (waves_per_group != 0 && waves_per_group != 4 && waves_per_group != 8 && waves_per_group != 16)
         waves_per_group = 0;
     if (max_groups < 0 || max_groups > sv::kGridMax) max_groups = 0;
     if (depth < 0 || depth > 4) depth = 0;
+    if (head_kernel < 0 || head_kernel > 2) head_kernel = 0;
     sv::set_tuning(waves_per_group, max_groups);
-    sv::set_chunk_tuning(waves_per_group, depth, max_groups);
+    sv::set_chunk_tuning(waves_per_group, depth, max_groups, head_kernel);
 }
 
 int specverify_propose(const int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max, int32_t K,
@@ -141,8 +155,23 @@ int launch_head(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, 
                 int32_t* argmax, float* logits, void* workspace, bool round, const int32_t* drafts_in,
                 int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max, int32_t* drafts_out,
                 hipStream_t stream) {
-    const sv::GemmCfg cfg = sv::gemm_config(V, H, S, sv::EPI_HEAD);
     char* ws = static_cast<char*>(workspace);
+    float* part_val = reinterpret_cast<float*>(ws);
+    int* part_idx = reinterpret_cast<int*>(ws + (size_t)4 * S * sv::kGridMax);
+    sv::ChunkCfg cc;
+    if (S <= 16 && sv::head_use_chunked(V, H) && sv::chunked_config(V, H, sv::EPI_HEAD, cc)) {
+        // ring kernel: argmax partials per workgroup, no hidden-axis split
+        sv::ChunkArgs c{};
+        c.w0 = wq; c.s0 = wscale; c.x = hidden;
+        c.V = V; c.H = H; c.S = S; c.nb = H / SV_BLOCK; c.nitems = cc.items; c.nkc = cc.nkc;
+        c.part_val = part_val; c.part_idx = part_idx; c.logits = logits;
+        hipError_t e = launch_chunked_matmul(cc, c, stream);
+        if (e != hipSuccess) return hip_fail(e, "verify matmul launch");
+        e = sv::launch_round_tail(part_val, part_idx, cc.grid, S, argmax, round ? drafts_in : nullptr, tokens, cap,
+                                  state, ngram_max, round ? drafts_out : nullptr, stream);
+        return e == hipSuccess ? SV_OK : hip_fail(e, "argmax/round tail launch");
+    }
+    const sv::GemmCfg cfg = sv::gemm_config(V, H, S, sv::EPI_HEAD);
     sv::GemmArgs a{};
     a.w0 = wq;
     a.s0 = wscale;
@@ -153,8 +182,8 @@ int launch_head(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, 
     a.nb = H / SV_BLOCK;
     a.nitems = (V + 15) / 16;
     a.ksplit = cfg.ksplit;
-    a.part_val = reinterpret_cast<float*>(ws);
-    a.part_idx = reinterpret_cast<int*>(ws + (size_t)4 * S * sv::kGridMax);
+    a.part_val = part_val;
+    a.part_idx = part_idx;
     a.logits = logits;
     if (cfg.ksplit > 1) a.kpart0 = reinterpret_cast<float*>(ws + sv::head_partials_bytes(S));
     hipError_t e = launch_matmul(sv::EPI_HEAD, cfg, a, stream);
@@ -201,6 +230,47 @@ int specverify_round(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_
     if (int st = check_device()) return st;
     return launch_head(wq, wscale, V, H, hidden, K + 1, argmax, logits, workspace, true, drafts_in, tokens, cap, state,
                        ngram_max, drafts_out, stream);
+}
+
+int specverify_gather_window(const int32_t* tokens, int32_t cap, int32_t* state, const int32_t* drafts, int32_t K,
+                             const uint16_t* table, int32_t V, int32_t H, uint16_t* window, hipStream_t stream) {
+    if (!tokens || !state || !table || !window || (K > 0 && !drafts))
+        return fail(SV_ERR_NULL, "tokens, state, drafts, table and window are required");
+    if (K < 0 || K > SV_MAX_S - 1) return fail(SV_ERR_SHAPE, "K=%d outside [0, %d]", K, SV_MAX_S - 1);
+    if (V < 1 || V > (1 << 30) || H < SV_BLOCK || H > 65536 || H % SV_BLOCK)
+        return fail(SV_ERR_SHAPE, "V=%d H=%d", V, H);
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(tokens, 4) || !aligned(state, 4) || (drafts && !aligned(drafts, 4)) || !aligned(table, 16) ||
+        !aligned(window, 16))
+        return fail(SV_ERR_ALIGN, "int32 buffers 4-byte, table and window 16-byte alignment required");
+    if (int st = check_device()) return st;
+    hipError_t e = sv::launch_gather_window(tokens, cap, state, drafts, K, table, V, H, window, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "gather launch");
+}
+
+int specverify_generate(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* table,
+                        int32_t K, int32_t rounds, int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max,
+                        int32_t* drafts, uint16_t* window, int32_t* argmax, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+    if (K < 1 || K > SV_MAX_S - 1) return fail(SV_ERR_SHAPE, "K=%d outside [1, %d]", K, SV_MAX_S - 1);
+    if (rounds < 0) return fail(SV_ERR_SHAPE, "rounds=%d < 0", rounds);
+    if (!table) return fail(SV_ERR_NULL, "table is required");
+    if (!aligned(table, 16)) return fail(SV_ERR_ALIGN, "table must be 16-byte aligned");
+    if (int st = check_head(wq, wscale, V, H, window, K + 1, argmax, nullptr, workspace, workspace_bytes)) return st;
+    if (!drafts || !tokens || !state) return fail(SV_ERR_NULL, "drafts, tokens and state are required");
+    if (ngram_max < 1 || ngram_max > SV_MAX_NGRAM) return fail(SV_ERR_SHAPE, "ngram_max=%d outside [1, %d]", ngram_max, SV_MAX_NGRAM);
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(drafts, 4) || !aligned(tokens, 4) || !aligned(state, 4))
+        return fail(SV_ERR_ALIGN, "int32 buffers must be 4-byte aligned");
+    if (int st = check_device()) return st;
+    for (int r = 0; r < rounds; ++r) {
+        hipError_t e = sv::launch_gather_window(tokens, cap, state, drafts, K, table, V, H, window, stream);
+        if (e != hipSuccess) return hip_fail(e, "gather launch");
+        if (int st = launch_head(wq, wscale, V, H, window, K + 1, argmax, nullptr, workspace, true, drafts, tokens,
+                                 cap, state, ngram_max, drafts, stream))
+            return st;
+    }
+    return SV_OK;
 }
 
 int specverify_accept(const int32_t* argmax, const int32_t* drafts, int32_t K, int32_t* tokens, int32_t cap,
@@ -333,7 +403,8 @@ int specverify_stack(const int8_t* wg, const uint16_t* sg, const int8_t* wu, con
         return fail(SV_ERR_NULL, "weights, scales, x, norm_out and workspace are required");
     if (L < 1 || L > 4096) return fail(SV_ERR_SHAPE, "L=%d outside [1, 4096]", L);
     if (S < 1 || S > 16) return fail(SV_ERR_SHAPE, "S=%d outside [1, 16]", S);
-    if (!stack_shape_ok(H, F)) return fail(SV_ERR_SHAPE, "H=%d and F=%d must be multiples of 512 in [512, 65536]", H, F);
+    if (!stack_shape_ok(H, F))
+        return fail(SV_ERR_SHAPE, "H=%d and F=%d must be multiples of 512 in [512, 65536] with H*F < 2^31", H, F);
     if (!(eps >= 0.0f)) return fail(SV_ERR_SHAPE, "eps must be >= 0");
     const void* ptrs16[] = {wg, sg, wu, su, wd, sd, x, norm_out, workspace};
     for (const void* p : ptrs16)

@@ -110,8 +110,8 @@ struct Unit {
 template <int NW, int DEPTH, int HOLD, int EPI>
 __global__ __launch_bounds__(NW * 64) void q8b32_chunked(ChunkArgs a) {
     static_assert(HOLD == 0 || DEPTH % HOLD == 0, "a ring cycle must cover whole tiles");
-    static_assert(16 % NW == 0 || NW == 16, "epilogue rows per wave");
-    constexpr int RPW = 16 / NW;                  // window rows each wave finishes per tile
+    static_assert(NW >= 1 && NW <= 16, "1 .. 16 waves");
+    constexpr int RPW = (16 + NW - 1) / NW;       // window rows each wave finishes per tile (rows >= 16 idle)
     __shared__ f32x4 red[2][NW][kWave];
     __shared__ __attribute__((aligned(16))) uint8_t xch[NW][2][kUnitBytes];
     __shared__ float inv_s[kTileRows];
@@ -218,12 +218,13 @@ __global__ __launch_bounds__(NW * 64) void q8b32_chunked(ChunkArgs a) {
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
             const int s = wave + j * NW;                       // window row (compile-time count)
-            const float* col = reinterpret_cast<const float*>(&red[buf][0][n + 16 * (s >> 2)]) + (s & 3);
+            const int sr = s & 15;                             // rows >= 16 read a real slot, store nothing
+            const float* col = reinterpret_cast<const float*>(&red[buf][0][n + 16 * (sr >> 2)]) + (sr & 3);
             float val = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) val += col[w * kWave * 4];
             const int v = crow<EPI>(it, n);
-            const bool ok = live && lane < 16 && s < a.S && v < a.V;
+            const bool ok = live && lane < 16 && s < 16 && s < a.S && v < a.V;
             if constexpr (EPI == EPI_GATEUP) {
                 const float up = __shfl_xor(val, 8, 16);
                 const float out = val / (1.0f + expf(-val)) * up;
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(NW * 64) void q8b32_chunked(ChunkArgs a) {
             int bi = best_i[j];
             argmax_group<16>(bv, bi);
             const int s = wave + j * NW;
-            const uint32_t off = lane == 0 && s < a.S ? ((uint32_t)s * kGridMax + blockIdx.x) * 4u : kPastEnd;
+            const uint32_t off = lane == 0 && s < 16 && s < a.S ? ((uint32_t)s * kGridMax + blockIdx.x) * 4u : kPastEnd;
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, bv), rpv, (int)off, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b32((uint32_t)bi, rpi, (int)off, 0, 0);
         }
@@ -365,6 +366,9 @@ ChunkFn pick_chunked(int nw, int hold, int depth) {
 #define SV_CH(NW, HOLD, DEPTH) \
     if (nw == NW && hold == HOLD && depth == DEPTH) return q8b32_chunked<NW, DEPTH, HOLD, EPI>;
     SV_CH(16, 0, 2) SV_CH(16, 1, 2) SV_CH(16, 1, 4) SV_CH(16, 2, 2)
+    SV_CH(14, 0, 2) SV_CH(14, 1, 2) SV_CH(14, 2, 2)
+    SV_CH(12, 0, 2) SV_CH(12, 0, 3) SV_CH(12, 1, 2) SV_CH(12, 2, 2)
+    SV_CH(10, 0, 2) SV_CH(10, 1, 2) SV_CH(10, 2, 2)
     SV_CH(8, 0, 2) SV_CH(8, 0, 3) SV_CH(8, 0, 4) SV_CH(8, 1, 2) SV_CH(8, 1, 4) SV_CH(8, 2, 2) SV_CH(8, 2, 4)
     SV_CH(4, 0, 2) SV_CH(4, 0, 3) SV_CH(4, 0, 4) SV_CH(4, 1, 4) SV_CH(4, 2, 4)
 #undef SV_CH
@@ -406,12 +410,20 @@ namespace {
 int g_chunk_nw = 0;       // tuning overrides, 0 = automatic
 int g_chunk_depth = 0;
 int g_grid_override_chunk = 0;
+int g_head_kernel = 0;    // 0 automatic, 1 one-pass-per-item kernel, 2 ring kernel
 }  // namespace
 
-void set_chunk_tuning(int waves, int depth, int max_groups) {
+void set_chunk_tuning(int waves, int depth, int max_groups, int head_kernel) {
     g_chunk_nw = waves;
     g_chunk_depth = depth;
     g_grid_override_chunk = max_groups;
+    g_head_kernel = head_kernel;
+}
+
+bool head_use_chunked(int V, int H) {
+    (void)V;
+    (void)H;
+    return g_head_kernel == 2;
 }
 
 bool chunked_config(int rows, int H, int epi, ChunkCfg& c) {
@@ -421,7 +433,7 @@ bool chunked_config(int rows, int H, int epi, ChunkCfg& c) {
     const int segs = nb / 4;
     // measured preference: the streamed-row down projection is fastest at 8 waves, the
     // held-row shapes at 16
-    const int pref[2][3] = {{16, 8, 4}, {8, 16, 4}};
+    const int pref[2][6] = {{16, 14, 12, 10, 8, 4}, {8, 16, 14, 12, 10, 4}};
     for (int nw : pref[epi == EPI_STORE ? 1 : 0]) {
         if (segs % nw) continue;
         if (g_chunk_nw && nw != g_chunk_nw) continue;
@@ -429,11 +441,18 @@ bool chunked_config(int rows, int H, int epi, ChunkCfg& c) {
         c.nkc = segs / nw;
         c.hold = c.nkc <= 2 ? c.nkc : 0;
         // deepest ring that compiles without spills at this width (see pick_chunked)
-        // held rows: 4 units in flight; streamed rows: the deepest ring that divides the chunks
+        // held rows: the deepest ring that compiles without spills; streamed rows: the
+        // shallowest ring that divides the chunks (measured: deeper rings hold more window-row
+        // registers than they gain)
         auto fits = [&](int d) { return chunked_fn(epi, nw, c.hold, d) && (c.hold || c.nkc % d == 0); };
         int depth = 0;
-        for (int d : {4, 3, 2})
-            if (!depth && fits(d)) depth = d;
+        if (c.hold) {
+            for (int d : {4, 3, 2})
+                if (!depth && fits(d)) depth = d;
+        } else {
+            for (int d : {2, 3, 4})
+                if (!depth && fits(d)) depth = d;
+        }
         if (g_chunk_depth && fits(g_chunk_depth)) depth = g_chunk_depth;       // else automatic
         if (!depth) continue;
         c.depth = depth;

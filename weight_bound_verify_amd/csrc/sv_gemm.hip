@@ -433,6 +433,7 @@ __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* _
     __shared__ __attribute__((aligned(16))) int32_t tk[kTailIds];
     __shared__ int32_t am[SV_MAX_S];
     __shared__ int new_len;
+    __shared__ int gated_s;
     __shared__ unsigned long long wbest[kTailThreads / kWave];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -482,14 +483,12 @@ __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* _
         if (lane == 0) {
             new_len = len0 + 1 + j;
             state[SV_STATE_LEN] = len0 + 1 + j;
-            state[SV_STATE_J] = j;
-            state[SV_STATE_ROUNDS] += 1;
-            state[SV_STATE_SUMJ] += j;
-            state[SV_STATE_HIST + j] += 1;
+            record_round(state, j);
+            gated_s = state[SV_STATE_GATED] != 0;
         }
     }
     __syncthreads();
-    propose_lds(tk, new_len, nmax, K, drafts_out, state, wbest);
+    propose_lds(tk, new_len, nmax, K, drafts_out, state, wbest, gated_s != 0);
 }
 
 // ------------------------------------------------------------------------------------------

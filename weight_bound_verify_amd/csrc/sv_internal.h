@@ -62,6 +62,9 @@ hipError_t launch_round_tail(const float* pv, const int* pi, int nparts, int S, 
                              int32_t* drafts_out, hipStream_t stream);
 hipError_t launch_propose(const int32_t* tokens, int cap, int32_t* state, int nmax, int K, int32_t* drafts,
                           hipStream_t stream);
+// Window rows [tokens[len-1], drafts (pads -> 0)] of a token-indexed table [V][H] into out [K+1][H].
+hipError_t launch_gather_window(const int32_t* tokens, int cap, int32_t* state, const int32_t* drafts, int K,
+                                const uint16_t* table, int V, int H, uint16_t* out, hipStream_t stream);
 hipError_t launch_accept(const int32_t* argmax, const int32_t* drafts, int K, int32_t* tokens,
                          int cap, int32_t* state, hipStream_t stream);
 // Per window row: t = sum of `ks` split partial sums [ks][S][N] (+ residual), y = fp16(t)
@@ -90,14 +93,16 @@ struct ChunkArgs {
     float* ss_out;             // EPI_STORE: [S][nitems] sum of squares of each stored 16-column tile, or null
 };
 struct ChunkCfg {
-    int nw;       // waves per workgroup (16, 8 or 4)
+    int nw;       // waves per workgroup (4 .. 16)
     int nkc;      // hidden-axis chunks per tile (chunk = nw x 128 bytes)
     int hold;     // nkc when the window rows stay in registers (nkc <= 2), else 0 (streamed with each unit)
     int depth;    // load units in flight per wave
     int grid;     // workgroups
     int items;    // tiles (16 rows; gate/up: 8 row pairs)
 };
-void set_chunk_tuning(int waves, int depth, int max_groups);
+void set_chunk_tuning(int waves, int depth, int max_groups, int head_kernel);
+// Whether the head matmul of this shape runs on the chunked ring kernel (when it applies).
+bool head_use_chunked(int V, int H);
 // False when H is not a whole number of 4-block segments for 4, 8 or 16 waves.
 bool chunked_config(int rows, int H, int epi, ChunkCfg& c);
 hipError_t launch_chunked(int epi, const ChunkCfg& c, const ChunkArgs& a, hipStream_t stream);

@@ -27,7 +27,38 @@ __global__ __launch_bounds__(kWave) void accept_kernel(const int32_t* __restrict
     accept_wave(argmax, drafts, K, tokens, cap, state, threadIdx.x);
 }
 
+// Window rows of a token-indexed stand-in model: row 0 = table[tokens[len-1]] (the anchor),
+// row i = table[drafts[i-1]] with a pad (-1) reading token 0's row.  One workgroup per row,
+// 16-byte copies.  An id outside [0, V) writes a zero row and sets the token flag; a length
+// outside [1, cap] writes zero rows and sets the capacity flag.
+__global__ __launch_bounds__(256) void gather_window_kernel(const int32_t* __restrict__ tokens, int cap,
+                                                            int32_t* __restrict__ state,
+                                                            const int32_t* __restrict__ drafts,
+                                                            const uint16_t* __restrict__ table, int V, int H,
+                                                            uint16_t* __restrict__ out) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    const int r = blockIdx.x;
+    const int len = state[SV_STATE_LEN];
+    const bool len_ok = len >= 1 && len <= cap;
+    int id;
+    if (r == 0) id = len_ok ? tokens[len - 1] : -1;
+    else id = drafts[r - 1] >= 0 ? drafts[r - 1] : 0;
+    const bool ok = len_ok && id >= 0 && id < V;
+    if (threadIdx.x == 0 && !ok) atomicOr(&state[SV_STATE_FLAGS], len_ok ? SV_FLAG_TOKEN : SV_FLAG_CAPACITY);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(table + (size_t)(ok ? id : 0) * H);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + (size_t)r * H);
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    for (int i = threadIdx.x; i < H / 8; i += 256) dst[i] = ok ? src[i] : zero;
+}
+
 }  // namespace
+
+hipError_t launch_gather_window(const int32_t* tokens, int cap, int32_t* state, const int32_t* drafts, int K,
+                                const uint16_t* table, int V, int H, uint16_t* out, hipStream_t stream) {
+    hipLaunchKernelGGL(gather_window_kernel, dim3(K + 1), dim3(256), 0, stream, tokens, cap, state, drafts, table, V,
+                       H, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_propose(const int32_t* tokens, int cap, int32_t* state, int nmax, int K, int32_t* drafts,
                           hipStream_t stream) {

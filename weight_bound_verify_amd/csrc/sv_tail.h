@@ -40,6 +40,29 @@ __device__ __forceinline__ void stage_ids(const int32_t* __restrict__ src, int n
     for (int i = done + tid; i < n; i += nt) dst[i] = src[i];
 }
 
+// Per-round statistics and the hit-rate gate ("Stream C - Speculative decoding", the shipped
+// app note: the drafter is dropped after gateAfter rounds that accepted nothing).  One thread.
+__device__ __forceinline__ void record_round(int32_t* state, int j) {
+    state[SV_STATE_J] = j;
+    const int rounds = state[SV_STATE_ROUNDS] + 1;
+    state[SV_STATE_ROUNDS] = rounds;
+    state[SV_STATE_SUMJ] += j;
+    state[SV_STATE_HIST + j] += 1;
+    const int zero_run = j == 0 ? state[SV_STATE_ZERO_RUN] + 1 : 0;
+    state[SV_STATE_ZERO_RUN] = zero_run;
+    const int gate_after = state[SV_STATE_GATE_AFTER];
+    if (gate_after > 0 && state[SV_STATE_GATED] == 0 && zero_run >= gate_after) state[SV_STATE_GATED] = rounds;
+}
+
+// The drafter's output once the hit-rate gate has fired: K pads, nothing matched.
+__device__ __forceinline__ void gated_drafts(int K, int32_t* drafts, int32_t* state) {
+    if (threadIdx.x < K) drafts[threadIdx.x] = -1;
+    if (threadIdx.x == 0) {
+        state[SV_STATE_NVALID] = 0;
+        state[SV_STATE_NUSED] = 0;
+    }
+}
+
 // Greedy accept by one wave ("Stream C - Speculative decoding", the delta and control-logic
 // proof; "Spec-decode on GDN hybrids", hybrid state discipline): lane i compares d_{i+1}
 // with the greedy id of window row i, a ballot finds the first miss j, the accepted drafts
@@ -60,10 +83,7 @@ __device__ __forceinline__ void accept_wave(const int32_t* argmax, const int32_t
     if (lane == j) tokens[len + j] = argmax[j];
     if (lane == 0) {
         state[SV_STATE_LEN] = len + 1 + j;
-        state[SV_STATE_J] = j;
-        state[SV_STATE_ROUNDS] += 1;
-        state[SV_STATE_SUMJ] += j;
-        state[SV_STATE_HIST + j] += 1;
+        if (K > 0) record_round(state, j);        // K = 0 is the anchor bootstrap, not a round
     }
 }
 
@@ -80,6 +100,10 @@ __device__ __forceinline__ void propose_block(const int32_t* tokens, int cap, in
                                               unsigned long long* wbest) {
     const int tid = threadIdx.x;
     const int nthreads = blockDim.x;
+    if (state[SV_STATE_GATED] != 0) {        // the hit-rate gate dropped the drafter
+        gated_drafts(K, drafts, state);
+        return;
+    }
     int len = state[SV_STATE_LEN];
     if (len < 0 || len > cap) {              // corrupt state: never read past the buffer
         if (tid == 0) state[SV_STATE_FLAGS] |= SV_FLAG_CAPACITY;
@@ -141,9 +165,13 @@ __device__ __forceinline__ void propose_block(const int32_t* tokens, int cap, in
 // Drafter over a stream held whole in LDS (`tk[0 .. len)`): the same rule as propose_block,
 // with no global reads.  Every thread of the workgroup must call it.
 __device__ __forceinline__ void propose_lds(const int32_t* tk, int len, int nmax, int K, int32_t* drafts,
-                                            int32_t* state, unsigned long long* wbest) {
+                                            int32_t* state, unsigned long long* wbest, bool gated) {
     const int tid = threadIdx.x;
     const int nthreads = blockDim.x;
+    if (gated) {                             // the hit-rate gate dropped the drafter (uniform)
+        gated_drafts(K, drafts, state);
+        return;
+    }
     int32_t suf[SV_MAX_NGRAM];
 #pragma unroll
     for (int i = 0; i < SV_MAX_NGRAM; ++i) suf[i] = (i < nmax && len - 1 - i >= 0) ? tk[len - 1 - i] : -1;

@@ -21,13 +21,14 @@ SV_MAX_NGRAM = 8
 SV_BLOCK = 32
 STATE_WORDS = 80
 STATE_LEN, STATE_J, STATE_NVALID, STATE_NUSED, STATE_FLAGS, STATE_ROUNDS, STATE_SUMJ, STATE_HIST = 0, 1, 2, 3, 4, 5, 6, 8
-FLAG_CAPACITY = 1
+STATE_GATE_AFTER, STATE_ZERO_RUN, STATE_GATED = 72, 73, 74
+FLAG_CAPACITY, FLAG_TOKEN = 1, 2
 STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_ALIGN", 4: "SV_ERR_WORKSPACE",
           5: "SV_ERR_CAPACITY", 6: "SV_ERR_HIP", 7: "SV_ERR_DEVICE"}
 
 EXPORTS = (
     "specverify_propose", "specverify_verify_workspace_bytes", "specverify_verify", "specverify_round",
-    "specverify_accept",
+    "specverify_accept", "specverify_gather_window", "specverify_generate",
     "specverify_rmsnorm", "specverify_stack_workspace_bytes", "specverify_gateup_silu_q8b32",
     "specverify_linear_q8b32", "specverify_linear_residual_rmsnorm_q8b32",
     "specverify_stack_forward_workspace_bytes", "specverify_stack", "specverify_set_tuning", "specverify_profile_next_matmul", "specverify_status_string", "specverify_last_error",
@@ -58,6 +59,9 @@ def load():
         "specverify_verify": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
         "specverify_round": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
         "specverify_accept": (_I, [_P, _P, _I, _P, _I, _P, _P]),
+        "specverify_gather_window": (_I, [_P, _I, _P, _P, _I, _P, _I, _I, _P, _P]),
+        "specverify_generate": (_I, [_P, _P, _I, _I, _P, _I, _I, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t,
+                                     _P]),
         "specverify_rmsnorm": (_I, [_P, _I, _I, ctypes.c_float, _P, _P]),
         "specverify_stack_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
         "specverify_gateup_silu_q8b32": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _P, _P, ctypes.c_size_t, _P]),
@@ -67,7 +71,7 @@ def load():
         "specverify_stack_forward_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
         "specverify_stack": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I, ctypes.c_float, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
-        "specverify_set_tuning": (None, [_I, _I, _I]),
+        "specverify_set_tuning": (None, [_I, _I, _I, _I]),
         "specverify_profile_next_matmul": (_I, [_P, _P]),
         "specverify_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "specverify_last_error": (ctypes.c_char_p, []),
@@ -123,8 +127,8 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
 
 
-def set_tuning(waves_per_group: int = 0, max_groups: int = 0, depth: int = 0) -> None:
-    load().specverify_set_tuning(int(waves_per_group), int(max_groups), int(depth))
+def set_tuning(waves_per_group: int = 0, max_groups: int = 0, depth: int = 0, head_kernel: int = 0) -> None:
+    load().specverify_set_tuning(int(waves_per_group), int(max_groups), int(depth), int(head_kernel))
 
 
 def profile_next_matmul(before, after, stream=None) -> None:
@@ -182,6 +186,33 @@ def accept(argmax, drafts, tokens, state, stream=None) -> None:
                                     _ptr(drafts, torch.int32, "drafts", K) if K > 0 else None, K,
                                     _ptr(tokens, torch.int32, "tokens"), tokens.numel(),
                                     _ptr(state, torch.int32, "state", STATE_WORDS), _stream(stream)))
+
+
+def gather_window(tokens, state, drafts, table, window, stream=None) -> None:
+    """window[0] = table[anchor], window[i] = table[drafts[i-1]] (pads read row 0)."""
+    V, H = table.shape
+    K = window.shape[0] - 1
+    if window.shape[1] != H:
+        raise ValueError("window and table widths differ")
+    _check(load().specverify_gather_window(
+        _ptr(tokens, torch.int32, "tokens"), tokens.numel(), _ptr(state, torch.int32, "state", STATE_WORDS),
+        _ptr(drafts, torch.int32, "drafts", K) if K > 0 else None, K, _ptr(table, torch.float16, "table"), V, H,
+        _ptr(window, torch.float16, "window"), _stream(stream)))
+
+
+def generate(wq, wscale, table, tokens, state, drafts, window, argmax, ws, rounds: int, ngram_max: int = 3,
+             stream=None) -> None:
+    """``rounds`` device-resident rounds: gather the window from ``table``, verify, accept, draft."""
+    V, H = wq.shape
+    K = drafts.numel()
+    if tuple(table.shape) != (V, H) or tuple(window.shape) != (K + 1, H) or tuple(wscale.shape) != (V, H // SV_BLOCK):
+        raise ValueError("shape mismatch")
+    _check(load().specverify_generate(
+        _ptr(wq, torch.int8, "wq"), _ptr(wscale, torch.float16, "wscale"), V, H, _ptr(table, torch.float16, "table"),
+        K, int(rounds), _ptr(tokens, torch.int32, "tokens"), tokens.numel(),
+        _ptr(state, torch.int32, "state", STATE_WORDS), int(ngram_max), _ptr(drafts, torch.int32, "drafts", K),
+        _ptr(window, torch.float16, "window"), _ptr(argmax, torch.int32, "argmax", K + 1),
+        _ptr(ws, torch.uint8, "workspace"), ws.numel(), _stream(stream)))
 
 
 def rmsnorm(x, y, eps: float = 1e-6, stream=None) -> None:
