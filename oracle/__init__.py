@@ -23,7 +23,7 @@ Parity status of every function is stated in its module docstring; all are pinne
 ``-m "not gpu"`` tests (brute force, closed forms, invariants, the pages' printed tables).
 """
 from .verify import (  # noqa: F401
-    dequantize, head_logits, argmax_lowest, top2_gap, admissible_sets, accept_length,
+    dequantize, head_logits, dequantize_q4b32, head_logits_q4b32, argmax_lowest, top2_gap, admissible_sets, accept_length,
     accept, propose_scan, NgramIndex, expected_tokens_per_round, greedy_decode,
     spec_decode, verify_round,
 )

@@ -37,6 +37,43 @@ def dequantize(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return q.astype(np.float64) * s
 
 
+def dequantize_q4b32(packed: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """fp64 weights from packed int4 codes and per-block-32 fp16 scales.
+
+    Pipelined-engine page, "Quantization on the GPU delegate" (int4 linear per-block-32,
+    the class it ships) and "Numerics gating" (QAT q4_0 weights are trained for the
+    per-block-32 absmax grid): a weight is its signed 4-bit code times the scale of its
+    32-wide block.  Storage: 16 bytes per block; byte i holds element i (low nibble) and
+    element i + 16 (high nibble) as offset binary, code = nibble - 8.
+    """
+    packed = np.asarray(packed, dtype=np.uint8)
+    scale = np.asarray(scale)
+    R, half = packed.shape
+    H = 2 * half
+    if H % BLOCK or scale.shape != (R, H // BLOCK):
+        raise ValueError("packed must be [rows, H/2] and scale [rows, H/32]")
+    by = packed.reshape(R, H // BLOCK, 16).astype(np.int64)
+    lo = (by & 0xF) - 8                                   # elements 0 .. 15 of each block
+    hi = (by >> 4) - 8                                    # elements 16 .. 31
+    codes = np.concatenate([lo, hi], axis=2).reshape(R, H)
+    return codes.astype(np.float64) * np.repeat(scale.astype(np.float64), BLOCK, axis=1)
+
+
+def head_logits_q4b32(packed: np.ndarray, scale: np.ndarray, hidden: np.ndarray, chunk: int = 8192) -> np.ndarray:
+    """All-position logits of an int4 per-block-32 head (see ``head_logits``)."""
+    h = np.asarray(hidden).astype(np.float64)
+    if h.ndim == 1:
+        h = h[None, :]
+    V = packed.shape[0]
+    out = np.empty((h.shape[0], V), dtype=np.float64)
+    for r0 in range(0, V, chunk):
+        r1 = min(V, r0 + chunk)
+        wd = dequantize_q4b32(packed[r0:r1], scale[r0:r1])
+        for s in range(h.shape[0]):
+            out[s, r0:r1] = wd @ h[s]
+    return out
+
+
 def head_logits(q: np.ndarray, scale: np.ndarray, hidden: np.ndarray, chunk: int = 8192) -> np.ndarray:
     """All-position logits L[s, v] = sum_k hidden[s, k] * Wd[v, k], in fp64.
 

@@ -63,3 +63,26 @@ def test_rmsnorm_without_mean_is_caught():
     x = np.full((1, 64), 3.0, dtype=np.float16)
     mutant = lambda x: (x / np.sqrt(np.sum(x.astype(np.float64) ** 2) + 1e-6)).astype(np.float16)
     assert (oracle.rmsnorm_fp16(x, 0.0) == 1).all() and not (mutant(x) == 1).all()
+
+
+def test_int4_nibble_order_swap_is_caught():
+    def mutant(packed, scale):                      # high nibble read as the first 16 elements
+        by = np.asarray(packed).reshape(packed.shape[0], -1, 16).astype(np.int64)
+        codes = np.concatenate([(by >> 4) - 8, (by & 15) - 8], axis=2).reshape(packed.shape[0], -1)
+        return codes * np.repeat(scale.astype(np.float64), 32, axis=1)
+    codes = np.array([((k * 5) % 15) - 7 for k in range(32)], dtype=np.int64)
+    p, s = synth.quantize_q4b32((codes.astype(np.float32) * np.float32(0.5))[None])
+    assert np.array_equal(oracle.dequantize_q4b32(p, s)[0], codes * 0.5)
+    assert not np.array_equal(mutant(p, s)[0], codes * 0.5)
+
+
+def test_int4_missing_offset_is_caught():
+    mutant = lambda packed, scale: np.repeat(scale.astype(np.float64), 32, axis=1) * np.concatenate(
+        [np.asarray(packed).reshape(1, -1, 16) & 15, np.asarray(packed).reshape(1, -1, 16) >> 4], axis=2).reshape(1, -1)
+    w = np.zeros((1, 32), dtype=np.float32)
+    w[0, 3] = 1.0
+    p, s = synth.quantize_q4b32(w)
+    e = np.zeros(32)
+    e[3] = 1.0
+    assert oracle.dequantize_q4b32(p, s)[0] @ e == float(s[0, 0]) * 7
+    assert mutant(p, s)[0] @ e != float(s[0, 0]) * 7

@@ -74,6 +74,53 @@ def quantize_q8b32(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return q.reshape(R, H), s16
 
 
+def quantize_q4b32(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-block-32 absmax symmetric int4 quantization of fp32 rows ``w[R, H]``.
+
+    scale = fp16(max|w| / 7) rounded to nearest-even; q = clamp(rint(w / scale), -7, 7) with
+    half-to-even rounding, computed in fp64; an all-zero block gets scale 0 and q = 0.
+    Packed 16 bytes per block, offset binary u = q + 8: byte i of block b holds element
+    32b + i in its low nibble and element 32b + 16 + i in its high nibble.
+    Returns ``packed`` uint8 ``[R, H/2]`` and ``scale`` fp16 ``[R, H/32]``.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    R, H = w.shape
+    if H % BLOCK:
+        raise ValueError(f"H={H} is not a multiple of {BLOCK}")
+    blocks = w.reshape(R, H // BLOCK, BLOCK)
+    m = np.abs(blocks).max(axis=2)
+    s16 = (m.astype(np.float64) / 7.0).astype(np.float16)
+    sf = s16.astype(np.float64)[..., None]
+    safe = np.where(sf > 0, sf, 1.0)
+    qf = np.where(sf > 0, np.rint(blocks.astype(np.float64) / safe), 0.0)
+    u = (np.clip(qf, -7, 7) + 8).astype(np.uint8)                     # [R, H/32, 32], 1 .. 15
+    packed = (u[:, :, :16] | (u[:, :, 16:] << 4)).astype(np.uint8)   # [R, H/32, 16]
+    return packed.reshape(R, H // 2), s16
+
+
+def quantized_head_q4(seq: np.random.SeedSequence, V: int, H: int,
+                      std: float = W_STD, workers: int | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """Draw fp32 N(0, std) weights ``[V, H]`` chunk by chunk (the same draws as
+    ``quantized_head``) and quantize them to packed int4 (q4b32)."""
+    if H % BLOCK:
+        raise ValueError(f"H={H} is not a multiple of {BLOCK}")
+    n_chunks = (V + ROWS_PER_CHUNK - 1) // ROWS_PER_CHUNK
+    children = seq.spawn(n_chunks)
+    q = np.empty((V, H // 2), dtype=np.uint8)
+    s = np.empty((V, H // BLOCK), dtype=np.float16)
+
+    def work(c: int) -> None:
+        r0 = c * ROWS_PER_CHUNK
+        r1 = min(V, r0 + ROWS_PER_CHUNK)
+        rng = np.random.default_rng(children[c])
+        w = rng.standard_normal((r1 - r0, H), dtype=np.float32) * np.float32(std)
+        q[r0:r1], s[r0:r1] = quantize_q4b32(w)
+
+    with ThreadPoolExecutor(workers or _workers()) as ex:
+        list(ex.map(work, range(n_chunks)))
+    return q, s
+
+
 def quantized_head(seq: np.random.SeedSequence, V: int, H: int,
                    std: float = W_STD, workers: int | None = None) -> tuple[np.ndarray, np.ndarray]:
     """Draw fp32 N(0, std) weights ``[V, H]`` chunk by chunk and quantize them (q8b32)."""
