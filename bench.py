@@ -35,6 +35,9 @@ WORKLOADS = {
                name="Qwen3-4B-shaped head H=2560 V=151936 K=8 S=9, n-gram drafts over 4096 Zipf(1.1) ids with 30% copied spans"),
     "c3": dict(cid=2, V=248320, H=2048, K=8, drafts="forced", ctx=4096, copy=0.30, layers=0,
                name="35B-A3B-shaped head H=2048 V=248320 K=8 S=9, drafts forced to match the first j~U{0..K} argmaxes"),
+    "c3q4": dict(cid=2, V=248320, H=2048, K=8, drafts="forced", ctx=4096, copy=0.30, layers=0, fmt="q4",
+                 name="35B-A3B-shaped int4 per-block-32 head H=2048 V=248320 K=8 S=9 (the same fp32 weights as c3), "
+                      "drafts forced to match the first j~U{0..K} argmaxes"),
     "c3s17": dict(cid=2, V=248320, H=2048, K=16, drafts="forced", ctx=4096, copy=0.30, layers=0,
                   name="35B-A3B-shaped head H=2048 V=248320 K=16 S=17, forced drafts"),
     "c4s2": dict(cid=3, V=248320, H=5120, K=1, drafts="ngram", ctx=16384, copy=0.20, layers=0,
@@ -53,9 +56,11 @@ WORKLOADS = {
 R_SETS = 64
 
 
-def head_bytes(V, H, S):
-    """Algorithmic HBM bytes of one head launch: int8 codes, fp16 block scales, fp16 window."""
-    return V * H + 2 * V * (H // 32) + 2 * S * H
+def head_bytes(V, H, S, fmt="q8"):
+    """Algorithmic HBM bytes of one head launch: int8 (or packed int4) codes, fp16 block
+    scales, fp16 window."""
+    codes = V * H // 2 if fmt == "q4" else V * H
+    return codes + 2 * V * (H // 32) + 2 * S * H
 
 
 def stack_bytes(layers, H, F, S):
@@ -90,7 +95,10 @@ def build_inputs(wl, args, torch, sv, synth):
     S = K + 1
     st = synth.streams(wl["cid"])
     t0 = time.time()
-    q, s = synth.quantized_head(st.weights, V, H)
+    if wl.get("fmt") == "q4":
+        q, s = synth.quantized_head_q4(st.weights, V, H)
+    else:
+        q, s = synth.quantized_head(st.weights, V, H)
     copies = args.rotate if args.rotate else (2 if V * H < 2 ** 31 else 1)
     wq = [torch.from_numpy(q).to(dev)]
     ws = [torch.from_numpy(s).to(dev)]
@@ -146,7 +154,10 @@ def cpu_baseline(wl, inp, table=None, seconds_budget=20.0):
             if table is not None:     # the stand-in model: rows of the oracle's own window
                 ids = [tokens[-1]] + [d if d >= 0 else 0 for d in drafts]
                 x = table[ids].cpu().numpy()
-            L = oracle.head_logits(inp["q"], inp["s"], x)
+            if wl.get("fmt") == "q4":
+                L = oracle.head_logits_q4b32(inp["q"], inp["s"], x)
+            else:
+                L = oracle.head_logits(inp["q"], inp["s"], x)
             a = oracle.argmax_lowest(L)
             if wl["drafts"] == "forced":
                 drafts, _ = synth.forced_drafts(rng, a, K, V)
@@ -228,7 +239,9 @@ def main():
         h_last = torch.from_numpy(synth.fp16_normal(synth.streams(wl["cid"]).h_last, (1, H))).to(dev)
     # anchor bootstrap: S = 1 verify of the last context row, then accept with K = 0 commits a0
     a0 = torch.empty(1, dtype=torch.int32, device=dev)
-    sv.verify(wq[0], ws[0], h_last, a0, sv.workspace(sv.verify_workspace_bytes(V, H, 1), dev))
+    head_verify = sv.verify_q4 if wl.get("fmt") == "q4" else sv.verify
+    head_round = sv.round_q4 if wl.get("fmt") == "q4" else sv.round
+    head_verify(wq[0], ws[0], h_last, a0, sv.workspace(sv.verify_workspace_bytes(V, H, 1), dev))
     sv.accept(a0, None, tokens, state)
 
     forced = None
@@ -237,7 +250,7 @@ def main():
         rng_d = np.random.default_rng(synth.streams(wl["cid"]).drafts)
         fd = np.empty((R_SETS, K), dtype=np.int32)
         for r in range(R_SETS):
-            sv.verify(wq[0], ws[0], hidden[r], argmax, work)
+            head_verify(wq[0], ws[0], hidden[r], argmax, work)
             torch.cuda.synchronize()
             fd[r], _ = synth.forced_drafts(rng_d, argmax.cpu().numpy(), K, V)
         forced = torch.from_numpy(fd).to(dev)
@@ -267,7 +280,7 @@ def main():
         else:
             x = hidden[r % R_SETS]
         d_in = forced[r % R_SETS] if forced is not None else drafts
-        sv.round(wq[c], ws[c], x, d_in, tokens, state, drafts, argmax, work)
+        head_round(wq[c], ws[c], x, d_in, tokens, state, drafts, argmax, work)
 
     for r in range(args.warmup):
         round_(r)
@@ -305,11 +318,11 @@ def main():
         if table is not None:
             sv.generate(wq[c], ws[c], table, tokens, state, drafts, window, argmax, work, 1, stream=stream)
         else:
-            sv.round(wq[c], ws[c], x, d_in, tokens, state, drafts, argmax, work, stream=stream)
+            head_round(wq[c], ws[c], x, d_in, tokens, state, drafts, argmax, work, stream=stream)
         durs.append((e0, e1))
     torch.cuda.synchronize()
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in durs]))
-    hb = head_bytes(V, H, S)
+    hb = head_bytes(V, H, S, wl.get("fmt", "q8"))
     achieved = hb / (kern_ms * 1e-3) / 1e9
 
     round_bytes = hb + (stack_bytes(wl["layers"], H, F, S) if wl["layers"] else 0)
@@ -326,7 +339,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8xf16->f32",
+        "dtype": "i4xf16->f32" if wl.get("fmt") == "q4" else "i8xf16->f32",
         "data": "synthetic",
         "config": {"workload": wl["name"], "V": V, "H": H, "S": S, "K": K, "layers": wl["layers"],
                    "drafts": wl["drafts"], "weight_copies": copies, "hidden_sets": R_SETS},
@@ -335,7 +348,8 @@ def main():
         "bytes_per_round": round_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": load_traffic(args.config),
-                     "kernel": "q8b32 head matmul with the fused argmax stage 1 (one launch per round)",
+                     "kernel": ("q4b32" if wl.get("fmt") == "q4" else "q8b32")
+                               + " head matmul with the fused argmax stage 1 (one launch per round)",
                      "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": hb},
         "accept_hist": hist,
         "tokens_per_round": round((args.steps + sum_j) / args.steps, 3),

@@ -156,6 +156,30 @@ int specverify_round(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_
                      hipStream_t stream);
 
 /*
+ * specverify_verify_q4b32 / specverify_round_q4b32 - the int4 per-block-32 head: the same
+ * contract as specverify_verify / specverify_round with half the weight bytes.
+ * Page: "Riding Apple's pipelined GPU engine", sections "Quantization on the GPU delegate"
+ * (int4 linear per-block-32, the int4 class that ships) and "Numerics gating" (QAT q4_0
+ * weights follow the per-block-32 absmax grid).
+ *   L[s, v] = sum_b f32(wscale[v, b]) * sum_{k in block b} code[v, k] * f32(hidden[s, k])
+ *   wq      uint8 [V][H/2]: per 32-block 16 bytes, byte i = (element i + 8) | (element i+16 + 8) << 4,
+ *           codes -8 .. 7 (the library's quantizer writes -7 .. 7); 16-byte aligned
+ *   wscale  fp16 [V][H/32], 16-byte aligned;   H: multiple of 256 in [256, 65536] that 8 or
+ *           16 blocks per wave cover with 1 .. 16 waves (e.g. 512, 1024, 2048, 2560, 3072,
+ *           4096, 5120 ...);   S = K+1: 1 .. 16
+ *   workspace  at least specverify_verify_workspace_bytes(V, H, S) bytes
+ * Other arguments and errors as for specverify_verify / specverify_round.
+ */
+int specverify_verify_q4b32(const uint8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
+                            const uint16_t* hidden, int32_t S, int32_t* argmax, float* logits,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+int specverify_round_q4b32(const uint8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
+                           const uint16_t* hidden, int32_t K, const int32_t* drafts_in,
+                           int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max,
+                           int32_t* drafts_out, int32_t* argmax, float* logits, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
  * specverify_gather_window - the window rows of a token-indexed stand-in model:
  *   window[0] = table[tokens[len-1]] (the anchor a0, len = state[0]),
  *   window[i] = table[drafts[i-1]] for i = 1 .. K, a pad (-1) reading token 0's row,

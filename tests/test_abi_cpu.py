@@ -161,6 +161,19 @@ def test_generate_and_gather_argument_errors(lib):
     assert gw(A16, 100, A16, A16, 8, A16, 1000, 256, A2, NULL) == 3
 
 
+def test_int4_head_argument_errors(lib):
+    ws = lib.specverify_verify_workspace_bytes(1000, 2048, 9)
+    f = lib.specverify_verify_q4b32
+    assert f(NULL, A16, 1000, 2048, A16, 9, A16, NULL, A16, ws, NULL) == 1
+    assert f(A16, A16, 1000, 2000, A16, 9, A16, NULL, A16, ws, NULL) == 2      # H not a multiple of 256
+    assert f(A16, A16, 1000, 2048, A16, 17, A16, NULL, A16, ws, NULL) == 2     # S <= 16
+    assert f(A2, A16, 1000, 2048, A16, 9, A16, NULL, A16, ws, NULL) == 3
+    assert f(A16, A16, 1000, 2048, A16, 9, A16, NULL, A16, 100, NULL) == 4
+    r = lib.specverify_round_q4b32
+    assert r(A16, A16, 1000, 2048, A16, 16, A16, A16, 100, A16, 3, A16, A16, NULL, A16, ws, NULL) == 2  # K <= 15
+    assert r(A16, A16, 1000, 2048, A16, 8, NULL, A16, 100, A16, 3, A16, A16, NULL, A16, ws, NULL) == 1
+
+
 def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(sv, "_lib", None)
     monkeypatch.setattr(sv, "LIB_PATH", str(tmp_path / "nope.so"))

@@ -232,6 +232,76 @@ int specverify_round(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_
                        ngram_max, drafts_out, stream);
 }
 
+namespace {
+
+int check_head_q4(const uint8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
+                  int32_t S, int32_t* argmax, float* logits, void* workspace, size_t workspace_bytes,
+                  sv::Q4Cfg& cfg) {
+    if (!wq || !wscale || !hidden || !argmax || !workspace) return fail(SV_ERR_NULL, "weights, scales, hidden, argmax and workspace are required");
+    if (V < 1 || V > (1 << 30)) return fail(SV_ERR_SHAPE, "V=%d outside [1, 2^30]", V);
+    if (S < 1 || S > 16) return fail(SV_ERR_SHAPE, "S=%d outside [1, 16]", S);
+    if (H < 256 || H > 65536 || !sv::q4_config(V, H, cfg))
+        return fail(SV_ERR_SHAPE, "H=%d: needs a multiple of 256 that 8 or 16 blocks per wave cover", H);
+    if (!aligned(wq, 16) || !aligned(wscale, 16) || !aligned(hidden, 16) || !aligned(workspace, 16) ||
+        !aligned(argmax, 4) || (logits && !aligned(logits, 4)))
+        return fail(SV_ERR_ALIGN, "codes, scales, hidden and workspace 16-byte; argmax, logits 4-byte");
+    if (workspace_bytes < sv::head_partials_bytes(S))
+        return fail(SV_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, sv::head_partials_bytes(S));
+    return SV_OK;
+}
+
+int launch_head_q4(const sv::Q4Cfg& cfg, const uint8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
+                   const uint16_t* hidden, int32_t S, int32_t* argmax, float* logits, void* workspace, bool round,
+                   const int32_t* drafts_in, int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max,
+                   int32_t* drafts_out, hipStream_t stream) {
+    char* ws = static_cast<char*>(workspace);
+    sv::Q4Args a{};
+    a.w = wq; a.s = wscale; a.x = hidden;
+    a.V = V; a.H = H; a.S = S; a.nb = H / SV_BLOCK; a.nitems = cfg.items;
+    a.part_val = reinterpret_cast<float*>(ws);
+    a.part_idx = reinterpret_cast<int*>(ws + (size_t)4 * S * sv::kGridMax);
+    a.logits = logits;
+    hipEvent_t before = g_prof_before, after = g_prof_after;
+    g_prof_before = g_prof_after = nullptr;
+    hipError_t e = before ? hipEventRecord(before, stream) : hipSuccess;
+    if (e == hipSuccess) e = sv::launch_q4(cfg, a, stream);
+    if (e == hipSuccess && after) e = hipEventRecord(after, stream);
+    if (e != hipSuccess) return hip_fail(e, "int4 verify matmul launch");
+    e = sv::launch_round_tail(a.part_val, a.part_idx, cfg.grid, S, argmax, round ? drafts_in : nullptr, tokens, cap,
+                              state, ngram_max, round ? drafts_out : nullptr, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "argmax/round tail launch");
+}
+
+}  // namespace
+
+int specverify_verify_q4b32(const uint8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
+                            int32_t S, int32_t* argmax, float* logits, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    sv::Q4Cfg cfg{};
+    if (int st = check_head_q4(wq, wscale, V, H, hidden, S, argmax, logits, workspace, workspace_bytes, cfg)) return st;
+    if (int st = check_device()) return st;
+    return launch_head_q4(cfg, wq, wscale, V, H, hidden, S, argmax, logits, workspace, false, nullptr, nullptr, 0,
+                          nullptr, 0, nullptr, stream);
+}
+
+int specverify_round_q4b32(const uint8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
+                           int32_t K, const int32_t* drafts_in, int32_t* tokens, int32_t cap, int32_t* state,
+                           int32_t ngram_max, int32_t* drafts_out, int32_t* argmax, float* logits, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+    if (K < 1 || K > 15) return fail(SV_ERR_SHAPE, "K=%d outside [1, 15]", K);
+    sv::Q4Cfg cfg{};
+    if (int st = check_head_q4(wq, wscale, V, H, hidden, K + 1, argmax, logits, workspace, workspace_bytes, cfg))
+        return st;
+    if (!drafts_in || !tokens || !state || !drafts_out) return fail(SV_ERR_NULL, "drafts, tokens and state are required");
+    if (ngram_max < 1 || ngram_max > SV_MAX_NGRAM) return fail(SV_ERR_SHAPE, "ngram_max=%d outside [1, %d]", ngram_max, SV_MAX_NGRAM);
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(drafts_in, 4) || !aligned(tokens, 4) || !aligned(state, 4) || !aligned(drafts_out, 4))
+        return fail(SV_ERR_ALIGN, "int32 buffers must be 4-byte aligned");
+    if (int st = check_device()) return st;
+    return launch_head_q4(cfg, wq, wscale, V, H, hidden, K + 1, argmax, logits, workspace, true, drafts_in, tokens,
+                          cap, state, ngram_max, drafts_out, stream);
+}
+
 int specverify_gather_window(const int32_t* tokens, int32_t cap, int32_t* state, const int32_t* drafts, int32_t K,
                              const uint16_t* table, int32_t V, int32_t H, uint16_t* window, hipStream_t stream) {
     if (!tokens || !state || !table || !window || (K > 0 && !drafts))

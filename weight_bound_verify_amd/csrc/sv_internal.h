@@ -73,6 +73,22 @@ constexpr int kRowNormMaxSplit = 8;
 hipError_t launch_row_norm(const float* part, int ks, int S, int N, const uint16_t* residual, uint16_t* y,
                            float eps, uint16_t* norm_out, hipStream_t stream);
 
+// Int4 per-block-32 head matmul with the argmax epilogue (sv_q4.hip).  Window rows S <= 16.
+struct Q4Args {
+    const uint8_t* w;          // [V][H/2] packed codes
+    const uint16_t* s;         // [V][H/32] fp16 scales
+    const uint16_t* x;         // [S][H] fp16 window rows
+    int V, H, S, nb, nitems;
+    float* part_val;           // per-workgroup argmax partials [S][kGridMax]
+    int* part_idx;
+    float* logits;             // [S][V] or null
+};
+struct Q4Cfg {
+    int nbw, nw, grid, items;
+};
+bool q4_config(int V, int H, Q4Cfg& c);
+hipError_t launch_q4(const Q4Cfg& c, const Q4Args& a, hipStream_t stream);
+
 // Chunked streaming matmul (dense stack, and heads whose hidden axis splits into whole 128-byte
 // wave segments): see sv_chunked.hip.  Window rows S <= 16.
 struct ChunkArgs {

@@ -28,7 +28,8 @@ STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_ALIGN", 4:
 
 EXPORTS = (
     "specverify_propose", "specverify_verify_workspace_bytes", "specverify_verify", "specverify_round",
-    "specverify_accept", "specverify_gather_window", "specverify_generate",
+    "specverify_accept", "specverify_gather_window", "specverify_generate", "specverify_verify_q4b32",
+    "specverify_round_q4b32",
     "specverify_rmsnorm", "specverify_stack_workspace_bytes", "specverify_gateup_silu_q8b32",
     "specverify_linear_q8b32", "specverify_linear_residual_rmsnorm_q8b32",
     "specverify_stack_forward_workspace_bytes", "specverify_stack", "specverify_set_tuning", "specverify_profile_next_matmul", "specverify_status_string", "specverify_last_error",
@@ -60,6 +61,9 @@ def load():
         "specverify_round": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
         "specverify_accept": (_I, [_P, _P, _I, _P, _I, _P, _P]),
         "specverify_gather_window": (_I, [_P, _I, _P, _P, _I, _P, _I, _I, _P, _P]),
+        "specverify_verify_q4b32": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+        "specverify_round_q4b32": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t,
+                                        _P]),
         "specverify_generate": (_I, [_P, _P, _I, _I, _P, _I, _I, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t,
                                      _P]),
         "specverify_rmsnorm": (_I, [_P, _I, _I, ctypes.c_float, _P, _P]),
@@ -172,6 +176,38 @@ def round(wq, wscale, hidden, drafts_in, tokens, state, drafts_out, argmax, ws, 
         raise ValueError("shape mismatch")
     _check(load().specverify_round(
         _ptr(wq, torch.int8, "wq"), _ptr(wscale, torch.float16, "wscale"), V, H,
+        _ptr(hidden, torch.float16, "hidden"), K, _ptr(drafts_in, torch.int32, "drafts_in", K),
+        _ptr(tokens, torch.int32, "tokens"), tokens.numel(), _ptr(state, torch.int32, "state", STATE_WORDS),
+        int(ngram_max), _ptr(drafts_out, torch.int32, "drafts_out", K), _ptr(argmax, torch.int32, "argmax", S),
+        _ptr(logits, torch.float32, "logits", S * V), _ptr(ws, torch.uint8, "workspace"), ws.numel(),
+        _stream(stream)))
+
+
+def verify_q4(wq4, wscale, hidden, argmax, ws, logits=None, stream=None) -> None:
+    """argmax[s] of the int4 per-block-32 head (codes uint8 [V, H/2]); optional fp32 logits."""
+    V, half = wq4.shape
+    H = 2 * half
+    S = hidden.shape[0]
+    if hidden.shape[1] != H or tuple(wscale.shape) != (V, H // SV_BLOCK):
+        raise ValueError("shape mismatch between wq4, wscale and hidden")
+    _check(load().specverify_verify_q4b32(
+        _ptr(wq4, torch.uint8, "wq4"), _ptr(wscale, torch.float16, "wscale"), V, H,
+        _ptr(hidden, torch.float16, "hidden"), S, _ptr(argmax, torch.int32, "argmax", S),
+        _ptr(logits, torch.float32, "logits", S * V), _ptr(ws, torch.uint8, "workspace"), ws.numel(),
+        _stream(stream)))
+
+
+def round_q4(wq4, wscale, hidden, drafts_in, tokens, state, drafts_out, argmax, ws, ngram_max: int = 3, logits=None,
+             stream=None) -> None:
+    """The fused round on the int4 head."""
+    V, half = wq4.shape
+    H = 2 * half
+    S = hidden.shape[0]
+    K = S - 1
+    if hidden.shape[1] != H or tuple(wscale.shape) != (V, H // SV_BLOCK) or drafts_in.numel() < K:
+        raise ValueError("shape mismatch")
+    _check(load().specverify_round_q4b32(
+        _ptr(wq4, torch.uint8, "wq4"), _ptr(wscale, torch.float16, "wscale"), V, H,
         _ptr(hidden, torch.float16, "hidden"), K, _ptr(drafts_in, torch.int32, "drafts_in", K),
         _ptr(tokens, torch.int32, "tokens"), tokens.numel(), _ptr(state, torch.int32, "state", STATE_WORDS),
         int(ngram_max), _ptr(drafts_out, torch.int32, "drafts_out", K), _ptr(argmax, torch.int32, "argmax", S),
