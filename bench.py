@@ -3,12 +3,18 @@
 A step is one device-resident verify round through the C ABI entry point specverify_round:
   int8 per-block-32 head matmul of the S = K+1 window + fused argmax
   -> greedy accept (commits 1 + j tokens) -> n-gram drafter for the next round
-(the dense-stack workload runs 36 x [rmsnorm, gate/up + SiLU*mul, down + residual] and a
-final rmsnorm in front of the head, through specverify_stack).  Inputs are seeded synthetic data resident in HBM before
-the timed region; hidden rows rotate over 64 sets and, for heads that could sit in the
-256 MB Infinity Cache, over several copies of the weights.
+The dense-stack workload runs 36 x [rmsnorm, gate/up + SiLU*mul, down + residual] and a final
+rmsnorm in front of the head, through specverify_stack; the int4 workload swaps in the int4
+per-block-32 head (specverify_round_q4b32); the generation-loop workload gathers each window
+from a token-indexed stand-in model on the device (specverify_generate).  Inputs are seeded
+synthetic data resident in HBM before the timed region; hidden rows rotate over 64 sets and, for
+heads that could sit in the 256 MB Infinity Cache, over several copies of the weights.
 
 Prints one JSON line.  --gpus N with N > 1 is not supported (one GPU per box).
+
+Host-only helpers for the profile summaries (no GPU needed):
+  bench.py summarize-trace DB OUT TITLE COMMAND [NOTE]
+  bench.py summarize-counters WORKLOAD KERNEL_SUBSTRING PROFILE_DIR COMMAND...
 """
 from __future__ import annotations
 
@@ -68,25 +74,86 @@ def stack_bytes(layers, H, F, S):
     return layers * (per + 2 * S * (H + 2 * F + H))
 
 
-def kernel_source_hash():
+def kernel_source_hash(fmt="q8"):
+    """Hash of the sources the head kernel of this weight format is built from."""
     h = hashlib.sha256()
-    for name in ("sv_gemm.hip", "sv_device.h"):
+    for name in (("sv_q4.hip",) if fmt == "q4" else ("sv_gemm.hip",)) + ("sv_device.h",):
         with open(os.path.join(ROOT, "weight_bound_verify_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
+def counters_path(workload):
+    fmt = WORKLOADS[workload].get("fmt", "q8")
+    return os.path.join(ROOT, "profiles", f"verify_{fmt}b32_{workload}_counters.json")
+
+
 def load_traffic(workload):
     """HBM traffic per launch of the head kernel from the committed counter summary, if it was
     taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"verify_q8b32_{workload}_counters.json")
+    path = counters_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(WORKLOADS[workload].get("fmt", "q8")):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def summarize_trace(db_path, out, title, cmd, note=""):
+    """Markdown per-kernel summary (calls, total, average duration) of a rocprofv3
+    --kernel-trace database; runs on the host, no GPU needed."""
+    import collections
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    st = collections.OrderedDict()
+    for n, s, e in db.execute("select name, start, end from kernels order by start"):
+        st.setdefault(n, []).append((e - s) / 1000.0)
+    tot = sum(sum(v) for v in st.values())
+    lines = [f"# {title}", "", "Command (from the repository root, TMPDIR=/tmp):", "", f"    {cmd}", ""]
+    if note:
+        lines += [note, ""]
+    lines += ["| kernel | calls | total us | average us | % |", "|---|---|---|---|---|"]
+    for n, v in sorted(st.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{n[:110]}` | {len(v)} | {sum(v):.1f} | {sum(v) / len(v):.3f} | {100 * sum(v) / tot:.1f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_counters(workload, kernel_sub, pdir, commands):
+    """HBM traffic per head launch from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per
+    dispatch) and the same counters on a 1 GiB device copy (bench.py --calib-copy), which fix the
+    factor from counter units to bytes.  Writes the counter summary that load_traffic reads."""
+    import sqlite3
+    import statistics
+
+    def vals(path, sub):
+        rows = sqlite3.connect(path).execute("select kernel_name, value from counters_collection").fetchall()
+        return [v for n, v in rows if sub in n], sorted(set(n for n, v in rows if sub in n))
+
+    f, names = vals(f"{pdir}/pmc_FETCH_SIZE/{workload}_results.db", kernel_sub)
+    w, _ = vals(f"{pdir}/pmc_WRITE_SIZE/{workload}_results.db", kernel_sub)
+    cf, _ = vals(f"{pdir}/calib_FETCH_SIZE/calib_results.db", "copyBuffer")
+    cw, _ = vals(f"{pdir}/calib_WRITE_SIZE/calib_results.db", "copyBuffer")
+    copy = 1 << 30
+    ff = round(copy / 1024 / statistics.median(cf[1:]), 1)   # the first copy is the host upload
+    fw = round(copy / 1024 / statistics.median(cw[1:]), 1)
+    fm, wm = statistics.median(f), statistics.median(w)
+    rec = {
+        "workload": workload, "kernel": names[0] if len(names) == 1 else names,
+        "kernel_source_hash": kernel_source_hash(WORKLOADS[workload].get("fmt", "q8")),
+        "fetch_size_kib_per_dispatch_median": fm, "write_size_kib_per_dispatch_median": wm,
+        "dispatches": len(f),
+        "calibration": {"copy_bytes": copy, "fetch_factor": ff, "write_factor": fw,
+                        "note": "a 1 GiB device copy reads and writes 1 GiB; the factors scale the counters to bytes"},
+        "traffic_bytes_per_launch": int(round((fm * ff + wm * fw) * 1024)),
+        "commands": commands,
+    }
+    with open(counters_path(workload), "w") as fo:
+        json.dump(rec, fo, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def build_inputs(wl, args, torch, sv, synth):
@@ -174,6 +241,14 @@ def cpu_baseline(wl, inp, table=None, seconds_budget=20.0):
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "summarize-trace":
+        # bench.py summarize-trace DB OUT TITLE COMMAND [NOTE]
+        summarize_trace(*sys.argv[2:])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "summarize-counters":
+        # bench.py summarize-counters WORKLOAD KERNEL_SUBSTRING PROFILE_DIR COMMAND...
+        summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
