@@ -86,3 +86,35 @@ def test_int4_missing_offset_is_caught():
     e[3] = 1.0
     assert oracle.dequantize_q4b32(p, s)[0] @ e == float(s[0, 0]) * 7
     assert mutant(p, s)[0] @ e != float(s[0, 0]) * 7
+
+
+def _sampling_law_pvalue():
+    """The law pin of speculative sampling (chi-square over the first three tokens)."""
+    from tests.test_oracle_sampling import Markov, _chi2_pvalue, _exact_law, _greedy_chain_drafter, _law_counts
+    model = Markov(4, 21)
+    counts = _law_counts(model, 1.0, 3, _greedy_chain_drafter(model), 3000)
+    return _chi2_pvalue(counts, _exact_law(model, 1.0))
+
+
+def test_residual_that_keeps_the_rejected_draft_is_caught(monkeypatch):
+    from oracle import sampling as smp
+    monkeypatch.setattr(smp, "residual", lambda p, d: np.asarray(p, dtype=np.float64))   # redraw from p itself
+    assert _sampling_law_pvalue() < 1e-6
+
+
+def test_accept_test_on_the_wrong_row_is_caught(monkeypatch):
+    from oracle import sampling as smp
+    orig = smp.sampling_verify
+
+    def mutant(L, drafts, T, seed, P0):             # d_{s+1} tested against row s+1, not row s
+        r = orig(L, drafts, T, seed, P0)
+        p, _ = smp.probabilities(L, T)
+        K = len(drafts)
+        pd = np.array([p[s + 1, d] if 0 <= d < p.shape[1] else 0.0 for s, d in enumerate(drafts)])
+        j = 0
+        while j < K and r["u_accept"][j] < pd[j]:
+            j += 1
+        r["j"], r["appended"] = j, list(drafts[:j]) + [int(r["sample"][j])]
+        return r
+    monkeypatch.setattr(smp, "sampling_verify", mutant)
+    assert _sampling_law_pvalue() < 1e-6
