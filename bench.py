@@ -44,6 +44,9 @@ WORKLOADS = {
     "c3q4": dict(cid=2, V=248320, H=2048, K=8, drafts="forced", ctx=4096, copy=0.30, layers=0, fmt="q4",
                  name="35B-A3B-shaped int4 per-block-32 head H=2048 V=248320 K=8 S=9 (the same fp32 weights as c3), "
                       "drafts forced to match the first j~U{0..K} argmaxes"),
+    "c3samp": dict(cid=2, V=248320, H=2048, K=8, drafts="forced", ctx=4096, copy=0.30, layers=0, temp=0.7,
+                   name="sampling verify at T=0.7: 35B-A3B-shaped head H=2048 V=248320 K=8 S=9, drafts forced to "
+                        "match the first j~U{0..K} argmaxes, kept with probability p(d) (speculative sampling)"),
     "c3s17": dict(cid=2, V=248320, H=2048, K=16, drafts="forced", ctx=4096, copy=0.30, layers=0,
                   name="35B-A3B-shaped head H=2048 V=248320 K=16 S=17, forced drafts"),
     "c4s2": dict(cid=3, V=248320, H=5120, K=1, drafts="ngram", ctx=16384, copy=0.20, layers=0,
@@ -60,6 +63,7 @@ WORKLOADS = {
                name="dense stack 36 x [4096->12288 gate/up, 12288->4096 down] + 4096x151936 head, K=8 S=9"),
 }
 R_SETS = 64
+SAMPLE_SEED = 0x5EED_0000_2026
 
 
 def head_bytes(V, H, S, fmt="q8"):
@@ -228,7 +232,10 @@ def cpu_baseline(wl, inp, table=None, seconds_budget=20.0):
             a = oracle.argmax_lowest(L)
             if wl["drafts"] == "forced":
                 drafts, _ = synth.forced_drafts(rng, a, K, V)
-            _, app = oracle.accept(a, drafts)
+            if wl.get("temp"):
+                app = oracle.sampling_verify(L, drafts, wl["temp"], SAMPLE_SEED, len(tokens))["appended"]
+            else:
+                _, app = oracle.accept(a, drafts)
             tokens += app
             rounds += 1
             el = time.perf_counter() - t0
@@ -236,8 +243,9 @@ def cpu_baseline(wl, inp, table=None, seconds_budget=20.0):
                 break
     return {"value": rounds / el, "unit": "rounds/s", "cores": 1, "kind": "oracle",
             "sample": f"{rounds} whole rounds of this workload (fp64 dequantize in 8192-row chunks, "
-                      f"fp64 logits for S={S}, argmax, accept, n-gram propose over the {len(inp['ctx'])}-id "
-                      f"context), single thread, {el:.1f} s"}
+                      f"fp64 logits for S={S}, "
+                      + ("softmax, Philox noise, residual draws, sampling accept" if wl.get("temp") else "argmax, accept")
+                      + f", n-gram propose over the {len(inp['ctx'])}-id context), single thread, {el:.1f} s"}
 
 
 def main():
@@ -299,7 +307,8 @@ def main():
     state[sv.STATE_LEN] = len(inp["ctx"])
     drafts = torch.empty(K, dtype=torch.int32, device=dev)
     argmax = torch.empty(S, dtype=torch.int32, device=dev)
-    work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev)
+    temp = wl.get("temp")
+    work = sv.workspace(sv.sample_workspace_bytes(V, H, S) if temp else sv.verify_workspace_bytes(V, H, S), dev)
 
     table = window = None
     if wl.get("model") == "table":
@@ -316,16 +325,28 @@ def main():
     a0 = torch.empty(1, dtype=torch.int32, device=dev)
     head_verify = sv.verify_q4 if wl.get("fmt") == "q4" else sv.verify
     head_round = sv.round_q4 if wl.get("fmt") == "q4" else sv.round
-    head_verify(wq[0], ws[0], h_last, a0, sv.workspace(sv.verify_workspace_bytes(V, H, 1), dev))
-    sv.accept(a0, None, tokens, state)
+    if temp:
+        # sampling: the anchor is a draw from the last context row, a one-row sampling round
+        lse0, zd0 = (torch.empty(1, dtype=torch.float32, device=dev) for _ in range(2))
+        sv.verify_sample(wq[0], ws[0], h_last, None, temp, SAMPLE_SEED, state, a0, lse0, zd0,
+                         sv.workspace(sv.sample_workspace_bytes(V, H, 1), dev))
+        sv.accept_sample(a0, lse0, zd0, None, V, SAMPLE_SEED, tokens, state)
+
+        def head_round(w_, s_, x_, d_in_, tokens_, state_, drafts_, argmax_, work_, stream=None):
+            sv.round_sample(w_, s_, x_, d_in_, temp, SAMPLE_SEED, tokens_, state_, drafts_, work_, 3, argmax_,
+                            stream=stream)
+    else:
+        head_verify(wq[0], ws[0], h_last, a0, sv.workspace(sv.verify_workspace_bytes(V, H, 1), dev))
+        sv.accept(a0, None, tokens, state)
 
     forced = None
     if wl["drafts"] == "forced":
         # drafts that match the first j ~ U{0..K} greedy ids of each hidden set (setup, untimed)
         rng_d = np.random.default_rng(synth.streams(wl["cid"]).drafts)
         fd = np.empty((R_SETS, K), dtype=np.int32)
+        gwork = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev)
         for r in range(R_SETS):
-            head_verify(wq[0], ws[0], hidden[r], argmax, work)
+            head_verify(wq[0], ws[0], hidden[r], argmax, gwork)
             torch.cuda.synchronize()
             fd[r], _ = synth.forced_drafts(rng_d, argmax.cpu().numpy(), K, V)
         forced = torch.from_numpy(fd).to(dev)
@@ -424,11 +445,16 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": load_traffic(args.config),
                      "kernel": ("q4b32" if wl.get("fmt") == "q4" else "q8b32")
-                               + " head matmul with the fused argmax stage 1 (one launch per round)",
+                               + (" head matmul with the fused sampling epilogue (log-sum-exp, Gumbel-max "
+                                  "draw) stage 1 (one launch per round)" if temp else
+                                  " head matmul with the fused argmax stage 1 (one launch per round)"),
                      "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": hb},
         "accept_hist": hist,
         "tokens_per_round": round((args.steps + sum_j) / args.steps, 3),
     }
+    if temp:
+        out["config"]["temperature"] = temp
+        out["config"]["seed"] = SAMPLE_SEED
     if inp["copy_frac"] is not None:
         out["config"]["context_copy_fraction"] = round(inp["copy_frac"], 3)
     if table is not None:

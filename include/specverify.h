@@ -5,6 +5,7 @@
  *   specverify_propose  n-gram prompt-lookup drafter over the committed token stream
  *   specverify_verify   int8 per-block-32 head matmul of the S = K+1 window + per-row argmax
  *   specverify_accept   greedy longest-prefix acceptance, commits 1 + j tokens
+ *   specverify_*_sample sampling verify at temperature > 0 (probabilities, residual redraw)
  * plus the dense weight-bound stack in front of the head (rmsnorm, gate/up + SiLU*mul,
  * down + residual) built on the same int8 matmul core.
  *
@@ -178,6 +179,53 @@ int specverify_round_q4b32(const uint8_t* wq, const uint16_t* wscale, int32_t V,
                            int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max,
                            int32_t* drafts_out, int32_t* argmax, float* logits, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Sampling verify (temperature > 0): specverify_verify_sample, specverify_accept_sample and
+ * the fused specverify_round_sample.
+ * Page: "Stream C - Speculative decoding", the deferred list (sampling stays lossless only if
+ * verify uses the target's probabilities and redraws a rejected position from the residual
+ * distribution).  The rule is standard speculative sampling for a drafter that proposes one
+ * token per position (the n-gram drafter, q = point mass at d):
+ *   z_s = L[s, :] / T,  p_s = softmax(z_s),  lse_s = log sum_v exp(z_s[v])
+ *   draft d_{s+1} is kept iff it is a vocabulary id and u_s < p_s(d_{s+1}) = exp(z_s[d] - lse_s)
+ *   at the first draft not kept (j), row j's token is drawn from max(0, p_j - e_d) renormalised
+ *   (the ids other than d_{j+1}); if all K are kept, row K's token is drawn from p_K;
+ *   the round appends d_1..d_j and that draw (len += 1 + j), as the greedy round does.
+ * Random numbers are Philox4x32-10 (Salmon et al., SC'11) with key = seed (low word first); a
+ * round that starts at len = state[0] = P0 uses for the draw of row s, id v the counter
+ * (v, P0, s/4, 0), word s%4, and for the test of d_{s+1} the counter (0, P0, s/4, 1), word
+ * s%4; a word w becomes u = (floor(w / 2^9) + 0.5) / 2^23.  Draws use Gumbel-max: the id of
+ * the largest z_s[v] - log(-log u), lowest id on equal keys.  Window rows S = K+1 <= 16.
+ *
+ * specverify_verify_sample - the head matmul with the sampling epilogue:
+ *   sample[s]  int32 [S]: row s's draw from its residual against d_{s+1} (row S-1: from p)
+ *   lse[s]     fp32 [S]:  lse_s;   zd[s] fp32 [S]: z_s[d_{s+1}] for rows with a vocabulary-id
+ *              draft (other entries are not written);   logits fp32 [S][V] or NULL (L, not z)
+ *   drafts     int32 [S-1] (NULL when S = 1);  state: state[0] gives P0 (read only)
+ *   temperature > 0, finite, with a finite inverse;  workspace: specverify_sample_workspace_bytes
+ * specverify_accept_sample - the accept step from those outputs (one wave); K in 0 .. 15, K = 0
+ *   commits sample[0] (the bootstrap draw of the anchor) and is not counted as a round.
+ * specverify_round_sample - verify_sample -> accept_sample -> specverify_propose in two
+ *   launches; sample / lse (may be NULL) receive the per-row draws and log-normalisers.
+ * Errors as for specverify_verify / specverify_round; SV_ERR_SHAPE for a temperature out of
+ * range or S > 16.
+ */
+size_t specverify_sample_workspace_bytes(int32_t V, int32_t H, int32_t S);
+int specverify_verify_sample(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
+                             const uint16_t* hidden, int32_t S, const int32_t* drafts,
+                             float temperature, uint64_t seed, const int32_t* state,
+                             int32_t* sample, float* lse, float* zd, float* logits,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+int specverify_accept_sample(const int32_t* sample, const float* lse, const float* zd,
+                             const int32_t* drafts, int32_t K, int32_t V, uint64_t seed,
+                             int32_t* tokens, int32_t cap, int32_t* state, hipStream_t stream);
+int specverify_round_sample(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
+                            const uint16_t* hidden, int32_t K, const int32_t* drafts_in,
+                            float temperature, uint64_t seed, int32_t* tokens, int32_t cap,
+                            int32_t* state, int32_t ngram_max, int32_t* drafts_out,
+                            int32_t* sample, float* lse, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /*
  * specverify_gather_window - the window rows of a token-indexed stand-in model:

@@ -174,6 +174,31 @@ def test_int4_head_argument_errors(lib):
     assert r(A16, A16, 1000, 2048, A16, 8, NULL, A16, 100, A16, 3, A16, A16, NULL, A16, ws, NULL) == 1
 
 
+def test_sampling_argument_errors(lib):
+    ws = lib.specverify_sample_workspace_bytes(1000, 256, 9)
+    assert ws > lib.specverify_verify_workspace_bytes(1000, 256, 9)
+    assert lib.specverify_sample_workspace_bytes(1000, 256, 17) == 0            # S <= 16
+    v = lib.specverify_verify_sample
+    assert v(A16, A16, 1000, 256, A16, 9, A16, 0.8, 1, NULL, A16, A16, A16, NULL, A16, ws, NULL) == 1   # state
+    assert v(A16, A16, 1000, 256, A16, 9, NULL, 0.8, 1, A16, A16, A16, A16, NULL, A16, ws, NULL) == 1   # drafts
+    assert v(A16, A16, 1000, 256, A16, 17, A16, 0.8, 1, A16, A16, A16, A16, NULL, A16, ws, NULL) == 2   # S
+    for bad_t in (0.0, -1.0, float("inf"), float("nan"), 1e-45):
+        assert v(A16, A16, 1000, 256, A16, 9, A16, bad_t, 1, A16, A16, A16, A16, NULL, A16, ws, NULL) == 2
+    assert b"temperature" in lib.specverify_last_error()
+    assert v(A16, A16, 1000, 256, A16, 9, A16, 0.8, 1, A16, A2, A16, A16, NULL, A16, ws, NULL) == 3     # sample
+    assert v(A16, A16, 1000, 256, A16, 9, A16, 0.8, 1, A16, A16, A16, A16, NULL, A16, ws - 1, NULL) == 4
+    a = lib.specverify_accept_sample
+    assert a(A16, A16, A16, NULL, 8, 1000, 1, A16, 100, A16, NULL) == 1         # drafts with K > 0
+    assert a(A16, A16, A16, A16, 16, 1000, 1, A16, 100, A16, NULL) == 2         # K <= 15
+    assert a(A16, A16, A16, A16, 8, 0, 1, A16, 100, A16, NULL) == 2             # V
+    assert a(A16, A16, A16, A16, 8, 1000, 1, A16, 0, A16, NULL) == 5            # cap
+    r = lib.specverify_round_sample
+    assert r(A16, A16, 1000, 256, A16, 16, A16, 0.8, 1, A16, 100, A16, 3, A16, NULL, NULL, A16, ws, NULL) == 2
+    assert r(A16, A16, 1000, 256, A16, 8, NULL, 0.8, 1, A16, 100, A16, 3, A16, NULL, NULL, A16, ws, NULL) == 1
+    assert r(A16, A16, 1000, 256, A16, 8, A16, 0.8, 1, A16, 100, A16, 9, A16, NULL, NULL, A16, ws, NULL) == 2
+    assert r(A16, A16, 1000, 256, A16, 8, A16, 0.8, 1, A16, 100, A16, 3, A16, NULL, NULL, A16, ws - 1, NULL) == 4
+
+
 def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(sv, "_lib", None)
     monkeypatch.setattr(sv, "LIB_PATH", str(tmp_path / "nope.so"))

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -230,6 +231,118 @@ int specverify_round(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_
     if (int st = check_device()) return st;
     return launch_head(wq, wscale, V, H, hidden, K + 1, argmax, logits, workspace, true, drafts_in, tokens, cap, state,
                        ngram_max, drafts_out, stream);
+}
+
+size_t specverify_sample_workspace_bytes(int32_t V, int32_t H, int32_t S) {
+    if (V < 1 || V > (1 << 30) || H < SV_BLOCK || H > 65536 || H % SV_BLOCK || S < 1 || S > 16) return 0;
+    return sv::sample_workspace_bytes(V, H, S);
+}
+
+namespace {
+
+// Sampling head: the matmul with the sampling epilogue (per-workgroup draw and log-sum-exp
+// partials, the draft logits into zd), then the tail that reduces them and, for a round,
+// accepts and drafts.  Workspace: [part_val, part_idx][part_m, part_l][zd, 256 B][split sums].
+int launch_sample_head(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
+                       int32_t S, const int32_t* drafts, float temperature, uint64_t seed, int32_t* state,
+                       float* zd, int32_t* sample, float* lse, float* logits, void* workspace, bool round,
+                       int32_t* tokens, int32_t cap, int32_t ngram_max, int32_t* drafts_out, hipStream_t stream) {
+    char* ws = static_cast<char*>(workspace);
+    const size_t hp = sv::head_partials_bytes(S);
+    const sv::GemmCfg cfg = sv::gemm_config(V, H, S, sv::EPI_SAMPLE);
+    sv::GemmArgs a{};
+    a.w0 = wq;
+    a.s0 = wscale;
+    a.x = hidden;
+    a.V = V;
+    a.H = H;
+    a.S = S;
+    a.nb = H / SV_BLOCK;
+    a.nitems = (V + 15) / 16;
+    a.ksplit = cfg.ksplit;
+    a.part_val = reinterpret_cast<float*>(ws);
+    a.part_idx = reinterpret_cast<int*>(ws + (size_t)4 * S * sv::kGridMax);
+    a.part_m = reinterpret_cast<float*>(ws + hp);
+    a.part_l = reinterpret_cast<float*>(ws + hp + (size_t)4 * S * sv::kGridMax);
+    a.zd = zd ? zd : reinterpret_cast<float*>(ws + 2 * hp);
+    a.logits = logits;
+    a.state = state;
+    a.drafts = drafts;
+    a.inv_temp = 1.0f / temperature;
+    a.key0 = (uint32_t)seed;
+    a.key1 = (uint32_t)(seed >> 32);
+    if (cfg.ksplit > 1) a.kpart0 = reinterpret_cast<float*>(ws + 2 * hp + 256);
+    hipError_t e = launch_matmul(sv::EPI_SAMPLE, cfg, a, stream);
+    if (e != hipSuccess) return hip_fail(e, "sampling verify matmul launch");
+    const int nparts = cfg.ksplit > 1 ? sv::combine_groups(V) : cfg.grid;
+    e = sv::launch_sample_tail(a.part_val, a.part_idx, a.part_m, a.part_l, nparts, S, V, a.zd, a.key0, a.key1, sample,
+                               lse, round ? drafts : nullptr, round ? tokens : nullptr, cap, state, ngram_max,
+                               round ? drafts_out : nullptr, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "sampling tail launch");
+}
+
+int check_temperature(float t) {
+    if (!(t > 0.0f) || !std::isfinite(t) || !std::isfinite(1.0f / t))
+        return fail(SV_ERR_SHAPE, "temperature %g must be positive, finite and have a finite inverse", (double)t);
+    return SV_OK;
+}
+
+}  // namespace
+
+int specverify_verify_sample(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
+                             int32_t S, const int32_t* drafts, float temperature, uint64_t seed,
+                             const int32_t* state, int32_t* sample, float* lse, float* zd, float* logits,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (int st = check_q8b32(wq, wscale, V, H, hidden, S, 16)) return st;
+    if (int st = check_temperature(temperature)) return st;
+    if (!state || !sample || !lse || !zd || !workspace || (S > 1 && !drafts))
+        return fail(SV_ERR_NULL, "state, sample, lse, zd, workspace (and drafts when S > 1) are required");
+    if (!aligned(state, 4) || !aligned(sample, 4) || !aligned(lse, 4) || !aligned(zd, 4) ||
+        (drafts && !aligned(drafts, 4)) || (logits && !aligned(logits, 4)) || !aligned(workspace, 16))
+        return fail(SV_ERR_ALIGN, "4-byte aligned buffers and a 16-byte aligned workspace are required");
+    const size_t need = sv::sample_workspace_bytes(V, H, S);
+    if (workspace_bytes < need) return fail(SV_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+    if (int st = check_device()) return st;
+    return launch_sample_head(wq, wscale, V, H, hidden, S, drafts, temperature, seed, const_cast<int32_t*>(state),
+                              zd, sample, lse, logits, workspace, false, nullptr, 0, 0, nullptr, stream);
+}
+
+int specverify_accept_sample(const int32_t* sample, const float* lse, const float* zd, const int32_t* drafts,
+                             int32_t K, int32_t V, uint64_t seed, int32_t* tokens, int32_t cap, int32_t* state,
+                             hipStream_t stream) {
+    if (!sample || !lse || !zd || !tokens || !state || (K > 0 && !drafts))
+        return fail(SV_ERR_NULL, "sample, lse, zd, tokens, state (and drafts when K > 0) are required");
+    if (K < 0 || K > 15) return fail(SV_ERR_SHAPE, "K=%d outside [0, 15]", K);
+    if (V < 1 || V > (1 << 30)) return fail(SV_ERR_SHAPE, "V=%d outside [1, 2^30]", V);
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(sample, 4) || !aligned(lse, 4) || !aligned(zd, 4) || !aligned(tokens, 4) || !aligned(state, 4) ||
+        (drafts && !aligned(drafts, 4)))
+        return fail(SV_ERR_ALIGN, "buffers must be 4-byte aligned");
+    if (int st = check_device()) return st;
+    hipError_t e = sv::launch_accept_sample(sample, lse, zd, drafts, K, V, (uint32_t)seed, (uint32_t)(seed >> 32),
+                                            tokens, cap, state, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "sampling accept launch");
+}
+
+int specverify_round_sample(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
+                            int32_t K, const int32_t* drafts_in, float temperature, uint64_t seed, int32_t* tokens,
+                            int32_t cap, int32_t* state, int32_t ngram_max, int32_t* drafts_out, int32_t* sample,
+                            float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (K < 1 || K > 15) return fail(SV_ERR_SHAPE, "K=%d outside [1, 15]", K);
+    if (int st = check_q8b32(wq, wscale, V, H, hidden, K + 1, 16)) return st;
+    if (int st = check_temperature(temperature)) return st;
+    if (!drafts_in || !tokens || !state || !drafts_out || !workspace)
+        return fail(SV_ERR_NULL, "drafts, tokens, state and workspace are required");
+    if (ngram_max < 1 || ngram_max > SV_MAX_NGRAM) return fail(SV_ERR_SHAPE, "ngram_max=%d outside [1, %d]", ngram_max, SV_MAX_NGRAM);
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(drafts_in, 4) || !aligned(tokens, 4) || !aligned(state, 4) || !aligned(drafts_out, 4) ||
+        (sample && !aligned(sample, 4)) || (lse && !aligned(lse, 4)) || !aligned(workspace, 16))
+        return fail(SV_ERR_ALIGN, "4-byte aligned buffers and a 16-byte aligned workspace are required");
+    const size_t need = sv::sample_workspace_bytes(V, H, K + 1);
+    if (workspace_bytes < need) return fail(SV_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+    if (int st = check_device()) return st;
+    return launch_sample_head(wq, wscale, V, H, hidden, K + 1, drafts_in, temperature, seed, state, nullptr, sample,
+                              lse, nullptr, workspace, true, tokens, cap, ngram_max, drafts_out, stream);
 }
 
 namespace {

@@ -65,4 +65,58 @@ __device__ __forceinline__ void argmax_group(float& v, int& i) {
     }
 }
 
+// Merge two partial log-sum-exp states (max m, sum of exp(z - m)) into (m, l); an empty state
+// has m = -inf.
+__device__ __forceinline__ void lse_merge(float& m, float& l, float om, float ol) {
+    const float M = fmaxf(m, om);
+    l = (m == -INFINITY ? 0.0f : l * __expf(m - M)) + (om == -INFINITY ? 0.0f : ol * __expf(om - M));
+    m = M;
+}
+
+// lse_merge over each aligned group of `width` lanes (xor butterfly); every lane of the group
+// ends with the group's state.
+template <int WIDTH>
+__device__ __forceinline__ void lse_merge_group(float& m, float& l) {
+#pragma unroll
+    for (int off = WIDTH / 2; off > 0; off >>= 1) {
+        const float om = __shfl_xor(m, off, WIDTH);
+        const float ol = __shfl_xor(l, off, WIDTH);
+        lse_merge(m, l, om, ol);
+    }
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2,
+// 3", SC'11): ten rounds of two 32x32 -> 64-bit products, the high halves folded into the
+// other two words with the key, the key advancing by the Weyl increments between rounds.
+struct Philox4 { uint32_t w[4]; };
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                  uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+        const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+        const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+    }
+    return Philox4{{c0, c1, c2, c3}};
+}
+
+// Word i (0..3) of a Philox block, with selects rather than a dynamic register index.
+__device__ __forceinline__ uint32_t philox_word(const Philox4& r, int i) {
+    return i == 0 ? r.w[0] : i == 1 ? r.w[1] : i == 2 ? r.w[2] : r.w[3];
+}
+
+// A 32-bit word -> (floor(w / 2^9) + 1/2) / 2^23, strictly inside (0, 1) and exact in fp32.
+__device__ __forceinline__ float uniform01(uint32_t w) {
+    return ((float)(w >> 9) + 0.5f) * (1.0f / 8388608.0f);
+}
+
+// Gumbel(0, 1) noise from a uniform: -log(-log u).
+__device__ __forceinline__ float gumbel(float u) {
+    return -__logf(-__logf(u));
+}
+
 }  // namespace sv

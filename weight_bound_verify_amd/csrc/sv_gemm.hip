@@ -86,12 +86,33 @@ struct Reducer {
     f32x4 (*red)[NW][MT][kWave];
     float best_v[MT][4];
     int best_i[MT][4];
+    // EPI_SAMPLE (MT = 1): running max of z and sum of exp(z - max) per window row of the
+    // lane, the draft each row leaves out of its draw, the round's start position
+    float run_m[4], run_l[4];
+    int excl[4];
+    uint32_t p0;
 
     __device__ __forceinline__ void init() {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) { best_v[mt][r] = -INFINITY; best_i[mt][r] = INT_MAX; }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { run_m[r] = -INFINITY; run_l[r] = 0.0f; excl[r] = -1; }
+        p0 = 0;
+    }
+
+    // Per-round inputs of the sampling epilogue (wave 0 only).
+    __device__ __forceinline__ void setup(const GemmArgs& a, int lane) {
+        if constexpr (EPI == EPI_SAMPLE) {
+            const int g = lane >> 4;
+            p0 = (uint32_t)a.state[SV_STATE_LEN];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = 4 * g + r;
+                excl[r] = s < a.S - 1 ? a.drafts[s] : -1;
+            }
+        }
     }
 
     __device__ __forceinline__ void run(const GemmArgs& a, const f32x4 (&acc)[MT], int it, int buf, int wave, int lane,
@@ -111,6 +132,40 @@ struct Reducer {
         }
         const int n = lane & 15, g = lane >> 4;
         const int v = tile_row<EPI>(it, n);
+        if constexpr (EPI == EPI_SAMPLE) {
+            // z = L / T; key = z + Gumbel noise of (row, id) with the row's draft left out;
+            // online log-sum-exp of z.  Ids arrive in increasing order, so a strict > keeps
+            // the lowest id on equal keys.
+            if (a.ksplit == 1 && 4 * g < a.S && v < a.V) {
+                const Philox4 rnd = philox4x32_10((uint32_t)v, p0, (uint32_t)g, 0u, a.key0, a.key1);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int s = 4 * g + r;
+                    if (s < a.S) {
+                        const float L = tot[0][r];
+                        if (a.logits) a.logits[(size_t)s * a.V + v] = L;
+                        const float z = L * a.inv_temp;
+                        const bool out = v == excl[r];
+                        if (out) a.zd[s] = z;
+                        const float key = out ? -INFINITY : z + gumbel(uniform01(rnd.w[r]));
+                        if (key > best_v[0][r]) { best_v[0][r] = key; best_i[0][r] = v; }
+                        if (z > run_m[r]) {
+                            run_l[r] = run_l[r] * __expf(run_m[r] - z) + 1.0f;
+                            run_m[r] = z;
+                        } else {
+                            run_l[r] += __expf(z - run_m[r]);
+                        }
+                    }
+                }
+            } else if (a.ksplit > 1) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int s = g * 4 + r;
+                    if (s < a.S && v < a.V) a.kpart0[(size_t)ks * a.S * a.V + (size_t)s * a.V + v] = tot[0][r];
+                }
+            }
+            return;
+        }
         if constexpr (EPI == EPI_GATEUP) {
             // lanes n < 8 hold the gate sums, lanes n + 8 the up sums of the same output rows
 #pragma unroll
@@ -154,9 +209,22 @@ struct Reducer {
             }
     }
 
-    // Per-workgroup argmax partials of the head (wave 0).
+    // Per-workgroup argmax partials of the head (wave 0); for sampling also the per-row
+    // (max, sum of exp) pairs, merged across the 16 lanes of a row in a fixed order.
     __device__ __forceinline__ void finish(const GemmArgs& a, int lane) {
         const int n = lane & 15, g = lane >> 4;
+        if constexpr (EPI == EPI_SAMPLE) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float m = run_m[r], l = run_l[r];
+                lse_merge_group<16>(m, l);
+                const int s = g * 4 + r;
+                if (n == 0 && s < a.S) {
+                    a.part_m[(size_t)s * kGridMax + blockIdx.x] = m;
+                    a.part_l[(size_t)s * kGridMax + blockIdx.x] = l;
+                }
+            }
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -201,6 +269,7 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
 
     Reducer<MT, NW, EPI> red_{red};
     red_.init();
+    if (wave == 0) red_.setup(a, lane);
 
     // loads: row half h feeds tile rows 8h .. 8h+7; lane l reads the tile row 8h + l/8, bytes
     // 16*(l%8) .. +15 of each 128-byte segment of the wave's range
@@ -282,7 +351,7 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
         process(rb, it, 1);
         it += step;
     }
-    if constexpr (EPI == EPI_HEAD)
+    if constexpr (EPI == EPI_HEAD || EPI == EPI_SAMPLE)
         if (a.ksplit == 1 && wave == 0) red_.finish(a, lane);
 }
 
@@ -329,6 +398,7 @@ __global__ __launch_bounds__(NW * 64) void q8b32_generic(GemmArgs a) {
     load_hidden<MT, NBW>(hid, a, bw0, nbw, n, g);
     Reducer<MT, NW, EPI> red_{red};
     red_.init();
+    if (wave == 0) red_.setup(a, lane);
 
     const int8_t* w = tile_up<EPI>(n) ? a.w1 : a.w0;
     const uint16_t* sc = tile_up<EPI>(n) ? a.s1 : a.s0;
@@ -372,7 +442,7 @@ __global__ __launch_bounds__(NW * 64) void q8b32_generic(GemmArgs a) {
         process(rb, it, 1);
         it += step;
     }
-    if constexpr (EPI == EPI_HEAD)
+    if constexpr (EPI == EPI_HEAD || EPI == EPI_SAMPLE)
         if (a.ksplit == 1 && wave == 0) red_.finish(a, lane);
 }
 
@@ -382,6 +452,13 @@ __global__ __launch_bounds__(256) void combine_kernel(GemmArgs a) {
     const int s = blockIdx.y;
     float bv = -INFINITY;
     int bi = INT_MAX;
+    float run_m = -INFINITY, run_l = 0.0f;        // EPI_SAMPLE: online log-sum-exp of z
+    uint32_t p0 = 0;
+    int excl = -1;
+    if constexpr (EPI == EPI_SAMPLE) {
+        p0 = (uint32_t)a.state[SV_STATE_LEN];
+        excl = s < a.S - 1 ? a.drafts[s] : -1;
+    }
     for (int v = blockIdx.x * 256 + threadIdx.x; v < a.V; v += gridDim.x * 256) {
         const size_t o = (size_t)s * a.V + v;
         const size_t plane = (size_t)a.S * a.V;
@@ -390,6 +467,21 @@ __global__ __launch_bounds__(256) void combine_kernel(GemmArgs a) {
         if constexpr (EPI == EPI_HEAD) {
             if (a.logits) a.logits[o] = t0;
             if (t0 > bv) { bv = t0; bi = v; }
+        } else if constexpr (EPI == EPI_SAMPLE) {
+            // the sampling epilogue of the matmul, one element at a time
+            if (a.logits) a.logits[o] = t0;
+            const float z = t0 * a.inv_temp;
+            const bool out = v == excl;
+            if (out) a.zd[s] = z;
+            const Philox4 rnd = philox4x32_10((uint32_t)v, p0, (uint32_t)(s >> 2), 0u, a.key0, a.key1);
+            const float key = out ? -INFINITY : z + gumbel(uniform01(philox_word(rnd, s & 3)));
+            if (key > bv) { bv = key; bi = v; }
+            if (z > run_m) {
+                run_l = run_l * __expf(run_m - z) + 1.0f;
+                run_m = z;
+            } else {
+                run_l += __expf(z - run_m);
+            }
         } else if constexpr (EPI == EPI_STORE) {
             if (a.residual) t0 += h2f(a.residual[o]);
             a.y[o] = f2h(t0);
@@ -399,17 +491,27 @@ __global__ __launch_bounds__(256) void combine_kernel(GemmArgs a) {
             a.y[o] = f2h(t0 / (1.0f + expf(-t0)) * t1);
         }
     }
-    if constexpr (EPI == EPI_HEAD) {
-        __shared__ float sv_[4];
+    if constexpr (EPI == EPI_HEAD || EPI == EPI_SAMPLE) {
+        __shared__ float sv_[4], sm_[4], sl_[4];
         __shared__ int si_[4];
         argmax_group<64>(bv, bi);
-        if ((threadIdx.x & 63) == 0) { sv_[threadIdx.x >> 6] = bv; si_[threadIdx.x >> 6] = bi; }
+        if constexpr (EPI == EPI_SAMPLE) lse_merge_group<64>(run_m, run_l);
+        if ((threadIdx.x & 63) == 0) {
+            sv_[threadIdx.x >> 6] = bv; si_[threadIdx.x >> 6] = bi;
+            sm_[threadIdx.x >> 6] = run_m; sl_[threadIdx.x >> 6] = run_l;
+        }
         __syncthreads();
         if (threadIdx.x == 0) {
-            for (int w = 1; w < 4; ++w)
+            for (int w = 1; w < 4; ++w) {
                 if (better(sv_[w], si_[w], bv, bi)) { bv = sv_[w]; bi = si_[w]; }
+                lse_merge(run_m, run_l, sm_[w], sl_[w]);
+            }
             a.part_val[(size_t)s * kGridMax + blockIdx.x] = bv;
             a.part_idx[(size_t)s * kGridMax + blockIdx.x] = bi;
+            if constexpr (EPI == EPI_SAMPLE) {
+                a.part_m[(size_t)s * kGridMax + blockIdx.x] = run_m;
+                a.part_l[(size_t)s * kGridMax + blockIdx.x] = run_l;
+            }
         }
     }
 }
@@ -496,22 +598,24 @@ __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* _
 // ------------------------------------------------------------------------------------------
 typedef void (*KernelFn)(GemmArgs);
 struct Shape { int mt, nbw, nw, epis; };
-constexpr int kH = 1 << EPI_HEAD, kS = 1 << EPI_STORE, kG = 1 << EPI_GATEUP;
+constexpr int kH = 1 << EPI_HEAD, kS = 1 << EPI_STORE, kG = 1 << EPI_GATEUP, kX = 1 << EPI_SAMPLE;
 
 // fast kernel: every wave owns exactly nbw blocks (a multiple of 4); listed in order of
 // preference within each MT; epis = the epilogues that compile for it without spills
 // within the LDS limit
 constexpr Shape kFast[] = {
-    {1, 4, 16, kH | kS | kG}, {1, 16, 5, kH | kS | kG}, {1, 8, 8, kH | kS | kG}, {1, 8, 10, kH | kS | kG},
-    {1, 16, 8, kH | kS | kG}, {1, 20, 8, kH | kS | kG}, {1, 8, 16, kH | kS}, {1, 16, 4, kH | kS | kG},
-    {1, 8, 4, kH | kS | kG}, {1, 4, 4, kH | kS | kG}, {1, 8, 2, kH | kS | kG},
+    {1, 4, 16, kH | kS | kG | kX}, {1, 16, 5, kH | kS | kG | kX}, {1, 8, 8, kH | kS | kG | kX},
+    {1, 8, 10, kH | kS | kG | kX}, {1, 16, 8, kH | kS | kG | kX}, {1, 20, 8, kH | kS | kG | kX},
+    {1, 8, 16, kH | kS}, {1, 16, 4, kH | kS | kG | kX}, {1, 8, 4, kH | kS | kG | kX},
+    {1, 4, 4, kH | kS | kG | kX}, {1, 8, 2, kH | kS | kG | kX},
     {2, 8, 8, kH}, {2, 8, 5, kH}, {2, 8, 4, kH}, {2, 4, 4, kH},
     {4, 4, 4, kH},
 };
 // generic kernel
 constexpr Shape kGeneric[] = {
-    {1, 4, 4, kH | kS | kG}, {1, 8, 4, kH | kS | kG}, {1, 16, 4, kH | kS | kG}, {1, 4, 8, kH | kS | kG},
-    {1, 8, 8, kH | kS | kG}, {1, 16, 8, kH | kS | kG}, {1, 4, 16, kH | kS}, {1, 8, 16, kH | kS},
+    {1, 4, 4, kH | kS | kG | kX}, {1, 8, 4, kH | kS | kG | kX}, {1, 16, 4, kH | kS | kG | kX},
+    {1, 4, 8, kH | kS | kG | kX}, {1, 8, 8, kH | kS | kG | kX}, {1, 16, 8, kH | kS | kG | kX},
+    {1, 4, 16, kH | kS | kX}, {1, 8, 16, kH | kS},
     {2, 4, 4, kH}, {2, 8, 4, kH}, {2, 4, 8, kH}, {2, 8, 8, kH},
     {4, 2, 4, kH}, {4, 4, 4, kH}, {4, 2, 8, kH},
 };
@@ -522,7 +626,7 @@ KernelFn pick_fast(const GemmCfg& c) {
     if (c.mt == MT && c.nbw == NBW && c.nw == NW) return q8b32_fast<MT, NBW, NW, EPI>;
     SV_SHAPE(1, 8, 8) SV_SHAPE(1, 8, 10) SV_SHAPE(1, 16, 8) SV_SHAPE(1, 16, 5) SV_SHAPE(1, 16, 4)
     SV_SHAPE(1, 8, 4) SV_SHAPE(1, 4, 4) SV_SHAPE(1, 8, 2) SV_SHAPE(1, 4, 16) SV_SHAPE(1, 20, 8)
-    if constexpr (EPI != EPI_GATEUP) { SV_SHAPE(1, 8, 16) }
+    if constexpr (EPI == EPI_HEAD || EPI == EPI_STORE) { SV_SHAPE(1, 8, 16) }
     if constexpr (EPI == EPI_HEAD) {
         SV_SHAPE(2, 8, 8) SV_SHAPE(2, 8, 5) SV_SHAPE(2, 8, 4) SV_SHAPE(2, 4, 4) SV_SHAPE(4, 4, 4)
     }
@@ -535,7 +639,8 @@ KernelFn pick_generic(const GemmCfg& c) {
 #define SV_SHAPE(MT, NBW, NW) \
     if (c.mt == MT && c.nbw == NBW && c.nw == NW) return q8b32_generic<MT, NBW, NW, EPI>;
     SV_SHAPE(1, 4, 4) SV_SHAPE(1, 8, 4) SV_SHAPE(1, 16, 4) SV_SHAPE(1, 4, 8) SV_SHAPE(1, 8, 8) SV_SHAPE(1, 16, 8)
-    if constexpr (EPI != EPI_GATEUP) { SV_SHAPE(1, 4, 16) SV_SHAPE(1, 8, 16) }
+    if constexpr (EPI != EPI_GATEUP) { SV_SHAPE(1, 4, 16) }
+    if constexpr (EPI == EPI_HEAD || EPI == EPI_STORE) { SV_SHAPE(1, 8, 16) }
     if constexpr (EPI == EPI_HEAD) {
         SV_SHAPE(2, 4, 4) SV_SHAPE(2, 8, 4) SV_SHAPE(2, 4, 8) SV_SHAPE(2, 8, 8)
         SV_SHAPE(4, 2, 4) SV_SHAPE(4, 4, 4) SV_SHAPE(4, 2, 8)
@@ -587,10 +692,12 @@ bool try_generic(int nb, int mt, int epi, int nw_fixed, GemmCfg& c) {
 KernelFn kernel_for(int epi, const GemmCfg& c) {
     if (c.fast) {
         if (epi == EPI_HEAD) return pick_fast<EPI_HEAD>(c);
+        if (epi == EPI_SAMPLE) return pick_fast<EPI_SAMPLE>(c);
         if (epi == EPI_STORE) return pick_fast<EPI_STORE>(c);
         return pick_fast<EPI_GATEUP>(c);
     }
     if (epi == EPI_HEAD) return pick_generic<EPI_HEAD>(c);
+    if (epi == EPI_SAMPLE) return pick_generic<EPI_SAMPLE>(c);
     if (epi == EPI_STORE) return pick_generic<EPI_STORE>(c);
     return pick_generic<EPI_GATEUP>(c);
 }
@@ -669,6 +776,13 @@ size_t head_workspace_bytes(int V, int H, int S) {
     return b;
 }
 
+size_t sample_workspace_bytes(int V, int H, int S) {
+    const GemmCfg c = gemm_config(V, H, S, EPI_SAMPLE);
+    size_t b = 2 * head_partials_bytes(S) + 256;
+    if (c.ksplit > 1) b += (size_t)4 * c.ksplit * S * V;
+    return b;
+}
+
 size_t stack_workspace_bytes(int N, int K, int S, bool gateup) {
     const GemmCfg c = gemm_config(N, K, S, gateup ? EPI_GATEUP : EPI_STORE);
     if (c.ksplit == 1) return 0;
@@ -684,6 +798,8 @@ hipError_t launch_q8b32(int epi, const GemmCfg& cfg, const GemmArgs& a, hipStrea
     const int cg = combine_groups(a.V);
     if (epi == EPI_HEAD)
         hipLaunchKernelGGL(combine_kernel<EPI_HEAD>, dim3(cg, a.S), dim3(256), 0, stream, a);
+    else if (epi == EPI_SAMPLE)
+        hipLaunchKernelGGL(combine_kernel<EPI_SAMPLE>, dim3(cg, a.S), dim3(256), 0, stream, a);
     else if (epi == EPI_STORE)
         hipLaunchKernelGGL(combine_kernel<EPI_STORE>, dim3(cg, a.S), dim3(256), 0, stream, a);
     else

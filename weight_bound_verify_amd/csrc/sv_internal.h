@@ -7,7 +7,9 @@
 
 namespace sv {
 
-enum Epi { EPI_HEAD = 0, EPI_STORE = 1, EPI_GATEUP = 2 };
+// EPI_SAMPLE: the head epilogue of sampling verify (per-row log-normaliser, a Gumbel-max
+// draw per row that leaves out the row's draft, the scaled logit of that draft).
+enum Epi { EPI_HEAD = 0, EPI_STORE = 1, EPI_GATEUP = 2, EPI_SAMPLE = 3 };
 
 constexpr int kGridMax = 4096;     // upper bound on workgroups of one q8b32 launch
 
@@ -41,11 +43,34 @@ struct GemmArgs {
     const uint16_t* residual;  // EPI_STORE: [S][V] fp16 or null
     float* kpart0;             // ksplit > 1: fp32 partial sums [ksplit][S][V]
     float* kpart1;             // ksplit > 1, EPI_GATEUP: partial sums of the up projection
+    // EPI_SAMPLE (S <= 16): z = L * inv_temp; row s leaves out draft drafts[s] (s < S-1) from
+    // its draw; part_val/part_idx then hold the best Gumbel key and its id, part_m/part_l the
+    // running max of z and the sum of exp(z - max); zd[s] = z of draft drafts[s].
+    const int32_t* state;      // round state: state[0] = P0, the position row 0 predicts
+    const int32_t* drafts;     // [S-1] or null (S = 1)
+    float inv_temp;
+    uint32_t key0, key1;       // Philox key = the 64-bit seed
+    float* part_m;             // [S][kGridMax]
+    float* part_l;
+    float* zd;                 // [S]
 };
 
 // Head workspace layout: per-workgroup argmax partials [S][kGridMax] (values, then indices),
 // then the split sums when the hidden axis is split across workgroups.
 constexpr size_t head_partials_bytes(int S) { return (size_t)8 * S * kGridMax; }
+// Sampling head: the head layout, then part_m, part_l [S][kGridMax] and zd [S] (256-byte
+// aligned blocks).
+size_t sample_workspace_bytes(int V, int H, int S);
+// Draw stage 2 of a sampling head launch (per-row draw, log-normaliser) and, when tokens !=
+// null, the sampling accept and the next drafts: one workgroup.  sample_out / lse_out may be
+// null in a round.
+hipError_t launch_sample_tail(const float* pv, const int* pi, const float* pm, const float* pl, int nparts, int S,
+                              int V, const float* zd, uint32_t key0, uint32_t key1, int32_t* sample_out,
+                              float* lse_out, const int32_t* drafts_in, int32_t* tokens, int cap, int32_t* state,
+                              int nmax, int32_t* drafts_out, hipStream_t stream);
+hipError_t launch_accept_sample(const int32_t* sample, const float* lse, const float* zd, const int32_t* drafts,
+                                int K, int V, uint32_t key0, uint32_t key1, int32_t* tokens, int cap,
+                                int32_t* state, hipStream_t stream);
 
 // Workspace bytes a head matmul of this shape needs.
 size_t head_workspace_bytes(int V, int H, int S);

@@ -87,6 +87,50 @@ __device__ __forceinline__ void accept_wave(const int32_t* argmax, const int32_t
     }
 }
 
+// Sampling accept by one wave (speculative sampling with a point-mass drafter; "Stream C -
+// Speculative decoding", the deferred list: probabilities and a residual redraw instead of an
+// argmax comparison).  Lane s < K keeps draft d_{s+1} iff it is a vocabulary id and
+// u_s < p_s(d) = exp(zd[s] - lse[s]), u_s the accept uniform of the round (Philox4x32-10
+// counter (0, len, s / 4, 1), word s % 4).  j = the first draft not kept; d_1..d_j and row j's
+// draw (its residual draw, or the bonus draw when j = K) are appended, so len advances by
+// 1 + j.  `mirror` (may be null) receives the same ids at the same positions.  A call that
+// could overflow `cap` writes no token and sets the sticky capacity flag.  Returns j, or -1.
+__device__ __forceinline__ int accept_sample_wave(const int32_t* sample, const float* lse, const float* zd,
+                                                  const int32_t* drafts, int K, int V, uint32_t key0,
+                                                  uint32_t key1, int32_t* tokens, int cap, int32_t* state,
+                                                  int lane, int32_t* mirror) {
+    const int len = state[SV_STATE_LEN];
+    if (len + K + 1 > cap || len < 0) {
+        if (lane == 0) state[SV_STATE_FLAGS] |= SV_FLAG_CAPACITY;
+        return -1;
+    }
+    int d = -1;
+    bool keep = false;
+    if (lane < K) {
+        d = drafts[lane];
+        if (d >= 0 && d < V) {
+            const Philox4 rnd = philox4x32_10(0u, (uint32_t)len, (uint32_t)(lane >> 2), 1u, key0, key1);
+            const float u = uniform01(philox_word(rnd, lane & 3));
+            keep = u < __expf(zd[lane] - lse[lane]);
+        }
+    }
+    const unsigned long long kept = __ballot(keep);
+    const int j = __builtin_ctzll(~kept);                // <= K: bit K is never set
+    if (lane < j) {
+        tokens[len + lane] = d;
+        if (mirror) mirror[len + lane] = d;
+    }
+    if (lane == j) {
+        tokens[len + j] = sample[j];
+        if (mirror) mirror[len + j] = sample[j];
+    }
+    if (lane == 0) {
+        state[SV_STATE_LEN] = len + 1 + j;
+        if (K > 0) record_round(state, j);        // K = 0 is the anchor bootstrap, not a round
+    }
+    return j;
+}
+
 // n-gram prompt lookup by a whole workgroup ("Stream C - Speculative decoding", the delta:
 // the last m ids of the stream index their most recent continuation; "Spec-decode on GDN
 // hybrids", harness lessons: the stream ends in the pending anchor, so drafts continue past

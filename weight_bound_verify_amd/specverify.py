@@ -29,7 +29,8 @@ STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_ALIGN", 4:
 EXPORTS = (
     "specverify_propose", "specverify_verify_workspace_bytes", "specverify_verify", "specverify_round",
     "specverify_accept", "specverify_gather_window", "specverify_generate", "specverify_verify_q4b32",
-    "specverify_round_q4b32",
+    "specverify_round_q4b32", "specverify_sample_workspace_bytes", "specverify_verify_sample",
+    "specverify_accept_sample", "specverify_round_sample",
     "specverify_rmsnorm", "specverify_stack_workspace_bytes", "specverify_gateup_silu_q8b32",
     "specverify_linear_q8b32", "specverify_linear_residual_rmsnorm_q8b32",
     "specverify_stack_forward_workspace_bytes", "specverify_stack", "specverify_set_tuning", "specverify_profile_next_matmul", "specverify_status_string", "specverify_last_error",
@@ -64,6 +65,12 @@ def load():
         "specverify_verify_q4b32": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
         "specverify_round_q4b32": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t,
                                         _P]),
+        "specverify_sample_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+        "specverify_verify_sample": (_I, [_P, _P, _I, _I, _P, _I, _P, ctypes.c_float, ctypes.c_uint64, _P, _P, _P,
+                                          _P, _P, _P, ctypes.c_size_t, _P]),
+        "specverify_accept_sample": (_I, [_P, _P, _P, _P, _I, _I, ctypes.c_uint64, _P, _I, _P, _P]),
+        "specverify_round_sample": (_I, [_P, _P, _I, _I, _P, _I, _P, ctypes.c_float, ctypes.c_uint64, _P, _I, _P,
+                                         _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
         "specverify_generate": (_I, [_P, _P, _I, _I, _P, _I, _I, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t,
                                      _P]),
         "specverify_rmsnorm": (_I, [_P, _I, _I, ctypes.c_float, _P, _P]),
@@ -213,6 +220,58 @@ def round_q4(wq4, wscale, hidden, drafts_in, tokens, state, drafts_out, argmax, 
         int(ngram_max), _ptr(drafts_out, torch.int32, "drafts_out", K), _ptr(argmax, torch.int32, "argmax", S),
         _ptr(logits, torch.float32, "logits", S * V), _ptr(ws, torch.uint8, "workspace"), ws.numel(),
         _stream(stream)))
+
+
+def sample_workspace_bytes(V: int, H: int, S: int) -> int:
+    return int(load().specverify_sample_workspace_bytes(V, H, S))
+
+
+def _seed(seed: int) -> int:
+    return int(seed) & ((1 << 64) - 1)
+
+
+def verify_sample(wq, wscale, hidden, drafts, temperature: float, seed: int, state, sample, lse, zd, ws, logits=None,
+                  stream=None) -> None:
+    """Sampling verify of the window: per-row residual draws, log-normalisers of L / T and the
+    scaled logits of the drafts (see specverify_verify_sample)."""
+    V, H = wq.shape
+    S = hidden.shape[0]
+    if hidden.shape[1] != H or tuple(wscale.shape) != (V, H // SV_BLOCK):
+        raise ValueError("shape mismatch between wq, wscale and hidden")
+    _check(load().specverify_verify_sample(
+        _ptr(wq, torch.int8, "wq"), _ptr(wscale, torch.float16, "wscale"), V, H,
+        _ptr(hidden, torch.float16, "hidden"), S, _ptr(drafts, torch.int32, "drafts", S - 1) if S > 1 else None,
+        float(temperature), _seed(seed), _ptr(state, torch.int32, "state", STATE_WORDS),
+        _ptr(sample, torch.int32, "sample", S), _ptr(lse, torch.float32, "lse", S), _ptr(zd, torch.float32, "zd", S),
+        _ptr(logits, torch.float32, "logits", S * V), _ptr(ws, torch.uint8, "workspace"), ws.numel(),
+        _stream(stream)))
+
+
+def accept_sample(sample, lse, zd, drafts, V: int, seed: int, tokens, state, stream=None) -> None:
+    """Sampling accept from verify_sample's outputs; ``sample`` holds K+1 draws."""
+    K = sample.numel() - 1
+    _check(load().specverify_accept_sample(
+        _ptr(sample, torch.int32, "sample"), _ptr(lse, torch.float32, "lse", K + 1),
+        _ptr(zd, torch.float32, "zd", K + 1), _ptr(drafts, torch.int32, "drafts", K) if K > 0 else None, K, int(V),
+        _seed(seed), _ptr(tokens, torch.int32, "tokens"), tokens.numel(),
+        _ptr(state, torch.int32, "state", STATE_WORDS), _stream(stream)))
+
+
+def round_sample(wq, wscale, hidden, drafts_in, temperature: float, seed: int, tokens, state, drafts_out, ws,
+                 ngram_max: int = 3, sample=None, lse=None, stream=None) -> None:
+    """verify_sample -> accept_sample -> propose, fused (see specverify_round_sample)."""
+    V, H = wq.shape
+    S = hidden.shape[0]
+    K = S - 1
+    if hidden.shape[1] != H or tuple(wscale.shape) != (V, H // SV_BLOCK) or drafts_in.numel() < K:
+        raise ValueError("shape mismatch")
+    _check(load().specverify_round_sample(
+        _ptr(wq, torch.int8, "wq"), _ptr(wscale, torch.float16, "wscale"), V, H,
+        _ptr(hidden, torch.float16, "hidden"), K, _ptr(drafts_in, torch.int32, "drafts_in", K), float(temperature),
+        _seed(seed), _ptr(tokens, torch.int32, "tokens"), tokens.numel(),
+        _ptr(state, torch.int32, "state", STATE_WORDS), int(ngram_max), _ptr(drafts_out, torch.int32, "drafts_out", K),
+        _ptr(sample, torch.int32, "sample", S), _ptr(lse, torch.float32, "lse", S), _ptr(ws, torch.uint8, "workspace"),
+        ws.numel(), _stream(stream)))
 
 
 def accept(argmax, drafts, tokens, state, stream=None) -> None:
