@@ -87,10 +87,14 @@ struct Reducer {
     float best_v[MT][4];
     int best_i[MT][4];
     // EPI_SAMPLE (MT = 1): running max of z and sum of exp(z - max) per window row of the
-    // lane, the draft each row leaves out of its draw, the round's start position
+    // lane, the draft each row leaves out of its draw, the round's start position, and three
+    // LDS slots of Gumbel noise [lane] (rows 4g..4g+3 of id n of an item), filled one item
+    // ahead by a wave other than wave 0 so the generator stays off the epilogue's path
     float run_m[4], run_l[4];
     int excl[4];
     uint32_t p0;
+    f32x4 (*noise)[kWave];
+    int kloc;                  // items this workgroup has processed
 
     __device__ __forceinline__ void init() {
 #pragma unroll
@@ -100,17 +104,49 @@ struct Reducer {
 #pragma unroll
         for (int r = 0; r < 4; ++r) { run_m[r] = -INFINITY; run_l[r] = 0.0f; excl[r] = -1; }
         p0 = 0;
+        kloc = 0;
     }
 
-    // Per-round inputs of the sampling epilogue (wave 0 only).
-    __device__ __forceinline__ void setup(const GemmArgs& a, int lane) {
+    // Per-round inputs of the sampling epilogue (every wave: the start position; wave 0: the
+    // drafts it leaves out), then the first item's noise.
+    __device__ __forceinline__ void setup(const GemmArgs& a, int wave, int lane) {
         if constexpr (EPI == EPI_SAMPLE) {
             const int g = lane >> 4;
             p0 = (uint32_t)a.state[SV_STATE_LEN];
+            if (wave == 0) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int s = 4 * g + r;
-                excl[r] = s < a.S - 1 ? a.drafts[s] : -1;
+                for (int r = 0; r < 4; ++r) {
+                    const int s = 4 * g + r;
+                    excl[r] = s < a.S - 1 ? a.drafts[s] : -1;
+                }
+            }
+            if (wave == (NW > 1 ? 1 : 0)) make_noise(a, blockIdx.x, 0, lane);
+        }
+    }
+
+    // Gumbel noise of item `item` into slot `slot`: lane (n, g) draws rows 4g..4g+3 of id
+    // 16 item + n from one Philox block (counter (v, P0, g, 0)).
+    __device__ __forceinline__ void make_noise(const GemmArgs& a, int item, int slot, int lane) {
+        const int n = lane & 15, g = lane >> 4;
+        const int v = item * kTileRows + n;
+        f32x4 out = {0.f, 0.f, 0.f, 0.f};
+        if (item < a.nitems && 4 * g < a.S && v < a.V) {
+            const Philox4 rnd = philox4x32_10((uint32_t)v, p0, (uint32_t)g, 0u, a.key0, a.key1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out[r] = gumbel(uniform01(rnd.w[r]));
+        }
+        noise[slot][lane] = out;
+    }
+
+    // Called at the start of each item by every wave: the item after this one gets its noise
+    // from wave 1 + (k mod (NW - 1)) while that wave's loads are in flight.  Slots rotate
+    // over three items, so the slot written (k + 1) was last read by wave 0 in the epilogue of
+    // item k - 2, which ended before that wave passed the barrier of item k - 1.
+    __device__ __forceinline__ void ahead(const GemmArgs& a, int next_item, int wave, int lane) {
+        if constexpr (EPI == EPI_SAMPLE) {
+            if (a.ksplit == 1) {
+                const int writer = NW > 1 ? 1 + kloc % (NW - 1) : 0;
+                if (wave == writer) make_noise(a, next_item, (kloc + 1) % 3, lane);
             }
         }
     }
@@ -120,6 +156,8 @@ struct Reducer {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) red[buf][wave][mt][lane] = acc[mt];
         lds_barrier();
+        const int kcur = kloc;
+        kloc = kcur + 1;
         if (wave != 0) return;
 
         f32x4 tot[MT];
@@ -137,7 +175,7 @@ struct Reducer {
             // online log-sum-exp of z.  Ids arrive in increasing order, so a strict > keeps
             // the lowest id on equal keys.
             if (a.ksplit == 1 && 4 * g < a.S && v < a.V) {
-                const Philox4 rnd = philox4x32_10((uint32_t)v, p0, (uint32_t)g, 0u, a.key0, a.key1);
+                const f32x4 gn = noise[kcur % 3][lane];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int s = 4 * g + r;
@@ -147,7 +185,7 @@ struct Reducer {
                         const float z = L * a.inv_temp;
                         const bool out = v == excl[r];
                         if (out) a.zd[s] = z;
-                        const float key = out ? -INFINITY : z + gumbel(uniform01(rnd.w[r]));
+                        const float key = out ? -INFINITY : z + gn[r];
                         if (key > best_v[0][r]) { best_v[0][r] = key; best_i[0][r] = v; }
                         if (z > run_m[r]) {
                             run_l[r] = run_l[r] * __expf(run_m[r] - z) + 1.0f;
@@ -257,6 +295,7 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
     static_assert(NBW % 4 == 0, "whole 128-byte segments");
     __shared__ f32x4 red[2][NW][MT][kWave];
     __shared__ __attribute__((aligned(16))) uint8_t xch[NW][2][2048];
+    __shared__ f32x4 noise[EPI == EPI_SAMPLE ? 3 : 1][kWave];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -269,7 +308,8 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
 
     Reducer<MT, NW, EPI> red_{red};
     red_.init();
-    if (wave == 0) red_.setup(a, lane);
+    red_.noise = noise;
+    red_.setup(a, wave, lane);
 
     // loads: row half h feeds tile rows 8h .. 8h+7; lane l reads the tile row 8h + l/8, bytes
     // 16*(l%8) .. +15 of each 128-byte segment of the wave's range
@@ -305,6 +345,7 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
     };
 
     auto process = [&](const FastRegs<NBW>& cur, int it, int buf) {
+        red_.ahead(a, it + gridDim.x, wave, lane);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         f32x4 acc[MT];
 #pragma unroll
@@ -384,6 +425,7 @@ __device__ __forceinline__ void load_generic(GenRegs<NBW>& r, const int8_t* __re
 template <int MT, int NBW, int NW, int EPI>
 __global__ __launch_bounds__(NW * 64) void q8b32_generic(GemmArgs a) {
     __shared__ f32x4 red[2][NW][MT][kWave];
+    __shared__ f32x4 noise[EPI == EPI_SAMPLE ? 3 : 1][kWave];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -398,7 +440,8 @@ __global__ __launch_bounds__(NW * 64) void q8b32_generic(GemmArgs a) {
     load_hidden<MT, NBW>(hid, a, bw0, nbw, n, g);
     Reducer<MT, NW, EPI> red_{red};
     red_.init();
-    if (wave == 0) red_.setup(a, lane);
+    red_.noise = noise;
+    red_.setup(a, wave, lane);
 
     const int8_t* w = tile_up<EPI>(n) ? a.w1 : a.w0;
     const uint16_t* sc = tile_up<EPI>(n) ? a.s1 : a.s0;
@@ -407,6 +450,7 @@ __global__ __launch_bounds__(NW * 64) void q8b32_generic(GemmArgs a) {
         load_generic<NBW>(r, w, sc, row, a.H, a.nb, bw0, nbw, g);
     };
     auto process = [&](const GenRegs<NBW>& cur, int it, int buf) {
+        red_.ahead(a, it + gridDim.x, wave, lane);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         f32x4 acc[MT];
 #pragma unroll
