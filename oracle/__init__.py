@@ -19,6 +19,8 @@ it follows (pages of the "Core AI model zoo" knowledge base):
 * "Flagship dramatic-speedup plan - the full stackable tuning set" (the tuning-stack
   page): baseline byte model, axis 4 (fused RMSNorm/SwiGLU).
 
+Tree verify (``tree.py``) follows the feasibility page's EAGLE-3 + tree handoff and deferred
+list (tree drafts, tree-mask verify, a walk down the tree instead of the linear accept).
 Sampling verify (``sampling.py``) follows the feasibility page's deferred list and the
 published speculative-sampling rule it refers to; its random numbers come from
 Philox4x32-10, implemented here from its published definition.
@@ -32,6 +34,7 @@ from .verify import (  # noqa: F401
     spec_decode, verify_round,
 )
 from .stack import rmsnorm_fp16, silu, linear_q8b32, mlp_block, stack_forward  # noqa: F401
+from .tree import tree_accept, propose_tree, path_tokens, tree_spec_decode  # noqa: F401
 from .sampling import (  # noqa: F401
     philox4, philox4x32_np, uniform01, noise_uniforms, accept_uniforms, probabilities, residual,
     gumbel_sample, sampling_verify, sample_decode, spec_sample_decode,

@@ -118,3 +118,28 @@ def test_accept_test_on_the_wrong_row_is_caught(monkeypatch):
         return r
     monkeypatch.setattr(smp, "sampling_verify", mutant)
     assert _sampling_law_pvalue() < 1e-6
+
+
+def test_tree_walk_that_ignores_the_parent_link_is_caught():
+    from tests.test_oracle_tree import _brute_force_accept, _random_tree
+
+    def mutant(a, parents, drafts):             # moves to any later node with the right token
+        K = len(parents)
+        c, path = 0, []
+        while True:
+            nxt = next((i for i in range(c + 1, K + 1) if drafts[i - 1] != PAD and drafts[i - 1] == a[c]), None)
+            if nxt is None:
+                break
+            path.append(nxt)
+            c = nxt
+        return len(path), [drafts[i - 1] for i in path] + [a[c]]
+    rng = np.random.default_rng(0)
+    caught = False
+    for _ in range(300):
+        K = int(rng.integers(2, 16))
+        parents, drafts = _random_tree(rng, K, 3)
+        a = [int(x) for x in rng.integers(0, 3, size=K + 1)]
+        good = _brute_force_accept(a, parents, drafts)
+        assert oracle.tree_accept(a, parents, drafts)[:2] == good
+        caught |= mutant(a, parents, drafts) != good
+    assert caught
