@@ -47,6 +47,10 @@ WORKLOADS = {
     "c3samp": dict(cid=2, V=248320, H=2048, K=8, drafts="forced", ctx=4096, copy=0.30, layers=0, temp=0.7,
                    name="sampling verify at T=0.7: 35B-A3B-shaped head H=2048 V=248320 K=8 S=9, drafts forced to "
                         "match the first j~U{0..K} argmaxes, kept with probability p(d) (speculative sampling)"),
+    "c3tree": dict(cid=2, V=248320, H=2048, K=8, drafts="ngram", ctx=4096, copy=0.30, layers=0, tree=(3, 4),
+                   name="tree verify: 35B-A3B-shaped head H=2048 V=248320, 8 tree nodes (S=9) from the 3 best "
+                        "n-gram matches continued 4 deep over 4096 Zipf(1.1) ids with 30% copied spans, "
+                        "greedy walk down the tree"),
     "c3s17": dict(cid=2, V=248320, H=2048, K=16, drafts="forced", ctx=4096, copy=0.30, layers=0,
                   name="35B-A3B-shaped head H=2048 V=248320 K=16 S=17, forced drafts"),
     "c4s2": dict(cid=3, V=248320, H=5120, K=1, drafts="ngram", ctx=16384, copy=0.20, layers=0,
@@ -221,7 +225,10 @@ def cpu_baseline(wl, inp, table=None, seconds_budget=20.0):
             x = hid[rounds % len(hid)]
             if wl["layers"]:
                 return None           # the fp64 oracle stack takes minutes per round
-            drafts, _, _ = oracle.propose_scan(tokens, 3, K)
+            if wl.get("tree"):
+                parents, drafts, _, _ = oracle.propose_tree(tokens, 3, K, *wl["tree"])
+            else:
+                drafts, _, _ = oracle.propose_scan(tokens, 3, K)
             if table is not None:     # the stand-in model: rows of the oracle's own window
                 ids = [tokens[-1]] + [d if d >= 0 else 0 for d in drafts]
                 x = table[ids].cpu().numpy()
@@ -234,6 +241,8 @@ def cpu_baseline(wl, inp, table=None, seconds_budget=20.0):
                 drafts, _ = synth.forced_drafts(rng, a, K, V)
             if wl.get("temp"):
                 app = oracle.sampling_verify(L, drafts, wl["temp"], SAMPLE_SEED, len(tokens))["appended"]
+            elif wl.get("tree"):
+                _, app, _ = oracle.tree_accept(a, parents, drafts)
             else:
                 _, app = oracle.accept(a, drafts)
             tokens += app
@@ -244,8 +253,10 @@ def cpu_baseline(wl, inp, table=None, seconds_budget=20.0):
     return {"value": rounds / el, "unit": "rounds/s", "cores": 1, "kind": "oracle",
             "sample": f"{rounds} whole rounds of this workload (fp64 dequantize in 8192-row chunks, "
                       f"fp64 logits for S={S}, "
-                      + ("softmax, Philox noise, residual draws, sampling accept" if wl.get("temp") else "argmax, accept")
-                      + f", n-gram propose over the {len(inp['ctx'])}-id context), single thread, {el:.1f} s"}
+                      + ("softmax, Philox noise, residual draws, sampling accept" if wl.get("temp") else
+                         "argmax, tree walk" if wl.get("tree") else "argmax, accept")
+                      + f", n-gram {'tree ' if wl.get('tree') else ''}propose over the {len(inp['ctx'])}-id "
+                      f"context), single thread, {el:.1f} s"}
 
 
 def main():
@@ -360,7 +371,16 @@ def main():
     # A round is verify -> accept -> propose (the next round's drafts), through the fused
     # entry point: one launch when the hidden axis needs no split.  The first drafts come
     # from a plain propose after the anchor bootstrap.
-    sv.propose(tokens, state, drafts, 3)
+    tree = wl.get("tree")
+    if tree:
+        parents = torch.empty(K, dtype=torch.int32, device=dev)
+        sv.propose_tree(tokens, state, parents, drafts, 3, tree[0], tree[1])
+
+        def head_round(w_, s_, x_, d_in_, tokens_, state_, drafts_, argmax_, work_, stream=None):
+            sv.round_tree(w_, s_, x_, parents, d_in_, tokens_, state_, parents, drafts_, argmax_, work_, 3,
+                          tree[0], tree[1], stream=stream)
+    else:
+        sv.propose(tokens, state, drafts, 3)
 
     def round_(r):
         c = r % copies
@@ -452,6 +472,8 @@ def main():
         "accept_hist": hist,
         "tokens_per_round": round((args.steps + sum_j) / args.steps, 3),
     }
+    if tree:
+        out["config"]["tree"] = {"branches": tree[0], "depth": tree[1], "nodes": K}
     if temp:
         out["config"]["temperature"] = temp
         out["config"]["seed"] = SAMPLE_SEED

@@ -6,6 +6,7 @@
  *   specverify_verify   int8 per-block-32 head matmul of the S = K+1 window + per-row argmax
  *   specverify_accept   greedy longest-prefix acceptance, commits 1 + j tokens
  *   specverify_*_sample sampling verify at temperature > 0 (probabilities, residual redraw)
+ *   specverify_*_tree   tree drafts (merged n-gram matches) and the greedy walk down the tree
  * plus the dense weight-bound stack in front of the head (rmsnorm, gate/up + SiLU*mul,
  * down + residual) built on the same int8 matmul core.
  *
@@ -226,6 +227,46 @@ int specverify_round_sample(const int8_t* wq, const uint16_t* wscale, int32_t V,
                             int32_t* state, int32_t ngram_max, int32_t* drafts_out,
                             int32_t* sample, float* lse, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/*
+ * Tree verify (greedy): specverify_propose_tree, specverify_accept_tree and the fused
+ * specverify_round_tree.
+ * Page: "Stream C - Speculative decoding", the EAGLE-3 + tree handoff and the deferred list
+ * (the drafter proposes a tree; one verify forward covers every node under a tree attention
+ * mask; the linear accept becomes a walk down the tree).
+ * Tree: K draft nodes (1 .. 15) under the anchor a0 (node 0); node i (1..K) has parent
+ * parents[i-1] (0 <= parents[i-1] < i) and token drafts[i-1] (-1 = a pad, never matched).
+ * Window row i is the row after the path root -> i, S = K+1 <= 16 rows (for a token-indexed
+ * model, specverify_gather_window of `drafts` gives them).
+ *   accept:  from node c = 0, move to the lowest-index child of c whose token is argmax[c];
+ *            repeat until none matches; append the path's tokens and argmax of the last node
+ *            (len += 1 + j, j = path length); statistics and the hit-rate gate as the linear
+ *            accept.  Children listed with a parent index >= their own index are ignored.
+ *   drafter: the `branches` (1 .. 4) best earlier end positions of the stream's suffix, ranked
+ *            as specverify_propose ranks them (longer match up to ngram_max, then more recent),
+ *            each continued for up to `depth` (1 .. K) tokens, inserted into a prefix tree in
+ *            rank order (a node is reused when its parent already has a child with that
+ *            token) until K nodes exist; free slots become pads under the root.  state[2]
+ *            = real nodes, state[3] = match length of the best position.  One branch of depth
+ *            K gives specverify_propose's drafts as a chain (parents 0, 1, 2, ...).
+ *   specverify_round_tree = specverify_verify(hidden, S = K+1) -> accept_tree -> propose_tree
+ *            in two launches; parents_out / drafts_out may alias parents_in / drafts_in.
+ * Arguments not listed are as for specverify_verify / specverify_round / specverify_propose.
+ * Errors: SV_ERR_SHAPE for K, branches, depth or ngram_max out of range; otherwise as those.
+ */
+int specverify_propose_tree(const int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max,
+                            int32_t K, int32_t branches, int32_t depth, int32_t* parents,
+                            int32_t* drafts, hipStream_t stream);
+int specverify_accept_tree(const int32_t* argmax, const int32_t* parents, const int32_t* drafts,
+                           int32_t K, int32_t* tokens, int32_t cap, int32_t* state,
+                           hipStream_t stream);
+int specverify_round_tree(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
+                          const uint16_t* hidden, int32_t K, const int32_t* parents_in,
+                          const int32_t* drafts_in, int32_t* tokens, int32_t cap, int32_t* state,
+                          int32_t ngram_max, int32_t branches, int32_t depth,
+                          int32_t* parents_out, int32_t* drafts_out, int32_t* argmax,
+                          float* logits, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /*
  * specverify_gather_window - the window rows of a token-indexed stand-in model:

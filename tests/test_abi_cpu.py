@@ -199,6 +199,28 @@ def test_sampling_argument_errors(lib):
     assert r(A16, A16, 1000, 256, A16, 8, A16, 0.8, 1, A16, 100, A16, 3, A16, NULL, NULL, A16, ws - 1, NULL) == 4
 
 
+def test_tree_argument_errors(lib):
+    pt = lib.specverify_propose_tree
+    assert pt(NULL, 100, A16, 3, 8, 2, 4, A16, A16, NULL) == 1
+    assert pt(A16, 100, A16, 3, 16, 2, 4, A16, A16, NULL) == 2              # K <= 15
+    assert pt(A16, 100, A16, 3, 8, 5, 4, A16, A16, NULL) == 2               # branches <= 4
+    assert pt(A16, 100, A16, 3, 8, 2, 9, A16, A16, NULL) == 2               # depth <= K
+    assert pt(A16, 100, A16, 3, 8, 2, 0, A16, A16, NULL) == 2               # depth >= 1
+    assert pt(A16, 100, A16, 9, 8, 2, 4, A16, A16, NULL) == 2               # ngram_max
+    assert pt(A16, 0, A16, 3, 8, 2, 4, A16, A16, NULL) == 5                 # cap
+    assert pt(A16, 100, A16, 3, 8, 2, 4, A2, A16, NULL) == 3
+    at = lib.specverify_accept_tree
+    assert at(A16, NULL, A16, 8, A16, 100, A16, NULL) == 1
+    assert at(A16, A16, A16, 0, A16, 100, A16, NULL) == 2
+    assert at(A16, A16, A16, 16, A16, 100, A16, NULL) == 2
+    rt = lib.specverify_round_tree
+    ws = lib.specverify_verify_workspace_bytes(1000, 256, 9)
+    assert rt(A16, A16, 1000, 256, A16, 8, NULL, A16, A16, 100, A16, 3, 2, 4, A16, A16, A16, NULL, A16, ws, NULL) == 1
+    assert rt(A16, A16, 1000, 256, A16, 16, A16, A16, A16, 100, A16, 3, 2, 4, A16, A16, A16, NULL, A16, ws, NULL) == 2
+    assert rt(A16, A16, 1000, 250, A16, 8, A16, A16, A16, 100, A16, 3, 2, 4, A16, A16, A16, NULL, A16, ws, NULL) == 2
+    assert rt(A16, A16, 1000, 256, A16, 8, A16, A16, A16, 100, A16, 3, 2, 4, A16, A16, A16, NULL, A16, 8, NULL) == 4
+
+
 def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(sv, "_lib", None)
     monkeypatch.setattr(sv, "LIB_PATH", str(tmp_path / "nope.so"))

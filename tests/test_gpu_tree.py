@@ -1,0 +1,227 @@
+"""GPU parity of tree verify (specverify_propose_tree / _accept_tree / _round_tree) against the
+CPU oracle (oracle/tree.py): the drafter and the walk bit-exactly, the fused round against the
+separate calls, a device-resident tree decoding loop against plain greedy decoding, and one
+branch against the linear round."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import tree as tr
+from weight_bound_verify_amd import specverify as sv
+from weight_bound_verify_amd import synth
+
+from gpu_util import dev, say, to_dev
+from test_oracle_tree import _random_tree
+
+pytestmark = pytest.mark.gpu
+
+
+def _state(n):
+    st = sv.new_state(dev())
+    st[sv.STATE_LEN] = n
+    return st
+
+
+@pytest.mark.parametrize("n,vocab,nmax,K,B,D", [
+    (1, 5, 3, 8, 2, 4), (2, 2, 3, 4, 4, 4), (40, 3, 3, 15, 4, 5), (300, 6, 3, 15, 3, 15),
+    (300, 4, 2, 8, 1, 8), (513, 10, 4, 12, 4, 3), (4096, 50, 3, 15, 4, 6), (16000, 8, 3, 15, 2, 7),
+    (20000, 5, 3, 10, 4, 10),            # longer than the LDS copy: the global-memory path
+])
+def test_propose_tree_matches_oracle(n, vocab, nmax, K, B, D):
+    rng = np.random.default_rng(n + K + B)
+    for case in range(4):
+        toks = rng.integers(0, vocab, size=n).astype(np.int32)
+        tokens = to_dev(np.concatenate([toks, np.zeros(8, dtype=np.int32)]))
+        state = _state(n)
+        parents = torch.full((K,), -9, dtype=torch.int32, device=dev())
+        drafts = torch.full((K,), -9, dtype=torch.int32, device=dev())
+        sv.propose_tree(tokens, state, parents, drafts, nmax, B, D)
+        torch.cuda.synchronize()
+        p_ref, d_ref, used, real = tr.propose_tree(list(toks), nmax, K, B, D)
+        assert parents.cpu().tolist() == p_ref and drafts.cpu().tolist() == d_ref, (case, n)
+        st = state.cpu().numpy()
+        assert st[sv.STATE_NVALID] == real and st[sv.STATE_NUSED] == used
+
+
+def test_propose_tree_one_branch_is_the_linear_drafter():
+    rng = np.random.default_rng(3)
+    for case in range(20):
+        n = int(rng.integers(2, 3000))
+        toks = rng.integers(0, int(rng.integers(2, 30)), size=n).astype(np.int32)
+        K = int(rng.integers(1, 16))
+        tokens = to_dev(toks)
+        st_a, st_b = _state(n), _state(n)
+        parents = torch.empty(K, dtype=torch.int32, device=dev())
+        d_tree = torch.empty(K, dtype=torch.int32, device=dev())
+        d_lin = torch.empty(K, dtype=torch.int32, device=dev())
+        sv.propose_tree(tokens, st_a, parents, d_tree, 3, 1, K)
+        sv.propose(tokens, st_b, d_lin, 3)
+        torch.cuda.synchronize()
+        assert torch.equal(d_tree, d_lin) and torch.equal(st_a, st_b)
+        real = int(st_a[sv.STATE_NVALID])
+        assert parents.cpu().tolist() == list(range(real)) + [0] * (K - real)
+
+
+def test_accept_tree_matches_oracle_random():
+    rng = np.random.default_rng(4)
+    for case in range(300):
+        K = int(rng.integers(1, 16))
+        V = int(rng.integers(2, 6))
+        parents, drafts = _random_tree(rng, K, V)
+        a = rng.integers(0, V, size=K + 1).astype(np.int32)
+        len0 = int(rng.integers(1, 50))
+        buf = np.full(len0 + K + 1 + 4, -5, dtype=np.int32)
+        tokens = to_dev(buf)
+        state = _state(len0)
+        sv.accept_tree(to_dev(a), to_dev(np.array(parents, dtype=np.int32)),
+                       to_dev(np.array(drafts, dtype=np.int32)), tokens, state)
+        torch.cuda.synchronize()
+        j, app, _ = tr.tree_accept(a, parents, drafts)
+        out = tokens.cpu().numpy()
+        st = state.cpu().numpy()
+        assert st[sv.STATE_LEN] == len0 + 1 + j and st[sv.STATE_J] == j, case
+        assert list(out[len0:len0 + j + 1]) == app, case
+        assert np.all(out[len0 + j + 1:] == -5) and np.all(out[:len0] == -5)
+
+
+def test_accept_tree_ignores_parents_that_do_not_precede_their_node():
+    # node 2 names itself as parent, node 3 names node 4: neither can be walked to
+    parents = [0, 2, 4, 3]
+    drafts = [7, 8, 9, 6]
+    a = np.array([7, 8, 9, 6, 1], dtype=np.int32)
+    tokens = to_dev(np.zeros(16, dtype=np.int32))
+    state = _state(2)
+    sv.accept_tree(to_dev(a), to_dev(np.array(parents, dtype=np.int32)), to_dev(np.array(drafts, dtype=np.int32)),
+                   tokens, state)
+    torch.cuda.synchronize()
+    assert int(state[sv.STATE_LEN]) == 4 and tokens[2:4].cpu().tolist() == [7, 8]
+
+
+def test_accept_tree_capacity_overflow_writes_nothing():
+    tokens = to_dev(np.full(8, -5, dtype=np.int32))
+    state = _state(4)
+    sv.accept_tree(to_dev(np.zeros(5, dtype=np.int32)), to_dev(np.zeros(4, dtype=np.int32)),
+                   to_dev(np.zeros(4, dtype=np.int32)), tokens, state)
+    torch.cuda.synchronize()
+    assert int(state[sv.STATE_LEN]) == 4 and int(state[sv.STATE_FLAGS]) & sv.FLAG_CAPACITY
+    assert tokens.cpu().tolist() == [-5] * 8
+
+
+def test_round_tree_equals_separate_calls():
+    V, H, K, B, D = 5000, 1024, 8, 3, 4
+    S = K + 1
+    rng = np.random.default_rng(12)
+    q, s = synth.quantized_head(np.random.SeedSequence(5), V, H)
+    wq, ws = to_dev(q), to_dev(s)
+    ctx = synth.zipf_context_with_copies(np.random.default_rng(3), 600, V, 0.3)[0].astype(np.int32)
+    cap = 2000
+    work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev())
+
+    def fresh():
+        t = torch.zeros(cap, dtype=torch.int32, device=dev())
+        t[:len(ctx)] = to_dev(ctx)
+        st = _state(len(ctx))
+        p = torch.empty(K, dtype=torch.int32, device=dev())
+        d = torch.empty(K, dtype=torch.int32, device=dev())
+        sv.propose_tree(t, st, p, d, 3, B, D)
+        return t, st, p, d
+
+    ta, sa, pa, da = fresh()
+    tb, sb, pb, db = fresh()
+    am_a = torch.empty(S, dtype=torch.int32, device=dev())
+    am_b = torch.empty(S, dtype=torch.int32, device=dev())
+    for r in range(30):
+        # rows favour the drafted tokens now and then so that some paths are accepted
+        hidden = to_dev(synth.fp16_normal(rng, (S, H)))
+        sv.round_tree(wq, ws, hidden, pa, da, ta, sa, pa, da, am_a, work, 3, B, D)
+        sv.verify(wq, ws, hidden, am_b, work)
+        sv.accept_tree(am_b, pb, db, tb, sb)
+        sv.propose_tree(tb, sb, pb, db, 3, B, D)
+        torch.cuda.synchronize()
+        assert torch.equal(am_a, am_b) and torch.equal(sa, sb), r
+        assert torch.equal(pa, pb) and torch.equal(da, db) and torch.equal(ta, tb), r
+    assert int(sa[sv.STATE_ROUNDS]) == 30
+
+
+def _device_tree_loop(q, s, table, ctx, n_new, K, B, D, linear=False):
+    """Greedy tree decoding on the device: window rows gathered from the token-indexed table
+    (the Markov stand-in: a node's row depends on its own token, which a tree attention mask
+    preserves), one fused round per step, no host synchronisation inside a round."""
+    V, H = q.shape
+    S = K + 1
+    cap = len(ctx) + n_new + 2 * S
+    buf = np.zeros(cap, dtype=np.int32)
+    buf[:len(ctx)] = ctx
+    tokens = to_dev(buf)
+    state = _state(len(ctx))
+    wq, ws, tab = to_dev(q), to_dev(s), to_dev(table)
+    work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev())
+    a0 = torch.empty(1, dtype=torch.int32, device=dev())
+    argmax = torch.empty(S, dtype=torch.int32, device=dev())
+    parents = torch.empty(K, dtype=torch.int32, device=dev())
+    drafts = torch.empty(K, dtype=torch.int32, device=dev())
+    window = torch.empty((S, H), dtype=torch.float16, device=dev())
+    h_last = torch.empty((1, H), dtype=torch.float16, device=dev())
+    sv.gather_window(tokens, state, drafts[:0], tab, h_last)
+    sv.verify(wq, ws, h_last, a0, sv.workspace(sv.verify_workspace_bytes(V, H, 1), dev()))
+    sv.accept(a0, None, tokens, state)                                  # anchor bootstrap
+    if linear:
+        sv.propose(tokens, state, drafts, 3)
+    else:
+        sv.propose_tree(tokens, state, parents, drafts, 3, B, D)
+    rounds = 0
+    while True:
+        torch.cuda.synchronize()
+        if int(state[sv.STATE_LEN]) >= len(ctx) + n_new:
+            break
+        sv.gather_window(tokens, state, drafts, tab, window)
+        if linear:
+            sv.round(wq, ws, window, drafts, tokens, state, drafts, argmax, work, 3)
+        else:
+            sv.round_tree(wq, ws, window, parents, drafts, tokens, state, parents, drafts, argmax, work, 3, B, D)
+        rounds += 1
+    torch.cuda.synchronize()
+    n = int(state[sv.STATE_LEN])
+    return tokens[:n].cpu().tolist(), state.cpu().numpy(), rounds
+
+
+@pytest.mark.parametrize("V,H,K,B,D", [(4096, 512, 8, 2, 4), (2048, 256, 15, 4, 5), (512, 128, 6, 3, 2)])
+def test_device_tree_loop_equals_greedy(V, H, K, B, D):
+    say(f"tree loop V={V} H={H} K={K} B={B} D={D}")
+    rng = np.random.default_rng(V + K + B)
+    q, s = synth.quantized_head(np.random.SeedSequence(V), V, H)
+    model = synth.MarkovHidden(rng, V, H)
+    ctx, _, _ = synth.uniform_context_with_span(rng, 512, V, 12, 16)
+    n_new = 200
+    got, stv, rounds = _device_tree_loop(q, s, model.table, ctx, n_new, K, B, D)
+    memo = {}
+
+    def logits_after(t):
+        if t not in memo:
+            memo[t] = oracle.head_logits(q, s, model.table[t][None])
+        return memo[t]
+
+    ref = list(ctx)
+    while len(ref) < len(got):
+        ref.append(int(oracle.argmax_lowest(logits_after(ref[-1]))[0]))
+    for p in range(len(ctx), len(got)):
+        if got[p] != ref[p]:
+            L = logits_after(got[p - 1])
+            assert oracle.top2_gap(L)[0] < 1e-3 and got[p] in oracle.admissible_sets(L)[0], p
+            break
+    assert stv[sv.STATE_FLAGS] == 0
+    say(f"  rounds {rounds}, tokens/round {(len(got) - len(ctx)) / max(rounds, 1):.2f}")
+    assert rounds < n_new
+
+
+def test_one_branch_tree_loop_equals_linear_loop():
+    V, H, K = 2048, 256, 8
+    rng = np.random.default_rng(7)
+    q, s = synth.quantized_head(np.random.SeedSequence(9), V, H)
+    model = synth.MarkovHidden(rng, V, H)
+    ctx, _, _ = synth.uniform_context_with_span(rng, 400, V, 10, 12)
+    a = _device_tree_loop(q, s, model.table, ctx, 150, K, 1, K)
+    b = _device_tree_loop(q, s, model.table, ctx, 150, K, 1, K, linear=True)
+    assert a[0] == b[0] and a[2] == b[2]
+    assert np.array_equal(a[1][sv.STATE_HIST:sv.STATE_HIST + K + 1], b[1][sv.STATE_HIST:sv.STATE_HIST + K + 1])

@@ -347,6 +347,83 @@ int specverify_round_sample(const int8_t* wq, const uint16_t* wscale, int32_t V,
 
 namespace {
 
+int check_tree_args(int32_t K, int32_t branches, int32_t depth, int32_t ngram_max) {
+    if (K < 1 || K > 15) return fail(SV_ERR_SHAPE, "tree nodes K=%d outside [1, 15]", K);
+    if (branches < 1 || branches > 4) return fail(SV_ERR_SHAPE, "branches=%d outside [1, 4]", branches);
+    if (depth < 1 || depth > K) return fail(SV_ERR_SHAPE, "depth=%d outside [1, K=%d]", depth, K);
+    if (ngram_max < 1 || ngram_max > SV_MAX_NGRAM) return fail(SV_ERR_SHAPE, "ngram_max=%d outside [1, %d]", ngram_max, SV_MAX_NGRAM);
+    return SV_OK;
+}
+
+}  // namespace
+
+int specverify_propose_tree(const int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max, int32_t K,
+                            int32_t branches, int32_t depth, int32_t* parents, int32_t* drafts, hipStream_t stream) {
+    if (!tokens || !state || !parents || !drafts) return fail(SV_ERR_NULL, "tokens, state, parents and drafts are required");
+    if (int st = check_tree_args(K, branches, depth, ngram_max)) return st;
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(tokens, 4) || !aligned(state, 4) || !aligned(parents, 4) || !aligned(drafts, 4))
+        return fail(SV_ERR_ALIGN, "int32 buffers must be 4-byte aligned");
+    if (int st = check_device()) return st;
+    hipError_t e = sv::launch_propose_tree(tokens, cap, state, ngram_max, K, branches, depth, parents, drafts, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "tree propose launch");
+}
+
+int specverify_accept_tree(const int32_t* argmax, const int32_t* parents, const int32_t* drafts, int32_t K,
+                           int32_t* tokens, int32_t cap, int32_t* state, hipStream_t stream) {
+    if (!argmax || !parents || !drafts || !tokens || !state)
+        return fail(SV_ERR_NULL, "argmax, parents, drafts, tokens and state are required");
+    if (K < 1 || K > 15) return fail(SV_ERR_SHAPE, "tree nodes K=%d outside [1, 15]", K);
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(argmax, 4) || !aligned(parents, 4) || !aligned(drafts, 4) || !aligned(tokens, 4) ||
+        !aligned(state, 4))
+        return fail(SV_ERR_ALIGN, "int32 buffers must be 4-byte aligned");
+    if (int st = check_device()) return st;
+    hipError_t e = sv::launch_accept_tree(argmax, parents, drafts, K, tokens, cap, state, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "tree accept launch");
+}
+
+int specverify_round_tree(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
+                          int32_t K, const int32_t* parents_in, const int32_t* drafts_in, int32_t* tokens,
+                          int32_t cap, int32_t* state, int32_t ngram_max, int32_t branches, int32_t depth,
+                          int32_t* parents_out, int32_t* drafts_out, int32_t* argmax, float* logits,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (int st = check_tree_args(K, branches, depth, ngram_max)) return st;
+    if (int st = check_head(wq, wscale, V, H, hidden, K + 1, argmax, logits, workspace, workspace_bytes)) return st;
+    if (!parents_in || !drafts_in || !tokens || !state || !parents_out || !drafts_out)
+        return fail(SV_ERR_NULL, "tree, tokens and state buffers are required");
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(parents_in, 4) || !aligned(drafts_in, 4) || !aligned(tokens, 4) || !aligned(state, 4) ||
+        !aligned(parents_out, 4) || !aligned(drafts_out, 4))
+        return fail(SV_ERR_ALIGN, "int32 buffers must be 4-byte aligned");
+    if (int st = check_device()) return st;
+    const int S = K + 1;
+    char* ws = static_cast<char*>(workspace);
+    const sv::GemmCfg cfg = sv::gemm_config(V, H, S, sv::EPI_HEAD);
+    sv::GemmArgs a{};
+    a.w0 = wq;
+    a.s0 = wscale;
+    a.x = hidden;
+    a.V = V;
+    a.H = H;
+    a.S = S;
+    a.nb = H / SV_BLOCK;
+    a.nitems = (V + 15) / 16;
+    a.ksplit = cfg.ksplit;
+    a.part_val = reinterpret_cast<float*>(ws);
+    a.part_idx = reinterpret_cast<int*>(ws + (size_t)4 * S * sv::kGridMax);
+    a.logits = logits;
+    if (cfg.ksplit > 1) a.kpart0 = reinterpret_cast<float*>(ws + sv::head_partials_bytes(S));
+    hipError_t e = launch_matmul(sv::EPI_HEAD, cfg, a, stream);
+    if (e != hipSuccess) return hip_fail(e, "tree verify matmul launch");
+    const int nparts = cfg.ksplit > 1 ? sv::combine_groups(V) : cfg.grid;
+    e = sv::launch_tree_tail(a.part_val, a.part_idx, nparts, S, argmax, parents_in, drafts_in, tokens, cap, state,
+                             ngram_max, branches, depth, parents_out, drafts_out, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "tree round tail launch");
+}
+
+namespace {
+
 int check_head_q4(const uint8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
                   int32_t S, int32_t* argmax, float* logits, void* workspace, size_t workspace_bytes,
                   sv::Q4Cfg& cfg) {

@@ -72,6 +72,17 @@ hipError_t launch_accept_sample(const int32_t* sample, const float* lse, const f
                                 int K, int V, uint32_t key0, uint32_t key1, int32_t* tokens, int cap,
                                 int32_t* state, hipStream_t stream);
 
+// Tree verify (sv_tree.hip), K <= 15 draft nodes: the round tail after a head matmul
+// (argmax, the walk down the tree, the next tree), and the standalone drafter and walk.
+hipError_t launch_tree_tail(const float* pv, const int* pi, int nparts, int S, int32_t* argmax,
+                            const int32_t* parents_in, const int32_t* drafts_in, int32_t* tokens, int cap,
+                            int32_t* state, int nmax, int branches, int depth, int32_t* parents_out,
+                            int32_t* drafts_out, hipStream_t stream);
+hipError_t launch_propose_tree(const int32_t* tokens, int cap, int32_t* state, int nmax, int K, int branches,
+                               int depth, int32_t* parents_out, int32_t* drafts_out, hipStream_t stream);
+hipError_t launch_accept_tree(const int32_t* argmax, const int32_t* parents, const int32_t* drafts, int K,
+                              int32_t* tokens, int cap, int32_t* state, hipStream_t stream);
+
 // Workspace bytes a head matmul of this shape needs.
 size_t head_workspace_bytes(int V, int H, int S);
 // Workspace bytes a store / gate-up matmul needs (non-zero only when ksplit > 1).

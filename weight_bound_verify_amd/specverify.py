@@ -30,7 +30,8 @@ EXPORTS = (
     "specverify_propose", "specverify_verify_workspace_bytes", "specverify_verify", "specverify_round",
     "specverify_accept", "specverify_gather_window", "specverify_generate", "specverify_verify_q4b32",
     "specverify_round_q4b32", "specverify_sample_workspace_bytes", "specverify_verify_sample",
-    "specverify_accept_sample", "specverify_round_sample",
+    "specverify_accept_sample", "specverify_round_sample", "specverify_propose_tree", "specverify_accept_tree",
+    "specverify_round_tree",
     "specverify_rmsnorm", "specverify_stack_workspace_bytes", "specverify_gateup_silu_q8b32",
     "specverify_linear_q8b32", "specverify_linear_residual_rmsnorm_q8b32",
     "specverify_stack_forward_workspace_bytes", "specverify_stack", "specverify_set_tuning", "specverify_profile_next_matmul", "specverify_status_string", "specverify_last_error",
@@ -71,6 +72,10 @@ def load():
         "specverify_accept_sample": (_I, [_P, _P, _P, _P, _I, _I, ctypes.c_uint64, _P, _I, _P, _P]),
         "specverify_round_sample": (_I, [_P, _P, _I, _I, _P, _I, _P, ctypes.c_float, ctypes.c_uint64, _P, _I, _P,
                                          _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+        "specverify_propose_tree": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P]),
+        "specverify_accept_tree": (_I, [_P, _P, _P, _I, _P, _I, _P, _P]),
+        "specverify_round_tree": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P,
+                                       ctypes.c_size_t, _P]),
         "specverify_generate": (_I, [_P, _P, _I, _I, _P, _I, _I, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t,
                                      _P]),
         "specverify_rmsnorm": (_I, [_P, _I, _I, ctypes.c_float, _P, _P]),
@@ -272,6 +277,43 @@ def round_sample(wq, wscale, hidden, drafts_in, temperature: float, seed: int, t
         _ptr(state, torch.int32, "state", STATE_WORDS), int(ngram_max), _ptr(drafts_out, torch.int32, "drafts_out", K),
         _ptr(sample, torch.int32, "sample", S), _ptr(lse, torch.float32, "lse", S), _ptr(ws, torch.uint8, "workspace"),
         ws.numel(), _stream(stream)))
+
+
+def propose_tree(tokens, state, parents, drafts, ngram_max: int = 3, branches: int = 2, depth: int = 4,
+                 stream=None) -> None:
+    """Tree drafts of ``tokens[:state[0]]``: K = drafts.numel() nodes (parents, tokens)."""
+    K = drafts.numel()
+    _check(load().specverify_propose_tree(_ptr(tokens, torch.int32, "tokens"), tokens.numel(),
+                                          _ptr(state, torch.int32, "state", STATE_WORDS), int(ngram_max), K,
+                                          int(branches), int(depth), _ptr(parents, torch.int32, "parents", K),
+                                          _ptr(drafts, torch.int32, "drafts"), _stream(stream)))
+
+
+def accept_tree(argmax, parents, drafts, tokens, state, stream=None) -> None:
+    """The greedy walk down the tree; ``argmax`` holds K+1 ids."""
+    K = argmax.numel() - 1
+    _check(load().specverify_accept_tree(_ptr(argmax, torch.int32, "argmax"), _ptr(parents, torch.int32, "parents", K),
+                                         _ptr(drafts, torch.int32, "drafts", K), K, _ptr(tokens, torch.int32, "tokens"),
+                                         tokens.numel(), _ptr(state, torch.int32, "state", STATE_WORDS),
+                                         _stream(stream)))
+
+
+def round_tree(wq, wscale, hidden, parents_in, drafts_in, tokens, state, parents_out, drafts_out, argmax, ws,
+               ngram_max: int = 3, branches: int = 2, depth: int = 4, logits=None, stream=None) -> None:
+    """verify(hidden, S = K+1) -> accept_tree -> propose_tree, fused."""
+    V, H = wq.shape
+    S = hidden.shape[0]
+    K = S - 1
+    if hidden.shape[1] != H or tuple(wscale.shape) != (V, H // SV_BLOCK) or drafts_in.numel() < K:
+        raise ValueError("shape mismatch")
+    _check(load().specverify_round_tree(
+        _ptr(wq, torch.int8, "wq"), _ptr(wscale, torch.float16, "wscale"), V, H,
+        _ptr(hidden, torch.float16, "hidden"), K, _ptr(parents_in, torch.int32, "parents_in", K),
+        _ptr(drafts_in, torch.int32, "drafts_in", K), _ptr(tokens, torch.int32, "tokens"), tokens.numel(),
+        _ptr(state, torch.int32, "state", STATE_WORDS), int(ngram_max), int(branches), int(depth),
+        _ptr(parents_out, torch.int32, "parents_out", K), _ptr(drafts_out, torch.int32, "drafts_out", K),
+        _ptr(argmax, torch.int32, "argmax", S), _ptr(logits, torch.float32, "logits", S * V),
+        _ptr(ws, torch.uint8, "workspace"), ws.numel(), _stream(stream)))
 
 
 def accept(argmax, drafts, tokens, state, stream=None) -> None:
