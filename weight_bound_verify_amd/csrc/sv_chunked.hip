@@ -49,24 +49,24 @@ __device__ __forceinline__ int crow(int it, int n) {
     return EPI == EPI_GATEUP ? it * 8 + (n & 7) : it * kTileRows + n;
 }
 
-// 1 / sqrt(sum_t ss[s][t] / H + eps) for the window rows s of this workgroup, summed in a
-// fixed order (per lane sequentially over t = lane, lane+64, ..., then a fixed butterfly),
-// so every workgroup and the final norm pass get the same value.  Written to inv[s].
+// 1 / sqrt(sum_t ss[s][t] / H + eps) for the window rows s of this workgroup, summed in one
+// fixed order: lane l folds partials 4l .. 4l+3, then 256 + 4l .. 256 + 4l + 3, ... in
+// sequence, then the lanes fold with a fixed butterfly.  Every workgroup and the final norm
+// pass use this order, so they get the same value.  Written to inv[s].
 template <int NW>
 __device__ __forceinline__ void norm_scales(const float* __restrict__ ss, int nt, int S, int H, float eps, int wave,
                                             int lane, float* inv) {
-    constexpr int kPer = 8;          // partials per lane per pass, all loads issued before the sums
     for (int s = wave; s < S; s += NW) {
         float t = 0.f;
-        for (int base = 0; base < nt; base += kPer * kWave) {
-            float v[kPer];
+        for (int base = 0; base < nt; base += 4 * kWave) {
+            float v[4];
 #pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-                const int i = base + j * kWave + lane;
-                v[j] = i < nt ? ss[(size_t)s * nt + i] : 0.f;
+            for (int e = 0; e < 4; ++e) {
+                const int i = base + 4 * lane + e;
+                v[e] = i < nt ? ss[(size_t)s * nt + i] : 0.f;
             }
 #pragma unroll
-            for (int j = 0; j < kPer; ++j) t += v[j];
+            for (int e = 0; e < 4; ++e) t += v[e];
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, kWave);
@@ -169,15 +169,17 @@ __global__ __launch_bounds__(NW * 64) void q8b32_chunked(ChunkArgs a) {
         }
     };
 
-    // ---- prologue: ring, held window rows, then the norm (its loads are the youngest) ----
+    // ---- prologue ------------------------------------------------------------------------
+    // Held rows: the window rows and the norm's sum-of-squares partials are issued first and
+    // the ring after them, so the norm waits for its own loads only while the ring's are in
+    // flight (issued the other way round, the norm's wait drained the whole ring).  The
+    // partials are read with uniform buffer loads (zeros past the end, and everywhere when
+    // there is no norm), each lane folding 4 consecutive partials, the order norm_scales uses.
     Unit<HOLD> ring[DEPTH];
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-        if constexpr (HOLD > 0) load(ring[d], d / HOLD, d % HOLD);
-        else load(ring[d], 0, d);
-    }
     f16x8 hold[HOLD ? HOLD : 1][4];
+    float inv = 1.0f;
     if constexpr (HOLD > 0) {
+        constexpr int RPN = (16 + NW - 1) / NW;            // window rows whose norm this wave folds
 #pragma unroll
         for (int c = 0; c < HOLD; ++c)
 #pragma unroll
@@ -185,17 +187,43 @@ __global__ __launch_bounds__(NW * 64) void q8b32_chunked(ChunkArgs a) {
                 hold[c][b] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                                            rx, (int)(xlane + (uint32_t)(c * NW * 4 + wave * 4 + b) * kBlock * 2u),
                                                            0, 0));
-    }
-    float inv = 1.0f;
-    if (a.norm_ss) {
-        norm_scales<NW>(a.norm_ss, a.norm_tiles, a.S, a.H, a.eps, wave, lane, inv_s);
+        // H <= 4096 here (at most two chunks of 16 x 128 bytes), so nt = H / 16 <= 256: one
+        // 4-wide load per lane and row covers all partials
+        const int nt = a.norm_tiles;
+        const __amdgpu_buffer_rsrc_t rn = buf_view(a.norm_ss, a.norm_ss ? (uint32_t)a.S * (uint32_t)nt * 4u : 0u);
+        f32x4 pv[RPN];
+#pragma unroll
+        for (int j = 0; j < RPN; ++j) {
+            const int s = wave + j * NW;
+            const uint32_t off = s < 16 && s < a.S && 4 * lane < nt ? ((uint32_t)s * nt + 4u * lane) * 4u : kPastEnd;
+            pv[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rn, (int)off, 0, 0));
+        }
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) load(ring[d], d / HOLD, d % HOLD);
+#pragma unroll
+        for (int j = 0; j < RPN; ++j) {
+            const int s = wave + j * NW;
+            float t = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t += pv[j][e];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, kWave);
+            if (lane == 0 && s < 16) inv_s[s] = 1.0f / sqrtf(t / (float)a.H + a.eps);
+        }
         lds_sync();
-        if (row_ok) inv = inv_s[n];
-        if constexpr (HOLD > 0) {
+        inv = a.norm_ss && row_ok ? inv_s[n] : 1.0f;
 #pragma unroll
-            for (int c = 0; c < HOLD; ++c)
+        for (int c = 0; c < HOLD; ++c)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) hold[c][b] = scale_f16x8(hold[c][b], inv);
+            for (int b = 0; b < 4; ++b) hold[c][b] = a.norm_ss ? scale_f16x8(hold[c][b], inv) : hold[c][b];
+    } else {
+        // streamed rows: the ring first, then the norm (its loads are the youngest)
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) load(ring[d], 0, d);
+        if (a.norm_ss) {
+            norm_scales<NW>(a.norm_ss, a.norm_tiles, a.S, a.H, a.eps, wave, lane, inv_s);
+            lds_sync();
+            if (row_ok) inv = inv_s[n];
         }
     }
 
