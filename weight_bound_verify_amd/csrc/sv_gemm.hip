@@ -576,7 +576,7 @@ __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* _
                                                                   int32_t* __restrict__ tokens, int cap,
                                                                   int32_t* __restrict__ state, int nmax,
                                                                   int32_t* __restrict__ drafts_out) {
-    __shared__ __attribute__((aligned(16))) int32_t tk[kTailIds];
+    __shared__ __attribute__((aligned(16))) int32_t tk[kTailIds + 8];    // + group reads past the end
     __shared__ int32_t am[SV_MAX_S];
     __shared__ int new_len;
     __shared__ int gated_s;
@@ -586,13 +586,23 @@ __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* _
     const int K = S - 1;
     const bool round = drafts_out != nullptr;
 
+    // Every load that does not depend on another is issued first: the stream's first
+    // min(cap, kTailIds) ids (whatever its length), the state, the drafts and the partials;
+    // the stream goes to LDS once the partials are reduced.
     int len0 = 0, d = -1;
     bool in_lds = false;
+    IdPrefix pre;
+    const int navail = round ? (cap < kTailIds ? cap : kTailIds) : 0;
+    const bool vec = round && (reinterpret_cast<uintptr_t>(tokens) & 15) == 0;
+    if (vec) prefix_load(tokens, navail, pre);
+    StateCache sc{0, 0};
     if (round) {
         len0 = state[SV_STATE_LEN];
-        if (wave == 0 && lane < K) d = drafts_in[lane];
+        if (wave == 0) {
+            sc = state_cache_load(state, lane);
+            if (lane < K) d = drafts_in[lane];
+        }
         in_lds = len0 >= 0 && len0 + K + 1 <= cap && len0 + K + 1 <= kTailIds;
-        if (in_lds) stage_ids(tokens, len0, tk);
     }
     for (int s = wave; s < S; s += kTailThreads / kWave) {
         float bv = -INFINITY;
@@ -614,6 +624,10 @@ __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* _
         if (lane == 0) { argmax[s] = bi; am[s] = bi; }
     }
     if (!round) return;
+    if (in_lds) {
+        if (vec) prefix_store(tokens, navail, pre, tk);
+        else stage_ids(tokens, len0, tk);
+    }
     __syncthreads();
     if (!in_lds) {                                     // long or corrupt stream: the global-memory path
         if (wave == 0) accept_wave(am, drafts_in, K, tokens, cap, state, lane);
@@ -626,11 +640,11 @@ __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* _
         const int j = __builtin_ctzll(~hit);           // <= K: bit K is never set
         if (lane < j) { tokens[len0 + lane] = d; tk[len0 + lane] = d; }
         if (lane == j) { tokens[len0 + j] = am[j]; tk[len0 + j] = am[j]; }
+        const int gated = record_round_cached(sc, state, j, lane);
         if (lane == 0) {
             new_len = len0 + 1 + j;
             state[SV_STATE_LEN] = len0 + 1 + j;
-            record_round(state, j);
-            gated_s = state[SV_STATE_GATED] != 0;
+            gated_s = gated != 0;
         }
     }
     __syncthreads();

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kTailThreads) void sample_tail_kernel(
     uint32_t key1, int32_t* __restrict__ sample_out, float* __restrict__ lse_out,
     const int32_t* __restrict__ drafts_in, int32_t* __restrict__ tokens, int cap, int32_t* __restrict__ state,
     int nmax, int32_t* __restrict__ drafts_out) {
-    __shared__ __attribute__((aligned(16))) int32_t tk[kTailIds];
+    __shared__ __attribute__((aligned(16))) int32_t tk[kTailIds + 8];    // + group reads past the end
     __shared__ int32_t draw_s[16];
     __shared__ float lse_s[16];
     __shared__ int new_len;
@@ -75,12 +75,18 @@ __global__ __launch_bounds__(kTailThreads) void sample_tail_kernel(
     const int K = S - 1;
     const bool round = tokens != nullptr;
 
+    // the stream's first min(cap, kTailIds) ids are loaded with the partials, whatever its length
     int len0 = 0;
     bool in_lds = false;
+    IdPrefix pre;
+    const int navail = round ? (cap < kTailIds ? cap : kTailIds) : 0;
+    const bool vec = round && (reinterpret_cast<uintptr_t>(tokens) & 15) == 0;
+    if (vec) prefix_load(tokens, navail, pre);
+    StateCache sc{0, 0};
     if (round) {
         len0 = state[SV_STATE_LEN];
+        if (wave == 0) sc = state_cache_load(state, lane);
         in_lds = len0 >= 0 && len0 + K + 1 <= cap && len0 + K + 1 <= kTailIds;
-        if (in_lds) stage_ids(tokens, len0, tk);
     }
     for (int s = wave; s < S; s += kTailThreads / kWave) {
         int draw;
@@ -94,6 +100,10 @@ __global__ __launch_bounds__(kTailThreads) void sample_tail_kernel(
         }
     }
     if (!round) return;
+    if (in_lds) {
+        if (vec) prefix_store(tokens, navail, pre, tk);
+        else stage_ids(tokens, len0, tk);
+    }
     __syncthreads();
     if (!in_lds) {                                     // long or corrupt stream: the global-memory path
         if (wave == 0) accept_sample_wave(draw_s, lse_s, zd, drafts_in, K, V, key0, key1, tokens, cap, state, lane,
@@ -103,10 +113,15 @@ __global__ __launch_bounds__(kTailThreads) void sample_tail_kernel(
         return;
     }
     if (wave == 0) {
-        const int j = accept_sample_wave(draw_s, lse_s, zd, drafts_in, K, V, key0, key1, tokens, cap, state, lane, tk);
+        const int j = accept_sample_wave(draw_s, lse_s, zd, drafts_in, K, V, key0, key1, tokens, cap, state, lane, tk,
+                                         &sc);
+        // the gate word after this round: recomputed from the cache as the accept recorded it
+        const int zero_run = j == 0 ? state_word(sc, SV_STATE_ZERO_RUN) + 1 : 0;
+        const int gate_after = state_word(sc, SV_STATE_GATE_AFTER);
+        const bool gated = state_word(sc, SV_STATE_GATED) != 0 || (K > 0 && gate_after > 0 && zero_run >= gate_after);
         if (lane == 0) {
             new_len = len0 + 1 + j;
-            gated_s = state[SV_STATE_GATED] != 0;
+            gated_s = gated;
         }
     }
     __syncthreads();

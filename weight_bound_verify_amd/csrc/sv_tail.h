@@ -3,6 +3,8 @@
 #pragma once
 
 #include "sv_device.h"
+
+#include <climits>
 #include "../../include/specverify.h"
 
 namespace sv {
@@ -40,6 +42,77 @@ __device__ __forceinline__ void stage_ids(const int32_t* __restrict__ src, int n
     for (int i = done + tid; i < n; i += nt) dst[i] = src[i];
 }
 
+// The first n ids of a 16-byte aligned stream held in registers by a whole workgroup (n <=
+// 16 ids per thread): thread t holds 16-byte pieces t, t + nt, t + 2 nt, t + 3 nt.  Loading
+// them does not depend on the stream length, so a round tail issues these loads together with
+// its other independent loads and stores them to LDS afterwards.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+struct IdPrefix { i32x4_t v[4]; };
+
+__device__ __forceinline__ void prefix_load(const int32_t* __restrict__ src, int n, IdPrefix& p) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int n4 = n >> 2;
+    const i32x4_t* s4 = reinterpret_cast<const i32x4_t*>(src);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = u * nt + tid;
+        p.v[u] = i < n4 ? s4[i] : i32x4_t{0, 0, 0, 0};
+    }
+}
+
+__device__ __forceinline__ void prefix_store(const int32_t* __restrict__ src, int n, const IdPrefix& p, int32_t* dst) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int n4 = n >> 2;
+    i32x4_t* d4 = reinterpret_cast<i32x4_t*>(dst);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = u * nt + tid;
+        if (i < n4) d4[i] = p.v[u];
+    }
+    for (int i = (n4 << 2) + tid; i < n; i += nt) dst[i] = src[i];
+}
+
+// Best (match length << 32 | end position) over the end positions e < len - 1 of a stream held
+// in LDS (`tk`, 16-byte aligned, at least len ids), for this thread's share: groups of four
+// consecutive end positions, group index = thread + k * threads.  A group reads its four ids
+// and the NM ids before it as 16-byte LDS reads and finds every match from registers (NM = 4
+// covers nmax <= 4, NM = 8 the rest), so the scan costs a few instructions per position.
+template <int NM>
+__device__ __forceinline__ unsigned long long scan_best_lds(const int32_t* tk, int len, int nmax,
+                                                            const int32_t (&suf)[SV_MAX_NGRAM]) {
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4* t4 = reinterpret_cast<const i32x4*>(tk);
+    unsigned long long best = 0;
+    const int ngroups = (len - 1 + 3) >> 2;                   // groups holding end positions 0 .. len-2
+    for (int gi = threadIdx.x; gi < ngroups; gi += blockDim.x) {
+        const int e0 = gi << 2;
+        int32_t w[NM + 4];                                      // ids e0 - NM .. e0 + 3
+#pragma unroll
+        for (int q = 0; q < NM / 4 + 1; ++q) {
+            const int vi = gi - NM / 4 + q;                     // vector index
+            const i32x4 v = vi >= 0 ? t4[vi] : i32x4{INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) w[4 * q + c] = v[c];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = e0 + j;
+            int l = 0;
+            bool run = true;
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                run = run && i < nmax && w[NM + j - i] == suf[i];
+                l += run ? 1 : 0;
+            }
+            if (l > 0 && e < len - 1) {
+                const unsigned long long key = ((unsigned long long)l << 32) | (unsigned)e;
+                best = key > best ? key : best;
+            }
+        }
+    }
+    return best;
+}
+
 // Per-round statistics and the hit-rate gate ("Stream C - Speculative decoding", the shipped
 // app note: the drafter is dropped after gateAfter rounds that accepted nothing).  One thread.
 __device__ __forceinline__ void record_round(int32_t* state, int j) {
@@ -52,6 +125,44 @@ __device__ __forceinline__ void record_round(int32_t* state, int j) {
     state[SV_STATE_ZERO_RUN] = zero_run;
     const int gate_after = state[SV_STATE_GATE_AFTER];
     if (gate_after > 0 && state[SV_STATE_GATED] == 0 && zero_run >= gate_after) state[SV_STATE_GATED] = rounds;
+}
+
+// The round state's words held by one wave (lane l: state[l] and state[64 + l]), loaded at the
+// start of a round tail together with its other loads, so recording the round needs no
+// read-modify-write round trip to memory after the accept.
+struct StateCache { int32_t lo, hi; };
+
+__device__ __forceinline__ StateCache state_cache_load(const int32_t* state, int lane) {
+    StateCache c;
+    c.lo = state[lane];
+    c.hi = lane < SV_STATE_WORDS - 64 ? state[64 + lane] : 0;
+    return c;
+}
+
+__device__ __forceinline__ int state_word(const StateCache& c, int idx) {      // idx uniform
+    const int lo = __shfl(c.lo, idx & 63, kWave), hi = __shfl(c.hi, idx & 63, kWave);
+    return idx < 64 ? lo : hi;
+}
+
+// record_round from the cached words, by the whole wave (same updates, same order of rules).
+// Returns the gate word after the round.
+__device__ __forceinline__ int record_round_cached(const StateCache& c, int32_t* state, int j, int lane) {
+    const int rounds = state_word(c, SV_STATE_ROUNDS) + 1;
+    const int sumj = state_word(c, SV_STATE_SUMJ) + j;
+    const int hist = state_word(c, SV_STATE_HIST + j) + 1;
+    const int zero_run = j == 0 ? state_word(c, SV_STATE_ZERO_RUN) + 1 : 0;
+    const int gate_after = state_word(c, SV_STATE_GATE_AFTER);
+    int gated = state_word(c, SV_STATE_GATED);
+    if (gate_after > 0 && gated == 0 && zero_run >= gate_after) gated = rounds;
+    if (lane == 0) {
+        state[SV_STATE_J] = j;
+        state[SV_STATE_ROUNDS] = rounds;
+        state[SV_STATE_SUMJ] = sumj;
+        state[SV_STATE_HIST + j] = hist;
+        state[SV_STATE_ZERO_RUN] = zero_run;
+        state[SV_STATE_GATED] = gated;
+    }
+    return gated;
 }
 
 // The drafter's output once the hit-rate gate has fired: K pads, nothing matched.
@@ -98,8 +209,8 @@ __device__ __forceinline__ void accept_wave(const int32_t* argmax, const int32_t
 __device__ __forceinline__ int accept_sample_wave(const int32_t* sample, const float* lse, const float* zd,
                                                   const int32_t* drafts, int K, int V, uint32_t key0,
                                                   uint32_t key1, int32_t* tokens, int cap, int32_t* state,
-                                                  int lane, int32_t* mirror) {
-    const int len = state[SV_STATE_LEN];
+                                                  int lane, int32_t* mirror, const StateCache* cache = nullptr) {
+    const int len = cache ? state_word(*cache, SV_STATE_LEN) : state[SV_STATE_LEN];
     if (len + K + 1 > cap || len < 0) {
         if (lane == 0) state[SV_STATE_FLAGS] |= SV_FLAG_CAPACITY;
         return -1;
@@ -124,7 +235,10 @@ __device__ __forceinline__ int accept_sample_wave(const int32_t* sample, const f
         tokens[len + j] = sample[j];
         if (mirror) mirror[len + j] = sample[j];
     }
-    if (lane == 0) {
+    if (cache) {
+        if (lane == 0) state[SV_STATE_LEN] = len + 1 + j;
+        if (K > 0) record_round_cached(*cache, state, j, lane);      // K = 0 is the bootstrap, not a round
+    } else if (lane == 0) {
         state[SV_STATE_LEN] = len + 1 + j;
         if (K > 0) record_round(state, j);        // K = 0 is the anchor bootstrap, not a round
     }
@@ -219,17 +333,7 @@ __device__ __forceinline__ void propose_lds(const int32_t* tk, int len, int nmax
     int32_t suf[SV_MAX_NGRAM];
 #pragma unroll
     for (int i = 0; i < SV_MAX_NGRAM; ++i) suf[i] = (i < nmax && len - 1 - i >= 0) ? tk[len - 1 - i] : -1;
-    unsigned long long best = 0;
-    for (int e = tid; e < len - 1; e += nthreads) {
-        int l = 0;
-#pragma unroll
-        for (int i = 0; i < SV_MAX_NGRAM; ++i)
-            if (l == i && i < nmax && e - i >= 0 && tk[e - i] == suf[i]) l = i + 1;
-        if (l > 0) {
-            const unsigned long long key = ((unsigned long long)l << 32) | (unsigned)e;
-            best = key > best ? key : best;
-        }
-    }
+    unsigned long long best = nmax <= 4 ? scan_best_lds<4>(tk, len, nmax, suf) : scan_best_lds<8>(tk, len, nmax, suf);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         const unsigned long long o = __shfl_xor(best, off, 64);

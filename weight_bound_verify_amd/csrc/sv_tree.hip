@@ -36,8 +36,8 @@ constexpr int kMaxBranches = 4;
 // (nothing written, capacity flag set).
 __device__ __forceinline__ int accept_tree_wave(const int32_t* am, const int32_t* parents, const int32_t* drafts,
                                                 int K, int32_t* tokens, int cap, int32_t* state, int lane,
-                                                int32_t* mirror) {
-    const int len = state[SV_STATE_LEN];
+                                                int32_t* mirror, const StateCache* cache = nullptr) {
+    const int len = cache ? state_word(*cache, SV_STATE_LEN) : state[SV_STATE_LEN];
     if (len + K + 1 > cap || len < 0) {
         if (lane == 0) state[SV_STATE_FLAGS] |= SV_FLAG_CAPACITY;
         return -1;
@@ -64,8 +64,9 @@ __device__ __forceinline__ int accept_tree_wave(const int32_t* am, const int32_t
         tokens[len + j] = fin;
         if (mirror) mirror[len + j] = fin;
         state[SV_STATE_LEN] = len + 1 + j;
-        record_round(state, j);
+        if (!cache) record_round(state, j);
     }
+    if (cache) record_round_cached(*cache, state, j, lane);
     return j;
 }
 
@@ -229,6 +230,8 @@ __global__ __launch_bounds__(kTreeThreads) void tree_tail_kernel(
     const int wave = threadIdx.x >> 6;
     const int K = S - 1;
     const int len0 = state[SV_STATE_LEN];
+    StateCache sc{0, 0};
+    if (wave == 0) sc = state_cache_load(state, lane);
     const bool in_lds = len0 >= 0 && len0 + K + 1 <= cap && len0 + K + 1 <= kTreeIds;
     if (in_lds) stage_ids(tokens, len0, tk);
     for (int s = wave; s < S; s += kTreeThreads / kWave) {
@@ -237,10 +240,15 @@ __global__ __launch_bounds__(kTreeThreads) void tree_tail_kernel(
     }
     __syncthreads();
     if (wave == 0) {
-        const int j = accept_tree_wave(am, parents_in, drafts_in, K, tokens, cap, state, lane, in_lds ? tk : nullptr);
+        const int j = accept_tree_wave(am, parents_in, drafts_in, K, tokens, cap, state, lane, in_lds ? tk : nullptr,
+                                       &sc);
+        // the gate word after this round, as the walk recorded it (no round recorded when j < 0)
+        const int zero_run = j == 0 ? state_word(sc, SV_STATE_ZERO_RUN) + 1 : 0;
+        const int gate_after = state_word(sc, SV_STATE_GATE_AFTER);
+        const bool gated = state_word(sc, SV_STATE_GATED) != 0 || (j >= 0 && gate_after > 0 && zero_run >= gate_after);
         if (lane == 0) {
             new_len = j >= 0 ? len0 + 1 + j : len0;
-            gated_s = state[SV_STATE_GATED] != 0;
+            gated_s = gated;
         }
     }
     __syncthreads();
