@@ -408,7 +408,8 @@ int specverify_stack(const int8_t* wg, const uint16_t* sg, const int8_t* wu, con
  * 0 = automatic) and, for the chunked stack kernels, load units in flight per wave (2 .. 4;
  * 0 = automatic; a depth that has no kernel for a shape falls back to the automatic one),
  * and the head matmul kernel family (0 = automatic, 1 = one pass per 16-row item, 2 = the
- * chunked ring kernel where the shape allows it, S <= 16).  Waves that do not divide a
+ * chunked ring kernel where the shape allows it, S <= 16, 3 = automatic except that a
+ * 17-row window uses two 16-row tiles instead of one tile plus the 17th row's dot products).  Waves that do not divide a
  * chunked shape make specverify_stack fail with SV_ERR_SHAPE.  Process-wide;
  * affects the *_workspace_bytes answers, so query them after changing it.  Not thread-safe
  * against concurrent calls.

@@ -15,6 +15,8 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("V,H,S", [
     (1, 32, 1), (15, 32, 2), (17, 64, 9), (1000, 256, 9), (1000, 256, 16), (1000, 256, 17),
     (333, 2048, 33), (100, 96, 64), (8192, 512, 9), (4099, 320, 5), (70000, 64, 3), (777, 5120, 2),
+    # 17 rows: one MFMA tile plus the 17th row's dot products (H = 512, 1024, 2048, 2560, 4096)
+    (3001, 512, 17), (1000, 1024, 17), (5003, 2048, 17), (2000, 2560, 17), (1500, 4096, 17),
 ])
 def test_verify_matches_oracle(V, H, S):
     say(f"verify V={V} H={H} S={S}")
@@ -149,3 +151,22 @@ def test_verify_ring_kernel_matches_oracle(V, H, S):
     check_logits(lg, L)
     check_argmax(a, L)
     assert np.array_equal(a, a2)
+
+
+def test_verify_17_rows_both_kernels_agree():
+    """A 17-row window through the one-tile-plus-dot-products kernel and through two 16-row
+    tiles: the same argmax wherever the top-2 gap is clear of the tolerance."""
+    V, H, S = 9000, 2048, 17
+    q, s = head(17, V, H)
+    hidden = synth.fp16_normal(np.random.default_rng(17), (S, H))
+    L = oracle.head_logits(q, s, hidden)
+    a1, l1 = gpu_verify(q, s, hidden)
+    sv.set_tuning(0, 0, 0, 3)
+    try:
+        a2, l2 = gpu_verify(q, s, hidden)
+    finally:
+        sv.set_tuning(0, 0, 0, 0)
+    check_logits(l1, L)
+    check_logits(l2, L)
+    check_argmax(a1, L)
+    check_argmax(a2, L)

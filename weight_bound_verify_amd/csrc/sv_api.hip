@@ -125,8 +125,8 @@ void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups, int32_t 
         waves_per_group = 0;
     if (max_groups < 0 || max_groups > sv::kGridMax) max_groups = 0;
     if (depth < 0 || depth > 4) depth = 0;
-    if (head_kernel < 0 || head_kernel > 2) head_kernel = 0;
-    sv::set_tuning(waves_per_group, max_groups);
+    if (head_kernel < 0 || head_kernel > 3) head_kernel = 0;
+    sv::set_tuning(waves_per_group, max_groups, head_kernel == 3 ? 1 : 0);
     sv::set_chunk_tuning(waves_per_group, depth, max_groups, head_kernel);
 }
 

@@ -44,6 +44,7 @@ namespace {
 
 int g_nw_override = 0;       // 0 = choose
 int g_grid_override = 0;     // 0 = choose
+int g_no_xr = 0;             // 1: a 17-row window uses the two-tile kernels (tuning experiments)
 
 // Workgroup barrier that orders LDS only, so prefetched global loads stay in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -289,13 +290,23 @@ struct FastRegs {
     uint32_t sc[NBW / 2];                          // fp16 scales of the lane's row, in pairs
 };
 
-template <int MT, int NBW, int NW, int EPI>
+// XR > 0 (head, MT = 1; instantiated for XR = 1): window rows 16 .. 16+XR-1 beyond the MFMA tile.  Each wave keeps its
+// blocks of them in LDS; after the exchange a lane holds 8 codes of one vocab row, and per block
+// it adds their dot product with the same 8 elements of each extra row (v_dot2, the row read
+// from LDS as a broadcast) times the block scale.  A window of 17 .. 16+XR rows then needs the
+// registers of a 16-row one and no split of the hidden axis.  The lanes' partial dots are
+// folded over the four k groups, then over the waves in a fixed order by wave 1 + r for extra
+// row r, which also keeps that row's running argmax.
+template <int MT, int NBW, int NW, int EPI, int XR = 0>
 __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
     constexpr int NSEG = NBW / 4;
     static_assert(NBW % 4 == 0, "whole 128-byte segments");
+    static_assert(XR == 0 || (MT == 1 && EPI == EPI_HEAD && XR < NW), "extra rows extend a one-tile head");
     __shared__ f32x4 red[2][NW][MT][kWave];
     __shared__ __attribute__((aligned(16))) uint8_t xch[NW][2][2048];
     __shared__ f32x4 noise[EPI == EPI_SAMPLE ? 3 : 1][kWave];
+    __shared__ __attribute__((aligned(16))) _Float16 xl[XR ? NW : 1][XR ? NBW : 1][XR ? XR : 1][kBlock];
+    __shared__ float xred[XR ? 2 : 1][XR ? NW : 1][XR ? XR : 1][kTileRows];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -305,6 +316,18 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
 
     f16x8 hid[NBW][MT];
     load_hidden<MT, NBW>(hid, a, bw0, NBW, n, g);
+    float xbest_v = -INFINITY;          // extra row (wave - 1), lanes 0..15: running argmax
+    int xbest_i = INT_MAX;
+    if constexpr (XR > 0) {
+        // rows 16 .. 16+XR-1 of this wave's blocks, 16 bytes per lane per step; rows >= S are zeros
+        for (int c = lane; c < NBW * XR * 4; c += kWave) {
+            const int i = c / (XR * 4), r = (c / 4) % XR, q = c % 4;
+            f16x8 v = {};
+            if (16 + r < a.S)
+                v = *reinterpret_cast<const f16x8*>(a.x + (size_t)(16 + r) * a.H + (size_t)(bw0 + i) * kBlock + 8 * q);
+            *reinterpret_cast<f16x8*>(&xl[wave][i][r][8 * q]) = v;
+        }
+    }
 
     Reducer<MT, NW, EPI> red_{red};
     red_.init();
@@ -350,6 +373,9 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
         f32x4 acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = zero;
+        float xacc[XR ? XR : 1];
+#pragma unroll
+        for (int r = 0; r < (XR ? XR : 1); ++r) xacc[r] = 0.f;
 #pragma unroll
         for (int t = 0; t < NSEG; ++t) {
             // exchange one segment: tile row r lands at r*128, 16-byte chunks XOR-swizzled by row
@@ -372,9 +398,48 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) acc[mt][r] = __builtin_fmaf(sc, d[r], acc[mt][r]);
                 }
+                if constexpr (XR > 0) {
+#pragma unroll
+                    for (int r = 0; r < XR; ++r) {
+                        const f16x8 xv = *reinterpret_cast<const f16x8*>(&xl[wave][i][r][8 * g]);
+                        float dt = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const f16x2 pa = {b[2 * e], b[2 * e + 1]};
+                            const f16x2 pb = {xv[2 * e], xv[2 * e + 1]};
+                            dt = __builtin_amdgcn_fdot2(pa, pb, dt, false);
+                        }
+                        xacc[r] = __builtin_fmaf(sc, dt, xacc[r]);
+                    }
+                    if constexpr (NBW >= 16) __builtin_amdgcn_sched_barrier(0);   // bound live temporaries
+                }
+            }
+        }
+        if constexpr (XR > 0) {
+            // fold the four k groups (lanes n, n+16, n+32, n+48), then hand the wave's partial
+            // to LDS; the item's barrier in red_.run orders it before the readers
+#pragma unroll
+            for (int r = 0; r < XR; ++r) {
+                float t = xacc[r];
+                t += __shfl_xor(t, 16, kWave);
+                t += __shfl_xor(t, 32, kWave);
+                if (g == 0) xred[buf][wave][r][n] = t;
             }
         }
         red_.run(a, acc, it, buf, wave, lane, ks);
+        if constexpr (XR > 0) {
+            const int r = wave - 1;                       // extra row handled by this wave
+            if (r >= 0 && r < XR && 16 + r < a.S) {
+                float val = xred[buf][0][r][n];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) val += xred[buf][w][r][n];
+                const int v = it * kTileRows + n;
+                if (lane < 16 && v < a.V) {
+                    if (a.logits) a.logits[(size_t)(16 + r) * a.V + v] = val;
+                    if (val > xbest_v) { xbest_v = val; xbest_i = v; }
+                }
+            }
+        }
     };
 
     const int step = gridDim.x;
@@ -394,6 +459,16 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
     }
     if constexpr (EPI == EPI_HEAD || EPI == EPI_SAMPLE)
         if (a.ksplit == 1 && wave == 0) red_.finish(a, lane);
+    if constexpr (XR > 0) {
+        const int r = wave - 1;
+        if (r >= 0 && r < XR && 16 + r < a.S) {
+            argmax_group<16>(xbest_v, xbest_i);
+            if (lane == 0) {
+                a.part_val[(size_t)(16 + r) * kGridMax + blockIdx.x] = xbest_v;
+                a.part_idx[(size_t)(16 + r) * kGridMax + blockIdx.x] = xbest_i;
+            }
+        }
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -655,7 +730,7 @@ __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* _
 // shape tables (every instantiation compiles without register spills on gfx950)
 // ------------------------------------------------------------------------------------------
 typedef void (*KernelFn)(GemmArgs);
-struct Shape { int mt, nbw, nw, epis; };
+struct Shape { int mt, nbw, nw, epis, xr = 0; };
 constexpr int kH = 1 << EPI_HEAD, kS = 1 << EPI_STORE, kG = 1 << EPI_GATEUP, kX = 1 << EPI_SAMPLE;
 
 // fast kernel: every wave owns exactly nbw blocks (a multiple of 4); listed in order of
@@ -668,6 +743,9 @@ constexpr Shape kFast[] = {
     {1, 4, 4, kH | kS | kG | kX}, {1, 8, 2, kH | kS | kG | kX},
     {2, 8, 8, kH}, {2, 8, 5, kH}, {2, 8, 4, kH}, {2, 4, 4, kH},
     {4, 4, 4, kH},
+    // S = 17: the one-tile kernel plus the 17th row's dot products (the shapes that compile
+    // without spills; 20 blocks x 8 waves does not)
+    {1, 4, 16, kH, 1}, {1, 8, 8, kH, 1}, {1, 16, 8, kH, 1}, {1, 16, 5, kH, 1}, {1, 8, 4, kH, 1}, {1, 4, 4, kH, 1},
 };
 // generic kernel
 constexpr Shape kGeneric[] = {
@@ -680,6 +758,16 @@ constexpr Shape kGeneric[] = {
 
 template <int EPI>
 KernelFn pick_fast(const GemmCfg& c) {
+    if constexpr (EPI == EPI_HEAD) {
+        if (c.xr) {
+#define SV_XR(NBW, NW, XR) \
+    if (c.mt == 1 && c.xr == XR && c.nbw == NBW && c.nw == NW) return q8b32_fast<1, NBW, NW, EPI, XR>;
+            SV_XR(4, 16, 1) SV_XR(8, 8, 1) SV_XR(16, 8, 1) SV_XR(16, 5, 1) SV_XR(8, 4, 1) SV_XR(4, 4, 1)
+#undef SV_XR
+            return nullptr;
+        }
+    }
+    if (c.xr) return nullptr;
 #define SV_SHAPE(MT, NBW, NW) \
     if (c.mt == MT && c.nbw == NBW && c.nw == NW) return q8b32_fast<MT, NBW, NW, EPI>;
     SV_SHAPE(1, 8, 8) SV_SHAPE(1, 8, 10) SV_SHAPE(1, 16, 8) SV_SHAPE(1, 16, 5) SV_SHAPE(1, 16, 4)
@@ -709,15 +797,15 @@ KernelFn pick_generic(const GemmCfg& c) {
 
 // Fast shape: the hidden axis splits into ks equal parts, each into nw waves of exactly
 // nbw blocks.
-bool try_fast(int nb, int mt, int epi, GemmCfg& c) {
+bool try_fast(int nb, int mt, int epi, GemmCfg& c, int xr = 0) {
     for (int ks = 1; ks <= 8; ++ks) {
         if (nb % ks) continue;
         const int nbk = nb / ks;
         for (const Shape& sh : kFast) {
-            if (sh.mt != mt || !(sh.epis & (1 << epi))) continue;
+            if (sh.mt != mt || sh.xr != xr || !(sh.epis & (1 << epi))) continue;
             if (g_nw_override && sh.nw != g_nw_override) continue;
             if (sh.nbw * sh.nw == nbk) {
-                c.mt = mt; c.nbw = sh.nbw; c.nw = sh.nw; c.ksplit = ks; c.fast = 1;
+                c.mt = mt; c.nbw = sh.nbw; c.nw = sh.nw; c.ksplit = ks; c.fast = 1; c.xr = xr;
                 return true;
             }
         }
@@ -790,9 +878,10 @@ int resident_groups(int epi, const GemmCfg& c) {
 
 }  // namespace
 
-void set_tuning(int waves_per_group, int max_groups) {
+void set_tuning(int waves_per_group, int max_groups, int no_extra_row) {
     g_nw_override = waves_per_group;
     g_grid_override = max_groups;
+    g_no_xr = no_extra_row;
 }
 
 GemmCfg gemm_config(int rows, int H, int S, int epi) {
@@ -803,7 +892,13 @@ GemmCfg gemm_config(int rows, int H, int S, int epi) {
     // needs more than one extra workgroup split of the hidden axis (each split adds partial
     // sums and a combine pass); an unsplit generic launch beats any split one.
     GemmCfg f{}, gen{};
-    const bool have_fast = try_fast(nb, mt, epi, f);
+    // 17 .. 20 window rows: the fast kernel with rows 16+ in LDS, unsplit, when a shape fits
+    bool have_fast = false;
+    if (epi == EPI_HEAD && S == 17 && !g_no_xr) {
+        have_fast = try_fast(nb, 1, epi, f, 1);
+        if (have_fast && f.ksplit > 1) have_fast = false;
+    }
+    if (!have_fast) have_fast = try_fast(nb, mt, epi, f);
     if (!(g_nw_override && try_generic(nb, mt, epi, g_nw_override, gen)))
         try_generic(nb, mt, epi, 0, gen);     // always succeeds: (mt, smallest nbw, 4 waves) exists
     const bool take_fast = have_fast && (f.ksplit == 1 || (gen.ksplit > 1 && f.ksplit <= gen.ksplit + 1));

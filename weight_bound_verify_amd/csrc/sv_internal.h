@@ -21,13 +21,15 @@ struct GemmCfg {
     int ksplit;   // split of the hidden axis across workgroups (>1 only for very long H)
     int grid;     // workgroups along the row axis
     int fast;     // 1: 128-byte-segment loads with an LDS exchange; 0: generic loads
+    int xr;       // head, mt = 1: window rows beyond the 16-row tile handled by dot products
+                  // from LDS (1 for a 17-row window), 0 otherwise
 };
 
 // epi = the epilogue kind (Epi); the stack epilogues take S <= 16.
 GemmCfg gemm_config(int rows, int H, int S, int epi);
 // Workgroups of the split-combine pass (also the number of argmax partials it writes).
 int combine_groups(int V);
-void set_tuning(int waves_per_group, int max_groups);
+void set_tuning(int waves_per_group, int max_groups, int no_extra_row);
 
 struct GemmArgs {
     const int8_t* w0;
