@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
     (333, 2048, 33), (100, 96, 64), (8192, 512, 9), (4099, 320, 5), (70000, 64, 3), (777, 5120, 2),
     # 17 rows: one MFMA tile plus the 17th row's dot products (H = 512, 1024, 2048, 2560, 4096)
     (3001, 512, 17), (1000, 1024, 17), (5003, 2048, 17), (2000, 2560, 17), (1500, 4096, 17),
+    (2500, 5120, 17),                 # 8 of each wave's 20 blocks of window rows held in LDS
 ])
 def test_verify_matches_oracle(V, H, S):
     say(f"verify V={V} H={H} S={S}")
@@ -153,10 +154,11 @@ def test_verify_ring_kernel_matches_oracle(V, H, S):
     assert np.array_equal(a, a2)
 
 
-def test_verify_17_rows_both_kernels_agree():
+@pytest.mark.parametrize("H", [2048, 5120])
+def test_verify_17_rows_both_kernels_agree(H):
     """A 17-row window through the one-tile-plus-dot-products kernel and through two 16-row
     tiles: the same argmax wherever the top-2 gap is clear of the tolerance."""
-    V, H, S = 9000, 2048, 17
+    V, S = 9000, 17
     q, s = head(17, V, H)
     hidden = synth.fp16_normal(np.random.default_rng(17), (S, H))
     L = oracle.head_logits(q, s, hidden)

@@ -297,16 +297,23 @@ struct FastRegs {
 // registers of a 16-row one and no split of the hidden axis.  The lanes' partial dots are
 // folded over the four k groups, then over the waves in a fixed order by wave 1 + r for extra
 // row r, which also keeps that row's running argmax.
-template <int MT, int NBW, int NW, int EPI, int XR = 0>
+//
+// HL > 0 (MT = 1): the window rows of each wave's last HL blocks sit in LDS instead of
+// registers (one 16-byte LDS read per block per lane), freeing 4 registers per block for shapes
+// that would otherwise spill.
+template <int MT, int NBW, int NW, int EPI, int XR = 0, int HL = 0>
 __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
     constexpr int NSEG = NBW / 4;
+    constexpr int HR = NBW - HL;                      // blocks whose window rows stay in registers
     static_assert(NBW % 4 == 0, "whole 128-byte segments");
     static_assert(XR == 0 || (MT == 1 && EPI == EPI_HEAD && XR < NW), "extra rows extend a one-tile head");
+    static_assert(HL == 0 || (MT == 1 && HL < NBW), "LDS-held blocks of a one-tile window");
     __shared__ f32x4 red[2][NW][MT][kWave];
     __shared__ __attribute__((aligned(16))) uint8_t xch[NW][2][2048];
     __shared__ f32x4 noise[EPI == EPI_SAMPLE ? 3 : 1][kWave];
     __shared__ __attribute__((aligned(16))) _Float16 xl[XR ? NW : 1][XR ? NBW : 1][XR ? XR : 1][kBlock];
     __shared__ float xred[XR ? 2 : 1][XR ? NW : 1][XR ? XR : 1][kTileRows];
+    __shared__ __attribute__((aligned(16))) _Float16 xh[HL ? NW : 1][HL ? HL : 1][HL ? kTileRows : 1][kBlock];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -314,8 +321,18 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
     const int ks = blockIdx.y;
     const int bw0 = (a.nb / a.ksplit) * ks + NBW * wave;     // every wave owns exactly NBW blocks
 
-    f16x8 hid[NBW][MT];
-    load_hidden<MT, NBW>(hid, a, bw0, NBW, n, g);
+    f16x8 hid[HR][MT];
+    load_hidden<MT, HR>(hid, a, bw0, HR, n, g);
+    if constexpr (HL > 0) {
+        // rows 0..15 of this wave's last HL blocks, 16 bytes per lane per step; rows >= S are zeros
+        for (int c = lane; c < HL * kTileRows * 4; c += kWave) {
+            const int j = c / (kTileRows * 4), r = (c / 4) % kTileRows, q = c % 4;
+            f16x8 v = {};
+            if (r < a.S)
+                v = *reinterpret_cast<const f16x8*>(a.x + (size_t)r * a.H + (size_t)(bw0 + HR + j) * kBlock + 8 * q);
+            *reinterpret_cast<f16x8*>(&xh[wave][j][r][8 * q]) = v;
+        }
+    }
     float xbest_v = -INFINITY;          // extra row (wave - 1), lanes 0..15: running argmax
     int xbest_i = INT_MAX;
     if constexpr (XR > 0) {
@@ -394,7 +411,9 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
                 const float sc = h2f((uint16_t)(cur.sc[i >> 1] >> (16 * (i & 1))));
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(hid[i][mt], b, zero, 0, 0, 0);
+                    const f16x8 aop = i < HR ? hid[i < HR ? i : 0][mt]
+                                             : *reinterpret_cast<const f16x8*>(&xh[wave][i >= HR ? i - HR : 0][n][8 * g]);
+                    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, b, zero, 0, 0, 0);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) acc[mt][r] = __builtin_fmaf(sc, d[r], acc[mt][r]);
                 }
@@ -746,6 +765,7 @@ constexpr Shape kFast[] = {
     // S = 17: the one-tile kernel plus the 17th row's dot products (the shapes that compile
     // without spills; 20 blocks x 8 waves does not)
     {1, 4, 16, kH, 1}, {1, 8, 8, kH, 1}, {1, 16, 8, kH, 1}, {1, 16, 5, kH, 1}, {1, 8, 4, kH, 1}, {1, 4, 4, kH, 1},
+    {1, 20, 8, kH, 1},              // window rows of 8 of the 20 blocks held in LDS
 };
 // generic kernel
 constexpr Shape kGeneric[] = {
@@ -763,6 +783,7 @@ KernelFn pick_fast(const GemmCfg& c) {
 #define SV_XR(NBW, NW, XR) \
     if (c.mt == 1 && c.xr == XR && c.nbw == NBW && c.nw == NW) return q8b32_fast<1, NBW, NW, EPI, XR>;
             SV_XR(4, 16, 1) SV_XR(8, 8, 1) SV_XR(16, 8, 1) SV_XR(16, 5, 1) SV_XR(8, 4, 1) SV_XR(4, 4, 1)
+            if (c.mt == 1 && c.xr == 1 && c.nbw == 20 && c.nw == 8) return q8b32_fast<1, 20, 8, EPI, 1, 8>;
 #undef SV_XR
             return nullptr;
         }
