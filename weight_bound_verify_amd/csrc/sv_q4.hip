@@ -13,10 +13,10 @@
 // The MFMA sums over its 32 k slots, so any fixed assignment of a block's elements to slots
 // works if the A operand (window rows) and the B operand (codes) use the same one.  Lane l
 // (row n = l % 16, group g = l / 16) reads ONE dword of its row's block, bytes 4g .. 4g+3:
-// their low nibbles are elements 4g .. 4g+3 (slots 0-3), their high nibbles elements
-// 16+4g .. 16+4g+3 (slots 4-7); the held window rows are loaded in that same order.  A
-// nibble placed under the fp16 exponent of 1024 (bit pattern 0x64uu) is 1024 + nibble
-// exactly; subtracting 1032 leaves the code.  Each wave loads 8 rows x 128 contiguous bytes
+// their low nibbles are elements 4g .. 4g+3, their high nibbles elements 16+4g .. 16+4g+3,
+// placed in the slot order of nib8_to_f16x8; the held window rows are loaded in that same
+// order.  A nibble placed under the fp16 exponent of 1024 is 1024 + nibble exactly (1024 + 16 x
+// nibble for a high nibble); an fp16 subtract (or scale and subtract) leaves the code.  Each wave loads 8 rows x 128 contiguous bytes
 // per instruction (8 int4 blocks of each row) and exchanges them into the MFMA layout through
 // its own two 2 KB LDS slots, 16-byte chunks XOR-swizzled by row (one chunk is one block).
 // The block scale is applied to the MFMA result one block later, so no instruction waits on
@@ -41,19 +41,34 @@ __device__ __forceinline__ void lds_barrier_q4() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// One dword of a block (bytes 4g .. 4g+3) -> its 8 codes in slot order: the four low nibbles,
-// then the four high nibbles.
+// One dword of a block (bytes 4g .. 4g+3) -> its 8 codes in slot order
+//   slots 0..7 = elements 4g, 4g+2, 4g+1, 4g+3, 16+4g, 16+4g+2, 16+4g+1, 16+4g+3.
+// Each half-word of the dword holds two bytes; masking one nibble of each half and OR-ing the
+// fp16 exponent of 1024 gives 1024 + nibble (a low nibble) or 1024 + 16 * nibble (a high
+// nibble, mantissa bits 4..7), both exact; subtracting 1032, or scaling by 1/16 and
+// subtracting 72, leaves the code exactly.  Nine instructions for eight codes.
+// (w & mask) | exponent as one v_bfi_b32 (the compiler otherwise emits an AND and an OR);
+// the mask in a scalar register, the exponent pattern in a vector one (one scalar operand
+// per instruction on this architecture).
+__device__ __forceinline__ uint32_t nib_under_exp(uint32_t w, uint32_t mask, uint32_t expo) {
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(mask), "v"(w), "v"(expo));
+    return r;
+}
+
 __device__ __forceinline__ f16x8 nib8_to_f16x8(uint32_t w) {
-    const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-    const uint32_t lo = w & 0x0F0F0F0Fu;
-    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-    const f16x2 p0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u)) - bias;
-    const f16x2 p1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u)) - bias;
-    const f16x2 p2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u)) - bias;
-    const f16x2 p3 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)) - bias;
+    const f16x2 bias_lo = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const f16x2 bias_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const uint32_t w8 = w >> 8;
+    const uint32_t expo = 0x64006400u;
+    const f16x2 e02 = __builtin_bit_cast(f16x2, nib_under_exp(w, 0x000F000Fu, expo)) - bias_lo;
+    const f16x2 e13 = __builtin_bit_cast(f16x2, nib_under_exp(w8, 0x000F000Fu, expo)) - bias_lo;
+    const f16x2 h02 = __builtin_bit_cast(f16x2, nib_under_exp(w, 0x00F000F0u, expo)) * sixteenth + bias_hi;
+    const f16x2 h13 = __builtin_bit_cast(f16x2, nib_under_exp(w8, 0x00F000F0u, expo)) * sixteenth + bias_hi;
     f16x8 r;
-    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    r[0] = e02[0]; r[1] = e02[1]; r[2] = e13[0]; r[3] = e13[1];
+    r[4] = h02[0]; r[5] = h02[1]; r[6] = h13[0]; r[7] = h13[1];
     return r;
 }
 
@@ -77,16 +92,17 @@ __global__ __launch_bounds__(NW * 64) void q4b32_head(Q4Args a) {
     const int bw0 = NBW * wave;                    // first block of this wave
     const int row_bytes = a.H / 2;
 
-    // window rows in slot order: elements 4g .. 4g+3 and 16+4g .. 16+4g+3 of each block
+    // window rows in slot order: elements 4g, 4g+2, 4g+1, 4g+3, then the same four + 16
     f16x8 hid[NBW];
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
         f16x8 h = {};
         if (n < a.S) {
             const uint16_t* xb = a.x + (size_t)n * a.H + (size_t)(bw0 + i) * kBlock + 4 * g;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(xb);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(xb + 16);
-            const u32x4 q = {lo.x, lo.y, hi.x, hi.y};
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(xb);        // elements 4g .. 4g+3
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(xb + 16);   // elements 16+4g .. 16+4g+3
+            const u32x4 q = {__builtin_amdgcn_perm(lo.y, lo.x, 0x05040100u), __builtin_amdgcn_perm(lo.y, lo.x, 0x07060302u),
+                             __builtin_amdgcn_perm(hi.y, hi.x, 0x05040100u), __builtin_amdgcn_perm(hi.y, hi.x, 0x07060302u)};
             h = __builtin_bit_cast(f16x8, q);
         }
         hid[i] = h;
