@@ -289,3 +289,53 @@ def test_verify_sample_full_35b_head_shape(V, H):
     _, lse_o = smp.probabilities(L, T)
     assert np.all(np.abs(lse - lse_o) <= _key_tol(L, T))
     check_draws(sample, L, drafts, T, seed, P0)
+
+
+def test_sampling_rounds_replay_from_a_graph():
+    """Sampling rounds captured once in a HIP graph and replayed three times continue the
+    stream exactly like the same rounds run eagerly (the draws depend only on the seed and the
+    stream position, both on the device)."""
+    V, H, K, T, R = 3000, 512, 6, 0.3, 6
+    S = K + 1
+    rng = np.random.default_rng(41)
+    q, s = head(43, V, H)
+    hid = [to_dev(synth.fp16_normal(rng, (S, H))) for _ in range(R)]
+    ctx = synth.zipf_context_with_copies(np.random.default_rng(4), 400, V, 0.3)[0].astype(np.int32)
+    cap = len(ctx) + 3 * R * S + 8
+
+    class SampleLoop:
+        def __init__(self):
+            self.tokens = torch.zeros(cap, dtype=torch.int32, device=dev())
+            self.tokens[:len(ctx)] = to_dev(ctx)
+            self.state = sv.new_state(dev())
+            self.state[sv.STATE_LEN] = len(ctx)
+            self.wq, self.ws = to_dev(q), to_dev(s)
+            self.work = sv.workspace(sv.sample_workspace_bytes(V, H, S), dev())
+            self.drafts = torch.empty(K, dtype=torch.int32, device=dev())
+            sv.propose(self.tokens, self.state, self.drafts, 3)
+
+        def run(self):
+            for r in range(R):
+                sv.round_sample(self.wq, self.ws, hid[r], self.drafts, T, 77, self.tokens, self.state, self.drafts,
+                                self.work)
+
+    eager = SampleLoop()
+    for _ in range(3):
+        eager.run()
+    torch.cuda.synchronize()
+    g = SampleLoop()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            g.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        _ = (g.state[sv.STATE_LEN] + 1).item()
+    assert torch.equal(g.tokens, eager.tokens) and torch.equal(g.state, eager.state)
+    assert torch.equal(g.drafts, eager.drafts)

@@ -225,3 +225,60 @@ def test_one_branch_tree_loop_equals_linear_loop():
     b = _device_tree_loop(q, s, model.table, ctx, 150, K, 1, K, linear=True)
     assert a[0] == b[0] and a[2] == b[2]
     assert np.array_equal(a[1][sv.STATE_HIST:sv.STATE_HIST + K + 1], b[1][sv.STATE_HIST:sv.STATE_HIST + K + 1])
+
+
+def test_tree_rounds_replay_from_a_graph():
+    """Tree rounds (gather the node rows, round_tree) captured once in a HIP graph and replayed
+    three times continue the stream exactly like the same rounds run eagerly."""
+    V, H, K, B, D, R = 2048, 256, 8, 3, 4, 6
+    S = K + 1
+    rng = np.random.default_rng(31)
+    q, s = synth.quantized_head(np.random.SeedSequence(33), V, H)
+    table = synth.MarkovHidden(rng, V, H).table
+    ctx, _, _ = synth.uniform_context_with_span(rng, 300, V, 10, 8)
+    cap = len(ctx) + 1 + 3 * R * S + 8
+
+    class TreeLoop:
+        def __init__(self):
+            buf = np.zeros(cap, dtype=np.int32)
+            buf[:len(ctx)] = ctx
+            self.tokens = to_dev(buf)
+            self.state = _state(len(ctx))
+            self.wq, self.ws, self.tab = to_dev(q), to_dev(s), to_dev(table)
+            self.work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev())
+            self.argmax = torch.empty(S, dtype=torch.int32, device=dev())
+            self.parents = torch.empty(K, dtype=torch.int32, device=dev())
+            self.drafts = torch.empty(K, dtype=torch.int32, device=dev())
+            self.window = torch.empty((S, H), dtype=torch.float16, device=dev())
+            h_last = torch.empty((1, H), dtype=torch.float16, device=dev())
+            a0 = torch.empty(1, dtype=torch.int32, device=dev())
+            sv.gather_window(self.tokens, self.state, self.drafts[:0], self.tab, h_last)
+            sv.verify(self.wq, self.ws, h_last, a0, sv.workspace(sv.verify_workspace_bytes(V, H, 1), dev()))
+            sv.accept(a0, None, self.tokens, self.state)
+            sv.propose_tree(self.tokens, self.state, self.parents, self.drafts, 3, B, D)
+
+        def run(self, n):
+            for _ in range(n):
+                sv.gather_window(self.tokens, self.state, self.drafts, self.tab, self.window)
+                sv.round_tree(self.wq, self.ws, self.window, self.parents, self.drafts, self.tokens, self.state,
+                              self.parents, self.drafts, self.argmax, self.work, 3, B, D)
+
+    eager = TreeLoop()
+    eager.run(3 * R)
+    torch.cuda.synchronize()
+    g = TreeLoop()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            g.run(R)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        _ = (g.state[sv.STATE_LEN] + 1).item()          # eager work between replays
+    assert torch.equal(g.tokens, eager.tokens) and torch.equal(g.state, eager.state)
+    assert torch.equal(g.parents, eager.parents) and torch.equal(g.drafts, eager.drafts)
