@@ -339,3 +339,43 @@ def test_sampling_rounds_replay_from_a_graph():
         _ = (g.state[sv.STATE_LEN] + 1).item()
     assert torch.equal(g.tokens, eager.tokens) and torch.equal(g.state, eager.state)
     assert torch.equal(g.drafts, eager.drafts)
+
+
+def test_sampling_rounds_hit_rate_gate():
+    """gate_after = 2 with a flat target (no draft is kept at T = 1 over 3000 ids): the gate
+    fires after the second round and the drafter then proposes only pads, even when the
+    stream's end would give it a match."""
+    V, H, K, T = 3000, 256, 8, 1.0
+    S = K + 1
+    rng = np.random.default_rng(61)
+    q, s = head(62, V, H)
+    wq, ws = to_dev(q), to_dev(s)
+    ctx = np.tile(np.arange(1, 40, dtype=np.int32), 10)
+    tokens = torch.zeros(len(ctx) + 64, dtype=torch.int32, device=dev())
+    tokens[:len(ctx)] = to_dev(ctx)
+    state = sv.new_state(dev())
+    state[sv.STATE_LEN] = len(ctx)
+    state[sv.STATE_GATE_AFTER] = 2
+    drafts = torch.empty(K, dtype=torch.int32, device=dev())
+    work = sv.workspace(sv.sample_workspace_bytes(V, H, S), dev())
+    sv.propose(tokens, state, drafts, 3)
+    torch.cuda.synchronize()
+    assert (drafts.cpu().numpy() >= 0).all()
+    hidden = to_dev(synth.fp16_normal(rng, (S, H)))
+    for r in range(4):
+        sv.round_sample(wq, ws, hidden, drafts, T, 5 + r, tokens, state, drafts, work)
+        torch.cuda.synchronize()
+        if int(state[sv.STATE_J]) != 0:
+            pytest.skip("a draft happened to be kept")
+    st = state.cpu().numpy()
+    assert st[sv.STATE_GATED] == 2 and st[sv.STATE_ZERO_RUN] == 4 and st[sv.STATE_ROUNDS] == 4
+    assert drafts.cpu().tolist() == [-1] * K
+    n = int(st[sv.STATE_LEN])
+    tokens[n - 1] = int(ctx[-1])
+    sv.propose(tokens, state, drafts, 3)
+    torch.cuda.synchronize()
+    assert drafts.cpu().tolist() == [-1] * K
+    state[sv.STATE_GATED] = 0
+    sv.propose(tokens, state, drafts, 3)
+    torch.cuda.synchronize()
+    assert (drafts.cpu().numpy() >= 0).any()

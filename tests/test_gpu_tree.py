@@ -282,3 +282,45 @@ def test_tree_rounds_replay_from_a_graph():
         _ = (g.state[sv.STATE_LEN] + 1).item()          # eager work between replays
     assert torch.equal(g.tokens, eager.tokens) and torch.equal(g.state, eager.state)
     assert torch.equal(g.parents, eager.parents) and torch.equal(g.drafts, eager.drafts)
+
+
+def test_tree_rounds_hit_rate_gate():
+    """gate_after = 2 with rows that never take a draft: the gate fires after the second round
+    and every later tree is pads, even when the stream's end would give the drafter a match."""
+    V, H, K, B, D = 3000, 256, 8, 3, 4
+    S = K + 1
+    rng = np.random.default_rng(51)
+    q, s = synth.quantized_head(np.random.SeedSequence(52), V, H)
+    wq, ws = to_dev(q), to_dev(s)
+    ctx = np.tile(np.arange(1, 40, dtype=np.int32), 10)            # repetitive: the branches share one path
+    tokens = torch.zeros(len(ctx) + 64, dtype=torch.int32, device=dev())
+    tokens[:len(ctx)] = to_dev(ctx)
+    state = _state(len(ctx))
+    state[sv.STATE_GATE_AFTER] = 2
+    parents = torch.empty(K, dtype=torch.int32, device=dev())
+    drafts = torch.empty(K, dtype=torch.int32, device=dev())
+    argmax = torch.empty(S, dtype=torch.int32, device=dev())
+    work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev())
+    sv.propose_tree(tokens, state, parents, drafts, 3, B, D)
+    torch.cuda.synchronize()
+    assert drafts.cpu().tolist() == [1, 2, 3, 4, -1, -1, -1, -1]
+    hidden = to_dev(synth.fp16_normal(rng, (S, H)))
+    for r in range(4):
+        sv.round_tree(wq, ws, hidden, parents, drafts, tokens, state, parents, drafts, argmax, work, 3, B, D)
+        torch.cuda.synchronize()
+        if int(state[sv.STATE_J]) != 0:
+            pytest.skip("a draft happened to match the synthetic rows")
+    st = state.cpu().numpy()
+    assert st[sv.STATE_GATED] == 2 and st[sv.STATE_ZERO_RUN] == 4 and st[sv.STATE_ROUNDS] == 4
+    assert drafts.cpu().tolist() == [-1] * K and parents.cpu().tolist() == [0] * K
+    # end the stream in a token the context repeats: gated, the drafter still emits pads ...
+    n = int(st[sv.STATE_LEN])
+    tokens[n - 1] = int(ctx[-1])
+    sv.propose_tree(tokens, state, parents, drafts, 3, B, D)
+    torch.cuda.synchronize()
+    assert drafts.cpu().tolist() == [-1] * K
+    # ... and with the gate cleared it proposes again
+    state[sv.STATE_GATED] = 0
+    sv.propose_tree(tokens, state, parents, drafts, 3, B, D)
+    torch.cuda.synchronize()
+    assert (drafts.cpu().numpy() >= 0).any()
