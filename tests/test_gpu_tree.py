@@ -11,7 +11,7 @@ from oracle import tree as tr
 from weight_bound_verify_amd import specverify as sv
 from weight_bound_verify_amd import synth
 
-from gpu_util import dev, say, to_dev
+from gpu_util import check_argmax, dev, say, to_dev
 from test_oracle_tree import _random_tree
 
 pytestmark = pytest.mark.gpu
@@ -324,3 +324,57 @@ def test_tree_rounds_hit_rate_gate():
     sv.propose_tree(tokens, state, parents, drafts, 3, B, D)
     torch.cuda.synchronize()
     assert (drafts.cpu().numpy() >= 0).any()
+
+
+def test_round_tree_full_35b_head_shape():
+    """One tree round at the full 35B-A3B-shaped head (V = 248320, H = 2048), 8 nodes from the
+    3 best matches at depth 4, in the launch configuration the bench uses: the argmax rows
+    against the oracle's logits (near-tie rule), then the walk (rows steered down a real
+    path), the committed stream and the next tree bit-exactly against the oracle applied to
+    the GPU's argmax rows."""
+    V, H, K, B, D = 248320, 2048, 8, 3, 4
+    S = K + 1
+    say(f"round_tree full V={V} H={H} K={K} B={B} D={D}")
+    q, s = synth.quantized_head(synth.streams(2).weights, V, H)
+    ctx = synth.zipf_context_with_copies(np.random.default_rng(35), 4096, V, 0.3)[0].astype(np.int32)
+    parents0, drafts0, _, real = tr.propose_tree(ctx, 3, K, B, D)
+    assert real == K and sum(p == 0 for p in parents0) >= 2       # a full tree that branches at the root
+    # row c steers the argmax to the token of node c's highest-index child (a leaf: a random
+    # id): fp16(50 x the dequantised weight row) wins by a wide margin, so the walk leaves the
+    # first branch and goes down to a leaf
+    rng = np.random.default_rng(31)
+
+    def steer(tok):
+        d = (q[tok].astype(np.float64).reshape(-1, 32) * s[tok].astype(np.float64)[:, None]).reshape(-1)
+        return (50.0 * d).astype(np.float16)
+
+    rows = []
+    for c in range(S):
+        kids = [i for i in range(1, K + 1) if parents0[i - 1] == c and drafts0[i - 1] != -1]
+        rows.append(steer(drafts0[kids[-1] - 1] if kids else int(rng.integers(0, V))))
+    hidden = np.stack(rows)
+    cap = len(ctx) + 64
+    tokens = torch.zeros(cap, dtype=torch.int32, device=dev())
+    tokens[:len(ctx)] = to_dev(ctx)
+    state = _state(len(ctx))
+    parents = torch.empty(K, dtype=torch.int32, device=dev())
+    drafts = torch.empty(K, dtype=torch.int32, device=dev())
+    sv.propose_tree(tokens, state, parents, drafts, 3, B, D)
+    torch.cuda.synchronize()
+    assert parents.cpu().tolist() == list(parents0) and drafts.cpu().tolist() == list(drafts0)
+    argmax = torch.empty(S, dtype=torch.int32, device=dev())
+    work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev())
+    sv.round_tree(to_dev(q), to_dev(s), to_dev(hidden), parents, drafts, tokens, state, parents, drafts, argmax,
+                  work, 3, B, D)
+    torch.cuda.synchronize()
+    a_gpu = argmax.cpu().numpy()
+    L = oracle.head_logits(q, s, hidden)
+    check_argmax(a_gpu, L)
+    j, app, path = tr.tree_accept(a_gpu, parents0, drafts0)
+    assert j >= 2 and path[0] != 1
+    st = state.cpu().numpy()
+    assert st[sv.STATE_J] == j and st[sv.STATE_LEN] == len(ctx) + 1 + j
+    stream = list(ctx) + app
+    assert tokens[:len(stream)].cpu().tolist() == stream
+    p1, d1, _, _ = tr.propose_tree(stream, 3, K, B, D)
+    assert parents.cpu().tolist() == list(p1) and drafts.cpu().tolist() == list(d1)
