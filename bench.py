@@ -77,23 +77,39 @@ def head_bytes(V, H, S, fmt="q8"):
     return codes + 2 * V * (H // 32) + 2 * S * H
 
 
+def gateup_bytes(H, F, S):
+    """Algorithmic HBM bytes of one gate/up launch of the dense stack: the int8 codes and fp16
+    scales of both matrices, the fp16 window rows in, m = silu(g)*u out, the norm's fp32
+    sum-of-squares partials in."""
+    return 2 * (F * H + 2 * F * (H // 32)) + 2 * S * H + 2 * S * F + 4 * S * (H // 16)
+
+
 def stack_bytes(layers, H, F, S):
     per = 3 * (F * H + 2 * F * (H // 32))
     return layers * (per + 2 * S * (H + 2 * F + H))
 
 
+def kernel_fmt(workload):
+    """Which kernel the roofline of a workload times: the stack's gate/up projection when the
+    workload has a dense stack (its dominant kernel), else the head of its weight format."""
+    wl = WORKLOADS[workload]
+    return "stack" if wl["layers"] else wl.get("fmt", "q8")
+
+
 def kernel_source_hash(fmt="q8"):
-    """Hash of the sources the head kernel of this weight format is built from."""
+    """Hash of the sources the timed kernel of this format is built from."""
     h = hashlib.sha256()
-    for name in (("sv_q4.hip",) if fmt == "q4" else ("sv_gemm.hip",)) + ("sv_device.h",):
+    src = {"q4": "sv_q4.hip", "stack": "sv_chunked.hip"}.get(fmt, "sv_gemm.hip")
+    for name in (src, "sv_device.h"):
         with open(os.path.join(ROOT, "weight_bound_verify_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def counters_path(workload):
-    fmt = WORKLOADS[workload].get("fmt", "q8")
-    return os.path.join(ROOT, "profiles", f"verify_{fmt}b32_{workload}_counters.json")
+    fmt = kernel_fmt(workload)
+    name = f"stack_gateup_q8b32_{workload}" if fmt == "stack" else f"verify_{fmt}b32_{workload}"
+    return os.path.join(ROOT, "profiles", f"{name}_counters.json")
 
 
 def load_traffic(workload):
@@ -104,7 +120,7 @@ def load_traffic(workload):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash(WORKLOADS[workload].get("fmt", "q8")):
+    if rec.get("kernel_source_hash") != kernel_source_hash(kernel_fmt(workload)):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -151,7 +167,7 @@ def summarize_counters(workload, kernel_sub, pdir, commands):
     fm, wm = statistics.median(f), statistics.median(w)
     rec = {
         "workload": workload, "kernel": names[0] if len(names) == 1 else names,
-        "kernel_source_hash": kernel_source_hash(WORKLOADS[workload].get("fmt", "q8")),
+        "kernel_source_hash": kernel_source_hash(kernel_fmt(workload)),
         "fetch_size_kib_per_dispatch_median": fm, "write_size_kib_per_dispatch_median": wm,
         "dispatches": len(f),
         "calibration": {"copy_bytes": copy, "fetch_factor": ff, "write_factor": fw,
@@ -418,20 +434,20 @@ def main():
     hist = (st1[sv.STATE_HIST:sv.STATE_HIST + K + 1] - st0[sv.STATE_HIST:sv.STATE_HIST + K + 1]).tolist()
     sum_j = int(st1[sv.STATE_SUMJ] - st0[sv.STATE_SUMJ])
 
-    # roofline of the dominant kernel, the q8b32 head matmul with its fused argmax stage 1:
-    # whole rounds launched one by one, HIP events recorded by the library on the launch
-    # stream right before and after the matmul kernel
+    # roofline of the dominant kernel: the head matmul with its fused argmax (or sampling)
+    # stage 1, or for the dense stack its gate/up projection (block 0 of a whole-stack call;
+    # every block's gate/up moves the same bytes).  Calls are launched one by one, with HIP
+    # events recorded by the library on the launch stream right before and after the kernel.
     stream = torch.cuda.current_stream()
     durs = []
     for i in range(args.kernel_reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        if wl["layers"]:
-            x, c = nbuf, i % copies            # the head of the stack, on its last input
-        else:
-            x, c = hidden[i % R_SETS], i % copies
+        x, c = hidden[i % R_SETS], i % copies
         d_in = forced[i % R_SETS] if forced is not None else drafts
         sv.profile_next_matmul(e0, e1, stream=stream)
-        if table is not None:
+        if wl["layers"]:
+            sv.stack(*inp["layers"], x, nbuf, swork, 1e-6, x_layers=xl_buf, stream=stream)
+        elif table is not None:
             sv.generate(wq[c], ws[c], table, tokens, state, drafts, window, argmax, work, 1, stream=stream)
         else:
             head_round(wq[c], ws[c], x, d_in, tokens, state, drafts, argmax, work, stream=stream)
@@ -439,7 +455,8 @@ def main():
     torch.cuda.synchronize()
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in durs]))
     hb = head_bytes(V, H, S, wl.get("fmt", "q8"))
-    achieved = hb / (kern_ms * 1e-3) / 1e9
+    kb = gateup_bytes(H, F, S) if wl["layers"] else hb
+    achieved = kb / (kern_ms * 1e-3) / 1e9
 
     round_bytes = hb + (stack_bytes(wl["layers"], H, F, S) if wl["layers"] else 0)
     rps = 1000.0 / ms
@@ -464,11 +481,14 @@ def main():
         "bytes_per_round": round_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": load_traffic(args.config),
-                     "kernel": ("q4b32" if wl.get("fmt") == "q4" else "q8b32")
-                               + (" head matmul with the fused sampling epilogue (log-sum-exp, Gumbel-max "
-                                  "draw) stage 1 (one launch per round)" if temp else
-                                  " head matmul with the fused argmax stage 1 (one launch per round)"),
-                     "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": hb},
+                     "kernel": (f"q8b32 gate/up projection of the dense stack with the RMSNorm in its prologue "
+                                f"and the SiLU-mul epilogue ({wl['layers']} launches per round, block 0 timed)"
+                                if wl["layers"] else
+                                ("q4b32" if wl.get("fmt") == "q4" else "q8b32")
+                                + (" head matmul with the fused sampling epilogue (log-sum-exp, Gumbel-max "
+                                   "draw) stage 1 (one launch per round)" if temp else
+                                   " head matmul with the fused argmax stage 1 (one launch per round)")),
+                     "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": kb},
         "accept_hist": hist,
         "tokens_per_round": round((args.steps + sum_j) / args.steps, 3),
     }

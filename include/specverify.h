@@ -418,12 +418,15 @@ void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups, int32_t 
                            int32_t head_kernel);
 
 /*
- * Timing hook for the dominant kernel.  The next int8 matmul that this thread enqueues through
- * any entry point (the head matmul of specverify_verify / _round, or a stack projection)
- * records `before` on its stream right before the matmul kernel and `after` right after it
- * (after its split-combine pass when the hidden axis is split across workgroups); the hook
- * is then cleared.  The events are the caller's (created on the current device, timing
- * enabled).  (NULL, NULL) clears a pending hook; one NULL alone is SV_ERR_NULL.
+ * Timing hook for the dominant kernel.  The next int8 or int4 matmul that this thread
+ * enqueues through any entry point (the head matmul of specverify_verify / _round / the
+ * sampling, tree and int4 variants, a per-op projection, or the first projection of
+ * specverify_stack: block 0's gate/up) is launched with `before` and `after` attached to its
+ * dispatch: they take the kernel's own start and end timestamps (the end of its
+ * split-combine pass when the hidden axis is split across workgroups), the clock a kernel
+ * trace reads; the hook is then cleared.  The events are the caller's (created on the
+ * current device, timing enabled).  (NULL, NULL) clears a pending hook; one NULL alone is
+ * SV_ERR_NULL.  Not for use under stream capture.
  */
 int specverify_profile_next_matmul(hipEvent_t before, hipEvent_t after);
 

@@ -66,31 +66,19 @@ int check_q8b32(const int8_t* w, const uint16_t* s, int32_t rows, int32_t H, con
     return SV_OK;
 }
 
-// The matmul (and its split combine), bracketed by the pending timing hook if one is set.
+// The matmul (and its split combine), timed by the pending hook's events if one is set.
 hipError_t launch_matmul(int epi, const sv::GemmCfg& cfg, const sv::GemmArgs& a, hipStream_t stream,
                          bool combine = true) {
     hipEvent_t before = g_prof_before, after = g_prof_after;
     g_prof_before = g_prof_after = nullptr;
-    if (before) {
-        hipError_t e = hipEventRecord(before, stream);
-        if (e != hipSuccess) return e;
-    }
-    hipError_t e = sv::launch_q8b32(epi, cfg, a, stream, combine);
-    if (e == hipSuccess && after) e = hipEventRecord(after, stream);
-    return e;
+    return sv::launch_q8b32(epi, cfg, a, stream, combine, before, after);
 }
 
-// The chunked head matmul, bracketed by the pending timing hook if one is set.
-hipError_t launch_chunked_matmul(const sv::ChunkCfg& cfg, const sv::ChunkArgs& a, hipStream_t stream) {
+// A chunked matmul (head or stack projection), timed by the pending hook's events if one is set.
+hipError_t launch_chunked_matmul(int epi, const sv::ChunkCfg& cfg, const sv::ChunkArgs& a, hipStream_t stream) {
     hipEvent_t before = g_prof_before, after = g_prof_after;
     g_prof_before = g_prof_after = nullptr;
-    if (before) {
-        hipError_t e = hipEventRecord(before, stream);
-        if (e != hipSuccess) return e;
-    }
-    hipError_t e = sv::launch_chunked(sv::EPI_HEAD, cfg, a, stream);
-    if (e == hipSuccess && after) e = hipEventRecord(after, stream);
-    return e;
+    return sv::launch_chunked(epi, cfg, a, stream, before, after);
 }
 
 }  // namespace
@@ -166,7 +154,7 @@ int launch_head(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, 
         c.w0 = wq; c.s0 = wscale; c.x = hidden;
         c.V = V; c.H = H; c.S = S; c.nb = H / SV_BLOCK; c.nitems = cc.items; c.nkc = cc.nkc;
         c.part_val = part_val; c.part_idx = part_idx; c.logits = logits;
-        hipError_t e = launch_chunked_matmul(cc, c, stream);
+        hipError_t e = launch_chunked_matmul(sv::EPI_HEAD, cc, c, stream);
         if (e != hipSuccess) return hip_fail(e, "verify matmul launch");
         e = sv::launch_round_tail(part_val, part_idx, cc.grid, S, argmax, round ? drafts_in : nullptr, tokens, cap,
                                   state, ngram_max, round ? drafts_out : nullptr, stream);
@@ -453,9 +441,7 @@ int launch_head_q4(const sv::Q4Cfg& cfg, const uint8_t* wq, const uint16_t* wsca
     a.logits = logits;
     hipEvent_t before = g_prof_before, after = g_prof_after;
     g_prof_before = g_prof_after = nullptr;
-    hipError_t e = before ? hipEventRecord(before, stream) : hipSuccess;
-    if (e == hipSuccess) e = sv::launch_q4(cfg, a, stream);
-    if (e == hipSuccess && after) e = hipEventRecord(after, stream);
+    hipError_t e = sv::launch_q4(cfg, a, stream, before, after);
     if (e != hipSuccess) return hip_fail(e, "int4 verify matmul launch");
     e = sv::launch_round_tail(a.part_val, a.part_idx, cfg.grid, S, argmax, round ? drafts_in : nullptr, tokens, cap,
                               state, ngram_max, round ? drafts_out : nullptr, stream);
@@ -706,7 +692,7 @@ int specverify_stack(const int8_t* wg, const uint16_t* sg, const int8_t* wu, con
         g.eps = eps;
         g.V = F; g.H = H; g.S = S; g.nb = H / SV_BLOCK; g.nitems = cg.items; g.nkc = cg.nkc;
         g.y = m;
-        e = sv::launch_chunked(sv::EPI_GATEUP, cg, g, stream);
+        e = launch_chunked_matmul(sv::EPI_GATEUP, cg, g, stream);
         if (e != hipSuccess) return hip_fail(e, "stack gate/up launch");
         sv::ChunkArgs d{};
         d.w0 = wd + (size_t)l * H * F;
@@ -716,7 +702,7 @@ int specverify_stack(const int8_t* wg, const uint16_t* sg, const int8_t* wu, con
         d.y = out;
         d.residual = cur;
         d.ss_out = ss;
-        e = sv::launch_chunked(sv::EPI_STORE, cd, d, stream);
+        e = launch_chunked_matmul(sv::EPI_STORE, cd, d, stream);
         if (e != hipSuccess) return hip_fail(e, "stack down launch");
         cur = out;
     }

@@ -496,10 +496,11 @@ bool chunked_config(int rows, int H, int epi, ChunkCfg& c) {
     return false;
 }
 
-hipError_t launch_chunked(int epi, const ChunkCfg& c, const ChunkArgs& a, hipStream_t stream) {
+hipError_t launch_chunked(int epi, const ChunkCfg& c, const ChunkArgs& a, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop) {
     ChunkFn fn = chunked_fn(epi, c.nw, c.hold, c.depth);
     if (!fn) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(fn, dim3(c.grid), dim3(c.nw * 64), 0, stream, a);
+    launch_timed(fn, dim3(c.grid), dim3(c.nw * 64), stream, start, stop, a);
     return hipGetLastError();
 }
 

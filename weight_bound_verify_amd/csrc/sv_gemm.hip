@@ -965,21 +965,24 @@ size_t stack_workspace_bytes(int N, int K, int S, bool gateup) {
     return (size_t)4 * c.ksplit * S * N * (gateup ? 2 : 1);
 }
 
-hipError_t launch_q8b32(int epi, const GemmCfg& cfg, const GemmArgs& a, hipStream_t stream, bool combine) {
+hipError_t launch_q8b32(int epi, const GemmCfg& cfg, const GemmArgs& a, hipStream_t stream, bool combine,
+                        hipEvent_t start, hipEvent_t stop) {
     KernelFn fn = kernel_for(epi, cfg);
     if (!fn) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(fn, dim3(cfg.grid, cfg.ksplit), dim3(cfg.nw * 64), 0, stream, a);
+    const bool split = cfg.ksplit > 1 && combine;
+    launch_timed(fn, dim3(cfg.grid, cfg.ksplit), dim3(cfg.nw * 64), stream, start, split ? nullptr : stop, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || cfg.ksplit == 1 || !combine) return e;
+    if (e != hipSuccess || !split) return e;
     const int cg = combine_groups(a.V);
+    const dim3 grid(cg, a.S), block(256);
     if (epi == EPI_HEAD)
-        hipLaunchKernelGGL(combine_kernel<EPI_HEAD>, dim3(cg, a.S), dim3(256), 0, stream, a);
+        launch_timed(combine_kernel<EPI_HEAD>, grid, block, stream, nullptr, stop, a);
     else if (epi == EPI_SAMPLE)
-        hipLaunchKernelGGL(combine_kernel<EPI_SAMPLE>, dim3(cg, a.S), dim3(256), 0, stream, a);
+        launch_timed(combine_kernel<EPI_SAMPLE>, grid, block, stream, nullptr, stop, a);
     else if (epi == EPI_STORE)
-        hipLaunchKernelGGL(combine_kernel<EPI_STORE>, dim3(cg, a.S), dim3(256), 0, stream, a);
+        launch_timed(combine_kernel<EPI_STORE>, grid, block, stream, nullptr, stop, a);
     else
-        hipLaunchKernelGGL(combine_kernel<EPI_GATEUP>, dim3(cg, a.S), dim3(256), 0, stream, a);
+        launch_timed(combine_kernel<EPI_GATEUP>, grid, block, stream, nullptr, stop, a);
     return hipGetLastError();
 }
 

@@ -1,11 +1,25 @@
 // Host-side internal interface between the C-ABI layer and the kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace sv {
+
+// Launch `fn`; when a start or stop event is given, the events take the timestamps of this
+// kernel's own dispatch packet (the same clock a kernel trace reads), not of a marker
+// enqueued before or after it.
+template <typename F, typename... Args>
+inline void launch_timed(F fn, dim3 grid, dim3 block, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
+                         Args... args) {
+    if (start || stop)
+        hipExtLaunchKernelGGL(fn, grid, block, 0, stream, start, stop, 0, args...);
+    else
+        hipLaunchKernelGGL(fn, grid, block, 0, stream, args...);
+}
+
 
 // EPI_SAMPLE: the head epilogue of sampling verify (per-row log-normaliser, a Gumbel-max
 // draw per row that leaves out the row's draft, the scaled logit of that draft).
@@ -91,8 +105,10 @@ size_t head_workspace_bytes(int V, int H, int S);
 size_t stack_workspace_bytes(int N, int K, int S, bool gateup);
 
 // The matmul and, when cfg.ksplit > 1 and `combine` is set, the pass that sums the split
-// partial sums into the epilogue's output.
-hipError_t launch_q8b32(int epi, const GemmCfg& cfg, const GemmArgs& a, hipStream_t stream, bool combine = true);
+// partial sums into the epilogue's output.  `start` / `stop` (optional) time the matmul's
+// dispatch through the combine pass.
+hipError_t launch_q8b32(int epi, const GemmCfg& cfg, const GemmArgs& a, hipStream_t stream, bool combine = true,
+                        hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // Argmax stage 2 of a head launch and, when drafts_out != null, the rest of the round
 // (accept, then the next drafts): one workgroup.
 hipError_t launch_round_tail(const float* pv, const int* pi, int nparts, int S, int32_t* argmax,
@@ -125,7 +141,8 @@ struct Q4Cfg {
     int nbw, nw, grid, items;
 };
 bool q4_config(int V, int H, Q4Cfg& c);
-hipError_t launch_q4(const Q4Cfg& c, const Q4Args& a, hipStream_t stream);
+hipError_t launch_q4(const Q4Cfg& c, const Q4Args& a, hipStream_t stream, hipEvent_t start = nullptr,
+                     hipEvent_t stop = nullptr);
 
 // Chunked streaming matmul (dense stack, and heads whose hidden axis splits into whole 128-byte
 // wave segments): see sv_chunked.hip.  Window rows S <= 16.
@@ -159,7 +176,8 @@ void set_chunk_tuning(int waves, int depth, int max_groups, int head_kernel);
 bool head_use_chunked(int V, int H);
 // False when H is not a whole number of 4-block segments for 4, 8 or 16 waves.
 bool chunked_config(int rows, int H, int epi, ChunkCfg& c);
-hipError_t launch_chunked(int epi, const ChunkCfg& c, const ChunkArgs& a, hipStream_t stream);
+hipError_t launch_chunked(int epi, const ChunkCfg& c, const ChunkArgs& a, hipStream_t stream,
+                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // ss[s][t] = sum of squares of the 16 fp16 values of x[s][16t .. 16t+15]
 hipError_t launch_row_ss(const uint16_t* x, int S, int H, float* ss, hipStream_t stream);
 // out = fp16(x * inv[s]), inv from the ss partials as the chunked gate/up prologue computes it

@@ -272,10 +272,10 @@ bool q4_config(int V, int H, Q4Cfg& c) {
     return false;
 }
 
-hipError_t launch_q4(const Q4Cfg& c, const Q4Args& a, hipStream_t stream) {
+hipError_t launch_q4(const Q4Cfg& c, const Q4Args& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     Q4Fn fn = pick_q4(c.nbw, c.nw);
     if (!fn) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(fn, dim3(c.grid), dim3(c.nw * 64), 0, stream, a);
+    launch_timed(fn, dim3(c.grid), dim3(c.nw * 64), stream, start, stop, a);
     return hipGetLastError();
 }
 
