@@ -379,3 +379,55 @@ def test_sampling_rounds_hit_rate_gate():
     sv.propose(tokens, state, drafts, 3)
     torch.cuda.synchronize()
     assert (drafts.cpu().numpy() >= 0).any()
+
+
+def test_round_sample_full_35b_head_shape():
+    """One sampling round at the full 35B-A3B-shaped head (V = 248320, H = 2048, K = 8,
+    T = 0.7) in the launch configuration the bench uses.  Rows 0..4 are steered onto drafts
+    1..5 (kept), row 5 onto a token other than draft 6 (rejected; the residual draw is that
+    token): the draws against the oracle's Gumbel keys, the keep decisions against the oracle's
+    accept uniforms, then the committed stream and the next drafts bit-exactly."""
+    V, H, K, T = 248320, 2048, 8, 0.7
+    S = K + 1
+    say(f"round_sample full V={V} H={H} K={K} T={T}")
+    q, s = synth.quantized_head(synth.streams(2).weights, V, H)
+    rng = np.random.default_rng(71)
+    ctx = synth.zipf_context_with_copies(np.random.default_rng(72), 4096, V, 0.3)[0].astype(np.int32)
+    P0 = len(ctx)
+    seed = 0x5EED_0F_5A3B
+
+    def steer(tok):
+        d = (q[tok].astype(np.float64).reshape(-1, 32) * s[tok].astype(np.float64)[:, None]).reshape(-1)
+        return (50.0 * d).astype(np.float16)
+
+    drafts = [int(x) for x in rng.choice(V, size=K, replace=False)]
+    other = int(ctx[1000]) if int(ctx[1000]) != drafts[5] else int(ctx[1001])   # in the context: the
+    # drafter then finds the committed stream's last id earlier and proposes real drafts
+    rows = [steer(drafts[i]) for i in range(5)] + [steer(other)]
+    rows += list(synth.fp16_normal(rng, (S - 6, H)))
+    hidden = np.stack(rows)
+    cap = P0 + 64
+    tokens = torch.zeros(cap, dtype=torch.int32, device=dev())
+    tokens[:P0] = to_dev(ctx)
+    state = sv.new_state(dev())
+    state[sv.STATE_LEN] = P0
+    d_in = to_dev(np.array(drafts, dtype=np.int32))
+    d_out = torch.empty(K, dtype=torch.int32, device=dev())
+    sample = torch.empty(S, dtype=torch.int32, device=dev())
+    lse = torch.empty(S, dtype=torch.float32, device=dev())
+    work = sv.workspace(sv.sample_workspace_bytes(V, H, S), dev())
+    sv.round_sample(to_dev(q), to_dev(s), to_dev(hidden), d_in, T, seed, tokens, state, d_out, work, 3, sample, lse)
+    torch.cuda.synchronize()
+    L = oracle.head_logits(q, s, hidden)
+    smp_d = sample.cpu().numpy()
+    check_draws(smp_d, L, drafts, T, seed, P0)
+    p, _ = smp.probabilities(L, T)
+    u = smp.accept_uniforms(seed, P0, K)
+    st = state.cpu().numpy()
+    j = int(st[sv.STATE_J])
+    assert j == 5 and all(u[i] < p[i, drafts[i]] for i in range(5)) and not u[5] < p[5, drafts[5]]
+    assert int(smp_d[5]) == other
+    stream = list(ctx) + drafts[:5] + [other]
+    assert st[sv.STATE_LEN] == len(stream) and tokens[:len(stream)].cpu().tolist() == stream
+    nxt = oracle.propose_scan(stream, 3, K)[0]
+    assert d_out.cpu().tolist() == list(nxt) and max(nxt) >= 0
