@@ -122,9 +122,12 @@ def test_verify_full_35b_head_shape(S):
     say(f"  argmax rows exempt by the 1e-3 gap rule: {ex}")
 
 
-def test_verify_full_large_hidden_shape_sampled_rows():
-    # 248320 x 5120 at S = 2; the oracle computes every row (fp64), the argmax is compared exactly
-    V, H, S = 248320, 5120, 2
+@pytest.mark.parametrize("S", [2, 9, 17])
+def test_verify_full_large_hidden_shape(S):
+    """248320 x 5120 at every window size of that workload, in the launch configuration the
+    bench uses (S = 17: the one-tile kernel with the 17th row's dot products and 8 of each
+    wave's 20 blocks of window rows in LDS); the oracle computes every logit in fp64."""
+    V, H = 248320, 5120
     say(f"full head V={V} H={H} S={S}")
     st = synth.streams(3)
     q, s = synth.quantized_head(st.weights, V, H)
