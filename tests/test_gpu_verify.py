@@ -122,6 +122,21 @@ def test_verify_full_35b_head_shape(S):
     say(f"  argmax rows exempt by the 1e-3 gap rule: {ex}")
 
 
+@pytest.mark.parametrize("V,H", [(151936, 2560), (151936, 4096)])
+def test_verify_full_151936_vocab_heads(V, H):
+    """The Qwen3-4B-shaped head (H = 2560: 8 blocks x 10 waves) and the dense stack's head
+    (H = 4096: 16 x 8) at full size and S = 9, in the launch configuration the bench uses."""
+    S = 9
+    say(f"full head V={V} H={H} S={S}")
+    st = synth.streams(1 if H == 2560 else 4)
+    q, s = synth.quantized_head(st.weights, V, H)
+    hidden = synth.fp16_normal(st.hidden, (S, H))
+    a, lg = gpu_verify(q, s, hidden)
+    L = oracle.head_logits(q, s, hidden)
+    check_logits(lg, L)
+    check_argmax(a, L)
+
+
 @pytest.mark.parametrize("S", [2, 9, 17])
 def test_verify_full_large_hidden_shape(S):
     """248320 x 5120 at every window size of that workload, in the launch configuration the
