@@ -306,6 +306,37 @@ int specverify_generate(const int8_t* wq, const uint16_t* wscale, int32_t V, int
                         hipStream_t stream);
 
 /*
+ * specverify_generate_sample / specverify_generate_tree - the same device-resident loop for
+ * sampling verify and for tree verify ("Riding Apple's pipelined GPU engine", "Why hand-rolled
+ * per-token loops lose"; "Stream C - Speculative decoding", the deferred list: sampling and
+ * tree proposals).  Each round is
+ *   specverify_gather_window(table, drafts) -> specverify_round_sample(window, drafts -> drafts)
+ *   specverify_gather_window(table, drafts) -> specverify_round_tree(window, tree -> tree)
+ * For a tree, window row i is the table row of node i's own token: under the token-indexed
+ * model that is the row after the path root -> i.  The sampling noise is keyed by `seed` and
+ * the stream position, so one seed serves every round of a stream.  Before the first call the
+ * stream must hold its anchor and `drafts` (and `parents`) the first proposal
+ * (specverify_propose / specverify_propose_tree).  Capacity: as specverify_generate.
+ * Capturable in a HIP graph.
+ *   table  fp16 [V][H];  window fp16 [K+1][H] scratch;  K 1 .. 15;  rounds >= 0
+ *   drafts int32 [K] (and parents int32 [K]), read and rewritten by every round
+ *   other arguments as for specverify_round_sample / specverify_round_tree; the sampling loop
+ *   writes no per-row draws or log-normalisers, the tree loop no logits.
+ * Errors: as specverify_generate, and as the round entry points.
+ */
+int specverify_generate_sample(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
+                               const uint16_t* table, int32_t K, int32_t rounds, float temperature,
+                               uint64_t seed, int32_t* tokens, int32_t cap, int32_t* state,
+                               int32_t ngram_max, int32_t* drafts, uint16_t* window,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+int specverify_generate_tree(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
+                             const uint16_t* table, int32_t K, int32_t rounds, int32_t* tokens,
+                             int32_t cap, int32_t* state, int32_t ngram_max, int32_t branches,
+                             int32_t depth, int32_t* parents, int32_t* drafts, uint16_t* window,
+                             int32_t* argmax, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
  * specverify_accept - greedy longest-prefix acceptance with the fused anchor.
  * Pages: "Stream C - Speculative decoding", sections "The delta" and "Control-logic proof"
  * (draft i is accepted iff it equals the greedy id of its position and every earlier draft

@@ -221,6 +221,42 @@ def test_tree_argument_errors(lib):
     assert rt(A16, A16, 1000, 256, A16, 8, A16, A16, A16, 100, A16, 3, 2, 4, A16, A16, A16, NULL, A16, 8, NULL) == 4
 
 
+def test_generation_loop_argument_errors(lib):
+    """The sampling and tree generation loops check their arguments before touching the
+    device: every case below returns its status without a GPU (a valid call fails only at the
+    device query here)."""
+    gs = lib.specverify_generate_sample
+    ws = lib.specverify_sample_workspace_bytes(1000, 256, 9)
+    ok = (A16, A16, 1000, 256, A16, 8, 3, 0.8, 1, A16, 100, A16, 3, A16, A16, A16, ws, NULL)
+
+    def with_(args, i, v):
+        a = list(args)
+        a[i] = v
+        return a
+    assert gs(*ok) in (6, 7)                                              # no device
+    assert gs(*with_(ok, 4, NULL)) == 1                                   # table
+    assert gs(*with_(ok, 14, NULL)) == 1                                  # window
+    assert gs(*with_(ok, 5, 16)) == 2                                     # K <= 15
+    assert gs(*with_(ok, 6, -1)) == 2                                     # rounds >= 0
+    assert gs(*with_(ok, 7, 0.0)) == 2                                    # temperature > 0
+    assert gs(*with_(ok, 4, A2)) == 3                                     # table alignment
+    assert gs(*with_(ok, 16, ws - 1)) == 4                                # workspace
+    assert gs(*with_(ok, 10, 0)) == 5                                     # cap
+    gt = lib.specverify_generate_tree
+    wt = lib.specverify_verify_workspace_bytes(1000, 256, 9)
+    ok = (A16, A16, 1000, 256, A16, 8, 3, A16, 100, A16, 3, 2, 4, A16, A16, A16, A16, A16, wt, NULL)
+    assert gt(*ok) in (6, 7)
+    assert gt(*with_(ok, 4, NULL)) == 1                                   # table
+    assert gt(*with_(ok, 13, NULL)) == 1                                  # parents
+    assert gt(*with_(ok, 5, 0)) == 2                                      # K >= 1
+    assert gt(*with_(ok, 11, 5)) == 2                                     # branches <= 4
+    assert gt(*with_(ok, 12, 9)) == 2                                     # depth <= K
+    assert gt(*with_(ok, 6, -2)) == 2                                     # rounds >= 0
+    assert gt(*with_(ok, 15, A2)) == 3                                    # window alignment
+    assert gt(*with_(ok, 18, 8)) == 4                                     # workspace
+    assert gt(*with_(ok, 8, 0)) == 5                                      # cap
+
+
 def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(sv, "_lib", None)
     monkeypatch.setattr(sv, "LIB_PATH", str(tmp_path / "nope.so"))

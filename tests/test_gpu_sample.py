@@ -431,3 +431,39 @@ def test_round_sample_full_35b_head_shape():
     assert st[sv.STATE_LEN] == len(stream) and tokens[:len(stream)].cpu().tolist() == stream
     nxt = oracle.propose_scan(stream, 3, K)[0]
     assert d_out.cpu().tolist() == list(nxt) and max(nxt) >= 0
+
+
+def test_generate_sample_equals_round_by_round():
+    """specverify_generate_sample over R rounds (one seed: the noise is keyed by the stream
+    position) leaves the stream, the state word and the next drafts bit-identical to R calls
+    of gather_window + round_sample with the same seed."""
+    V, H, K, T, R = 3000, 512, 6, 0.3, 25
+    S = K + 1
+    rng = np.random.default_rng(91)
+    q, s = head(92, V, H)
+    model = synth.MarkovHidden(rng, V, H)
+    ctx, _, _ = synth.uniform_context_with_span(rng, 400, V, 12, 16)
+    wq, ws, tab = to_dev(q), to_dev(s), to_dev(model.table)
+    cap = len(ctx) + R * S + 8
+    seed = 0xC0FFEE
+
+    def fresh():
+        t = torch.zeros(cap, dtype=torch.int32, device=dev())
+        t[:len(ctx)] = to_dev(ctx)
+        st = sv.new_state(dev())
+        st[sv.STATE_LEN] = len(ctx)
+        d = torch.empty(K, dtype=torch.int32, device=dev())
+        sv.propose(t, st, d, 3)
+        return t, st, d
+
+    work = sv.workspace(sv.sample_workspace_bytes(V, H, S), dev())
+    window = torch.empty((S, H), dtype=torch.float16, device=dev())
+    ta, sa, da = fresh()
+    sv.generate_sample(wq, ws, tab, ta, sa, da, window, work, R, T, seed)
+    tb, sb, db = fresh()
+    for _ in range(R):
+        sv.gather_window(tb, sb, db, tab, window)
+        sv.round_sample(wq, ws, window, db, T, seed, tb, sb, db, work)
+    torch.cuda.synchronize()
+    assert int(sa[sv.STATE_ROUNDS]) == R and int(sa[sv.STATE_FLAGS]) == 0
+    assert torch.equal(sa, sb) and torch.equal(ta, tb) and torch.equal(da, db)

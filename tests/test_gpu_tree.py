@@ -378,3 +378,45 @@ def test_round_tree_full_35b_head_shape():
     assert tokens[:len(stream)].cpu().tolist() == stream
     p1, d1, _, _ = tr.propose_tree(stream, 3, K, B, D)
     assert parents.cpu().tolist() == list(p1) and drafts.cpu().tolist() == list(d1)
+
+
+def test_generate_tree_equals_round_by_round():
+    """specverify_generate_tree over R rounds leaves the stream, the state word and the next
+    tree bit-identical to R calls of gather_window + round_tree (the loop the greedy-equality
+    test above checks against plain greedy decoding)."""
+    V, H, K, B, D, R = 4096, 512, 8, 3, 4, 150
+    S = K + 1
+    rng = np.random.default_rng(81)
+    q, s = synth.quantized_head(np.random.SeedSequence(82), V, H)
+    model = synth.MarkovHidden(rng, V, H)
+    ctx, _, _ = synth.uniform_context_with_span(rng, 512, V, 12, 16)
+    wq, ws, tab = to_dev(q), to_dev(s), to_dev(model.table)
+    cap = len(ctx) + R * S + 8
+
+    def fresh():
+        t = torch.zeros(cap, dtype=torch.int32, device=dev())
+        t[:len(ctx)] = to_dev(ctx)
+        st = _state(len(ctx))
+        h_last = torch.empty((1, H), dtype=torch.float16, device=dev())
+        a0 = torch.empty(1, dtype=torch.int32, device=dev())
+        sv.gather_window(t, st, torch.empty(0, dtype=torch.int32, device=dev()), tab, h_last)
+        sv.verify(wq, ws, h_last, a0, sv.workspace(sv.verify_workspace_bytes(V, H, 1), dev()))
+        sv.accept(a0, None, t, st)
+        p = torch.empty(K, dtype=torch.int32, device=dev())
+        d = torch.empty(K, dtype=torch.int32, device=dev())
+        sv.propose_tree(t, st, p, d, 3, B, D)
+        return t, st, p, d
+
+    work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev())
+    window = torch.empty((S, H), dtype=torch.float16, device=dev())
+    argmax = torch.empty(S, dtype=torch.int32, device=dev())
+    ta, sa, pa, da = fresh()
+    sv.generate_tree(wq, ws, tab, ta, sa, pa, da, window, argmax, work, R, 3, B, D)
+    tb, sb, pb, db = fresh()
+    for _ in range(R):
+        sv.gather_window(tb, sb, db, tab, window)
+        sv.round_tree(wq, ws, window, pb, db, tb, sb, pb, db, argmax, work, 3, B, D)
+    torch.cuda.synchronize()
+    assert int(sa[sv.STATE_ROUNDS]) == R and int(sa[sv.STATE_FLAGS]) == 0
+    assert torch.equal(sa, sb) and torch.equal(ta, tb) and torch.equal(pa, pb) and torch.equal(da, db)
+    assert int(sa[sv.STATE_SUMJ]) > 0                              # the tree drafter took drafts

@@ -269,6 +269,15 @@ int launch_sample_head(const int8_t* wq, const uint16_t* wscale, int32_t V, int3
     return e == hipSuccess ? SV_OK : hip_fail(e, "sampling tail launch");
 }
 
+// Checks shared by the generation loops: the token-indexed table and the window it fills.
+int check_table(const uint16_t* table, const uint16_t* window, int32_t K, int32_t rounds) {
+    if (K < 1 || K > 15) return fail(SV_ERR_SHAPE, "K=%d outside [1, 15]", K);
+    if (rounds < 0) return fail(SV_ERR_SHAPE, "rounds=%d < 0", rounds);
+    if (!table || !window) return fail(SV_ERR_NULL, "table and window are required");
+    if (!aligned(table, 16) || !aligned(window, 16)) return fail(SV_ERR_ALIGN, "table and window must be 16-byte aligned");
+    return SV_OK;
+}
+
 int check_temperature(float t) {
     if (!(t > 0.0f) || !std::isfinite(t) || !std::isfinite(1.0f / t))
         return fail(SV_ERR_SHAPE, "temperature %g must be positive, finite and have a finite inverse", (double)t);
@@ -333,6 +342,32 @@ int specverify_round_sample(const int8_t* wq, const uint16_t* wscale, int32_t V,
                               lse, nullptr, workspace, true, tokens, cap, ngram_max, drafts_out, stream);
 }
 
+int specverify_generate_sample(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
+                               const uint16_t* table, int32_t K, int32_t rounds, float temperature, uint64_t seed,
+                               int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max, int32_t* drafts,
+                               uint16_t* window, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (int st = check_table(table, window, K, rounds)) return st;
+    if (int st = check_q8b32(wq, wscale, V, H, window, K + 1, 16)) return st;
+    if (int st = check_temperature(temperature)) return st;
+    if (!drafts || !tokens || !state || !workspace) return fail(SV_ERR_NULL, "drafts, tokens, state and workspace are required");
+    if (ngram_max < 1 || ngram_max > SV_MAX_NGRAM) return fail(SV_ERR_SHAPE, "ngram_max=%d outside [1, %d]", ngram_max, SV_MAX_NGRAM);
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(drafts, 4) || !aligned(tokens, 4) || !aligned(state, 4) || !aligned(workspace, 16))
+        return fail(SV_ERR_ALIGN, "4-byte aligned buffers and a 16-byte aligned workspace are required");
+    const size_t need = sv::sample_workspace_bytes(V, H, K + 1);
+    if (workspace_bytes < need) return fail(SV_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+    if (int st = check_device()) return st;
+    for (int r = 0; r < rounds; ++r) {
+        hipError_t e = sv::launch_gather_window(tokens, cap, state, drafts, K, table, V, H, window, stream);
+        if (e != hipSuccess) return hip_fail(e, "gather launch");
+        if (int st = launch_sample_head(wq, wscale, V, H, window, K + 1, drafts, temperature, seed, state, nullptr,
+                                        nullptr, nullptr, nullptr, workspace, true, tokens, cap, ngram_max, drafts,
+                                        stream))
+            return st;
+    }
+    return SV_OK;
+}
+
 namespace {
 
 int check_tree_args(int32_t K, int32_t branches, int32_t depth, int32_t ngram_max) {
@@ -371,20 +406,13 @@ int specverify_accept_tree(const int32_t* argmax, const int32_t* parents, const 
     return e == hipSuccess ? SV_OK : hip_fail(e, "tree accept launch");
 }
 
-int specverify_round_tree(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
-                          int32_t K, const int32_t* parents_in, const int32_t* drafts_in, int32_t* tokens,
-                          int32_t cap, int32_t* state, int32_t ngram_max, int32_t branches, int32_t depth,
-                          int32_t* parents_out, int32_t* drafts_out, int32_t* argmax, float* logits,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (int st = check_tree_args(K, branches, depth, ngram_max)) return st;
-    if (int st = check_head(wq, wscale, V, H, hidden, K + 1, argmax, logits, workspace, workspace_bytes)) return st;
-    if (!parents_in || !drafts_in || !tokens || !state || !parents_out || !drafts_out)
-        return fail(SV_ERR_NULL, "tree, tokens and state buffers are required");
-    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
-    if (!aligned(parents_in, 4) || !aligned(drafts_in, 4) || !aligned(tokens, 4) || !aligned(state, 4) ||
-        !aligned(parents_out, 4) || !aligned(drafts_out, 4))
-        return fail(SV_ERR_ALIGN, "int32 buffers must be 4-byte aligned");
-    if (int st = check_device()) return st;
+namespace {
+
+// The tree round's launches (head matmul, then the tree tail); arguments already checked.
+int launch_tree_round(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
+                      int32_t K, const int32_t* parents_in, const int32_t* drafts_in, int32_t* tokens, int32_t cap,
+                      int32_t* state, int32_t ngram_max, int32_t branches, int32_t depth, int32_t* parents_out,
+                      int32_t* drafts_out, int32_t* argmax, float* logits, void* workspace, hipStream_t stream) {
     const int S = K + 1;
     char* ws = static_cast<char*>(workspace);
     const sv::GemmCfg cfg = sv::gemm_config(V, H, S, sv::EPI_HEAD);
@@ -408,6 +436,50 @@ int specverify_round_tree(const int8_t* wq, const uint16_t* wscale, int32_t V, i
     e = sv::launch_tree_tail(a.part_val, a.part_idx, nparts, S, argmax, parents_in, drafts_in, tokens, cap, state,
                              ngram_max, branches, depth, parents_out, drafts_out, stream);
     return e == hipSuccess ? SV_OK : hip_fail(e, "tree round tail launch");
+}
+
+}  // namespace
+
+int specverify_round_tree(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* hidden,
+                          int32_t K, const int32_t* parents_in, const int32_t* drafts_in, int32_t* tokens,
+                          int32_t cap, int32_t* state, int32_t ngram_max, int32_t branches, int32_t depth,
+                          int32_t* parents_out, int32_t* drafts_out, int32_t* argmax, float* logits,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (int st = check_tree_args(K, branches, depth, ngram_max)) return st;
+    if (int st = check_head(wq, wscale, V, H, hidden, K + 1, argmax, logits, workspace, workspace_bytes)) return st;
+    if (!parents_in || !drafts_in || !tokens || !state || !parents_out || !drafts_out)
+        return fail(SV_ERR_NULL, "tree, tokens and state buffers are required");
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(parents_in, 4) || !aligned(drafts_in, 4) || !aligned(tokens, 4) || !aligned(state, 4) ||
+        !aligned(parents_out, 4) || !aligned(drafts_out, 4))
+        return fail(SV_ERR_ALIGN, "int32 buffers must be 4-byte aligned");
+    if (int st = check_device()) return st;
+    return launch_tree_round(wq, wscale, V, H, hidden, K, parents_in, drafts_in, tokens, cap, state, ngram_max,
+                             branches, depth, parents_out, drafts_out, argmax, logits, workspace, stream);
+}
+
+int specverify_generate_tree(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* table,
+                             int32_t K, int32_t rounds, int32_t* tokens, int32_t cap, int32_t* state,
+                             int32_t ngram_max, int32_t branches, int32_t depth, int32_t* parents, int32_t* drafts,
+                             uint16_t* window, int32_t* argmax, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    if (int st = check_table(table, window, K, rounds)) return st;
+    if (int st = check_tree_args(K, branches, depth, ngram_max)) return st;
+    if (int st = check_head(wq, wscale, V, H, window, K + 1, argmax, nullptr, workspace, workspace_bytes)) return st;
+    if (!parents || !drafts || !tokens || !state) return fail(SV_ERR_NULL, "parents, drafts, tokens and state are required");
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(parents, 4) || !aligned(drafts, 4) || !aligned(tokens, 4) || !aligned(state, 4))
+        return fail(SV_ERR_ALIGN, "int32 buffers must be 4-byte aligned");
+    if (int st = check_device()) return st;
+    for (int r = 0; r < rounds; ++r) {
+        // a node's row is the row of its own token under the token-indexed model
+        hipError_t e = sv::launch_gather_window(tokens, cap, state, drafts, K, table, V, H, window, stream);
+        if (e != hipSuccess) return hip_fail(e, "gather launch");
+        if (int st = launch_tree_round(wq, wscale, V, H, window, K, parents, drafts, tokens, cap, state, ngram_max,
+                                       branches, depth, parents, drafts, argmax, nullptr, workspace, stream))
+            return st;
+    }
+    return SV_OK;
 }
 
 namespace {

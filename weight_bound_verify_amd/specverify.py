@@ -31,7 +31,7 @@ EXPORTS = (
     "specverify_accept", "specverify_gather_window", "specverify_generate", "specverify_verify_q4b32",
     "specverify_round_q4b32", "specverify_sample_workspace_bytes", "specverify_verify_sample",
     "specverify_accept_sample", "specverify_round_sample", "specverify_propose_tree", "specverify_accept_tree",
-    "specverify_round_tree",
+    "specverify_round_tree", "specverify_generate_sample", "specverify_generate_tree",
     "specverify_rmsnorm", "specverify_stack_workspace_bytes", "specverify_gateup_silu_q8b32",
     "specverify_linear_q8b32", "specverify_linear_residual_rmsnorm_q8b32",
     "specverify_stack_forward_workspace_bytes", "specverify_stack", "specverify_set_tuning", "specverify_profile_next_matmul", "specverify_status_string", "specverify_last_error",
@@ -78,6 +78,10 @@ def load():
                                        ctypes.c_size_t, _P]),
         "specverify_generate": (_I, [_P, _P, _I, _I, _P, _I, _I, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t,
                                      _P]),
+        "specverify_generate_sample": (_I, [_P, _P, _I, _I, _P, _I, _I, ctypes.c_float, ctypes.c_uint64, _P, _I, _P,
+                                            _I, _P, _P, _P, ctypes.c_size_t, _P]),
+        "specverify_generate_tree": (_I, [_P, _P, _I, _I, _P, _I, _I, _P, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
         "specverify_rmsnorm": (_I, [_P, _I, _I, ctypes.c_float, _P, _P]),
         "specverify_stack_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
         "specverify_gateup_silu_q8b32": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _P, _P, ctypes.c_size_t, _P]),
@@ -348,6 +352,37 @@ def generate(wq, wscale, table, tokens, state, drafts, window, argmax, ws, round
         _ptr(wq, torch.int8, "wq"), _ptr(wscale, torch.float16, "wscale"), V, H, _ptr(table, torch.float16, "table"),
         K, int(rounds), _ptr(tokens, torch.int32, "tokens"), tokens.numel(),
         _ptr(state, torch.int32, "state", STATE_WORDS), int(ngram_max), _ptr(drafts, torch.int32, "drafts", K),
+        _ptr(window, torch.float16, "window"), _ptr(argmax, torch.int32, "argmax", K + 1),
+        _ptr(ws, torch.uint8, "workspace"), ws.numel(), _stream(stream)))
+
+
+def generate_sample(wq, wscale, table, tokens, state, drafts, window, ws, rounds: int, temperature: float,
+                    seed: int, ngram_max: int = 3, stream=None) -> None:
+    """``rounds`` device-resident sampling rounds: gather the window, verify_sample, accept, draft."""
+    V, H = wq.shape
+    K = drafts.numel()
+    if tuple(table.shape) != (V, H) or tuple(window.shape) != (K + 1, H) or tuple(wscale.shape) != (V, H // SV_BLOCK):
+        raise ValueError("shape mismatch")
+    _check(load().specverify_generate_sample(
+        _ptr(wq, torch.int8, "wq"), _ptr(wscale, torch.float16, "wscale"), V, H, _ptr(table, torch.float16, "table"),
+        K, int(rounds), float(temperature), _seed(seed), _ptr(tokens, torch.int32, "tokens"), tokens.numel(),
+        _ptr(state, torch.int32, "state", STATE_WORDS), int(ngram_max), _ptr(drafts, torch.int32, "drafts", K),
+        _ptr(window, torch.float16, "window"), _ptr(ws, torch.uint8, "workspace"), ws.numel(), _stream(stream)))
+
+
+def generate_tree(wq, wscale, table, tokens, state, parents, drafts, window, argmax, ws, rounds: int,
+                  ngram_max: int = 3, branches: int = 2, depth: int = 4, stream=None) -> None:
+    """``rounds`` device-resident tree rounds: gather the node rows, verify, walk, draft the next tree."""
+    V, H = wq.shape
+    K = drafts.numel()
+    if (tuple(table.shape) != (V, H) or tuple(window.shape) != (K + 1, H) or tuple(wscale.shape) != (V, H // SV_BLOCK)
+            or parents.numel() != K):
+        raise ValueError("shape mismatch")
+    _check(load().specverify_generate_tree(
+        _ptr(wq, torch.int8, "wq"), _ptr(wscale, torch.float16, "wscale"), V, H, _ptr(table, torch.float16, "table"),
+        K, int(rounds), _ptr(tokens, torch.int32, "tokens"), tokens.numel(),
+        _ptr(state, torch.int32, "state", STATE_WORDS), int(ngram_max), int(branches), int(depth),
+        _ptr(parents, torch.int32, "parents", K), _ptr(drafts, torch.int32, "drafts", K),
         _ptr(window, torch.float16, "window"), _ptr(argmax, torch.int32, "argmax", K + 1),
         _ptr(ws, torch.uint8, "workspace"), ws.numel(), _stream(stream)))
 
