@@ -91,3 +91,39 @@ def test_round_argmax_matches_oracle_and_workspace_is_shared_across_window_sizes
         L = oracle.head_logits(q, s, hidden[r])
         check_argmax(am.cpu().numpy(), L)
         assert int(a1[0]) == int(am[0]) or oracle.top2_gap(L)[0] < 1e-3
+
+
+@pytest.mark.parametrize("ctx_len", [16380, 32755, 40000])
+def test_round_long_streams_equal_separate_calls(ctx_len):
+    """Streams around the round tail's LDS copy (32768 ids): below it, growing across it
+    within the rounds, and above it (the tail's global-memory path).  The fused round against
+    the separate calls, and the last drafts against the oracle's drafter."""
+    V, H, K = 5000, 512, 8
+    S = K + 1
+    say(f"round long stream {ctx_len}")
+    rng = np.random.default_rng(ctx_len)
+    q, s = synth.quantized_head(np.random.SeedSequence(ctx_len), V, H)
+    ctx, _ = synth.zipf_context_with_copies(rng, ctx_len, V, 0.3)
+    wq, ws = to_dev(q), to_dev(s)
+    cap = ctx_len + 400
+    t_ref, st_ref = _state_tokens(ctx, cap)
+    t_f, st_f = _state_tokens(ctx, cap)
+    d_ref = torch.empty(K, dtype=torch.int32, device=dev())
+    d_f = torch.empty(K, dtype=torch.int32, device=dev())
+    a_ref = torch.empty(S, dtype=torch.int32, device=dev())
+    a_f = torch.empty(S, dtype=torch.int32, device=dev())
+    work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev())
+    sv.propose(t_ref, st_ref, d_ref)
+    sv.propose(t_f, st_f, d_f)
+    for r in range(25):
+        hd = to_dev(synth.fp16_normal(rng, (S, H)))
+        sv.verify(wq, ws, hd, a_ref, work)
+        sv.accept(a_ref, d_ref, t_ref, st_ref)
+        sv.propose(t_ref, st_ref, d_ref)
+        sv.round(wq, ws, hd, d_f, t_f, st_f, d_f, a_f, work)
+        torch.cuda.synchronize()
+        assert torch.equal(a_f, a_ref) and torch.equal(d_f, d_ref), r
+        assert torch.equal(st_f, st_ref) and torch.equal(t_f, t_ref), r
+    n = int(st_f[sv.STATE_LEN])
+    assert n >= ctx_len + 25 and int(st_f[sv.STATE_FLAGS]) == 0
+    assert d_f.cpu().tolist() == list(oracle.propose_scan(t_f[:n].cpu().tolist(), 3, K)[0])

@@ -165,14 +165,19 @@ def test_accept_sample_matches_oracle_decisions():
     assert kept_total > 0 and rejected_total > 0
 
 
-def test_round_sample_equals_separate_calls():
+@pytest.mark.parametrize("ctx_len", [600, 32755, 40000])
+def test_round_sample_equals_separate_calls(ctx_len):
+    """The fused sampling round against the separate calls, for streams below the round tail's
+    LDS copy (32768 ids), growing across it within the rounds, and above it (the tail's
+    global-memory path)."""
     V, H, K, T = 5000, 1024, 8, 0.9
     S = K + 1
+    say(f"round_sample vs separate calls, context {ctx_len}")
     rng = np.random.default_rng(12)
     q, s = head(5, V, H)
     wq, ws = to_dev(q), to_dev(s)
-    ctx = synth.zipf_context_with_copies(np.random.default_rng(3), 600, V, 0.3)[0].astype(np.int32)
-    cap = 2000
+    ctx = synth.zipf_context_with_copies(np.random.default_rng(3), ctx_len, V, 0.3)[0].astype(np.int32)
+    cap = ctx_len + 1400
     work = sv.workspace(sv.sample_workspace_bytes(V, H, S), dev())
 
     def fresh():

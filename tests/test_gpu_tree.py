@@ -26,7 +26,7 @@ def _state(n):
 @pytest.mark.parametrize("n,vocab,nmax,K,B,D", [
     (1, 5, 3, 8, 2, 4), (2, 2, 3, 4, 4, 4), (40, 3, 3, 15, 4, 5), (300, 6, 3, 15, 3, 15),
     (300, 4, 2, 8, 1, 8), (513, 10, 4, 12, 4, 3), (4096, 50, 3, 15, 4, 6), (16000, 8, 3, 15, 2, 7),
-    (20000, 5, 3, 10, 4, 10),            # longer than the LDS copy: the global-memory path
+    (20000, 5, 3, 10, 4, 10), (33000, 7, 3, 12, 3, 6),   # the last is longer than the LDS copy: global memory
 ])
 def test_propose_tree_matches_oracle(n, vocab, nmax, K, B, D):
     rng = np.random.default_rng(n + K + B)
@@ -108,14 +108,18 @@ def test_accept_tree_capacity_overflow_writes_nothing():
     assert tokens.cpu().tolist() == [-5] * 8
 
 
-def test_round_tree_equals_separate_calls():
+@pytest.mark.parametrize("ctx_len", [600, 32755, 40000])
+def test_round_tree_equals_separate_calls(ctx_len):
+    """The fused tree round against the separate calls, for streams below the tail's LDS copy
+    (32768 ids), growing across it within the rounds, and above it (global memory)."""
     V, H, K, B, D = 5000, 1024, 8, 3, 4
     S = K + 1
+    say(f"round_tree vs separate calls, context {ctx_len}")
     rng = np.random.default_rng(12)
     q, s = synth.quantized_head(np.random.SeedSequence(5), V, H)
     wq, ws = to_dev(q), to_dev(s)
-    ctx = synth.zipf_context_with_copies(np.random.default_rng(3), 600, V, 0.3)[0].astype(np.int32)
-    cap = 2000
+    ctx = synth.zipf_context_with_copies(np.random.default_rng(3), ctx_len, V, 0.3)[0].astype(np.int32)
+    cap = ctx_len + 1400
     work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev())
 
     def fresh():

@@ -661,7 +661,7 @@ __global__ __launch_bounds__(256) void combine_kernel(GemmArgs a) {
 // so the tail costs about one memory round trip; accept and drafter then work from LDS.
 // A kernel boundary, not a device-scope fence in every matmul workgroup, orders the partials.
 constexpr int kTailThreads = 1024;
-constexpr int kTailIds = 16384;                      // stream ids the tail can hold in LDS
+constexpr int kTailIds = 32768;                      // stream ids the tail can hold in LDS (128 KB)
 
 __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* __restrict__ pv,
                                                                   const int* __restrict__ pi, int nparts, int S,
@@ -685,7 +685,7 @@ __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* _
     // the stream goes to LDS once the partials are reduced.
     int len0 = 0, d = -1;
     bool in_lds = false;
-    IdPrefix pre;
+    IdPrefix<kTailIds / (4 * kTailThreads)> pre;
     const int navail = round ? (cap < kTailIds ? cap : kTailIds) : 0;
     const bool vec = round && (reinterpret_cast<uintptr_t>(tokens) & 15) == 0;
     if (vec) prefix_load(tokens, navail, pre);

@@ -23,7 +23,7 @@ namespace sv {
 namespace {
 
 constexpr int kTailThreads = 1024;
-constexpr int kTailIds = 16384;                      // stream ids the tail can hold in LDS
+constexpr int kTailIds = 32768;                      // stream ids the tail can hold in LDS (128 KB)
 
 // Reduce row s's partials: the best (key, id), lowest id on equal keys, and the merged
 // log-sum-exp state.  Each lane folds its partials in increasing order, then the wave folds
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kTailThreads) void sample_tail_kernel(
     // the stream's first min(cap, kTailIds) ids are loaded with the partials, whatever its length
     int len0 = 0;
     bool in_lds = false;
-    IdPrefix pre;
+    IdPrefix<kTailIds / (4 * kTailThreads)> pre;
     const int navail = round ? (cap < kTailIds ? cap : kTailIds) : 0;
     const bool vec = round && (reinterpret_cast<uintptr_t>(tokens) & 15) == 0;
     if (vec) prefix_load(tokens, navail, pre);

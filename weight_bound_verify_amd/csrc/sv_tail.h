@@ -43,29 +43,33 @@ __device__ __forceinline__ void stage_ids(const int32_t* __restrict__ src, int n
 }
 
 // The first n ids of a 16-byte aligned stream held in registers by a whole workgroup (n <=
-// 16 ids per thread): thread t holds 16-byte pieces t, t + nt, t + 2 nt, t + 3 nt.  Loading
+// 4 NP ids per thread): thread t holds 16-byte pieces t, t + nt, ..., t + (NP-1) nt.  Loading
 // them does not depend on the stream length, so a round tail issues these loads together with
 // its other independent loads and stores them to LDS afterwards.
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
-struct IdPrefix { i32x4_t v[4]; };
+template <int NP>
+struct IdPrefix { i32x4_t v[NP]; };
 
-__device__ __forceinline__ void prefix_load(const int32_t* __restrict__ src, int n, IdPrefix& p) {
+template <int NP>
+__device__ __forceinline__ void prefix_load(const int32_t* __restrict__ src, int n, IdPrefix<NP>& p) {
     const int tid = threadIdx.x, nt = blockDim.x;
     const int n4 = n >> 2;
     const i32x4_t* s4 = reinterpret_cast<const i32x4_t*>(src);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NP; ++u) {
         const int i = u * nt + tid;
         p.v[u] = i < n4 ? s4[i] : i32x4_t{0, 0, 0, 0};
     }
 }
 
-__device__ __forceinline__ void prefix_store(const int32_t* __restrict__ src, int n, const IdPrefix& p, int32_t* dst) {
+template <int NP>
+__device__ __forceinline__ void prefix_store(const int32_t* __restrict__ src, int n, const IdPrefix<NP>& p,
+                                             int32_t* dst) {
     const int tid = threadIdx.x, nt = blockDim.x;
     const int n4 = n >> 2;
     i32x4_t* d4 = reinterpret_cast<i32x4_t*>(dst);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NP; ++u) {
         const int i = u * nt + tid;
         if (i < n4) d4[i] = p.v[u];
     }

@@ -27,7 +27,7 @@ namespace sv {
 namespace {
 
 constexpr int kTreeThreads = 1024;
-constexpr int kTreeIds = 16384;                      // stream ids held in LDS
+constexpr int kTreeIds = 32768;                      // stream ids held in LDS (128 KB)
 constexpr int kMaxBranches = 4;
 
 // Walk down the tree by one wave (lane i holds node i+1).  `am` holds the argmax of every
