@@ -296,8 +296,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(each box has one MI355X); use --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the vocab-sharded head "
+              "and the tensor-parallel stack are a design, not code); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
