@@ -262,3 +262,14 @@ def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(sv, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         sv.load()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: any other count exits with status 2 and says so, before
+    touching torch or the library."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2 and "one GPU" in res.stderr and res.stdout == ""
