@@ -10,7 +10,7 @@ from a token-indexed stand-in model on the device (specverify_generate).  Inputs
 synthetic data resident in HBM before the timed region; hidden rows rotate over 64 sets and, for
 heads that could sit in the 256 MB Infinity Cache, over several copies of the weights.
 
-Prints one JSON line.  --gpus N with N > 1 is not supported (one GPU per box).
+Prints one JSON line.  --gpus N with N > 1 is refused: the library has no multi-GPU path.
 
 Host-only helpers for the profile summaries (no GPU needed):
   bench.py summarize-trace DB OUT TITLE COMMAND [NOTE]
