@@ -5,8 +5,10 @@ A step is one device-resident verify round through the C ABI entry point specver
   -> greedy accept (commits 1 + j tokens) -> n-gram drafter for the next round
 The dense-stack workload runs 36 x [rmsnorm, gate/up + SiLU*mul, down + residual] and a final
 rmsnorm in front of the head, through specverify_stack; the int4 workload swaps in the int4
-per-block-32 head (specverify_round_q4b32); the generation-loop workload gathers each window
-from a token-indexed stand-in model on the device (specverify_generate).  Inputs are seeded
+per-block-32 head (specverify_round_q4b32); the sampling and tree workloads run
+specverify_round_sample and specverify_round_tree; the generation-loop workload gathers each
+window from a token-indexed stand-in model on the device (specverify_generate).  The roofline
+object times the dominant kernel: the head matmul, or the stack's gate/up projection.  Inputs are seeded
 synthetic data resident in HBM before the timed region; hidden rows rotate over 64 sets and, for
 heads that could sit in the 256 MB Infinity Cache, over several copies of the weights.
 
