@@ -5,8 +5,12 @@
  *   specverify_propose  n-gram prompt-lookup drafter over the committed token stream
  *   specverify_verify   int8 per-block-32 head matmul of the S = K+1 window + per-row argmax
  *   specverify_accept   greedy longest-prefix acceptance, commits 1 + j tokens
+ *   specverify_round    the three fused: verify -> accept -> the next drafts
  *   specverify_*_sample sampling verify at temperature > 0 (probabilities, residual redraw)
  *   specverify_*_tree   tree drafts (merged n-gram matches) and the greedy walk down the tree
+ *   specverify_*_q4b32  the same head with int4 per-block-32 codes
+ *   specverify_generate[_sample|_tree]  many rounds back to back on the device, window rows
+ *                       gathered from a token-indexed stand-in model (specverify_gather_window)
  * plus the dense weight-bound stack in front of the head (rmsnorm, gate/up + SiLU*mul,
  * down + residual) built on the same int8 matmul core.
  *
