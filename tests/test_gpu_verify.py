@@ -190,3 +190,27 @@ def test_verify_17_rows_both_kernels_agree(H):
     check_logits(l2, L)
     check_argmax(a1, L)
     check_argmax(a2, L)
+
+
+@pytest.mark.parametrize("V,H,S", [(20000, 2048, 9), (900, 16384, 40)])
+def test_timing_hook_brackets_exactly_one_matmul(V, H, S):
+    """specverify_profile_next_matmul attaches the caller's events to the next matmul's dispatch
+    (through the combine pass when the hidden axis is split, the second shape): both events
+    complete with a positive duration, the results are those of an untimed call, and the hook
+    is consumed, so the next call runs untimed."""
+    q, s = head(23, V, H)
+    hidden = to_dev(synth.fp16_normal(np.random.default_rng(9), (S, H)))
+    wq, ws = to_dev(q), to_dev(s)
+    work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev())
+    a0 = torch.empty(S, dtype=torch.int32, device=dev())
+    a1 = torch.empty(S, dtype=torch.int32, device=dev())
+    a2 = torch.empty(S, dtype=torch.int32, device=dev())
+    sv.verify(wq, ws, hidden, a0, work)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sv.profile_next_matmul(e0, e1)
+    sv.verify(wq, ws, hidden, a1, work)
+    sv.verify(wq, ws, hidden, a2, work)                  # the hook is spent: untimed
+    torch.cuda.synchronize()
+    assert e0.query() and e1.query()
+    assert e0.elapsed_time(e1) > 0.0
+    assert torch.equal(a0, a1) and torch.equal(a0, a2)
