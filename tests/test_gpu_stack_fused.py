@@ -189,3 +189,29 @@ def test_stack_eps_and_zero_rows():
         m = oracle.mlp_block(prev, layers[li], eps=1e-3, return_parts=True)[1]["m"]
         _check_f16(xl[li], prev.astype(np.float64) + oracle.linear_q8b32(*layers[li][2], m))
         prev = xl[li]
+
+
+def test_stack_timing_hook_times_the_first_gate_up():
+    """specverify_profile_next_matmul before specverify_stack attaches the events to block 0's
+    gate/up launch: both complete with a positive duration shorter than the whole call, and
+    every output is bit-identical to an untimed call."""
+    rng = np.random.default_rng(15)
+    H, F, S, L = 1024, 2048, 9, 4
+    _, mats = _stacked(rng, L, H, F)
+    x = synth.fp16_normal(rng, (S, H))
+    ref = _run(mats, x, L)
+    dm = [to_dev(m) for m in mats]
+    xd = to_dev(x)
+    xl = torch.empty((L, S, H), dtype=torch.float16, device=dev())
+    nrm = torch.empty((S, H), dtype=torch.float16, device=dev())
+    ws = sv.workspace(sv.stack_forward_workspace_bytes(H, F, S), dev())
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sv.profile_next_matmul(e0, e1)
+    a.record()
+    sv.stack(*dm, xd, nrm, ws, 1e-6, x_layers=xl)
+    b.record()
+    torch.cuda.synchronize()
+    t_gu, t_all = e0.elapsed_time(e1), a.elapsed_time(b)
+    assert 0.0 < t_gu < t_all
+    assert np.array_equal(xl.cpu().numpy(), ref[1]) and np.array_equal(nrm.cpu().numpy(), ref[2])
