@@ -293,9 +293,7 @@ struct FastRegs {
 // XR > 0 (head, MT = 1; instantiated for XR = 1): window rows 16 .. 16+XR-1 beyond the MFMA tile.  Each wave keeps its
 // blocks of them in LDS; per block a second MFMA takes the extra row, read from LDS as a
 // broadcast, as all 16 of its A rows against the same codes, so each lane receives the row's
-// full dot product with its vocab row, and adds it times the block scale.  (Shapes that also
-// hold window blocks in LDS would spill with the MFMA's result registers; they take the dot
-// product of each lane's 8 elements with v_dot2 and fold the four k groups.)  A window of
+// full dot product with its vocab row, and adds it times the block scale.  A window of
 // 17 .. 16+XR rows then needs the registers of a 16-row one and no split of the hidden axis.
 // The waves' partials are folded in a fixed order by wave 1 + r for extra row r, which also
 // keeps that row's running argmax.
@@ -307,7 +305,6 @@ template <int MT, int NBW, int NW, int EPI, int XR = 0, int HL = 0>
 __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
     constexpr int NSEG = NBW / 4;
     constexpr int HR = NBW - HL;                      // blocks whose window rows stay in registers
-    constexpr bool kXrMfma = HL == 0;                 // extra rows by MFMA (LDS-held shapes: by v_dot2, to fit)
     static_assert(NBW % 4 == 0, "whole 128-byte segments");
     static_assert(XR == 0 || (MT == 1 && EPI == EPI_HEAD && XR < NW), "extra rows extend a one-tile head");
     static_assert(HL == 0 || (MT == 1 && HL < NBW), "LDS-held blocks of a one-tile window");
@@ -423,41 +420,22 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
                 if constexpr (XR > 0) {
 #pragma unroll
                     for (int r = 0; r < XR; ++r) {
+                        // extra row r repeated on all 16 A rows: every output row of this MFMA is
+                        // its full 32-element dot with vocab row n, summed over the k groups
                         const f16x8 xv = *reinterpret_cast<const f16x8*>(&xl[wave][i][r][8 * g]);
-                        if constexpr (kXrMfma) {
-                            // extra row r repeated on all 16 A rows: every output row of this MFMA
-                            // is its full 32-element dot with vocab row n, summed over the k groups
-                            const f32x4 d2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, b, zero, 0, 0, 0);
-                            xacc[r] = __builtin_fmaf(sc, d2[0], xacc[r]);
-                        } else {
-                            // this lane's 8 elements only (v_dot2); the k groups are folded later
-                            float dt = 0.f;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const f16x2 pa = {b[2 * e], b[2 * e + 1]};
-                                const f16x2 pb = {xv[2 * e], xv[2 * e + 1]};
-                                dt = __builtin_amdgcn_fdot2(pa, pb, dt, false);
-                            }
-                            xacc[r] = __builtin_fmaf(sc, dt, xacc[r]);
-                        }
+                        const f32x4 d2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, b, zero, 0, 0, 0);
+                        xacc[r] = __builtin_fmaf(sc, d2[0], xacc[r]);
                     }
                     if constexpr (NBW >= 16) __builtin_amdgcn_sched_barrier(0);   // bound live temporaries
                 }
             }
         }
         if constexpr (XR > 0) {
-            // lanes n of group 0 hand the wave's partial to LDS (the dot products first fold
-            // the four k groups, lanes n, n+16, n+32, n+48); the item's barrier in red_.run
-            // orders it before the readers
+            // the MFMA already summed the k groups: lanes n of group 0 hand the wave's partial
+            // to LDS; the item's barrier in red_.run orders it before the readers
 #pragma unroll
-            for (int r = 0; r < XR; ++r) {
-                float t = xacc[r];
-                if constexpr (!kXrMfma) {
-                    t += __shfl_xor(t, 16, kWave);
-                    t += __shfl_xor(t, 32, kWave);
-                }
-                if (g == 0) xred[buf][wave][r][n] = t;
-            }
+            for (int r = 0; r < XR; ++r)
+                if (g == 0) xred[buf][wave][r][n] = xacc[r];
         }
         red_.run(a, acc, it, buf, wave, lane, ks);
         if constexpr (XR > 0) {
@@ -799,7 +777,7 @@ KernelFn pick_fast(const GemmCfg& c) {
 #define SV_XR(NBW, NW, XR) \
     if (c.mt == 1 && c.xr == XR && c.nbw == NBW && c.nw == NW) return q8b32_fast<1, NBW, NW, EPI, XR>;
             SV_XR(4, 16, 1) SV_XR(8, 8, 1) SV_XR(16, 8, 1) SV_XR(16, 5, 1) SV_XR(8, 4, 1) SV_XR(4, 4, 1)
-            if (c.mt == 1 && c.xr == 1 && c.nbw == 20 && c.nw == 8) return q8b32_fast<1, 20, 8, EPI, 1, 8>;
+            if (c.mt == 1 && c.xr == 1 && c.nbw == 20 && c.nw == 8) return q8b32_fast<1, 20, 8, EPI, 1, 12>;
 #undef SV_XR
             return nullptr;
         }
