@@ -393,6 +393,14 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
         float xacc[XR ? XR : 1];
 #pragma unroll
         for (int r = 0; r < (XR ? XR : 1); ++r) xacc[r] = 0.f;
+        // without extra rows each block's scale is applied one block later, so no instruction
+        // waits on a just-issued MFMA (the accumulation order is unchanged); with them the extra
+        // row's MFMA already fills that gap, and the delay measured slower
+        constexpr bool kDelay = XR == 0;
+        f32x4 dprev[MT];
+        float scprev = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) dprev[mt] = zero;
 #pragma unroll
         for (int t = 0; t < NSEG; ++t) {
             // exchange one segment: tile row r lands at r*128, 16-byte chunks XOR-swizzled by row
@@ -414,8 +422,14 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
                     const f16x8 aop = i < HR ? hid[i < HR ? i : 0][mt]
                                              : *reinterpret_cast<const f16x8*>(&xh[wave][i >= HR ? i - HR : 0][n][8 * g]);
                     const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, b, zero, 0, 0, 0);
+                    if constexpr (kDelay) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[mt][r] = __builtin_fmaf(sc, d[r], acc[mt][r]);
+                        for (int r = 0; r < 4; ++r) acc[mt][r] = __builtin_fmaf(scprev, dprev[mt][r], acc[mt][r]);
+                        dprev[mt] = d;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[mt][r] = __builtin_fmaf(sc, d[r], acc[mt][r]);
+                    }
                 }
                 if constexpr (XR > 0) {
 #pragma unroll
@@ -428,7 +442,14 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
                     }
                     if constexpr (NBW >= 16) __builtin_amdgcn_sched_barrier(0);   // bound live temporaries
                 }
+                scprev = sc;
             }
+        }
+        if constexpr (kDelay) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[mt][r] = __builtin_fmaf(scprev, dprev[mt][r], acc[mt][r]);
         }
         if constexpr (XR > 0) {
             // the MFMA already summed the k groups: lanes n of group 0 hand the wave's partial
