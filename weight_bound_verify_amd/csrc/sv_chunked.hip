@@ -288,6 +288,10 @@ __global__ __launch_bounds__(NW * 64) void q8b32_chunked(ChunkArgs a) {
             const int row = 8 * h + lrow;
             *reinterpret_cast<u32x4*>(xs + row * 128 + 16 * (lchunk ^ (row & 7))) = cur.w[h];
         }
+        // each block's scale is applied one block later (the last one after the loop), so no
+        // instruction waits on a just-issued MFMA; the accumulation order is unchanged
+        f32x4 dprev = zero;
+        float scprev = 0.f;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int chunk = 2 * b + (g >> 1);
@@ -296,10 +300,16 @@ __global__ __launch_bounds__(NW * 64) void q8b32_chunked(ChunkArgs a) {
             const u32x2 scw = EPI == EPI_GATEUP ? (cur.sc | cur.sc2) : cur.sc;
             const float sc = h2f((uint16_t)(scw[b >> 1] >> (16 * (b & 1))));
             const f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(aops[b], bop, zero, 0, 0, 0);
+            if (b > 0) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(sc, dd[r], acc[r]);
+                for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(scprev, dprev[r], acc[r]);
+            }
+            dprev = dd;
+            scprev = sc;
             if constexpr (NW == 16) __builtin_amdgcn_sched_barrier(0);   // bound live temporaries at 16 waves
         }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(scprev, dprev[r], acc[r]);
     };
 
     if constexpr (HOLD > 0) {
