@@ -93,8 +93,12 @@ __device__ __forceinline__ unsigned long long scan_best_lds(const int32_t* tk, i
         int32_t w[NM + 4];                                      // ids e0 - NM .. e0 + 3
 #pragma unroll
         for (int q = 0; q < NM / 4 + 1; ++q) {
-            const int vi = gi - NM / 4 + q;                     // vector index
-            const i32x4 v = vi >= 0 ? t4[vi] : i32x4{INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+            // every read stays inside the array (the index is clamped, then the sentinel
+            // replaces what precedes the stream): a read below it through a generic pointer
+            // would leave the LDS window
+            const int vi = gi - NM / 4 + q;
+            i32x4 v = t4[vi < 0 ? 0 : vi];
+            if (vi < 0) v = i32x4{INT_MIN, INT_MIN, INT_MIN, INT_MIN};
 #pragma unroll
             for (int c = 0; c < 4; ++c) w[4 * q + c] = v[c];
         }

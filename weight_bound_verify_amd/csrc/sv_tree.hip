@@ -70,36 +70,88 @@ __device__ __forceinline__ int accept_tree_wave(const int32_t* am, const int32_t
     return j;
 }
 
-// Block-wide maximum of one 64-bit key per thread; every thread gets the result.
-__device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v, unsigned long long* wslot,
-                                                            unsigned long long* result) {
+// Insert key k into a descending list of kMaxBranches keys (keys are distinct).
+__device__ __forceinline__ void top_insert(unsigned long long (&top)[kMaxBranches], unsigned long long k) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const unsigned long long o = __shfl_xor(v, off, 64);
-        v = o > v ? o : v;
-    }
-    const int tid = threadIdx.x;
-    if ((tid & 63) == 0) wslot[tid >> 6] = v;
-    __syncthreads();
-    if (tid < kWave) {
-        unsigned long long b = tid < (int)(blockDim.x / kWave) ? wslot[tid] : 0ull;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const unsigned long long o = __shfl_xor(b, off, 64);
-            b = o > b ? o : b;
-        }
-        if (tid == 0) *result = b;
-    }
-    __syncthreads();
-    return *result;
+    for (int b = 0; b < kMaxBranches; ++b)
+        if (k > top[b]) { const unsigned long long t = top[b]; top[b] = k; k = t; }
 }
 
-// Tree drafter over the stream `st[0 .. len)` (LDS or global memory), whole workgroup.
-// `keys` (LDS, kMaxBranches + 1 entries) and `wslot` (one per wave) are scratch.
-__device__ __forceinline__ void propose_tree_block(const int32_t* st, int len, int nmax, int K, int branches,
-                                                   int depth, int32_t* parents_out, int32_t* drafts_out,
-                                                   int32_t* state, bool gated, unsigned long long* keys,
-                                                   unsigned long long* wslot) {
+// This thread's four best keys (l << 32 | e) over the end positions e < len - 1 of a stream in
+// LDS (`tk`, 16-byte aligned): groups of four end positions from 16-byte reads, as the linear
+// drafter's scan (NM = 4 covers nmax <= 4, NM = 8 the rest).
+template <int NM>
+__device__ __forceinline__ void scan_top_lds(const int32_t* tk, int len, int nmax, const int32_t (&suf)[SV_MAX_NGRAM],
+                                             unsigned long long (&top)[kMaxBranches]) {
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4* t4 = reinterpret_cast<const i32x4*>(tk);
+    const int ngroups = (len - 1 + 3) >> 2;
+    for (int gi = threadIdx.x; gi < ngroups; gi += blockDim.x) {
+        const int e0 = gi << 2;
+        int32_t w[NM + 4];
+#pragma unroll
+        for (int q = 0; q < NM / 4 + 1; ++q) {
+            // every read stays inside the array (the index is clamped, then the sentinel
+            // replaces what precedes the stream): a read below it through a generic pointer
+            // would leave the LDS window
+            const int vi = gi - NM / 4 + q;
+            i32x4 v = t4[vi < 0 ? 0 : vi];
+            if (vi < 0) v = i32x4{INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) w[4 * q + c] = v[c];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = e0 + j;
+            int l = 0;
+            bool run = true;
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                run = run && i < nmax && w[NM + j - i] == suf[i];
+                l += run ? 1 : 0;
+            }
+            if (l > 0 && e < len - 1) top_insert(top, ((unsigned long long)l << 32) | (unsigned)e);
+        }
+    }
+}
+
+// The same over a stream in global memory, one end position per thread and step.
+__device__ __forceinline__ void scan_top_global(const int32_t* st, int len, int nmax,
+                                                const int32_t (&suf)[SV_MAX_NGRAM],
+                                                unsigned long long (&top)[kMaxBranches]) {
+    for (int e = threadIdx.x; e < len - 1; e += blockDim.x) {
+        int l = 0;
+#pragma unroll
+        for (int i = 0; i < SV_MAX_NGRAM; ++i)
+            if (l == i && i < nmax && e - i >= 0 && st[e - i] == suf[i]) l = i + 1;
+        if (l > 0) top_insert(top, ((unsigned long long)l << 32) | (unsigned)e);
+    }
+}
+
+// The best `branches` of 64 candidate keys (one per lane; distinct or zero), in order, by
+// `branches` wave maxima each below the previous one; every lane gets them.
+__device__ __forceinline__ void wave_top(unsigned long long cand, int branches, unsigned long long (&out)[kMaxBranches]) {
+    unsigned long long thr = ~0ull;
+#pragma unroll
+    for (int b = 0; b < kMaxBranches; ++b) {
+        unsigned long long v = b < branches && cand < thr ? cand : 0ull;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const unsigned long long o = __shfl_xor(v, off, 64);
+            v = o > v ? o : v;
+        }
+        out[b] = b < branches ? v : 0ull;
+        thr = v;
+    }
+}
+
+// Tree drafter over the stream `st[0 .. len)` (LDS when `in_lds`, else global memory), whole
+// workgroup.  `keys` (LDS, kMaxBranches + 1 entries) and `wkeys` (kMaxBranches per wave) are
+// scratch.
+__device__ __forceinline__ void propose_tree_block(const int32_t* st, bool in_lds, int len, int nmax, int K,
+                                                   int branches, int depth, int32_t* parents_out,
+                                                   int32_t* drafts_out, int32_t* state, bool gated,
+                                                   unsigned long long* keys, unsigned long long* wkeys) {
     const int tid = threadIdx.x;
     if (gated) {
         if (tid < K) { parents_out[tid] = 0; drafts_out[tid] = -1; }
@@ -111,39 +163,54 @@ __device__ __forceinline__ void propose_tree_block(const int32_t* st, int len, i
     for (int i = 0; i < SV_MAX_NGRAM; ++i) suf[i] = (i < nmax && len - 1 - i >= 0) ? st[len - 1 - i] : -1;
     // the four best keys (l << 32 | e) of this thread's end positions, best first
     unsigned long long top[kMaxBranches] = {0ull, 0ull, 0ull, 0ull};
-    for (int e = tid; e < len - 1; e += blockDim.x) {
-        int l = 0;
+    if (in_lds) {
+        if (nmax <= 4) scan_top_lds<4>(st, len, nmax, suf, top);
+        else scan_top_lds<8>(st, len, nmax, suf, top);
+    } else {
+        scan_top_global(st, len, nmax, suf, top);
+    }
+    // the global best `branches` keys: the wave's best from its lanes' lists (the best b of a
+    // set lie among the best b of every part), one barrier, then wave 0 over the waves' lists
+    const int lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x / kWave;
+    unsigned long long wbest[kMaxBranches];
+    {
+        // lane candidates: its own list, merged round by round below the previous maximum
+        unsigned long long thr = ~0ull;
 #pragma unroll
-        for (int i = 0; i < SV_MAX_NGRAM; ++i)
-            if (l == i && i < nmax && e - i >= 0 && st[e - i] == suf[i]) l = i + 1;
-        if (l > 0) {
-            unsigned long long k = ((unsigned long long)l << 32) | (unsigned)e;
+        for (int b = 0; b < kMaxBranches; ++b) {
+            unsigned long long mine = 0ull;
 #pragma unroll
-            for (int b = 0; b < kMaxBranches; ++b) {       // sorted insertion
-                if (k > top[b]) { const unsigned long long t = top[b]; top[b] = k; k = t; }
+            for (int r = 0; r < kMaxBranches; ++r)
+                if (top[r] < thr && top[r] > mine) mine = top[r];
+            unsigned long long v = b < branches ? mine : 0ull;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const unsigned long long o = __shfl_xor(v, off, 64);
+                v = o > v ? o : v;
             }
+            wbest[b] = v;
+            thr = v;
         }
     }
-    // the global best `branches` keys: each round takes the largest key below the previous one
-    unsigned long long thr = ~0ull;
-    for (int b = 0; b < branches; ++b) {
-        unsigned long long mine = 0ull;
+    if (lane < kMaxBranches) {
+        unsigned long long v = 0ull;
 #pragma unroll
-        for (int t = kMaxBranches - 1; t >= 0; --t)
-            if (top[t] < thr && top[t] > mine) mine = top[t];
-        const unsigned long long best = block_max_u64(mine, wslot, &keys[kMaxBranches]);
-        if (tid == 0) keys[b] = best;
-        thr = best;
-        if (best == 0ull) {                             // no further match (uniform)
-            if (tid == 0)
-                for (int r = b + 1; r < branches; ++r) keys[r] = 0ull;
-            break;
-        }
+        for (int b = 0; b < kMaxBranches; ++b)
+            if (b == lane) v = wbest[b];
+        wkeys[wave * kMaxBranches + lane] = v;
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        const unsigned long long cand = tid < nwaves * kMaxBranches ? wkeys[tid] : 0ull;
+        unsigned long long best[kMaxBranches];
+        wave_top(cand, branches, best);
+        if (tid == 0)
+#pragma unroll
+            for (int b = 0; b < kMaxBranches; ++b) keys[b] = best[b];
     }
     __syncthreads();
     if (tid >= kWave) return;
     // wave 0: lane = branch * 16 + depth slot
-    const int lane = tid;
     const int b = lane >> 4, d = lane & 15;
     int e[kMaxBranches], clen[kMaxBranches];
 #pragma unroll
@@ -220,23 +287,32 @@ __global__ __launch_bounds__(kTreeThreads) void tree_tail_kernel(
     const int32_t* __restrict__ parents_in, const int32_t* __restrict__ drafts_in, int32_t* __restrict__ tokens,
     int cap, int32_t* __restrict__ state, int nmax, int branches, int depth, int32_t* __restrict__ parents_out,
     int32_t* __restrict__ drafts_out) {
-    __shared__ __attribute__((aligned(16))) int32_t tk[kTreeIds];
+    __shared__ __attribute__((aligned(16))) int32_t tk[kTreeIds + 8];    // + group reads past the end
     __shared__ int32_t am[16];
     __shared__ int new_len;
     __shared__ int gated_s;
     __shared__ unsigned long long keys[kMaxBranches + 1];
-    __shared__ unsigned long long wslot[kTreeThreads / kWave];
+    __shared__ unsigned long long wkeys[kMaxBranches * (kTreeThreads / kWave)];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int K = S - 1;
+    // every independent load first: the stream's first min(cap, kTreeIds) ids (whatever its
+    // length), the state and the partials; the stream goes to LDS once the partials are reduced
+    IdPrefix<kTreeIds / (4 * kTreeThreads)> pre;
+    const int navail = cap < kTreeIds ? cap : kTreeIds;
+    const bool vec = (reinterpret_cast<uintptr_t>(tokens) & 15) == 0;
+    if (vec) prefix_load(tokens, navail, pre);
     const int len0 = state[SV_STATE_LEN];
     StateCache sc{0, 0};
     if (wave == 0) sc = state_cache_load(state, lane);
     const bool in_lds = len0 >= 0 && len0 + K + 1 <= cap && len0 + K + 1 <= kTreeIds;
-    if (in_lds) stage_ids(tokens, len0, tk);
     for (int s = wave; s < S; s += kTreeThreads / kWave) {
         const int bi = reduce_argmax_row(pv, pi, nparts, s, lane);
         if (lane == 0) { argmax[s] = bi; am[s] = bi; }
+    }
+    if (in_lds) {
+        if (vec) prefix_store(tokens, navail, pre, tk);
+        else stage_ids(tokens, len0, tk);
     }
     __syncthreads();
     if (wave == 0) {
@@ -261,7 +337,8 @@ __global__ __launch_bounds__(kTreeThreads) void tree_tail_kernel(
             len = 0;
         }
     }
-    propose_tree_block(st, len, nmax, K, branches, depth, parents_out, drafts_out, state, gated_s != 0, keys, wslot);
+    propose_tree_block(st, in_lds, len, nmax, K, branches, depth, parents_out, drafts_out, state, gated_s != 0, keys,
+                       wkeys);
 }
 
 __global__ __launch_bounds__(kTreeThreads) void propose_tree_kernel(const int32_t* __restrict__ tokens, int cap,
@@ -269,9 +346,9 @@ __global__ __launch_bounds__(kTreeThreads) void propose_tree_kernel(const int32_
                                                                    int branches, int depth,
                                                                    int32_t* __restrict__ parents_out,
                                                                    int32_t* __restrict__ drafts_out) {
-    __shared__ __attribute__((aligned(16))) int32_t tk[kTreeIds];
+    __shared__ __attribute__((aligned(16))) int32_t tk[kTreeIds + 8];    // + group reads past the end
     __shared__ unsigned long long keys[kMaxBranches + 1];
-    __shared__ unsigned long long wslot[kTreeThreads / kWave];
+    __shared__ unsigned long long wkeys[kMaxBranches * (kTreeThreads / kWave)];
     int len = state[SV_STATE_LEN];
     const bool gated = state[SV_STATE_GATED] != 0;
     if (len < 0 || len > cap) {
@@ -279,12 +356,13 @@ __global__ __launch_bounds__(kTreeThreads) void propose_tree_kernel(const int32_
         len = 0;
     }
     const int32_t* st = tokens;
-    if (len <= kTreeIds) {
+    const bool in_lds = len <= kTreeIds;
+    if (in_lds) {
         stage_ids(tokens, len, tk);
         __syncthreads();
         st = tk;
     }
-    propose_tree_block(st, len, nmax, K, branches, depth, parents_out, drafts_out, state, gated, keys, wslot);
+    propose_tree_block(st, in_lds, len, nmax, K, branches, depth, parents_out, drafts_out, state, gated, keys, wkeys);
 }
 
 __global__ __launch_bounds__(kWave) void accept_tree_kernel(const int32_t* __restrict__ argmax,
