@@ -22,8 +22,8 @@
 // The block scale is applied to the MFMA result one block later, so no instruction waits on
 // a just-issued MFMA.  A workgroup owns 16 vocab rows at a time; its NW waves split the
 // hidden axis (NBW blocks each) and reduce through LDS in a fixed order; wave w then keeps the
-// running (value, lowest index) of window rows w, w + NW, ...  The next item's loads are
-// issued before the current item's math.
+// running (value, lowest index) of window rows w, w + NW, ...  The next two items' loads are
+// in flight during the current item's math.
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -184,17 +184,23 @@ __global__ __launch_bounds__(NW * 64) void q4b32_head(Q4Args a) {
 
     const int step = gridDim.x;
     const int last = a.nitems - 1;
-    Q4Regs<NBW> ra, rb;
-    int it = blockIdx.x;
+    // three register sets: two items' loads stay in flight while one is processed
+    Q4Regs<NBW> ra, rb, rc;
+    int it = blockIdx.x, k = 0;
     load(ra, it);
+    load(rb, min(it + step, last));
     while (true) {
         if (it >= a.nitems) break;
-        load(rb, min(it + step, last));
-        process(ra, it, 0);
+        load(rc, min(it + 2 * step, last));
+        process(ra, it, k++ & 1);
         it += step;
         if (it >= a.nitems) break;
-        load(ra, min(it + step, last));
-        process(rb, it, 1);
+        load(ra, min(it + 2 * step, last));
+        process(rb, it, k++ & 1);
+        it += step;
+        if (it >= a.nitems) break;
+        load(rb, min(it + 2 * step, last));
+        process(rc, it, k++ & 1);
         it += step;
     }
 #pragma unroll
