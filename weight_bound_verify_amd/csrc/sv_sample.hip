@@ -84,9 +84,9 @@ __global__ __launch_bounds__(kTailThreads) void sample_tail_kernel(
     if (vec) prefix_load(tokens, navail, pre);
     StateCache sc{0, 0};
     if (round) {
-        // every wave holds the state words: the length then arrives as a vector load, which
-        // the partial loads below never wait for (a scalar load would be waited for first)
-        sc = state_cache_load(state, lane);
+        len0 = state[SV_STATE_LEN];
+        if (wave == 0) sc = state_cache_load(state, lane);
+        in_lds = len0 >= 0 && len0 + K + 1 <= cap && len0 + K + 1 <= kTailIds;
     }
     for (int s = wave; s < S; s += kTailThreads / kWave) {
         int draw;
@@ -100,10 +100,8 @@ __global__ __launch_bounds__(kTailThreads) void sample_tail_kernel(
         }
     }
     if (!round) return;
-    len0 = state_word(sc, SV_STATE_LEN);
-    in_lds = len0 >= 0 && len0 + K + 1 <= cap && len0 + K + 1 <= kTailIds;
     if (in_lds) {
-        if (vec) prefix_store(tokens, navail, len0, pre, tk);
+        if (vec) prefix_store(tokens, navail, pre, tk);
         else stage_ids(tokens, len0, tk);
     }
     __syncthreads();

@@ -62,23 +62,18 @@ __device__ __forceinline__ void prefix_load(const int32_t* __restrict__ src, int
     }
 }
 
-// Ids [0, n) of the stream into LDS from the pieces prefix_load fetched for its first n_loaded
-// ids (n <= n_loaded): the whole pieces up to the one holding id n - 1, so up to three ids past
-// n are written as well (dst holds them); ids beyond the last whole piece come from src.
 template <int NP>
-__device__ __forceinline__ void prefix_store(const int32_t* __restrict__ src, int n_loaded, int n,
-                                             const IdPrefix<NP>& p, int32_t* dst) {
+__device__ __forceinline__ void prefix_store(const int32_t* __restrict__ src, int n, const IdPrefix<NP>& p,
+                                             int32_t* dst) {
     const int tid = threadIdx.x, nt = blockDim.x;
-    const int full = n_loaded >> 2;
-    const int need = (n + 3) >> 2;
-    const int np = need < full ? need : full;
+    const int n4 = n >> 2;
     i32x4_t* d4 = reinterpret_cast<i32x4_t*>(dst);
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
         const int i = u * nt + tid;
-        if (i < np) d4[i] = p.v[u];
+        if (i < n4) d4[i] = p.v[u];
     }
-    for (int i = (np << 2) + tid; i < n; i += nt) dst[i] = src[i];
+    for (int i = (n4 << 2) + tid; i < n; i += nt) dst[i] = src[i];
 }
 
 // Best (match length << 32 | end position) over the end positions e < len - 1 of a stream held

@@ -302,17 +302,16 @@ __global__ __launch_bounds__(kTreeThreads) void tree_tail_kernel(
     const int navail = cap < kTreeIds ? cap : kTreeIds;
     const bool vec = (reinterpret_cast<uintptr_t>(tokens) & 15) == 0;
     if (vec) prefix_load(tokens, navail, pre);
-    // every wave holds the state words: the length then arrives as a vector load, which the
-    // partial loads below never wait for (a scalar load would be waited for first)
-    const StateCache sc = state_cache_load(state, lane);
+    const int len0 = state[SV_STATE_LEN];
+    StateCache sc{0, 0};
+    if (wave == 0) sc = state_cache_load(state, lane);
+    const bool in_lds = len0 >= 0 && len0 + K + 1 <= cap && len0 + K + 1 <= kTreeIds;
     for (int s = wave; s < S; s += kTreeThreads / kWave) {
         const int bi = reduce_argmax_row(pv, pi, nparts, s, lane);
         if (lane == 0) { argmax[s] = bi; am[s] = bi; }
     }
-    const int len0 = state_word(sc, SV_STATE_LEN);
-    const bool in_lds = len0 >= 0 && len0 + K + 1 <= cap && len0 + K + 1 <= kTreeIds;
     if (in_lds) {
-        if (vec) prefix_store(tokens, navail, len0, pre, tk);
+        if (vec) prefix_store(tokens, navail, pre, tk);
         else stage_ids(tokens, len0, tk);
     }
     __syncthreads();
