@@ -26,6 +26,7 @@ def _gpu_verify_q4(p, s, hidden, want_logits=True):
 
 
 @pytest.mark.parametrize("V,H,S", [(1, 256, 1), (17, 256, 9), (1000, 512, 9), (4099, 2048, 16), (777, 2560, 5),
+                                   (33, 2048, 9), (16, 4096, 3),
                                    (3000, 4096, 9), (513, 5120, 2), (70000, 1024, 3)])
 def test_verify_q4_matches_oracle(V, H, S):
     say(f"verify q4 V={V} H={H} S={S}")
