@@ -769,17 +769,19 @@ constexpr int kH = 1 << EPI_HEAD, kS = 1 << EPI_STORE, kG = 1 << EPI_GATEUP, kX 
 // preference within each MT; epis = the epilogues that compile for it without spills
 // within the LDS limit
 constexpr Shape kFast[] = {
-    // order = preference where several shapes cover the hidden axis (measured: 8 x 10 beats
-    // 16 x 5 at H = 2560, 16 x 8 and 8 x 16 are even at H = 4096)
-    {1, 4, 16, kH | kS | kG | kX}, {1, 8, 10, kH | kS | kG | kX}, {1, 16, 5, kH | kS | kG | kX},
-    {1, 8, 8, kH | kS | kG | kX}, {1, 16, 8, kH | kS | kG | kX}, {1, 20, 8, kH | kS | kG | kX},
+    // order = preference where several shapes cover the hidden axis (measured: at H = 2048
+    // 8 x 8 beats 4 x 16 for the argmax head, 80.6 against 82.9 us at S = 9, and loses for the
+    // sampling head, 83.9 against 82.3 us; 8 x 10 beats 16 x 5 at H = 2560; 16 x 8 and 8 x 16
+    // are even at H = 4096)
+    {1, 8, 8, kH}, {1, 4, 16, kH | kS | kG | kX}, {1, 8, 8, kS | kG | kX}, {1, 8, 10, kH | kS | kG | kX},
+    {1, 16, 5, kH | kS | kG | kX}, {1, 16, 8, kH | kS | kG | kX}, {1, 20, 8, kH | kS | kG | kX},
     {1, 8, 16, kH | kS}, {1, 16, 4, kH | kS | kG | kX}, {1, 8, 4, kH | kS | kG | kX},
     {1, 4, 4, kH | kS | kG | kX}, {1, 8, 2, kH | kS | kG | kX},
     {2, 8, 8, kH}, {2, 8, 5, kH}, {2, 8, 4, kH}, {2, 4, 4, kH},
     {4, 4, 4, kH},
     // S = 17: the one-tile kernel plus the 17th row's dot products (the shapes that compile
-    // without spills; 20 blocks x 8 waves does not)
-    {1, 4, 16, kH, 1}, {1, 8, 8, kH, 1}, {1, 16, 8, kH, 1}, {1, 16, 5, kH, 1}, {1, 8, 4, kH, 1}, {1, 4, 4, kH, 1},
+    // without spills; 20 blocks x 8 waves does not); 8 x 8 before 4 x 16 as for S <= 16
+    {1, 8, 8, kH, 1}, {1, 4, 16, kH, 1}, {1, 16, 8, kH, 1}, {1, 16, 5, kH, 1}, {1, 8, 4, kH, 1}, {1, 4, 4, kH, 1},
     {1, 20, 8, kH, 1},              // window rows of 8 of the 20 blocks held in LDS
 };
 // generic kernel
