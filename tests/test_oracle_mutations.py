@@ -143,3 +143,35 @@ def test_tree_walk_that_ignores_the_parent_link_is_caught():
         assert oracle.tree_accept(a, parents, drafts)[:2] == good
         caught |= mutant(a, parents, drafts) != good
     assert caught
+
+
+def test_stack_forward_mutants_are_caught():
+    """Three plausible composition mistakes in the stack driver (the last block dropped, the
+    blocks run in reverse, the final norm left out), each caught by the hand-built stack of
+    tests/test_oracle_stack.py (coordinate 2 reached only by A then B; the final norm of e_0 is
+    5.65625)."""
+    from test_oracle_stack import _mover
+    A, B = _mover(0, 1), _mover(1, 2)
+    x = np.zeros((1, 32), np.float16)
+    x[0, 0] = 1
+
+    def drop_last(x16, layers, eps):
+        for layer in layers[:-1]:
+            x16 = oracle.mlp_block(x16, layer, eps)
+        return oracle.rmsnorm_fp16(x16, eps)
+
+    def reversed_order(x16, layers, eps):
+        for layer in layers[::-1]:
+            x16 = oracle.mlp_block(x16, layer, eps)
+        return oracle.rmsnorm_fp16(x16, eps)
+
+    def no_final_norm(x16, layers, eps):
+        for layer in layers:
+            x16 = oracle.mlp_block(x16, layer, eps)
+        return x16
+
+    assert oracle.stack_forward(x, [A, B], eps=0.0)[0, 2] > 0
+    assert drop_last(x, [A, B], 0.0)[0, 2] == 0
+    assert reversed_order(x, [A, B], 0.0)[0, 2] == 0
+    assert oracle.stack_forward(x, [B], eps=0.0)[0, 0] == 5.65625
+    assert no_final_norm(x, [B], 0.0)[0, 0] != 5.65625

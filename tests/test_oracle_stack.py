@@ -74,3 +74,43 @@ def test_stack_forward_stays_finite_with_residual_and_norm():
     out = oracle.stack_forward(x, layers)
     assert np.isfinite(out.astype(np.float64)).all()
     assert np.sqrt(np.mean(out.astype(np.float64) ** 2, axis=1)) == pytest.approx(np.ones(3), abs=5e-3)
+
+
+def _mover(src, dst, up_scale=1.0 / 16):
+    """A 32-wide block whose gate and up rows read only coordinate `src` (codes 1, unit gate
+    scale, up scale `up_scale`) and whose down projection writes m[0] to coordinate `dst`: on
+    an input with x[src] = 0 it is the identity (silu(0) = 0)."""
+    H = F = 32
+    qg = np.zeros((F, H), np.int8); qu = np.zeros((F, H), np.int8); qd = np.zeros((H, F), np.int8)
+    qg[0, src] = 1
+    qu[0, src] = 1
+    qd[dst, 0] = 1
+    ones = np.ones((F, 1), np.float16)
+    return ((qg, ones), (qu, np.full((F, 1), up_scale, np.float16)), (qd, np.ones((H, 1), np.float16)))
+
+
+def test_stack_forward_layer_order_drop_repeat_and_final_norm():
+    """Hand-built stack on x = e_0 (H = 32, eps = 0): A moves coordinate 0 into 1, B moves 1 into
+    2, so B alone is the identity and only A-then-B reaches coordinate 2.  The final weightless
+    norm of e_0 is fp16(sqrt(32)) = 5.65625 at coordinate 0.  A dropped, repeated or reordered
+    layer, or a missing final norm, changes a known entry."""
+    A, B = _mover(0, 1), _mover(1, 2)
+    x = np.zeros((1, 32), np.float16)
+    x[0, 0] = 1
+    run = lambda layers: oracle.stack_forward(x, layers, eps=0.0)[0].astype(np.float64)
+    out_b = run([B])
+    assert out_b[0] == 5.65625 and not out_b[1:].any()          # identity block, then the final norm
+    assert np.array_equal(run([]), out_b)                         # no block: the final norm alone
+    out_a, out_ab, out_ba, out_aa = run([A]), run([A, B]), run([B, A]), run([A, A])
+    assert out_a[1] > 0 and out_a[2] == 0 and not out_a[3:].any()
+    assert np.array_equal(out_ba, out_a)                          # B first sees x[1] = 0
+    assert out_ab[2] > 0 and out_ab[1] > 0                        # A first feeds B
+    assert not np.array_equal(out_ab, out_ba)
+    # a repeated A moves coordinate 0 into 1 twice: a larger share at coordinate 1
+    assert out_aa[1] / out_aa[0] > out_a[1] / out_a[0]
+    # every output row has unit rms (the final norm), up to fp16 rounding
+    for o in (out_a, out_ab, out_aa):
+        assert np.sqrt(np.mean(o * o)) == pytest.approx(1.0, abs=2e-3)
+    # three layers: A, B, then a mover of 2 into 3 reaches coordinate 3 only in that order
+    C = _mover(2, 3)
+    assert run([A, B, C])[3] > 0 and run([A, C, B])[3] == 0 and run([C, A, B])[3] == 0
