@@ -62,7 +62,11 @@ typedef enum {
  *   [2] n_valid  non-pad drafts written by the last specverify_propose
  *   [3] n_used   n-gram order that matched in the last propose (0 = no match)
  *   [4] flags    sticky error bits: bit 0 = a call would have overflowed `cap` or found
- *                len outside [0, cap] (that call wrote no token)
+ *                len outside [0, cap] (that call wrote no token); bit 1 = a gathered token
+ *                id was outside [0, V); bit 2 = the id an accept would commit after the
+ *                accepted drafts was -1, i.e. that window row had no argmax or draw (every
+ *                logit NaN, e.g. from an overflowed activation): that call wrote no token
+ *                and recorded no round
  *   [5] rounds   number of accept calls that committed tokens
  *   [6] sum_j    sum of j over those calls
  *   [7] reserved
@@ -88,6 +92,7 @@ typedef enum {
 #define SV_STATE_GATED 74
 #define SV_FLAG_CAPACITY 1
 #define SV_FLAG_TOKEN 2    /* a token id outside [0, V) was gathered (its row read as zeros) */
+#define SV_FLAG_ARGMAX 4   /* the row whose id would be committed had no argmax (all NaN)    */
 
 /*
  * specverify_propose - n-gram prompt-lookup drafter.
@@ -125,7 +130,8 @@ int specverify_propose(const int32_t* tokens, int32_t cap, int32_t* state, int32
  *
  *   L[s, v]   = sum_b f32(wscale[v, b]) * sum_{k in block b} f32(wq[v, k]) * f32(hidden[s, k])
  *   argmax[s] = min { v : L[s, v] = max_v' L[s, v'] }   (largest logit, lowest id on ties)
- * Products are exact, accumulation is fp32.
+ * Products are exact, accumulation is fp32.  A NaN logit never wins; a row whose logits are
+ * all NaN gets argmax -1, which the accept steps refuse to commit (flag bit 2).
  *   wq        int8 [V][H] row-major (vocab row contiguous), 16-byte aligned
  *   wscale    fp16 [V][H/32] row-major (block b of row v at v*H/32 + b), 16-byte aligned
  *   V         1 .. 2^30;   H: multiple of 32, 32 .. 65536
@@ -444,10 +450,11 @@ int specverify_stack(const int8_t* wg, const uint16_t* sg, const int8_t* wu, con
  * 0 = automatic; a depth that has no kernel for a shape falls back to the automatic one),
  * and the head matmul kernel family (0 = automatic, 1 = one pass per 16-row item, 2 = the
  * chunked ring kernel where the shape allows it, S <= 16, 3 = automatic except that a
- * 17-row window uses two 16-row tiles instead of one tile plus the 17th row's dot products).  Waves that do not divide a
- * chunked shape make specverify_stack fail with SV_ERR_SHAPE.  Process-wide;
- * affects the *_workspace_bytes answers, so query them after changing it.  Not thread-safe
- * against concurrent calls.
+ * 17-row window uses two 16-row tiles instead of one tile plus the 17th row's dot
+ * products).  Waves that do not divide a chunked shape make specverify_stack fail with
+ * SV_ERR_SHAPE.  The override belongs to the calling thread: it affects only calls made from
+ * that thread (including its *_workspace_bytes answers, so query them after changing it),
+ * and other threads keep the automatic choice.  (0, 0, 0, 0) restores it.
  */
 void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups, int32_t depth,
                            int32_t head_kernel);

@@ -41,7 +41,8 @@ def test_header_constants_match_binding():
                        ("SV_STATE_WORDS", sv.STATE_WORDS), ("SV_STATE_LEN", sv.STATE_LEN),
                        ("SV_STATE_FLAGS", sv.STATE_FLAGS), ("SV_STATE_HIST", sv.STATE_HIST),
                        ("SV_STATE_GATE_AFTER", sv.STATE_GATE_AFTER), ("SV_STATE_ZERO_RUN", sv.STATE_ZERO_RUN),
-                       ("SV_STATE_GATED", sv.STATE_GATED), ("SV_FLAG_TOKEN", sv.FLAG_TOKEN)]:
+                       ("SV_STATE_GATED", sv.STATE_GATED), ("SV_FLAG_TOKEN", sv.FLAG_TOKEN),
+                       ("SV_FLAG_CAPACITY", sv.FLAG_CAPACITY), ("SV_FLAG_ARGMAX", sv.FLAG_ARGMAX)]:
         assert re.search(rf"#define {macro} {val}\b", text), macro
 
 

@@ -1,7 +1,14 @@
 """GPU parity of specverify_stack (the whole dense stack in two chunked launches per block, its
-RMSNorm carried as per-tile sum-of-squares partials) against the CPU oracle, teacher-forced
-block by block: every block output the library writes to x_layers is compared with the oracle
-block applied to the library's own input of that block."""
+RMSNorm carried as per-tile sum-of-squares partials) against the CPU oracle.
+
+A single-block call is checked teacher-forced at both of its stages against oracle.mlp_block:
+m = silu(g)*u (read back from the workspace) against the oracle's m from the same input, then
+the block output against x + m_gpu Wd^T.  A multi-block call is checked by exact equality: every
+block output it writes to x_layers must equal, bit for bit, a single-block call on that block's
+input (the previous output), because both compute the same sums in the same order (the norm
+partials of a caller's input are summed in the order the down epilogue uses).  So every block of
+a multi-block call meets the single-block bound.  The dense-stack workload itself (36 blocks of
+4096 -> 12288 -> 4096 at S = 9, then the 151936-row head) is checked this way in full."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +17,7 @@ import oracle
 from weight_bound_verify_amd import specverify as sv
 from weight_bound_verify_amd import synth
 
-from gpu_util import dev, say, to_dev
+from gpu_util import check_argmax, check_logits, dev, gpu_verify, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -85,12 +92,31 @@ SHAPES = [
 ]
 
 
+def _check_block(x, layer, xl0, nrm, m_gpu, ss, eps=1e-6):
+    """One block from input x, teacher-forced at both stages: the GPU's m = silu(g)*u within one
+    fp16 rounding of the oracle's m from the same input (the norm and both projections of
+    gate/up; plus the effect of normalised elements whose fp16 rounding fp32 cannot decide),
+    the block output within one rounding of x + m_gpu Wd^T (the down projection, residual and
+    store), the down epilogue's sum-of-squares partials and the final norm."""
+    S, H = x.shape
+    _, parts = oracle.mlp_block(x, layer, eps=eps, return_parts=True)
+    ref_m = oracle.silu(parts["g"]) * parts["u"]
+    ulp = np.spacing(np.abs(ref_m.astype(np.float16))).astype(np.float64)
+    rms = np.sqrt(np.mean(ref_m * ref_m, axis=-1, keepdims=True))
+    err = np.abs(m_gpu.astype(np.float64) - ref_m)
+    bad = np.argwhere(~(err <= ulp + 1e-5 * rms + _m_bound(x, parts, layer, eps)))
+    assert bad.size == 0, f"m: {len(bad)} outside, first {bad[:3].tolist()} err {err[tuple(bad[0])]}"
+    _check_f16(xl0, x.astype(np.float64) + oracle.linear_q8b32(*layer[2], m_gpu), slack=1e-5)
+    out = xl0.astype(np.float64)
+    # the down epilogue's per-16-column sums of squares of the stored fp16 outputs
+    ref_ss = (out.reshape(S, H // 16, 16) ** 2).sum(-1)
+    assert np.allclose(ss, ref_ss, rtol=1e-5, atol=0), "sum-of-squares partials"
+    _check_f16(nrm, out / np.sqrt(np.mean(out * out, axis=1, keepdims=True) + eps), slack=1e-5)
+
+
 @pytest.mark.parametrize("H,F,S,L", SHAPES)
 def test_stack_block_by_block_teacher_forced(H, F, S, L):
-    """Each block on its own (L = 1 per call), teacher-forced at both stages: the GPU's
-    m = silu(g)*u must be within one fp16 rounding of the oracle's m from the same input
-    (the norm and both projections of gate/up), and the block output within one rounding of
-    x + m_gpu Wd^T (the down projection, residual and store)."""
+    """Each block on its own (L = 1 per call), checked at both stages against the oracle."""
     say(f"stack block by block H={H} F={F} S={S} L={L}")
     rng = np.random.default_rng(H + 3 * F + S + L)
     layers, mats = _stacked(rng, L, H, F)
@@ -98,29 +124,15 @@ def test_stack_block_by_block_teacher_forced(H, F, S, L):
     for li in range(L):
         one = [m[li:li + 1] for m in mats]
         _, xl, nrm, m_gpu, ss = _run(one, x, 1, want_ws=True)
-        _, parts = oracle.mlp_block(x, layers[li], return_parts=True)
-        ref_m = oracle.silu(parts["g"]) * parts["u"]
-        ulp = np.spacing(np.abs(ref_m.astype(np.float16))).astype(np.float64)
-        rms = np.sqrt(np.mean(ref_m * ref_m, axis=-1, keepdims=True))
-        err = np.abs(m_gpu.astype(np.float64) - ref_m)
-        bad = np.argwhere(~(err <= ulp + 1e-5 * rms + _m_bound(x, parts, layers[li])))
-        assert bad.size == 0, f"m: {len(bad)} outside, first {bad[:3].tolist()} err {err[tuple(bad[0])]}"
-        _check_f16(xl[0], x.astype(np.float64) + oracle.linear_q8b32(*layers[li][2], m_gpu), slack=1e-5)
-        out = xl[0].astype(np.float64)
-        # the down epilogue's per-16-column sums of squares of the stored fp16 outputs
-        ref_ss = (out.reshape(S, H // 16, 16) ** 2).sum(-1)
-        assert np.allclose(ss, ref_ss, rtol=1e-5, atol=0), "sum-of-squares partials"
-        _check_f16(nrm, out / np.sqrt(np.mean(out * out, axis=1, keepdims=True) + 1e-6), slack=1e-5)
+        _check_block(x, layers[li], xl[0], nrm, m_gpu, ss)
         x = xl[0]
 
 
 @pytest.mark.parametrize("H,F,S,L", [sh for sh in SHAPES if sh[3] > 1])
-def test_stack_matches_oracle_per_block(H, F, S, L):
-    """The multi-block call (each block's norm from the previous down epilogue's partials),
-    every block output against the oracle block on the library's own input of that block.
-    Allowed error: one fp16 rounding of the output, 1e-4 of the row rms, and the effect of
-    m = silu(g)*u rounding to the other fp16 neighbour (fp32 versus fp64 before rounding):
-    at most one m ulp per term of the down projection, bounded by 4 ulps x |Wd| summed."""
+def test_stack_equals_chained_single_blocks(H, F, S, L):
+    """The multi-block call (each block's norm from the previous down epilogue's partials) writes
+    the same bits as L single-block calls chained on its own outputs, each of which is checked
+    against the oracle as above; its final norm equals the last single-block call's."""
     say(f"stack H={H} F={F} S={S} L={L}")
     rng = np.random.default_rng(H + 3 * F + S + L)
     layers, mats = _stacked(rng, L, H, F)
@@ -129,20 +141,12 @@ def test_stack_matches_oracle_per_block(H, F, S, L):
     assert np.array_equal(x_out, x), "x must be left unchanged when x_layers is given"
     prev = x
     for li in range(L):
-        _, parts = oracle.mlp_block(prev, layers[li], return_parts=True)
-        ref = prev.astype(np.float64) + parts["y"]
-        wd = np.abs(oracle.dequantize(*layers[li][2]))
-        ulp_m = np.spacing(np.abs(parts["m"])).astype(np.float64)          # [S][F]
-        flip = 4.0 * np.sqrt((ulp_m ** 2) @ (wd.T ** 2))                   # rms-style bound of sparse flips
-        got = xl[li].astype(np.float64)
-        ulp = np.spacing(np.abs(ref.astype(np.float16))).astype(np.float64)
-        rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
-        err = np.abs(got - ref)
-        bad = np.argwhere(~(err <= ulp + 1e-4 * rms + flip))
-        assert bad.size == 0, f"block {li}: {len(bad)} outside, first {bad[:3].tolist()} err {err[tuple(bad[0])]}"
+        one = [m[li:li + 1] for m in mats]
+        _, xl1, nrm1, m_gpu, ss = _run(one, prev, 1, want_ws=True)
+        assert np.array_equal(xl1[0], xl[li]), f"block {li}: multi-block output differs from a single-block call"
+        _check_block(prev, layers[li], xl1[0], nrm1, m_gpu, ss)
         prev = xl[li]
-    last = xl[L - 1].astype(np.float64)
-    _check_f16(nrm, last / np.sqrt(np.mean(last * last, axis=1, keepdims=True) + 1e-6), slack=1e-5)
+    assert np.array_equal(nrm, nrm1), "final norm differs from the last single-block call's"
 
 
 def test_stack_in_place_is_bit_identical_to_layer_outputs():
@@ -176,7 +180,8 @@ def test_stack_depth_variants_bit_identical():
 
 
 def test_stack_eps_and_zero_rows():
-    """An all-zero window row stays zero through the blocks (rmsnorm of 0 is 0 with eps > 0)."""
+    """An all-zero window row stays zero through the blocks (rmsnorm of 0 is 0 with eps > 0);
+    every block equals a single-block call on its input and meets the oracle bound at eps = 1e-3."""
     rng = np.random.default_rng(8)
     H, F, S, L = 512, 1024, 4, 2
     layers, mats = _stacked(rng, L, H, F)
@@ -186,8 +191,9 @@ def test_stack_eps_and_zero_rows():
     assert (xl[:, 2] == 0).all() and (nrm[2] == 0).all()
     prev = x
     for li in range(L):
-        m = oracle.mlp_block(prev, layers[li], eps=1e-3, return_parts=True)[1]["m"]
-        _check_f16(xl[li], prev.astype(np.float64) + oracle.linear_q8b32(*layers[li][2], m))
+        _, xl1, nrm1, m_gpu, ss = _run([m[li:li + 1] for m in mats], prev, 1, eps=1e-3, want_ws=True)
+        assert np.array_equal(xl1[0], xl[li])
+        _check_block(prev, layers[li], xl1[0], nrm1, m_gpu, ss, eps=1e-3)
         prev = xl[li]
 
 
@@ -215,3 +221,96 @@ def test_stack_timing_hook_times_the_first_gate_up():
     t_gu, t_all = e0.elapsed_time(e1), a.elapsed_time(b)
     assert 0.0 < t_gu < t_all
     assert np.array_equal(xl.cpu().numpy(), ref[1]) and np.array_equal(nrm.cpu().numpy(), ref[2])
+
+
+# ---------------------------------------------------------------------------------------------
+# The dense-stack workload in full: 36 blocks of 4096 -> 12288 -> 4096 at S = 9 through one
+# specverify_stack call (the call the dense-stack bench times), then the 151936 x 4096 head.
+# Layer l's three matrices are seeded row rotations of three drawn base matrices (distinct
+# layers with the drawn value distribution, built on the device in seconds), so a dropped,
+# repeated or reordered block changes the outputs.
+# ---------------------------------------------------------------------------------------------
+C5_H, C5_F, C5_S, C5_L, C5_V = 4096, 12288, 9, 36, 151936
+
+
+def _c5_layer(base, shifts, li):
+    """Layer li's ((qg, sg), (qu, su), (qd, sd)) on the host: base matrix m rotated by shifts[li, m] rows."""
+    return tuple((np.roll(q, int(shifts[li, m]), axis=0), np.roll(s, int(shifts[li, m]), axis=0))
+                 for m, (q, s) in enumerate(base))
+
+
+@pytest.fixture(scope="module")
+def c5_stack():
+    H, F, S, L = C5_H, C5_F, C5_S, C5_L
+    say("C5 stack: drawing the base matrices")
+    rng = np.random.default_rng(20261206)
+    base = [synth.quantized_head(np.random.SeedSequence(20261206 + i), r, c)
+            for i, (r, c) in enumerate([(F, H), (F, H), (H, F)])]
+    shifts = np.stack([rng.integers(1, n, size=L) for n in (F, F, H)], axis=1)     # [L][3]
+    mats = []
+    for m, (q, s) in enumerate(base):
+        qd, sd = to_dev(q), to_dev(s)
+        Q = torch.empty((L,) + q.shape, dtype=torch.int8, device=dev())
+        Sc = torch.empty((L,) + s.shape, dtype=torch.float16, device=dev())
+        for li in range(L):
+            Q[li].copy_(torch.roll(qd, int(shifts[li, m]), 0))
+            Sc[li].copy_(torch.roll(sd, int(shifts[li, m]), 0))
+        mats += [Q, Sc]
+        del qd, sd
+    x = synth.fp16_normal(rng, (S, H))
+    xd = to_dev(x)
+    xl = torch.full((L, S, H), float("nan"), dtype=torch.float16, device=dev())
+    nrm = torch.full((S, H), float("nan"), dtype=torch.float16, device=dev())
+    ws = sv.workspace(sv.stack_forward_workspace_bytes(H, F, S), dev())
+    say("C5 stack: the 36-block call")
+    sv.stack(*mats, xd, nrm, ws, 1e-6, x_layers=xl)
+    torch.cuda.synchronize()
+    xl_h, nrm_h = xl.cpu().numpy(), nrm.cpu().numpy()
+    say("C5 stack: 36 single-block calls on the call's own block inputs")
+    singles, equal = [], []
+    xl1 = torch.empty((1, S, H), dtype=torch.float16, device=dev())
+    nrm1 = torch.empty((S, H), dtype=torch.float16, device=dev())
+    for li in range(L):
+        prev = xd if li == 0 else xl[li - 1]
+        sv.stack(*[m[li:li + 1] for m in mats], prev.clone(), nrm1, ws, 1e-6, x_layers=xl1)
+        torch.cuda.synchronize()
+        w = ws.cpu().numpy()
+        m_gpu = w[:2 * S * F].view(np.float16).reshape(S, F).copy()
+        off = (2 * S * F + 255) // 256 * 256
+        ss = w[off:off + 4 * S * (H // 16)].view(np.float32).reshape(S, H // 16).copy()
+        singles.append((xl1[0].cpu().numpy(), nrm1.cpu().numpy(), m_gpu, ss))
+        equal.append(bool(torch.equal(xl1[0], xl[li])))
+    del mats
+    torch.cuda.empty_cache()
+    return dict(base=base, shifts=shifts, x=x, xl=xl_h, nrm=nrm_h, singles=singles, equal=equal,
+                nrm_last_equal=bool(np.array_equal(singles[-1][1], nrm_h)))
+
+
+def test_c5_stack_equals_chained_single_blocks(c5_stack):
+    """Every block output of the 36-block call equals a single-block call on its input, and the
+    call's norm_out equals the last single-block call's."""
+    bad = [li for li, ok in enumerate(c5_stack["equal"]) if not ok]
+    assert not bad, f"blocks {bad} differ from single-block calls"
+    assert c5_stack["nrm_last_equal"]
+
+
+@pytest.mark.parametrize("lo", range(0, C5_L, 6))
+def test_c5_stack_blocks_against_oracle(c5_stack, lo):
+    """Blocks lo .. lo+5 of the 36-block call, teacher-forced against oracle.mlp_block."""
+    for li in range(lo, min(lo + 6, C5_L)):
+        say(f"C5 block {li}")
+        x_in = c5_stack["x"] if li == 0 else c5_stack["xl"][li - 1]
+        xl0, nrm1, m_gpu, ss = c5_stack["singles"][li]
+        _check_block(x_in, _c5_layer(c5_stack["base"], c5_stack["shifts"], li), xl0, nrm1, m_gpu, ss)
+
+
+def test_c5_head_after_the_stack(c5_stack):
+    """The 151936 x 4096 head on the stack's norm_out: argmax against the oracle's on the same
+    rows (near-tie rule) and logits within the tolerance."""
+    say("C5 head")
+    q, s = synth.quantized_head(np.random.SeedSequence(20261207), C5_V, C5_H)
+    nrm = c5_stack["nrm"]
+    a_gpu, lg = gpu_verify(q, s, nrm)
+    L = oracle.head_logits(q, s, nrm)
+    check_argmax(a_gpu, L)
+    check_logits(lg, L)

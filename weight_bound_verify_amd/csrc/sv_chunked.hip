@@ -363,8 +363,12 @@ __global__ __launch_bounds__(NW * 64) void q8b32_chunked(ChunkArgs a) {
     }
 }
 
-// ss[s][t] = sum over the 16 columns of tile t of fp16(x[s, k])^2, in column order: the
-// partials of a stream that did not come out of a down projection (the stack's input).
+// ss[s][t] = sum over the 16 columns of tile t of fp16(x[s, k])^2: the partials of a stream
+// that did not come out of a down projection (the stack's input).  The square of an fp16
+// value is exact in fp32, and the 16 squares are added in the order of the down epilogue's
+// butterfly (columns k and k+8, then +4, +2, +1), so a stream gets the same partials here as
+// from a down projection that stored it: a block computes the same bits whether its input
+// came from the previous block of one call or from the caller.
 __global__ __launch_bounds__(256) void row_ss_kernel(const uint16_t* __restrict__ x, int S, int H,
                                                      float* __restrict__ ss) {
     const int nt = H / kTileRows;
@@ -372,13 +376,17 @@ __global__ __launch_bounds__(256) void row_ss_kernel(const uint16_t* __restrict_
     const int t = blockIdx.x * 256 + threadIdx.x;
     if (s >= S || t >= nt) return;
     const uint16_t* p = x + (size_t)s * H + (size_t)t * kTileRows;
-    float acc = 0.f;
+    float sq[kTileRows];
 #pragma unroll
     for (int k = 0; k < kTileRows; ++k) {
         const float q = h2f(p[k]);
-        acc = __builtin_fmaf(q, q, acc);
+        sq[k] = q * q;
     }
-    ss[(size_t)s * nt + t] = acc;
+#pragma unroll
+    for (int w = kTileRows / 2; w > 0; w >>= 1)
+#pragma unroll
+        for (int k = 0; k < w; ++k) sq[k] = sq[k] + sq[k + w];
+    ss[(size_t)s * nt + t] = sq[0];
 }
 
 // out[s, k] = fp16(x[s, k] * inv[s]) with inv from the ss partials exactly as the gate/up
@@ -445,10 +453,10 @@ int chunked_resident(ChunkFn fn, int nw) {
 }  // namespace
 
 namespace {
-int g_chunk_nw = 0;       // tuning overrides, 0 = automatic
-int g_chunk_depth = 0;
-int g_grid_override_chunk = 0;
-int g_head_kernel = 0;    // 0 automatic, 1 one-pass-per-item kernel, 2 ring kernel
+thread_local int g_chunk_nw = 0;       // tuning overrides of the calling thread, 0 = automatic
+thread_local int g_chunk_depth = 0;
+thread_local int g_grid_override_chunk = 0;
+thread_local int g_head_kernel = 0;    // 0 automatic, 1 one-pass-per-item kernel, 2 ring kernel
 }  // namespace
 
 void set_chunk_tuning(int waves, int depth, int max_groups, int head_kernel) {

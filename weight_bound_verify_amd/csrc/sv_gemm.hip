@@ -13,8 +13,9 @@
 //                         registers for the whole launch.
 //   D (16 x 16) fp32    = lane l holds window rows 4*(l/16) .. +3 of weight row l%16, so the
 //                         block scale of that weight row multiplies all four in fp32:
-//                         acc += scale * D.  The sum over one block is exact (integer codes
-//                         times fp16 values); only the cross-block accumulation rounds.
+//                         acc += scale * D.  Every product (an integer code times an fp16
+//                         value) is exact in fp32; the sums, within a block and across blocks,
+//                         round in fp32.
 // A workgroup owns 16 weight rows at a time ("item"); its NW waves split the hidden axis,
 // each holding its share of the window rows in registers, and reduce through LDS in a fixed
 // order (deterministic).  The head epilogue keeps a running (value, lowest index) argmax
@@ -42,9 +43,9 @@ namespace sv {
 
 namespace {
 
-int g_nw_override = 0;       // 0 = choose
-int g_grid_override = 0;     // 0 = choose
-int g_no_xr = 0;             // 1: a 17-row window uses the two-tile kernels (tuning experiments)
+thread_local int g_nw_override = 0;       // tuning overrides of the calling thread, 0 = choose
+thread_local int g_grid_override = 0;     // 0 = choose
+thread_local int g_no_xr = 0;            // 1: a 17-row window uses the two-tile kernels (tuning experiments)
 
 // Workgroup barrier that orders LDS only, so prefetched global loads stay in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -728,7 +729,7 @@ __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* _
                 if (better(v[u], ix[u], bv, bi)) { bv = v[u]; bi = ix[u]; }
         }
         argmax_group<64>(bv, bi);
-        if (lane == 0) { argmax[s] = bi; am[s] = bi; }
+        if (lane == 0) { argmax[s] = argmax_id(bi); am[s] = argmax_id(bi); }
     }
     if (!round) return;
     if (in_lds) {
@@ -745,13 +746,22 @@ __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* _
     if (wave == 0) {                                   // accept_wave, with the stream mirrored in LDS
         const unsigned long long hit = __ballot(lane < K && d >= 0 && d == am[lane < K ? lane : 0]);
         const int j = __builtin_ctzll(~hit);           // <= K: bit K is never set
-        if (lane < j) { tokens[len0 + lane] = d; tk[len0 + lane] = d; }
-        if (lane == j) { tokens[len0 + j] = am[j]; tk[len0 + j] = am[j]; }
-        const int gated = record_round_cached(sc, state, j, lane);
-        if (lane == 0) {
-            new_len = len0 + 1 + j;
-            state[SV_STATE_LEN] = len0 + 1 + j;
-            gated_s = gated != 0;
+        const int aj = am[j];
+        if (aj < 0) {                                  // row j had no greedy id: commit nothing
+            if (lane == 0) {
+                state[SV_STATE_FLAGS] = state_word(sc, SV_STATE_FLAGS) | SV_FLAG_ARGMAX;
+                new_len = len0;
+                gated_s = state_word(sc, SV_STATE_GATED) != 0;
+            }
+        } else {
+            if (lane < j) { tokens[len0 + lane] = d; tk[len0 + lane] = d; }
+            if (lane == j) { tokens[len0 + j] = aj; tk[len0 + j] = aj; }
+            const int gated = record_round_cached(sc, state, j, lane);
+            if (lane == 0) {
+                new_len = len0 + 1 + j;
+                state[SV_STATE_LEN] = len0 + 1 + j;
+                gated_s = gated != 0;
+            }
         }
     }
     __syncthreads();

@@ -15,7 +15,7 @@ constexpr int kChunk = 8192;                 // stream ids staged in LDS per pas
 __global__ __launch_bounds__(kProposeThreads) void propose_kernel(const int32_t* __restrict__ tokens,
                                                                   int cap, int32_t* __restrict__ state,
                                                                   int nmax, int K, int32_t* __restrict__ drafts) {
-    __shared__ int32_t tk[kHalo + kChunk];
+    __shared__ __attribute__((aligned(16))) int32_t tk[kHalo + kChunk];
     __shared__ unsigned long long wbest[kProposeThreads / kWave];
     propose_block(tokens, cap, state, nmax, K, drafts, tk, kChunk, wbest);
 }

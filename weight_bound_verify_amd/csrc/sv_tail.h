@@ -13,13 +13,13 @@ constexpr int kHalo = SV_MAX_NGRAM;   // ids before an LDS chunk that a match ma
 
 // Copy src[0 .. n) to LDS dst[0 .. n) with the whole workgroup, several 16-byte loads in
 // flight per thread (a strided one-id-per-iteration loop would wait on every load).  Ids
-// src[i] with i outside [0, n) are never read.  `src` must be 16-byte aligned for the
-// vector part; otherwise single ids are copied.
+// src[i] with i outside [0, n) are never read.  The 16-byte vector path is taken only when
+// both `src` and `dst` are 16-byte aligned; otherwise single ids are copied.
 __device__ __forceinline__ void stage_ids(const int32_t* __restrict__ src, int n, int32_t* dst) {
     typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
     const int tid = threadIdx.x, nt = blockDim.x;
     int done = 0;
-    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+    if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0) {
         const int n4 = n >> 2;
         const i32x4* s4 = reinterpret_cast<const i32x4*>(src);
         i32x4* d4 = reinterpret_cast<i32x4*>(dst);
@@ -77,28 +77,33 @@ __device__ __forceinline__ void prefix_store(const int32_t* __restrict__ src, in
 }
 
 // Best (match length << 32 | end position) over the end positions e < len - 1 of a stream held
-// in LDS (`tk`, 16-byte aligned, at least len ids), for this thread's share: groups of four
-// consecutive end positions, group index = thread + k * threads.  A group reads its four ids
-// and the NM ids before it as 16-byte LDS reads and finds every match from registers (NM = 4
-// covers nmax <= 4, NM = 8 the rest), so the scan costs a few instructions per position.
+// in LDS (`tk`, 16-byte aligned, at least len ids and readable up to the next multiple of four
+// past len - 1), for the share of thread `tid` of `nthreads`: groups of four consecutive end
+// positions, group index = tid + k * nthreads.  A group reads its four ids and the NM ids
+// before it as 16-byte LDS reads and finds every match from registers (NM = 4 covers nmax <= 4,
+// NM = 8 the rest), so the scan costs a few instructions per position.  A position before the
+// stream start never matches (its position, not its value, rules it out), and the read index
+// is clamped at zero so no read leaves the array.  Host-callable so that its index arithmetic
+// can be checked on the CPU.
 template <int NM>
-__device__ __forceinline__ unsigned long long scan_best_lds(const int32_t* tk, int len, int nmax,
-                                                            const int32_t (&suf)[SV_MAX_NGRAM]) {
+__host__ __device__ __forceinline__ unsigned long long scan_best_lds(const int32_t* tk, int len, int nmax,
+                                                                     const int32_t (&suf)[SV_MAX_NGRAM], int tid,
+                                                                     int nthreads) {
     typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
     const i32x4* t4 = reinterpret_cast<const i32x4*>(tk);
     unsigned long long best = 0;
     const int ngroups = (len - 1 + 3) >> 2;                   // groups holding end positions 0 .. len-2
-    for (int gi = threadIdx.x; gi < ngroups; gi += blockDim.x) {
+    for (int gi = tid; gi < ngroups; gi += nthreads) {
         const int e0 = gi << 2;
         int32_t w[NM + 4];                                      // ids e0 - NM .. e0 + 3
 #pragma unroll
         for (int q = 0; q < NM / 4 + 1; ++q) {
-            // every read stays inside the array (the index is clamped, then the sentinel
-            // replaces what precedes the stream): a read below it through a generic pointer
-            // would leave the LDS window
+            // the index is clamped so every read stays inside the array: the compiler merges
+            // neighbouring groups' reads into one base and offsets and issues them
+            // unconditionally, and a read below the array through a generic pointer would leave
+            // the LDS window; what a clamped read returns is never compared (see below)
             const int vi = gi - NM / 4 + q;
-            i32x4 v = t4[vi < 0 ? 0 : vi];
-            if (vi < 0) v = i32x4{INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+            const i32x4 v = t4[vi < 0 ? 0 : vi];
 #pragma unroll
             for (int c = 0; c < 4; ++c) w[4 * q + c] = v[c];
         }
@@ -109,7 +114,7 @@ __device__ __forceinline__ unsigned long long scan_best_lds(const int32_t* tk, i
             bool run = true;
 #pragma unroll
             for (int i = 0; i < NM; ++i) {
-                run = run && i < nmax && w[NM + j - i] == suf[i];
+                run = run && i < nmax && e - i >= 0 && w[NM + j - i] == suf[i];
                 l += run ? 1 : 0;
             }
             if (l > 0 && e < len - 1) {
@@ -119,6 +124,56 @@ __device__ __forceinline__ unsigned long long scan_best_lds(const int32_t* tk, i
         }
     }
     return best;
+}
+
+constexpr int kMaxBranches = 4;                // branches of the tree drafter
+
+// Insert key k into a descending list of kMaxBranches keys (keys are distinct).
+__host__ __device__ __forceinline__ void top_insert(unsigned long long (&top)[kMaxBranches], unsigned long long k) {
+#pragma unroll
+    for (int b = 0; b < kMaxBranches; ++b)
+        if (k > top[b]) { const unsigned long long t = top[b]; top[b] = k; k = t; }
+}
+
+// The four best keys (l << 32 | e) of thread `tid` of `nthreads` over the end positions
+// e < len - 1 of a stream in LDS (`tk`, 16-byte aligned, readable up to the next multiple of
+// four past len - 1): groups of four end positions from 16-byte reads, as the linear
+// drafter's scan (NM = 4 covers nmax <= 4, NM = 8 the rest).  A position before the stream
+// start never matches (its position rules it out), and the read index is clamped at zero so
+// no read leaves the array (the compiler issues neighbouring groups' reads unconditionally
+// from one base, and through a generic pointer a read below the array would leave the LDS
+// window).  Host-callable so that its index arithmetic can be checked on the CPU.
+template <int NM>
+__host__ __device__ __forceinline__ void scan_top_lds(const int32_t* tk, int len, int nmax,
+                                                      const int32_t (&suf)[SV_MAX_NGRAM],
+                                                      unsigned long long (&top)[kMaxBranches], int tid,
+                                                      int nthreads) {
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4* t4 = reinterpret_cast<const i32x4*>(tk);
+    const int ngroups = (len - 1 + 3) >> 2;
+    for (int gi = tid; gi < ngroups; gi += nthreads) {
+        const int e0 = gi << 2;
+        int32_t w[NM + 4];
+#pragma unroll
+        for (int q = 0; q < NM / 4 + 1; ++q) {
+            const int vi = gi - NM / 4 + q;
+            const i32x4 v = t4[vi < 0 ? 0 : vi];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) w[4 * q + c] = v[c];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = e0 + j;
+            int l = 0;
+            bool run = true;
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                run = run && i < nmax && e - i >= 0 && w[NM + j - i] == suf[i];
+                l += run ? 1 : 0;
+            }
+            if (l > 0 && e < len - 1) top_insert(top, ((unsigned long long)l << 32) | (unsigned)e);
+        }
+    }
 }
 
 // Per-round statistics and the hit-rate gate ("Stream C - Speculative decoding", the shipped
@@ -182,11 +237,18 @@ __device__ __forceinline__ void gated_drafts(int K, int32_t* drafts, int32_t* st
     }
 }
 
+// Argmax stage 2 leaves INT_MAX when no logit of a row compared greater than -inf (every
+// logit NaN, e.g. after an overflowed activation); such a row has no greedy id and is
+// reported as -1.
+__device__ __forceinline__ int argmax_id(int bi) { return bi == INT_MAX ? -1 : bi; }
+
 // Greedy accept by one wave ("Stream C - Speculative decoding", the delta and control-logic
 // proof; "Spec-decode on GDN hybrids", hybrid state discipline): lane i compares d_{i+1}
 // with the greedy id of window row i, a ballot finds the first miss j, the accepted drafts
 // and argmax[j] (correction or bonus) are appended and len advances by 1 + j.  A call that
-// could overflow `cap` writes no token and sets the sticky capacity flag.
+// could overflow `cap` writes no token and sets the sticky capacity flag; a call whose
+// argmax[j] is -1 (that row had no greedy id) writes no token, records no round and sets the
+// sticky argmax flag.
 __device__ __forceinline__ void accept_wave(const int32_t* argmax, const int32_t* drafts, int K, int32_t* tokens,
                                             int cap, int32_t* state, int lane) {
     const int len = state[SV_STATE_LEN];
@@ -198,8 +260,13 @@ __device__ __forceinline__ void accept_wave(const int32_t* argmax, const int32_t
     if (lane < K) { d = drafts[lane]; a = argmax[lane]; }
     const unsigned long long hit = __ballot(lane < K && d >= 0 && d == a);
     const int j = __builtin_ctzll(~hit);                 // <= K: bit K is never set
+    const int aj = argmax[j];                            // the correction or bonus id (uniform)
+    if (aj < 0) {
+        if (lane == 0) state[SV_STATE_FLAGS] |= SV_FLAG_ARGMAX;
+        return;
+    }
     if (lane < j) tokens[len + lane] = d;
-    if (lane == j) tokens[len + j] = argmax[j];
+    if (lane == j) tokens[len + j] = aj;
     if (lane == 0) {
         state[SV_STATE_LEN] = len + 1 + j;
         if (K > 0) record_round(state, j);        // K = 0 is the anchor bootstrap, not a round
@@ -235,6 +302,10 @@ __device__ __forceinline__ int accept_sample_wave(const int32_t* sample, const f
     }
     const unsigned long long kept = __ballot(keep);
     const int j = __builtin_ctzll(~kept);                // <= K: bit K is never set
+    if (sample[j] < 0) {                                 // row j drew nothing (every key NaN)
+        if (lane == 0) state[SV_STATE_FLAGS] |= SV_FLAG_ARGMAX;
+        return -1;
+    }
     if (lane < j) {
         tokens[len + lane] = d;
         if (mirror) mirror[len + lane] = d;
@@ -341,7 +412,8 @@ __device__ __forceinline__ void propose_lds(const int32_t* tk, int len, int nmax
     int32_t suf[SV_MAX_NGRAM];
 #pragma unroll
     for (int i = 0; i < SV_MAX_NGRAM; ++i) suf[i] = (i < nmax && len - 1 - i >= 0) ? tk[len - 1 - i] : -1;
-    unsigned long long best = nmax <= 4 ? scan_best_lds<4>(tk, len, nmax, suf) : scan_best_lds<8>(tk, len, nmax, suf);
+    unsigned long long best = nmax <= 4 ? scan_best_lds<4>(tk, len, nmax, suf, tid, nthreads)
+                                         : scan_best_lds<8>(tk, len, nmax, suf, tid, nthreads);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         const unsigned long long o = __shfl_xor(best, off, 64);

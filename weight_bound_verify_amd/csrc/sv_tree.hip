@@ -28,7 +28,6 @@ namespace {
 
 constexpr int kTreeThreads = 1024;
 constexpr int kTreeIds = 32768;                      // stream ids held in LDS (128 KB)
-constexpr int kMaxBranches = 4;
 
 // Walk down the tree by one wave (lane i holds node i+1).  `am` holds the argmax of every
 // window row.  Appends the path's tokens and the final argmax to `tokens` (and `mirror` when
@@ -55,12 +54,16 @@ __device__ __forceinline__ int accept_tree_wave(const int32_t* am, const int32_t
         c = nxt + 1;
         ++j;
     }
+    const int fin = am[c];                             // the correction or bonus id (uniform)
+    if (fin < 0) {                                     // that row had no greedy id: commit nothing
+        if (lane == 0) state[SV_STATE_FLAGS] |= SV_FLAG_ARGMAX;
+        return -1;
+    }
     if (pos >= 0) {
         tokens[len + pos] = tok;
         if (mirror) mirror[len + pos] = tok;
     }
     if (lane == 0) {
-        const int fin = am[c];
         tokens[len + j] = fin;
         if (mirror) mirror[len + j] = fin;
         state[SV_STATE_LEN] = len + 1 + j;
@@ -68,51 +71,6 @@ __device__ __forceinline__ int accept_tree_wave(const int32_t* am, const int32_t
     }
     if (cache) record_round_cached(*cache, state, j, lane);
     return j;
-}
-
-// Insert key k into a descending list of kMaxBranches keys (keys are distinct).
-__device__ __forceinline__ void top_insert(unsigned long long (&top)[kMaxBranches], unsigned long long k) {
-#pragma unroll
-    for (int b = 0; b < kMaxBranches; ++b)
-        if (k > top[b]) { const unsigned long long t = top[b]; top[b] = k; k = t; }
-}
-
-// This thread's four best keys (l << 32 | e) over the end positions e < len - 1 of a stream in
-// LDS (`tk`, 16-byte aligned): groups of four end positions from 16-byte reads, as the linear
-// drafter's scan (NM = 4 covers nmax <= 4, NM = 8 the rest).
-template <int NM>
-__device__ __forceinline__ void scan_top_lds(const int32_t* tk, int len, int nmax, const int32_t (&suf)[SV_MAX_NGRAM],
-                                             unsigned long long (&top)[kMaxBranches]) {
-    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-    const i32x4* t4 = reinterpret_cast<const i32x4*>(tk);
-    const int ngroups = (len - 1 + 3) >> 2;
-    for (int gi = threadIdx.x; gi < ngroups; gi += blockDim.x) {
-        const int e0 = gi << 2;
-        int32_t w[NM + 4];
-#pragma unroll
-        for (int q = 0; q < NM / 4 + 1; ++q) {
-            // every read stays inside the array (the index is clamped, then the sentinel
-            // replaces what precedes the stream): a read below it through a generic pointer
-            // would leave the LDS window
-            const int vi = gi - NM / 4 + q;
-            i32x4 v = t4[vi < 0 ? 0 : vi];
-            if (vi < 0) v = i32x4{INT_MIN, INT_MIN, INT_MIN, INT_MIN};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) w[4 * q + c] = v[c];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = e0 + j;
-            int l = 0;
-            bool run = true;
-#pragma unroll
-            for (int i = 0; i < NM; ++i) {
-                run = run && i < nmax && w[NM + j - i] == suf[i];
-                l += run ? 1 : 0;
-            }
-            if (l > 0 && e < len - 1) top_insert(top, ((unsigned long long)l << 32) | (unsigned)e);
-        }
-    }
 }
 
 // The same over a stream in global memory, one end position per thread and step.
@@ -164,8 +122,8 @@ __device__ __forceinline__ void propose_tree_block(const int32_t* st, bool in_ld
     // the four best keys (l << 32 | e) of this thread's end positions, best first
     unsigned long long top[kMaxBranches] = {0ull, 0ull, 0ull, 0ull};
     if (in_lds) {
-        if (nmax <= 4) scan_top_lds<4>(st, len, nmax, suf, top);
-        else scan_top_lds<8>(st, len, nmax, suf, top);
+        if (nmax <= 4) scan_top_lds<4>(st, len, nmax, suf, top, threadIdx.x, blockDim.x);
+        else scan_top_lds<8>(st, len, nmax, suf, top, threadIdx.x, blockDim.x);
     } else {
         scan_top_global(st, len, nmax, suf, top);
     }
@@ -307,7 +265,7 @@ __global__ __launch_bounds__(kTreeThreads) void tree_tail_kernel(
     if (wave == 0) sc = state_cache_load(state, lane);
     const bool in_lds = len0 >= 0 && len0 + K + 1 <= cap && len0 + K + 1 <= kTreeIds;
     for (int s = wave; s < S; s += kTreeThreads / kWave) {
-        const int bi = reduce_argmax_row(pv, pi, nparts, s, lane);
+        const int bi = argmax_id(reduce_argmax_row(pv, pi, nparts, s, lane));
         if (lane == 0) { argmax[s] = bi; am[s] = bi; }
     }
     if (in_lds) {

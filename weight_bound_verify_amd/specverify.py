@@ -22,7 +22,7 @@ SV_BLOCK = 32
 STATE_WORDS = 80
 STATE_LEN, STATE_J, STATE_NVALID, STATE_NUSED, STATE_FLAGS, STATE_ROUNDS, STATE_SUMJ, STATE_HIST = 0, 1, 2, 3, 4, 5, 6, 8
 STATE_GATE_AFTER, STATE_ZERO_RUN, STATE_GATED = 72, 73, 74
-FLAG_CAPACITY, FLAG_TOKEN = 1, 2
+FLAG_CAPACITY, FLAG_TOKEN, FLAG_ARGMAX = 1, 2, 4
 STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_ALIGN", 4: "SV_ERR_WORKSPACE",
           5: "SV_ERR_CAPACITY", 6: "SV_ERR_HIP", 7: "SV_ERR_DEVICE"}
 
