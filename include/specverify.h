@@ -168,6 +168,25 @@ int specverify_round(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_
                      hipStream_t stream);
 
 /*
+ * specverify_round_noalloc - specverify_round for callers that cannot allocate device memory
+ * or hand the library a workspace: code under HIP graph capture that must not allocate,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments, results and errors
+ * as specverify_round, minus the workspace: its scratch (the head's per-workgroup argmax
+ * partials) is a library-held static device array of 2 MiB, one per GPU, kept until the
+ * process ends.  The call allocates nothing.  Every call on one GPU shares that GPU's array,
+ * and nothing in it needs to start at zero: calls on one stream are ordered, but calls that
+ * overlap on one GPU (streams not ordered against each other) race and must not be made.
+ * The array holds the argmax partials of any window (S <= SV_MAX_S), and the split sums of a
+ * hidden axis split across workgroups when they fit: a shape whose specverify_verify_
+ * workspace_bytes answer exceeds 2 MiB (a split hidden axis over a large vocabulary, e.g.
+ * V = 30000 at H = 16384) fails with SV_ERR_SHAPE before anything is enqueued.
+ */
+int specverify_round_noalloc(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
+                             const uint16_t* hidden, int32_t K, const int32_t* drafts_in, int32_t* tokens,
+                             int32_t cap, int32_t* state, int32_t ngram_max, int32_t* drafts_out,
+                             int32_t* argmax, float* logits, hipStream_t stream);
+
+/*
  * specverify_verify_q4b32 / specverify_round_q4b32 - the int4 per-block-32 head: the same
  * contract as specverify_verify / specverify_round with half the weight bytes.
  * Page: "Riding Apple's pipelined GPU engine", sections "Quantization on the GPU delegate"

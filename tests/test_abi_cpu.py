@@ -274,3 +274,17 @@ def test_bench_refuses_more_than_one_gpu():
     res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
                          text=True, timeout=120)
     assert res.returncode == 2 and "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_round_noalloc_refuses_scratch_beyond_its_static_array(lib):
+    """A split hidden axis over a large vocabulary needs more than the 2 MiB library-held
+    scratch: refused on the host (SV_ERR_SHAPE) before any HIP call, with the sizes in the
+    message; argument errors come first as for specverify_round."""
+    call = lib.specverify_round_noalloc
+    assert call(A16, A16, 30000, 16384, A16, 8, A16, A16, 100, A16, 3, A16, A16, NULL, NULL) == 2
+    msg = lib.specverify_last_error().decode()
+    assert "4614912" in msg and "2097152" in msg
+    assert call(NULL, A16, 1000, 256, A16, 8, A16, A16, 100, A16, 3, A16, A16, NULL, NULL) == 1
+    assert call(A16, A16, 1000, 256, A16, 0, A16, A16, 100, A16, 3, A16, A16, NULL, NULL) == 2      # K
+    assert call(A16, A16, 1000, 256, A16, 8, A16, A16, 100, A16, 9, A16, A16, NULL, NULL) == 2      # ngram
+    assert call(A16, A16, 1000, 256, A16, 8, A16, A16, 100, A16, 3, A16, A2, NULL, NULL) == 3       # argmax

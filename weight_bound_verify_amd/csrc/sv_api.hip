@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/specverify.h"
@@ -218,6 +219,63 @@ int specverify_round(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_
         return fail(SV_ERR_ALIGN, "int32 buffers must be 4-byte aligned");
     if (int st = check_device()) return st;
     return launch_head(wq, wscale, V, H, hidden, K + 1, argmax, logits, workspace, true, drafts_in, tokens, cap, state,
+                       ngram_max, drafts_out, stream);
+}
+
+namespace {
+
+// Scratch of specverify_round_noalloc: the head workspace (per-workgroup argmax partials for
+// the largest window; split sums too when a split hidden axis needs them and they fit), in a
+// file-scope device array.  Each GPU the library runs on holds its own
+// copy until the process ends.  Host code never passes `scratch` itself to a kernel (on the
+// host it names a stand-in, not the device copy): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current, and is kept here.
+constexpr size_t kStaticScratchBytes = sv::head_partials_bytes(SV_MAX_S);      // 2 MiB
+__device__ __align__(256) char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_addr[64];            // per device; guarded by g_scratch_mu
+
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(SV_ERR_DEVICE, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return SV_OK;
+}
+
+}  // namespace
+
+int specverify_round_noalloc(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H,
+                             const uint16_t* hidden, int32_t K, const int32_t* drafts_in, int32_t* tokens,
+                             int32_t cap, int32_t* state, int32_t ngram_max, int32_t* drafts_out, int32_t* argmax,
+                             float* logits, hipStream_t stream) {
+    if (K < 1 || K > SV_MAX_S - 1) return fail(SV_ERR_SHAPE, "K=%d outside [1, %d]", K, SV_MAX_S - 1);
+    if (int st = check_q8b32(wq, wscale, V, H, hidden, K + 1, SV_MAX_S)) return st;
+    if (!argmax || !drafts_in || !tokens || !state || !drafts_out)
+        return fail(SV_ERR_NULL, "argmax, drafts, tokens and state are required");
+    if (ngram_max < 1 || ngram_max > SV_MAX_NGRAM) return fail(SV_ERR_SHAPE, "ngram_max=%d outside [1, %d]", ngram_max, SV_MAX_NGRAM);
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(argmax, 4) || (logits && !aligned(logits, 4)) || !aligned(drafts_in, 4) || !aligned(tokens, 4) ||
+        !aligned(state, 4) || !aligned(drafts_out, 4))
+        return fail(SV_ERR_ALIGN, "int32 buffers and logits must be 4-byte aligned");
+    const size_t need = sv::head_workspace_bytes(V, H, K + 1);
+    if (need > kStaticScratchBytes)
+        return fail(SV_ERR_SHAPE,
+                    "V=%d H=%d S=%d needs %zu bytes of scratch (the hidden axis is split across workgroups); the "
+                    "library-held scratch holds %zu bytes: use specverify_round with a workspace",
+                    V, H, K + 1, need, kStaticScratchBytes);
+    if (int st = check_device()) return st;
+    void* ws = nullptr;
+    if (int st = scratch_address(&ws)) return st;
+    return launch_head(wq, wscale, V, H, hidden, K + 1, argmax, logits, ws, true, drafts_in, tokens, cap, state,
                        ngram_max, drafts_out, stream);
 }
 

@@ -28,6 +28,7 @@ STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_ALIGN", 4:
 
 EXPORTS = (
     "specverify_propose", "specverify_verify_workspace_bytes", "specverify_verify", "specverify_round",
+    "specverify_round_noalloc",
     "specverify_accept", "specverify_gather_window", "specverify_generate", "specverify_verify_q4b32",
     "specverify_round_q4b32", "specverify_sample_workspace_bytes", "specverify_verify_sample",
     "specverify_accept_sample", "specverify_round_sample", "specverify_propose_tree", "specverify_accept_tree",
@@ -61,6 +62,7 @@ def load():
         "specverify_verify_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
         "specverify_verify": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
         "specverify_round": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+        "specverify_round_noalloc": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P]),
         "specverify_accept": (_I, [_P, _P, _I, _P, _I, _P, _P]),
         "specverify_gather_window": (_I, [_P, _I, _P, _P, _I, _P, _I, _I, _P, _P]),
         "specverify_verify_q4b32": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -197,6 +199,22 @@ def round(wq, wscale, hidden, drafts_in, tokens, state, drafts_out, argmax, ws, 
         int(ngram_max), _ptr(drafts_out, torch.int32, "drafts_out", K), _ptr(argmax, torch.int32, "argmax", S),
         _ptr(logits, torch.float32, "logits", S * V), _ptr(ws, torch.uint8, "workspace"), ws.numel(),
         _stream(stream)))
+
+
+def round_noalloc(wq, wscale, hidden, drafts_in, tokens, state, drafts_out, argmax, ngram_max: int = 3, logits=None,
+                  stream=None) -> None:
+    """``round`` with the library's own static scratch instead of a workspace (allocates nothing)."""
+    V, H = wq.shape
+    S = hidden.shape[0]
+    K = S - 1
+    if hidden.shape[1] != H or tuple(wscale.shape) != (V, H // SV_BLOCK) or drafts_in.numel() < K:
+        raise ValueError("shape mismatch")
+    _check(load().specverify_round_noalloc(
+        _ptr(wq, torch.int8, "wq"), _ptr(wscale, torch.float16, "wscale"), V, H,
+        _ptr(hidden, torch.float16, "hidden"), K, _ptr(drafts_in, torch.int32, "drafts_in", K),
+        _ptr(tokens, torch.int32, "tokens"), tokens.numel(), _ptr(state, torch.int32, "state", STATE_WORDS),
+        int(ngram_max), _ptr(drafts_out, torch.int32, "drafts_out", K), _ptr(argmax, torch.int32, "argmax", S),
+        _ptr(logits, torch.float32, "logits", S * V), _stream(stream)))
 
 
 def verify_q4(wq4, wscale, hidden, argmax, ws, logits=None, stream=None) -> None:
