@@ -7,10 +7,19 @@ The dense-stack workload runs 36 x [rmsnorm, gate/up + SiLU*mul, down + residual
 rmsnorm in front of the head, through specverify_stack; the int4 workload swaps in the int4
 per-block-32 head (specverify_round_q4b32); the sampling and tree workloads run
 specverify_round_sample and specverify_round_tree; the generation-loop workload gathers each
-window from a token-indexed stand-in model on the device (specverify_generate).  The roofline
+window from a token-indexed stand-in model on the device (specverify_generate); the script
+workload verifies windows of a stand-in target whose greedy continuation is a fixed script,
+so that drafts are accepted at a rate strictly between 0 and 1; the decode workload times
+plain S = 1 greedy steps.  The roofline
 object times the dominant kernel: the head matmul, or the stack's gate/up projection.  Inputs are seeded
 synthetic data resident in HBM before the timed region; hidden rows rotate over 64 sets and, for
 heads that could sit in the 256 MB Infinity Cache, over several copies of the weights.
+
+Beyond the K timed steps (the headline value), every run also times batches of rounds (64,
+or 8 for the dense stack; median and interquartile range of rounds/s), the same batches on one
+weight copy when the weights rotate over several, and the verify forward at the workload's S
+against S = 1 (c_v(S) = t(S) / t(1)).  The oracle baseline runs on all host cores and on one
+thread, plus a GEMM-only time with the fp64 dequantized weights cached.
 
 Prints one JSON line.  --gpus N with N > 1 is refused: the library has no multi-GPU path.
 
@@ -55,6 +64,9 @@ WORKLOADS = {
                         "greedy walk down the tree"),
     "c3s17": dict(cid=2, V=248320, H=2048, K=16, drafts="forced", ctx=4096, copy=0.30, layers=0,
                   name="35B-A3B-shaped head H=2048 V=248320 K=16 S=17, forced drafts"),
+    "c4s1": dict(cid=3, V=248320, H=5120, K=0, drafts="none", ctx=16384, copy=0.20, layers=0,
+                 name="decode step of the large-hidden head H=5120 V=248320 S=1 (plain greedy decoding: one-row "
+                      "verify, the anchor committed), the c_v(S) denominator"),
     "c4s2": dict(cid=3, V=248320, H=5120, K=1, drafts="ngram", ctx=16384, copy=0.20, layers=0,
                  name="large-hidden head H=5120 V=248320 K=1 S=2, n-gram drafts over 16384 Zipf(1.1) ids with 20% copied spans"),
     "c4s9": dict(cid=3, V=248320, H=5120, K=8, drafts="ngram", ctx=16384, copy=0.20, layers=0,
@@ -65,6 +77,11 @@ WORKLOADS = {
                   name="generation loop: 35B-A3B-shaped head H=2048 V=248320 K=8 S=9 under a token-indexed stand-in "
                        "model (window rows gathered from a seeded fp16 N(0,1) table [V, H]), n-gram drafts, "
                        "device-resident rounds through specverify_generate"),
+    "c3tied": dict(cid=2, V=248320, H=2048, K=8, drafts="ngram", ctx=4096, copy=0.30, layers=0, model="script",
+                   name="generation loop with acceptance 0 < alpha < 1: 35B-A3B-shaped head H=2048 V=248320 K=8 S=9 "
+                        "under a stand-in target whose greedy continuation is a fixed script (Zipf(1.1) ids with 30% "
+                        "copied spans; window row at position p = sign of the head's code row of the scripted id), "
+                        "n-gram drafts over the first 4096 script ids and the committed stream"),
     "c5": dict(cid=4, V=151936, H=4096, K=8, drafts="ngram", ctx=4096, copy=0.30, layers=36, F=12288,
                name="dense stack 36 x [4096->12288 gate/up, 12288->4096 down] + 4096x151936 head, K=8 S=9"),
 }
@@ -199,9 +216,17 @@ def build_inputs(wl, args, torch, sv, synth):
         wq.append(wq[0].clone())
         ws.append(ws[0].clone())
     rng_h = np.random.default_rng(st.hidden)
-    hidden = torch.from_numpy(synth.fp16_normal(rng_h, (R_SETS, S, wl["H"]))).to(dev)
+    hidden_np = synth.fp16_normal(rng_h, (R_SETS, S, wl["H"]))
+    hidden = torch.from_numpy(hidden_np).to(dev)
     rng_c = np.random.default_rng(st.context)
-    if wl["copy"] is None:
+    script = rows = None
+    if wl.get("model") == "script":
+        # the script: the context, then everything the target will commit (and a margin)
+        n = wl["ctx"] + (args.warmup + args.steps + args.kernel_reps + 2 * args.batches * args.batch_rounds + 64) * S
+        script, frac = synth.zipf_context_with_copies(rng_c, n, V, wl["copy"])
+        ctx = script[:wl["ctx"]].copy()
+        rows = torch.from_numpy(synth.ScriptHidden(q, script).rows()).to(dev)
+    elif wl["copy"] is None:
         ctx, _, _ = synth.uniform_context_with_span(rng_c, wl["ctx"], V, 12, 16)
         frac = None
     else:
@@ -222,94 +247,194 @@ def build_inputs(wl, args, torch, sv, synth):
                 layers[2 * m][li].copy_(torch.from_numpy(qq))
                 layers[2 * m + 1][li].copy_(torch.from_numpy(ss))
     print(f"# inputs ready in {time.time() - t0:.1f} s (weight copies: {copies})", file=sys.stderr, flush=True)
-    return dict(q=q, s=s, wq=wq, ws=ws, hidden=hidden, ctx=ctx, copy_frac=frac, layers=layers, copies=copies)
+    return dict(q=q, s=s, wq=wq, ws=ws, hidden=hidden, hidden_np=hidden_np, ctx=ctx, copy_frac=frac, layers=layers,
+                copies=copies, script=script, rows=rows)
 
 
-def cpu_baseline(wl, inp, table=None, seconds_budget=20.0):
-    """The oracle as it stands, timed on the host on a bounded sample of whole rounds."""
+def _blas_threads():
+    from threadpoolctl import threadpool_info
+    n = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+    return n[0] if n else None
+
+
+class _OracleRound:
+    """One whole round of the oracle as it stands (propose, logits, argmax, accept) on the
+    workload's inputs, on a host copy of the stream."""
+
+    def __init__(self, wl, inp, table):
+        import oracle
+        from weight_bound_verify_amd import synth
+        self.oracle, self.synth, self.wl, self.inp = oracle, synth, wl, inp
+        self.table = table.cpu().numpy() if table is not None else None
+        self.rows = inp["rows"].cpu().numpy() if inp["rows"] is not None else None
+        self.rng = np.random.default_rng(12345)
+        self.tokens = list(inp["ctx"])
+        self.r = 0
+
+    def window(self, drafts):
+        K = self.wl["K"]
+        if self.table is not None:
+            return self.table[[self.tokens[-1]] + [d if d >= 0 else 0 for d in drafts]]
+        if self.rows is not None:
+            p = len(self.tokens) - 1
+            return self.rows[p:p + K + 1]
+        return self.inp["hidden_np"][self.r % 4]
+
+    def logits(self, x):
+        if self.wl.get("fmt") == "q4":
+            return self.oracle.head_logits_q4b32(self.inp["q"], self.inp["s"], x)
+        return self.oracle.head_logits(self.inp["q"], self.inp["s"], x)
+
+    def __call__(self):
+        oracle, wl, K = self.oracle, self.wl, self.wl["K"]
+        if K == 0:                                          # a decode step: S = 1, commit the argmax
+            x = self.inp["hidden_np"][self.r % 4][:1]
+            self.tokens.append(int(oracle.argmax_lowest(self.logits(x))[0]))
+            self.r += 1
+            return
+        if wl.get("tree"):
+            parents, drafts, _, _ = oracle.propose_tree(self.tokens, 3, K, *wl["tree"])
+        else:
+            drafts, _, _ = oracle.propose_scan(self.tokens, 3, K)
+        L = self.logits(self.window(drafts))
+        a = oracle.argmax_lowest(L)
+        if wl["drafts"] == "forced":
+            drafts, _ = self.synth.forced_drafts(self.rng, a, K, wl["V"])
+        if wl.get("temp"):
+            app = oracle.sampling_verify(L, drafts, wl["temp"], SAMPLE_SEED, len(self.tokens))["appended"]
+        elif wl.get("tree"):
+            _, app, _ = oracle.tree_accept(a, parents, drafts)
+        else:
+            _, app = oracle.accept(a, drafts)
+        self.tokens += app
+        self.r += 1
+
+
+def _time_rounds(fn, max_rounds, budget):
+    ts = []
+    while len(ts) < max_rounds and sum(ts) < budget:
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return ts
+
+
+def cpu_baseline(wl, inp, table=None, budget=15.0):
+    """The oracle as it stands, timed on the host: whole rounds on all host cores (BLAS threads
+    = cores), then on one thread, then the GEMM-only part (the window's fp64 logits against a
+    cached fp64 dequantized head)."""
     import oracle
     from threadpoolctl import threadpool_limits
-    from weight_bound_verify_amd import synth
 
-    V, H, K = wl["V"], wl["H"], wl["K"]
-    S = K + 1
-    rng = np.random.default_rng(12345)
-    hid = inp["hidden"][:4].cpu().numpy()
-    tokens = list(inp["ctx"])
+    cores = len(os.sched_getaffinity(0))
     if wl["layers"]:
-        return _cpu_baseline_stack(wl, inp, hid, tokens)
-    rounds = 0
-    t0 = time.perf_counter()
+        return _cpu_baseline_stack(wl, inp, cores)
+    S = wl["K"] + 1
+    with threadpool_limits(limits=cores):
+        blas = _blas_threads()
+        t_all = _time_rounds(_OracleRound(wl, inp, table), 4, budget)
     with threadpool_limits(limits=1):
-        while True:
-            x = hid[rounds % len(hid)]
-            if wl.get("tree"):
-                parents, drafts, _, _ = oracle.propose_tree(tokens, 3, K, *wl["tree"])
-            else:
-                drafts, _, _ = oracle.propose_scan(tokens, 3, K)
-            if table is not None:     # the stand-in model: rows of the oracle's own window
-                ids = [tokens[-1]] + [d if d >= 0 else 0 for d in drafts]
-                x = table[ids].cpu().numpy()
-            if wl.get("fmt") == "q4":
-                L = oracle.head_logits_q4b32(inp["q"], inp["s"], x)
-            else:
-                L = oracle.head_logits(inp["q"], inp["s"], x)
-            a = oracle.argmax_lowest(L)
-            if wl["drafts"] == "forced":
-                drafts, _ = synth.forced_drafts(rng, a, K, V)
-            if wl.get("temp"):
-                app = oracle.sampling_verify(L, drafts, wl["temp"], SAMPLE_SEED, len(tokens))["appended"]
-            elif wl.get("tree"):
-                _, app, _ = oracle.tree_accept(a, parents, drafts)
-            else:
-                _, app = oracle.accept(a, drafts)
-            tokens += app
-            rounds += 1
-            el = time.perf_counter() - t0
-            if el > seconds_budget or rounds >= 8:
-                break
-    return {"value": rounds / el, "unit": "rounds/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rounds} whole rounds of this workload (fp64 dequantize in 8192-row chunks, "
-                      f"fp64 logits for S={S}, "
-                      + ("softmax, Philox noise, residual draws, sampling accept" if wl.get("temp") else
-                         "argmax, tree walk" if wl.get("tree") else "argmax, accept")
-                      + f", n-gram {'tree ' if wl.get('tree') else ''}propose over the {len(inp['ctx'])}-id "
-                      f"context), single thread, {el:.1f} s"}
+        t_one = _time_rounds(_OracleRound(wl, inp, table), 3, budget)
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        wd = (oracle.dequantize_q4b32 if wl.get("fmt") == "q4" else oracle.dequantize)(inp["q"], inp["s"])
+        t_deq = time.perf_counter() - t0
+        xs = [inp["hidden_np"][i % 4][:S].astype(np.float64) for i in range(5)]
+        t_g = []
+        for x in xs:
+            t0 = time.perf_counter()
+            _ = x @ wd.T
+            t_g.append(time.perf_counter() - t0)
+        del wd
+    med = float(np.median(t_all))
+    kind = ("softmax, Philox noise, residual draws, sampling accept" if wl.get("temp") else
+            "argmax, tree walk" if wl.get("tree") else "argmax, accept")
+    return {"value": 1.0 / med, "unit": "rounds/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(t_all)} whole rounds of this workload, median {med:.2f} s per round (fp64 dequantize in "
+                      f"8192-row chunks, fp64 logits for S={S}, {kind}, n-gram "
+                      f"{'tree ' if wl.get('tree') else ''}propose over the {len(inp['ctx'])}-id context and what "
+                      f"the rounds commit), on all {cores} host cores (BLAS threads {blas})",
+            "blas_threads": blas,
+            "single_thread": {"value": 1.0 / float(np.median(t_one)), "unit": "rounds/s", "rounds": len(t_one)},
+            "gemm_only": {"value": 1.0 / float(np.median(t_g)), "unit": "rounds/s", "cores": cores,
+                          "sample": f"median of {len(t_g)} fp64 [{S}, H] x [H, V] products against the fp64 head "
+                                    f"dequantized once ({t_deq:.1f} s) and cached"}}
 
 
-def _cpu_baseline_stack(wl, inp, hid, tokens, seconds_budget=8.0):
+def _cpu_baseline_stack(wl, inp, cores, budget=8.0):
     """The dense-stack round is about a minute of oracle time, so the oracle runs a bounded
     sample: blocks in order (their exact weights, read back from the device) until the budget
     is spent, then one head round on their output, scaled to a whole round as L x mean block +
-    head round."""
+    head round; once on all host cores and once on one thread.  GEMM-only: the three
+    projections of two blocks and the head's logits against cached fp64 dequantized weights."""
     import oracle
     from threadpoolctl import threadpool_limits
 
     K, L = wl["K"], wl["layers"]
-    t0 = time.perf_counter()
-    tb = []
-    with threadpool_limits(limits=1):
-        x = hid[0]
+    S = K + 1
+    hid = inp["hidden_np"][0]
+
+    def layer(li):
+        return [(inp["layers"][2 * m][li].cpu().numpy(), inp["layers"][2 * m + 1][li].cpu().numpy())
+                for m in range(3)]
+
+    def sample():
+        tb = []
+        x = hid
         for li in range(L):
-            layer = [(inp["layers"][2 * m][li].cpu().numpy(), inp["layers"][2 * m + 1][li].cpu().numpy())
-                     for m in range(3)]
+            lay = layer(li)
             t1 = time.perf_counter()
-            x = oracle.mlp_block(x, layer)
+            x = oracle.mlp_block(x, lay)
             tb.append(time.perf_counter() - t1)
-            if sum(tb) > seconds_budget:
+            if sum(tb) > budget:
                 break
         t1 = time.perf_counter()
-        drafts, _, _ = oracle.propose_scan(tokens, 3, K)
-        L_ = oracle.head_logits(inp["q"], inp["s"], oracle.rmsnorm_fp16(x))
-        oracle.accept(oracle.argmax_lowest(L_), drafts)
+        drafts, _, _ = oracle.propose_scan(list(inp["ctx"]), 3, K)
+        Lg = oracle.head_logits(inp["q"], inp["s"], oracle.rmsnorm_fp16(x))
+        oracle.accept(oracle.argmax_lowest(Lg), drafts)
         th = time.perf_counter() - t1
-    el = time.perf_counter() - t0
-    per_round = L * float(np.mean(tb)) + th
-    return {"value": 1.0 / per_round, "unit": "rounds/s", "cores": 1, "kind": "oracle",
-            "sample": f"blocks 0..{len(tb) - 1} of the {L} (fp64 dequantize and the three projections each, "
-                      f"{np.mean(tb):.2f} s per block) and one head round on their output (final norm, fp64 "
-                      f"logits, argmax, accept, n-gram propose: {th:.2f} s), scaled to a whole round as "
-                      f"{L} x block + head; single thread, {sum(tb) + th:.1f} s of oracle work"}
+        return L * float(np.mean(tb)) + th, len(tb), float(np.mean(tb)), th
+
+    with threadpool_limits(limits=cores):
+        blas = _blas_threads()
+        per_all, nb, tblock, thead = sample()
+    with threadpool_limits(limits=1):
+        per_one, nb1, _, _ = sample()
+    with threadpool_limits(limits=cores):
+        x = hid.astype(np.float64)
+        tg = []
+        for li in range(2):
+            for qm, sm in layer(li):
+                wd = oracle.dequantize(qm, sm)
+                xin = np.ones((S, wd.shape[1]))
+                t1 = time.perf_counter()
+                _ = xin @ wd.T
+                tg.append(time.perf_counter() - t1)
+        wd = oracle.dequantize(inp["q"], inp["s"])
+        t1 = time.perf_counter()
+        _ = x @ wd.T
+        th_g = time.perf_counter() - t1
+        del wd
+    per_gemm = L * 3 * float(np.mean(tg)) + th_g
+    return {"value": 1.0 / per_all, "unit": "rounds/s", "cores": cores, "kind": "oracle",
+            "sample": f"blocks 0..{nb - 1} of the {L} (fp64 dequantize and the three projections each, {tblock:.2f} s "
+                      f"per block) and one head round on their output (final norm, fp64 logits, argmax, accept, "
+                      f"n-gram propose: {thead:.2f} s), scaled to a whole round as {L} x block + head; on all {cores} "
+                      f"host cores (BLAS threads {blas})",
+            "blas_threads": blas,
+            "single_thread": {"value": 1.0 / per_one, "unit": "rounds/s", "blocks_sampled": nb1},
+            "gemm_only": {"value": 1.0 / per_gemm, "unit": "rounds/s", "cores": cores,
+                          "sample": f"fp64 products of the 6 projections of blocks 0 and 1 (mean {np.mean(tg):.3f} s) "
+                                    f"and the head ({th_g:.2f} s) against cached fp64 dequantized weights, scaled to "
+                                    f"{L} x 3 projections + head"}}
+
+
+def _batch_stats(ms_per_batch, rounds_per_batch):
+    r = np.array([rounds_per_batch * 1000.0 / m for m in ms_per_batch])
+    q1, med, q3 = np.percentile(r, [25, 50, 75])
+    return {"rounds_per_batch": rounds_per_batch, "batches": len(r), "median_rounds_per_s": round(float(med), 2),
+            "iqr_rounds_per_s": [round(float(q1), 2), round(float(q3), 2)],
+            "median_us_per_round": round(1e6 / float(med), 3)}
 
 
 def main():
@@ -327,6 +452,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=0, help="weight copies to rotate (0 = automatic)")
+    ap.add_argument("--batches", type=int, default=10, help="batches of rounds for the median and IQR")
+    ap.add_argument("--batch-rounds", type=int, default=0, help="rounds per batch (0 = 64, 8 for the dense stack)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=50, help="isolated head launches timed for the roofline")
     ap.add_argument("--calib-copy", action="store_true", help="run a 1 GiB device copy (counter calibration) and exit")
@@ -358,23 +485,27 @@ def main():
     wl = WORKLOADS[args.config]
     V, H, K = wl["V"], wl["H"], wl["K"]
     S = K + 1
+    if not args.batch_rounds:
+        args.batch_rounds = 8 if wl["layers"] else 64
     inp = build_inputs(wl, args, torch, sv, synth)
     wq, ws, hidden = inp["wq"], inp["ws"], inp["hidden"]
     copies = inp["copies"]
+    decode = K == 0
 
     # device-resident round state
-    total_rounds = args.warmup + args.steps + args.kernel_reps + 8
+    total_rounds = args.warmup + args.steps + args.kernel_reps + 2 * args.batches * args.batch_rounds + 8
     cap = len(inp["ctx"]) + total_rounds * S + 2 * S
     tokens = torch.zeros(cap, dtype=torch.int32, device=dev)
     tokens[:len(inp["ctx"])] = torch.from_numpy(inp["ctx"]).to(dev)
     state = sv.new_state(dev)
     state[sv.STATE_LEN] = len(inp["ctx"])
-    drafts = torch.empty(K, dtype=torch.int32, device=dev)
+    drafts = torch.empty(max(K, 1), dtype=torch.int32, device=dev)
     argmax = torch.empty(S, dtype=torch.int32, device=dev)
     temp = wl.get("temp")
     work = sv.workspace(sv.sample_workspace_bytes(V, H, S) if temp else sv.verify_workspace_bytes(V, H, S), dev)
+    work1 = sv.workspace(sv.verify_workspace_bytes(V, H, 1), dev)
 
-    table = window = None
+    table = window = rows = None
     if wl.get("model") == "table":
         # token-indexed stand-in model: hidden row of a window position = table[token]
         gen = torch.Generator(device=dev)
@@ -383,8 +514,18 @@ def main():
         window = torch.empty((S, H), dtype=torch.float16, device=dev)
         h_last = torch.empty((1, H), dtype=torch.float16, device=dev)
         sv.gather_window(tokens, state, drafts[:0], table, h_last)      # the context's last token
+    elif wl.get("model") == "script":
+        # position-indexed stand-in: the window at stream length n is rows[n-1 .. n-1+K], picked on
+        # the device from the state word (specverify_gather_positions, no host synchronisation)
+        rows = inp["rows"]
+        window = torch.empty((S, H), dtype=torch.float16, device=dev)
+        h_last = rows[len(inp["ctx"]) - 1:len(inp["ctx"])].clone()
     else:
         h_last = torch.from_numpy(synth.fp16_normal(synth.streams(wl["cid"]).h_last, (1, H))).to(dev)
+
+    def gather_script(stream=None):
+        sv.gather_positions(state, cap, rows, window, stream=stream)
+
     # anchor bootstrap: S = 1 verify of the last context row, then accept with K = 0 commits a0
     a0 = torch.empty(1, dtype=torch.int32, device=dev)
     head_verify = sv.verify_q4 if wl.get("fmt") == "q4" else sv.verify
@@ -400,7 +541,7 @@ def main():
             sv.round_sample(w_, s_, x_, d_in_, temp, SAMPLE_SEED, tokens_, state_, drafts_, work_, 3, argmax_,
                             stream=stream)
     else:
-        head_verify(wq[0], ws[0], h_last, a0, sv.workspace(sv.verify_workspace_bytes(V, H, 1), dev))
+        head_verify(wq[0], ws[0], h_last, a0, work1)
         sv.accept(a0, None, tokens, state)
 
     forced = None
@@ -420,6 +561,9 @@ def main():
         nbuf = torch.empty((S, H), dtype=torch.float16, device=dev)
         xl_buf = torch.empty((wl["layers"], S, H), dtype=torch.float16, device=dev)
         swork = sv.workspace(sv.stack_forward_workspace_bytes(H, F, S), dev)
+        nbuf1 = torch.empty((1, H), dtype=torch.float16, device=dev)
+        xl_buf1 = torch.empty((wl["layers"], 1, H), dtype=torch.float16, device=dev)
+        swork1 = sv.workspace(sv.stack_forward_workspace_bytes(H, F, 1), dev)
 
     # A round is verify -> accept -> propose (the next round's drafts), through the fused
     # entry point: one launch when the hidden axis needs no split.  The first drafts come
@@ -432,14 +576,23 @@ def main():
         def head_round(w_, s_, x_, d_in_, tokens_, state_, drafts_, argmax_, work_, stream=None):
             sv.round_tree(w_, s_, x_, parents, d_in_, tokens_, state_, parents, drafts_, argmax_, work_, 3,
                           tree[0], tree[1], stream=stream)
-    else:
+    elif not decode:
         sv.propose(tokens, state, drafts, 3)
 
-    def round_(r):
-        c = r % copies
+    def round_(r, single=False):
+        c = 0 if single else r % copies
+        if decode:
+            # a plain greedy step: one-row verify, the argmax committed as the next anchor
+            head_verify(wq[c], ws[c], hidden[r % R_SETS][:1], a0, work1)
+            sv.accept(a0, None, tokens, state)
+            return
         if table is not None:
             # gather the window [a0, drafts] from the stand-in model, verify, accept, draft
             sv.generate(wq[c], ws[c], table, tokens, state, drafts, window, argmax, work, 1)
+            return
+        if rows is not None:
+            gather_script()
+            head_round(wq[c], ws[c], window, drafts, tokens, state, drafts, argmax, work)
             return
         if wl["layers"]:
             # the whole stack in one call (2 launches per block); the round's input rows stay
@@ -450,6 +603,31 @@ def main():
             x = hidden[r % R_SETS]
         d_in = forced[r % R_SETS] if forced is not None else drafts
         head_round(wq[c], ws[c], x, d_in, tokens, state, drafts, argmax, work)
+
+    def verify_forward(r, rows_):
+        """The verify forward alone at `rows_` window rows (the stack in front for the dense
+        stack): the numerator and denominator of c_v(S)."""
+        c = r % copies
+        x = hidden[r % R_SETS][:rows_]
+        if wl["layers"]:
+            if rows_ == 1:
+                sv.stack(*inp["layers"], x, nbuf1, swork1, 1e-6, x_layers=xl_buf1)
+                x = nbuf1
+            else:
+                sv.stack(*inp["layers"], x, nbuf, swork, 1e-6, x_layers=xl_buf)
+                x = nbuf
+        head_verify(wq[c], ws[c], x, argmax[:rows_], work if rows_ > 1 else work1)
+
+    def time_batches(fn, n, per):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        evs[0].record()
+        for b in range(n):
+            for i in range(per):
+                fn(b * per + i)
+            evs[b + 1].record()
+        torch.cuda.synchronize()
+        return [evs[b].elapsed_time(evs[b + 1]) for b in range(n)]
 
     for r in range(args.warmup):
         round_(r)
@@ -466,10 +644,35 @@ def main():
     st1 = state.cpu().numpy()
     if st1[sv.STATE_FLAGS]:
         raise RuntimeError(f"device state flags {st1[sv.STATE_FLAGS]}")
-    rounds = int(st1[sv.STATE_ROUNDS] - st0[sv.STATE_ROUNDS])
-    assert rounds == args.steps
-    hist = (st1[sv.STATE_HIST:sv.STATE_HIST + K + 1] - st0[sv.STATE_HIST:sv.STATE_HIST + K + 1]).tolist()
-    sum_j = int(st1[sv.STATE_SUMJ] - st0[sv.STATE_SUMJ])
+    if decode:
+        assert st1[sv.STATE_LEN] - st0[sv.STATE_LEN] == args.steps
+        hist, sum_j = [args.steps], 0
+    else:
+        rounds = int(st1[sv.STATE_ROUNDS] - st0[sv.STATE_ROUNDS])
+        assert rounds == args.steps
+        hist = (st1[sv.STATE_HIST:sv.STATE_HIST + K + 1] - st0[sv.STATE_HIST:sv.STATE_HIST + K + 1]).tolist()
+        sum_j = int(st1[sv.STATE_SUMJ] - st0[sv.STATE_SUMJ])
+
+    # batches of rounds (median, IQR), rotated weights and one copy; c_v(S)
+    base = args.warmup + args.steps
+    batches = _batch_stats(time_batches(lambda i: round_(base + i), args.batches, args.batch_rounds),
+                           args.batch_rounds)
+    single = None
+    if copies > 1:
+        single = _batch_stats(time_batches(lambda i: round_(base + i, single=True), args.batches, args.batch_rounds),
+                              args.batch_rounds)
+    cv = None
+    if not temp and not tree:
+        t_s = time_batches(lambda i: verify_forward(i, S), args.batches, args.batch_rounds)
+        t_1 = time_batches(lambda i: verify_forward(i, 1), args.batches, args.batch_rounds)
+        us_s = 1000.0 * float(np.median(t_s)) / args.batch_rounds
+        us_1 = 1000.0 * float(np.median(t_1)) / args.batch_rounds
+        cv = {"S": S, "us_verify_S": round(us_s, 3), "us_verify_1": round(us_1, 3), "c_v": round(us_s / us_1, 4),
+              "note": "median over batches of the verify forward alone (matmul and argmax"
+                      + (", with the dense stack in front" if wl["layers"] else "") + ") at S rows and at one row"}
+    st2 = state.cpu().numpy()
+    if st2[sv.STATE_FLAGS]:
+        raise RuntimeError(f"device state flags {st2[sv.STATE_FLAGS]}")
 
     # roofline of the dominant kernel: the head matmul with its fused argmax (or sampling)
     # stage 1, or for the dense stack its gate/up projection (block 0 of a whole-stack call;
@@ -484,8 +687,13 @@ def main():
         sv.profile_next_matmul(e0, e1, stream=stream)
         if wl["layers"]:
             sv.stack(*inp["layers"], x, nbuf, swork, 1e-6, x_layers=xl_buf, stream=stream)
+        elif decode:
+            head_verify(wq[c], ws[c], x[:1], a0, work1, stream=stream)
         elif table is not None:
             sv.generate(wq[c], ws[c], table, tokens, state, drafts, window, argmax, work, 1, stream=stream)
+        elif rows is not None:
+            gather_script(stream)
+            head_round(wq[c], ws[c], window, drafts, tokens, state, drafts, argmax, work, stream=stream)
         else:
             head_round(wq[c], ws[c], x, d_in, tokens, state, drafts, argmax, work, stream=stream)
         durs.append((e0, e1))
@@ -526,9 +734,17 @@ def main():
                                    "draw) stage 1 (one launch per round)" if temp else
                                    " head matmul with the fused argmax stage 1 (one launch per round)")),
                      "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": kb},
+        "batches": dict(batches, weight_copies=copies,
+                        pct_of_peak_hbm=round(100.0 * round_bytes * batches["median_rounds_per_s"] / 1e9
+                                              / PEAK_HBM_GBPS, 2)),
         "accept_hist": hist,
         "tokens_per_round": round((args.steps + sum_j) / args.steps, 3),
     }
+    if single is not None:
+        out["batches_single_copy"] = dict(single, weight_copies=1, note="the same rounds on one weight copy, which "
+                                          "the 256 MB Infinity Cache can partly serve across rounds")
+    if cv is not None:
+        out["c_v"] = cv
     if tree:
         out["config"]["tree"] = {"branches": tree[0], "depth": tree[1], "nodes": K}
     if temp:
@@ -536,7 +752,7 @@ def main():
         out["config"]["seed"] = SAMPLE_SEED
     if inp["copy_frac"] is not None:
         out["config"]["context_copy_fraction"] = round(inp["copy_frac"], 3)
-    if table is not None:
+    if table is not None or rows is not None:
         # tokens/s accounting against the feasibility page's C-value model: with each draft
         # accepted independently with probability alpha, a round commits
         # E(alpha, K) = (1 - alpha^(K+1)) / (1 - alpha) tokens; alpha estimated from the
@@ -548,6 +764,9 @@ def main():
         out["alpha_hat"] = round(alpha, 4)
         out["expected_tokens_per_round"] = round(e_model, 3)
         out["gated_at_round"] = int(st1[sv.STATE_GATED])
+    if rows is not None:
+        n = int(st2[sv.STATE_LEN])
+        out["script_reproduced"] = bool(np.array_equal(tokens[:n].cpu().numpy(), inp["script"][:n]))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, table)
     print(json.dumps(out), flush=True)

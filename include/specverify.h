@@ -314,6 +314,22 @@ int specverify_gather_window(const int32_t* tokens, int32_t cap, int32_t* state,
                              int32_t H, uint16_t* window, hipStream_t stream);
 
 /*
+ * specverify_gather_positions - the window rows of a position-indexed stand-in model, whose
+ * row after a prefix of p + 1 ids is rows[p] whatever the ids (a target whose greedy
+ * continuation is fixed in advance, e.g. a recorded trajectory):
+ *   window[i] = rows[len - 1 + i] for i = 0 .. K, len = state[0]
+ * so rounds over such a target stay on the device.  Rows after a rejected draft are never used
+ * by an accept, so this is a valid target for speculative decoding ("Stream C - Speculative
+ * decoding", control-logic proof: the committed stream is the target's greedy stream).
+ *   rows    fp16 [nrows][H], 16-byte aligned;  window fp16 [K+1][H] output, 16-byte aligned
+ *   K       0 .. SV_MAX_S-1;  cap: capacity of the caller's token buffer (len is checked against it)
+ * A position outside [0, nrows) or a length outside [1, cap] writes a zero row and sets bit 0
+ * of state[4].
+ */
+int specverify_gather_positions(int32_t* state, int32_t cap, const uint16_t* rows, int32_t nrows, int32_t H,
+                                int32_t K, uint16_t* window, hipStream_t stream);
+
+/*
  * specverify_generate - `rounds` speculative-decoding rounds enqueued back to back with no
  * host synchronisation ("Riding Apple's pipelined GPU engine", "Why hand-rolled per-token
  * loops lose": encode and return, only sampled ids leave the GPU).  Each round is

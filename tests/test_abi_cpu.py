@@ -288,3 +288,13 @@ def test_round_noalloc_refuses_scratch_beyond_its_static_array(lib):
     assert call(A16, A16, 1000, 256, A16, 0, A16, A16, 100, A16, 3, A16, A16, NULL, NULL) == 2      # K
     assert call(A16, A16, 1000, 256, A16, 8, A16, A16, 100, A16, 9, A16, A16, NULL, NULL) == 2      # ngram
     assert call(A16, A16, 1000, 256, A16, 8, A16, A16, 100, A16, 3, A16, A2, NULL, NULL) == 3       # argmax
+
+
+def test_gather_positions_argument_errors(lib):
+    call = lib.specverify_gather_positions
+    assert call(NULL, 10, A16, 40, 256, 4, A16, NULL) == 1
+    assert call(A16, 10, A16, 40, 250, 4, A16, NULL) == 2          # H % 32
+    assert call(A16, 10, A16, 0, 256, 4, A16, NULL) == 2            # no rows
+    assert call(A16, 10, A16, 40, 256, 64, A16, NULL) == 2          # K
+    assert call(A16, 0, A16, 40, 256, 4, A16, NULL) == 5            # cap
+    assert call(A16, 10, A2, 40, 256, 4, A16, NULL) == 3            # rows alignment

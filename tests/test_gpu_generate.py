@@ -158,3 +158,81 @@ def test_graph_replay_equals_eager_rounds():
     got, st_g = g.result()
     assert got == want
     assert np.array_equal(st_g, st_e)
+
+
+@pytest.mark.parametrize("V,H,K,n_max", [(5000, 512, 8, 3), (30000, 1024, 4, 3), (2048, 256, 16, 2)])
+def test_script_target_rounds_equal_oracle_spec_decode(V, H, K, n_max):
+    """The stand-in target whose greedy continuation is a fixed script (Zipf ids with 30% copied
+    spans; the window row at position p is the sign pattern of the scripted id's code row), run
+    round after round on the device (specverify_gather_positions picks the window from the
+    state word, then the fused round), against oracle.spec_decode with the same target: identical committed streams,
+    accept length per round and histogram; greedy decoding of the target reproduces the script;
+    the acceptance rate lies strictly between 0 and 1."""
+    say(f"script target V={V} H={H} K={K} n={n_max}")
+    S = K + 1
+    rng = np.random.default_rng(V + K)
+    q, s = synth.quantized_head(np.random.SeedSequence(V + H), V, H)
+    ctx_len, rounds = 600, 120
+    script, _ = synth.zipf_context_with_copies(rng, ctx_len + rounds * S + 2 * S, V, 0.3)
+    model = synth.ScriptHidden(q, script)
+    rows = to_dev(model.rows())
+    cap = len(script)
+    buf = np.zeros(cap, np.int32)
+    buf[:ctx_len] = script[:ctx_len]
+    tokens, state = to_dev(buf), sv.new_state(dev())
+    state[sv.STATE_LEN] = ctx_len
+    wq, ws = to_dev(q), to_dev(s)
+    work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev())
+    a0 = torch.empty(1, dtype=torch.int32, device=dev())
+    sv.verify(wq, ws, rows[ctx_len - 1:ctx_len].clone(), a0, sv.workspace(sv.verify_workspace_bytes(V, H, 1), dev()))
+    sv.accept(a0, None, tokens, state)
+    drafts = torch.empty(K, dtype=torch.int32, device=dev())
+    sv.propose(tokens, state, drafts, n_max)
+    window = torch.empty((S, H), dtype=torch.float16, device=dev())
+    am = torch.empty(S, dtype=torch.int32, device=dev())
+    js = []
+    for _ in range(rounds):
+        sv.gather_positions(state, cap, rows, window)
+        sv.round(wq, ws, window, drafts, tokens, state, drafts, am, work, n_max)
+        js.append(state[sv.STATE_J].clone())
+    torch.cuda.synchronize()
+    st = state.cpu().numpy()
+    assert st[sv.STATE_FLAGS] == 0 and st[sv.STATE_ROUNDS] == rounds
+    n = int(st[sv.STATE_LEN])
+    got = tokens[:n].cpu().tolist()
+    assert got == script[:n].tolist(), "greedy decoding of the script target is the script"
+
+    def argmax_fn(rws):
+        return oracle.argmax_lowest(oracle.head_logits(q, s, rws))
+
+    stats = {}
+    ref = oracle.spec_decode(script[:ctx_len].tolist(), model, argmax_fn, n - ctx_len, K, n_max, stats=stats)
+    assert got == ref
+    j_dev = [int(j) for j in torch.stack(js).cpu().tolist()]
+    assert j_dev == stats["accepted"][:rounds]
+    hist = np.bincount(j_dev, minlength=K + 1)
+    assert hist.tolist() == st[sv.STATE_HIST:sv.STATE_HIST + K + 1].tolist()
+    alpha = sum(j_dev) / (sum(j_dev) + int(hist[:K].sum()))
+    assert 0.0 < alpha < 1.0, alpha
+
+
+def test_gather_positions_rows_and_out_of_range():
+    """window[i] = rows[len - 1 + i]; a position past the rows or a bad length writes a zero row
+    and sets the capacity flag."""
+    rows = to_dev(synth.fp16_normal(np.random.default_rng(5), (40, 256)))
+    win = torch.full((5, 256), float("nan"), dtype=torch.float16, device=dev())
+    st = sv.new_state(dev())
+    st[sv.STATE_LEN] = 10
+    sv.gather_positions(st, 100, rows, win)
+    torch.cuda.synchronize()
+    assert torch.equal(win, rows[9:14]) and int(st[sv.STATE_FLAGS]) == 0
+    st[sv.STATE_LEN] = 38                                  # positions 37 .. 41: the last two are past the rows
+    sv.gather_positions(st, 100, rows, win)
+    torch.cuda.synchronize()
+    assert torch.equal(win[:3], rows[37:40]) and not win[3:].any()
+    assert int(st[sv.STATE_FLAGS]) == sv.FLAG_CAPACITY
+    st[sv.STATE_FLAGS] = 0
+    st[sv.STATE_LEN] = 101                                 # longer than the token buffer
+    sv.gather_positions(st, 100, rows, win)
+    torch.cuda.synchronize()
+    assert not win.any() and int(st[sv.STATE_FLAGS]) == sv.FLAG_CAPACITY

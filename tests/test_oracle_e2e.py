@@ -144,3 +144,23 @@ def test_gate_with_never_hitting_and_always_hitting_drafters():
     got = oracle.spec_decode(ctx, hidden_fn, argmax_fn, n_new, K, 3, drafter=perfect, stats=st, gate_after=1)
     assert got == ref[:len(ctx) + n_new]
     assert st["gated_after_round"] is None and set(st["accepted"]) == {K}
+
+
+def test_script_target_greedy_decoding_reproduces_the_script():
+    """The script stand-in (row at position p = sign pattern of the scripted id's code row):
+    plain greedy decoding and speculative decoding with the n-gram drafter both reproduce the
+    script, and the drafter's acceptance rate lies strictly between 0 and 1 (the script copies
+    30% of its spans, as the contexts do)."""
+    V, H, K = 3000, 256, 8
+    q, s = synth.quantized_head(np.random.SeedSequence(77), V, H)
+    script, _ = synth.zipf_context_with_copies(np.random.default_rng(78), 1200, V, 0.3)
+    model = synth.ScriptHidden(q, script)
+    argmax_fn = lambda rows: oracle.argmax_lowest(oracle.head_logits(q, s, rows))
+    ctx = script[:400].tolist()
+    assert oracle.greedy_decode(ctx, model, argmax_fn, 200) == script[:600].tolist()
+    st = {}
+    assert oracle.spec_decode(ctx, model, argmax_fn, 700, K, 3, stats=st) == script[:1100].tolist()
+    js = np.array(st["accepted"])
+    alpha = js.sum() / (js.sum() + (js < K).sum())
+    assert 0.0 < alpha < 1.0
+    assert np.array_equal(model.rows()[399], model(script[:400]))

@@ -624,6 +624,19 @@ int specverify_gather_window(const int32_t* tokens, int32_t cap, int32_t* state,
     return e == hipSuccess ? SV_OK : hip_fail(e, "gather launch");
 }
 
+int specverify_gather_positions(int32_t* state, int32_t cap, const uint16_t* rows, int32_t nrows, int32_t H,
+                                int32_t K, uint16_t* window, hipStream_t stream) {
+    if (!state || !rows || !window) return fail(SV_ERR_NULL, "state, rows and window are required");
+    if (K < 0 || K > SV_MAX_S - 1) return fail(SV_ERR_SHAPE, "K=%d outside [0, %d]", K, SV_MAX_S - 1);
+    if (nrows < 1 || H < SV_BLOCK || H > 65536 || H % SV_BLOCK) return fail(SV_ERR_SHAPE, "nrows=%d H=%d", nrows, H);
+    if (cap < 1) return fail(SV_ERR_CAPACITY, "cap=%d", cap);
+    if (!aligned(state, 4) || !aligned(rows, 16) || !aligned(window, 16))
+        return fail(SV_ERR_ALIGN, "state 4-byte, rows and window 16-byte alignment required");
+    if (int st = check_device()) return st;
+    hipError_t e = sv::launch_gather_positions(state, cap, rows, nrows, H, K + 1, window, stream);
+    return e == hipSuccess ? SV_OK : hip_fail(e, "gather launch");
+}
+
 int specverify_generate(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, const uint16_t* table,
                         int32_t K, int32_t rounds, int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max,
                         int32_t* drafts, uint16_t* window, int32_t* argmax, void* workspace,

@@ -119,6 +119,9 @@ hipError_t launch_propose(const int32_t* tokens, int cap, int32_t* state, int nm
 // Window rows [tokens[len-1], drafts (pads -> 0)] of a token-indexed table [V][H] into out [K+1][H].
 hipError_t launch_gather_window(const int32_t* tokens, int cap, int32_t* state, const int32_t* drafts, int K,
                                 const uint16_t* table, int V, int H, uint16_t* out, hipStream_t stream);
+// Window rows [rows[len-1], ..., rows[len-1+S-1]] of a position-indexed model [nrows][H] into out [S][H].
+hipError_t launch_gather_positions(int32_t* state, int cap, const uint16_t* rows, int nrows, int H, int S,
+                                   uint16_t* out, hipStream_t stream);
 hipError_t launch_accept(const int32_t* argmax, const int32_t* drafts, int K, int32_t* tokens,
                          int cap, int32_t* state, hipStream_t stream);
 // Per window row: t = sum of `ks` split partial sums [ks][S][N] (+ residual), y = fp16(t)

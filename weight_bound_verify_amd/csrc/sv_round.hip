@@ -51,7 +51,31 @@ __global__ __launch_bounds__(256) void gather_window_kernel(const int32_t* __res
     for (int i = threadIdx.x; i < H / 8; i += 256) dst[i] = ok ? src[i] : zero;
 }
 
+// Window rows of a position-indexed stand-in model: row i = rows[len - 1 + i] (the row after a
+// prefix of len + i ids), one workgroup per row, 16-byte copies.  A position outside
+// [0, nrows) or a length outside [1, cap] writes a zero row and sets the capacity flag.
+__global__ __launch_bounds__(256) void gather_positions_kernel(int32_t* __restrict__ state, int cap,
+                                                               const uint16_t* __restrict__ rows, int nrows, int H,
+                                                               uint16_t* __restrict__ out) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    const int r = blockIdx.x;
+    const int len = state[SV_STATE_LEN];
+    const long long p = (long long)len - 1 + r;
+    const bool ok = len >= 1 && len <= cap && p >= 0 && p < nrows;
+    if (threadIdx.x == 0 && !ok) atomicOr(&state[SV_STATE_FLAGS], SV_FLAG_CAPACITY);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(rows + (size_t)(ok ? p : 0) * H);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + (size_t)r * H);
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    for (int i = threadIdx.x; i < H / 8; i += 256) dst[i] = ok ? src[i] : zero;
+}
+
 }  // namespace
+
+hipError_t launch_gather_positions(int32_t* state, int cap, const uint16_t* rows, int nrows, int H, int S,
+                                   uint16_t* out, hipStream_t stream) {
+    hipLaunchKernelGGL(gather_positions_kernel, dim3(S), dim3(256), 0, stream, state, cap, rows, nrows, H, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_gather_window(const int32_t* tokens, int cap, int32_t* state, const int32_t* drafts, int K,
                                 const uint16_t* table, int V, int H, uint16_t* out, hipStream_t stream) {

@@ -29,7 +29,7 @@ STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_ALIGN", 4:
 EXPORTS = (
     "specverify_propose", "specverify_verify_workspace_bytes", "specverify_verify", "specverify_round",
     "specverify_round_noalloc",
-    "specverify_accept", "specverify_gather_window", "specverify_generate", "specverify_verify_q4b32",
+    "specverify_accept", "specverify_gather_window", "specverify_gather_positions", "specverify_generate", "specverify_verify_q4b32",
     "specverify_round_q4b32", "specverify_sample_workspace_bytes", "specverify_verify_sample",
     "specverify_accept_sample", "specverify_round_sample", "specverify_propose_tree", "specverify_accept_tree",
     "specverify_round_tree", "specverify_generate_sample", "specverify_generate_tree",
@@ -65,6 +65,7 @@ def load():
         "specverify_round_noalloc": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P]),
         "specverify_accept": (_I, [_P, _P, _I, _P, _I, _P, _P]),
         "specverify_gather_window": (_I, [_P, _I, _P, _P, _I, _P, _I, _I, _P, _P]),
+        "specverify_gather_positions": (_I, [_P, _I, _P, _I, _I, _I, _P, _P]),
         "specverify_verify_q4b32": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
         "specverify_round_q4b32": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t,
                                         _P]),
@@ -357,6 +358,17 @@ def gather_window(tokens, state, drafts, table, window, stream=None) -> None:
         _ptr(tokens, torch.int32, "tokens"), tokens.numel(), _ptr(state, torch.int32, "state", STATE_WORDS),
         _ptr(drafts, torch.int32, "drafts", K) if K > 0 else None, K, _ptr(table, torch.float16, "table"), V, H,
         _ptr(window, torch.float16, "window"), _stream(stream)))
+
+
+def gather_positions(state, cap: int, rows, window, stream=None) -> None:
+    """window[i] = rows[state[0] - 1 + i] (a position-indexed stand-in model); ``cap`` is the
+    token buffer's capacity."""
+    S, H = window.shape
+    if rows.shape[1] != H:
+        raise ValueError("rows and window must have the same width")
+    _check(load().specverify_gather_positions(_ptr(state, torch.int32, "state", STATE_WORDS), int(cap),
+                                              _ptr(rows, torch.float16, "rows"), rows.shape[0], H, S - 1,
+                                              _ptr(window, torch.float16, "window"), _stream(stream)))
 
 
 def generate(wq, wscale, table, tokens, state, drafts, window, argmax, ws, rounds: int, ngram_max: int = 3,

@@ -261,3 +261,27 @@ class HashHidden:
         digest = hashlib.blake2b(b, digest_size=8, key=self.salt.to_bytes(8, "little")).digest()
         rng = np.random.default_rng(int.from_bytes(digest, "little"))
         return rng.standard_normal(self.H, dtype=np.float32).astype(np.float16)
+
+
+class ScriptHidden:
+    """A stand-in target whose greedy continuation is a fixed script ``T`` (ids): the hidden
+    row at position p (the row after a prefix of p + 1 ids) is sign(q[T[p + 1]]) as fp16, the
+    sign pattern of the head's own code row of the scripted id.  That row's logit on its own
+    id sums |code| x scale over the whole hidden axis, every other id's logit is a signed random
+    walk, so the argmax is the scripted id by a wide margin, and greedy decoding of the script
+    reproduces it.  Rows depend only on the position; rows after a rejected draft are never
+    used by an accept, so this is a valid target for speculative decoding.  With T built like
+    the contexts (Zipf ids and copied spans), the n-gram drafter's acceptance rate lies
+    strictly between 0 and 1.
+
+    ``rows()`` gives all rows [len(T) - 1, H]: row p belongs to position p."""
+
+    def __init__(self, q: np.ndarray, script: np.ndarray):
+        self.q = q
+        self.script = np.asarray(script, dtype=np.int64)
+
+    def rows(self) -> np.ndarray:
+        return np.sign(self.q[self.script[1:]]).astype(np.float16)
+
+    def __call__(self, prefix) -> np.ndarray:
+        return np.sign(self.q[self.script[len(prefix)]]).astype(np.float16)
