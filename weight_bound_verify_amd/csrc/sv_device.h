@@ -48,6 +48,29 @@ __device__ __forceinline__ uint16_t f2h(float f) {            // round to neares
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads and stores in flight are not
+// waited for (a plain __syncthreads() also waits for every outstanding global store).  For
+// barriers across which only LDS data is exchanged.
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Maximum of a 32-bit unsigned value over the 64 lanes of a wave, returned to every lane: DPP
+// steps within quads, half rows and rows, then row broadcasts carry each row's maximum into the
+// last row, whose lane 63 holds the wave's maximum (max is idempotent, so lanes combined twice
+// do no harm).  All lanes of the wave must be active.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Argmax order: larger value first, then lower index.  -0.0 == +0.0.
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);

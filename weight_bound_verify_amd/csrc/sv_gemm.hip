@@ -670,12 +670,15 @@ __global__ __launch_bounds__(256) void combine_kernel(GemmArgs a) {
 
 // Round tail, one workgroup of kTailThreads: reduce the per-workgroup argmax partials of the
 // head launch in a fixed order into argmax[S] and, for a round (drafts_out != null), run the
-// greedy accept and draft the next round.  The loads that do not depend on the argmax (state,
-// drafts, the whole stream when it fits in LDS) are issued together with the partial loads,
-// so the tail costs about one memory round trip; accept and drafter then work from LDS.
+// greedy accept and draft the next round.  The argmax is the critical path, so each wave's
+// partial loads are issued first; the loads that do not depend on the argmax (state, drafts,
+// the whole stream when it fits in LDS) follow at once, so the tail costs about one memory
+// round trip; accept and drafter then work from LDS, behind barriers that order LDS only.
 // A kernel boundary, not a device-scope fence in every matmul workgroup, orders the partials.
 constexpr int kTailThreads = 1024;
 constexpr int kTailIds = 32768;                      // stream ids the tail can hold in LDS (128 KB)
+constexpr int kTailPart = 8;                         // partial loads in flight per lane and row
+constexpr int kTailHead = 8192;                      // stream ids loaded before the length is known
 
 __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* __restrict__ pv,
                                                                   const int* __restrict__ pi, int nparts, int S,
@@ -693,61 +696,93 @@ __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* _
     const int wave = threadIdx.x >> 6;
     const int K = S - 1;
     const bool round = drafts_out != nullptr;
+    constexpr int kWaves = kTailThreads / kWave;
+    // the stream length first (a scalar load): the stream beyond its first kTailHead ids is
+    // loaded only up to it
+    const int len_s = round ? state[SV_STATE_LEN] : 0;
 
-    // Every load that does not depend on another is issued first: the stream's first
-    // min(cap, kTailIds) ids (whatever its length), the state, the drafts and the partials;
-    // the stream goes to LDS once the partials are reduced.
+    // the first kTailPart * 64 partials of this wave's first window row
+    float v0[kTailPart];
+    int i0[kTailPart];
+#pragma unroll
+    for (int u = 0; u < kTailPart; ++u) {
+        const int p = u * kWave + lane;
+        const bool ok = wave < S && p < nparts;
+        v0[u] = ok ? pv[(size_t)wave * kGridMax + p] : -INFINITY;
+        i0[u] = ok ? pi[(size_t)wave * kGridMax + p] : INT_MAX;
+    }
+
+    // then every other load that does not depend on the argmax: the stream's first
+    // min(cap, kTailHead) ids (whatever its length), then the rest of the stream up to its length,
+    // the state and the drafts; the stream goes to LDS once the partials are reduced
     int len0 = 0, d = -1;
     bool in_lds = false;
-    IdPrefix<kTailIds / (4 * kTailThreads)> pre;
+    IdPrefix<kTailHead / (4 * kTailThreads)> pre;
+    IdPrefix<(kTailIds - kTailHead) / (4 * kTailThreads)> pre2;
     const int navail = round ? (cap < kTailIds ? cap : kTailIds) : 0;
+    const int nhead = navail < kTailHead ? navail : kTailHead;
     const bool vec = round && (reinterpret_cast<uintptr_t>(tokens) & 15) == 0;
-    if (vec) prefix_load(tokens, navail, pre);
+    if (vec) prefix_load(tokens, nhead, pre);
     StateCache sc{0, 0};
     if (round) {
-        len0 = state[SV_STATE_LEN];
+        len0 = len_s;
         if (wave == 0) {
             sc = state_cache_load(state, lane);
             if (lane < K) d = drafts_in[lane];
         }
         in_lds = len0 >= 0 && len0 + K + 1 <= cap && len0 + K + 1 <= kTailIds;
     }
-    for (int s = wave; s < S; s += kTailThreads / kWave) {
+    for (int s = wave; s < S; s += kWaves) {
         float bv = -INFINITY;
         int bi = INT_MAX;
-        for (int p0 = 0; p0 < nparts; p0 += 8 * kWave) {            // 8 loads in flight per lane
-            float v[8];
-            int ix[8];
+        for (int p0 = 0; p0 < nparts; p0 += kTailPart * kWave) {
+            float v[kTailPart];
+            int ix[kTailPart];
+            if (s == wave && p0 == 0) {                                 // issued above
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int p = p0 + u * kWave + lane;
-                v[u] = p < nparts ? pv[(size_t)s * kGridMax + p] : -INFINITY;
-                ix[u] = p < nparts ? pi[(size_t)s * kGridMax + p] : INT_MAX;
+                for (int u = 0; u < kTailPart; ++u) { v[u] = v0[u]; ix[u] = i0[u]; }
+            } else {
+#pragma unroll
+                for (int u = 0; u < kTailPart; ++u) {
+                    const int p = p0 + u * kWave + lane;
+                    v[u] = p < nparts ? pv[(size_t)s * kGridMax + p] : -INFINITY;
+                    ix[u] = p < nparts ? pi[(size_t)s * kGridMax + p] : INT_MAX;
+                }
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < kTailPart; ++u)
                 if (better(v[u], ix[u], bv, bi)) { bv = v[u]; bi = ix[u]; }
         }
         argmax_group<64>(bv, bi);
         if (lane == 0) { argmax[s] = argmax_id(bi); am[s] = argmax_id(bi); }
     }
     if (!round) return;
+    // the stream beyond its first kTailHead ids, up to its length (known by now)
+    const int nrest = in_lds && len0 > kTailHead ? len0 : kTailHead;
+    if (vec) prefix_load_from(tokens, kTailHead, nrest, pre2);
     if (in_lds) {
-        if (vec) prefix_store(tokens, navail, pre, tk);
-        else stage_ids(tokens, len0, tk);
+        if (vec) {
+            prefix_store(tokens, nhead < len0 ? nhead : len0, pre, tk);
+            prefix_store_from(tokens, kTailHead, nrest, pre2, tk);
+            for (int i = ((len0 >> 2) << 2) + threadIdx.x; i < len0; i += kTailThreads)      // the ragged end
+                if (i >= kTailHead) tk[i] = tokens[i];
+        } else {
+            stage_ids(tokens, len0, tk);
+        }
     }
-    __syncthreads();
     if (!in_lds) {                                     // long or corrupt stream: the global-memory path
-        if (wave == 0) accept_wave(am, drafts_in, K, tokens, cap, state, lane);
         __syncthreads();
+        if (wave == 0) accept_wave(am, drafts_in, K, tokens, cap, state, lane);
+        __syncthreads();                               // the drafter reads the stream and state just written
         propose_block(tokens, cap, state, nmax, K, drafts_out, tk, kTailIds - kHalo, wbest);
         return;
     }
+    barrier_lds();
     if (wave == 0) {                                   // accept_wave, with the stream mirrored in LDS
         const unsigned long long hit = __ballot(lane < K && d >= 0 && d == am[lane < K ? lane : 0]);
-        const int j = __builtin_ctzll(~hit);           // <= K: bit K is never set
+        const int j = __builtin_ctzll(~hit);
         const int aj = am[j];
-        if (aj < 0) {                                  // row j had no greedy id: commit nothing
+        if (aj < 0) {
             if (lane == 0) {
                 state[SV_STATE_FLAGS] = state_word(sc, SV_STATE_FLAGS) | SV_FLAG_ARGMAX;
                 new_len = len0;
@@ -764,7 +799,7 @@ __global__ __launch_bounds__(kTailThreads) void round_tail_kernel(const float* _
             }
         }
     }
-    __syncthreads();
+    barrier_lds();                                     // the drafter reads only LDS (tk, new_len, gated_s)
     propose_lds(tk, new_len, nmax, K, drafts_out, state, wbest, gated_s != 0);
 }
 

@@ -104,14 +104,15 @@ __global__ __launch_bounds__(kTailThreads) void sample_tail_kernel(
         if (vec) prefix_store(tokens, navail, pre, tk);
         else stage_ids(tokens, len0, tk);
     }
-    __syncthreads();
     if (!in_lds) {                                     // long or corrupt stream: the global-memory path
+        __syncthreads();
         if (wave == 0) accept_sample_wave(draw_s, lse_s, zd, drafts_in, K, V, key0, key1, tokens, cap, state, lane,
                                           nullptr);
         __syncthreads();
         propose_block(tokens, cap, state, nmax, K, drafts_out, tk, kTailIds - kHalo, wbest);
         return;
     }
+    barrier_lds();                                     // the stream and the draws are in LDS
     if (wave == 0) {
         const int j = accept_sample_wave(draw_s, lse_s, zd, drafts_in, K, V, key0, key1, tokens, cap, state, lane, tk,
                                          &sc);
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(kTailThreads) void sample_tail_kernel(
             gated_s = gated;
         }
     }
-    __syncthreads();
+    barrier_lds();                                     // the drafter reads only LDS (tk, new_len, gated_s)
     propose_lds(tk, new_len, nmax, K, drafts_out, state, wbest, gated_s != 0);
 }
 

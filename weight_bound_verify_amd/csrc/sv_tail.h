@@ -62,6 +62,33 @@ __device__ __forceinline__ void prefix_load(const int32_t* __restrict__ src, int
     }
 }
 
+// Ids [lo, n) of a 16-byte aligned stream (lo a multiple of 4 * blockDim.x), in the layout of
+// prefix_load over [lo, lo + 4 NP blockDim.x): piece u of thread t holds ids lo + 4 (u nt + t).
+template <int NP>
+__device__ __forceinline__ void prefix_load_from(const int32_t* __restrict__ src, int lo, int n, IdPrefix<NP>& p) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int n4 = n >> 2, lo4 = lo >> 2;
+    const i32x4_t* s4 = reinterpret_cast<const i32x4_t*>(src);
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+        const int i = lo4 + u * nt + tid;
+        p.v[u] = i < n4 ? s4[i] : i32x4_t{0, 0, 0, 0};
+    }
+}
+
+template <int NP>
+__device__ __forceinline__ void prefix_store_from(const int32_t* __restrict__ src, int lo, int n,
+                                                  const IdPrefix<NP>& p, int32_t* dst) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int n4 = n >> 2, lo4 = lo >> 2;
+    i32x4_t* d4 = reinterpret_cast<i32x4_t*>(dst);
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+        const int i = lo4 + u * nt + tid;
+        if (i < n4) d4[i] = p.v[u];
+    }
+}
+
 template <int NP>
 __device__ __forceinline__ void prefix_store(const int32_t* __restrict__ src, int n, const IdPrefix<NP>& p,
                                              int32_t* dst) {
@@ -114,7 +141,8 @@ __host__ __device__ __forceinline__ unsigned long long scan_best_lds(const int32
             bool run = true;
 #pragma unroll
             for (int i = 0; i < NM; ++i) {
-                run = run && i < nmax && e - i >= 0 && w[NM + j - i] == suf[i];
+                // position e - i = e0 + (j - i) lies before the stream only when i > j and e0 < i - j
+                run = run && i < nmax && (i <= j || e0 >= i - j) && w[NM + j - i] == suf[i];
                 l += run ? 1 : 0;
             }
             if (l > 0 && e < len - 1) {
@@ -168,7 +196,7 @@ __host__ __device__ __forceinline__ void scan_top_lds(const int32_t* tk, int len
             bool run = true;
 #pragma unroll
             for (int i = 0; i < NM; ++i) {
-                run = run && i < nmax && e - i >= 0 && w[NM + j - i] == suf[i];
+                run = run && i < nmax && (i <= j || e0 >= i - j) && w[NM + j - i] == suf[i];
                 l += run ? 1 : 0;
             }
             if (l > 0 && e < len - 1) top_insert(top, ((unsigned long long)l << 32) | (unsigned)e);
@@ -203,8 +231,7 @@ __device__ __forceinline__ StateCache state_cache_load(const int32_t* state, int
 }
 
 __device__ __forceinline__ int state_word(const StateCache& c, int idx) {      // idx uniform
-    const int lo = __shfl(c.lo, idx & 63, kWave), hi = __shfl(c.hi, idx & 63, kWave);
-    return idx < 64 ? lo : hi;
+    return idx < 64 ? __builtin_amdgcn_readlane(c.lo, idx) : __builtin_amdgcn_readlane(c.hi, idx - 64);
 }
 
 // record_round from the cached words, by the whole wave (same updates, same order of rules).
@@ -353,12 +380,12 @@ __device__ __forceinline__ void propose_block(const int32_t* tokens, int cap, in
 
     unsigned long long best = 0;
     for (int base = 0; base < len - 1; base += chunk) {
-        __syncthreads();
+        barrier_lds();
         // tk[t] holds stream id base - kHalo + t; ids before the stream start are never compared
         const int lo = base - kHalo < 0 ? 0 : base - kHalo;
         const int hi = base + chunk < len ? base + chunk : len;
         stage_ids(tokens + lo, hi - lo, tk + (lo - (base - kHalo)));
-        __syncthreads();
+        barrier_lds();
         const int end = min(base + chunk, len - 1);     // e in [base, end)
         for (int e = base + tid; e < end; e += nthreads) {
             int l = 0;
@@ -378,7 +405,7 @@ __device__ __forceinline__ void propose_block(const int32_t* tokens, int cap, in
         best = o > best ? o : best;
     }
     if ((tid & 63) == 0) wbest[tid >> 6] = best;
-    __syncthreads();
+    barrier_lds();
     if (tid < kWave) {
         unsigned long long b = tid < nthreads / kWave ? wbest[tid] : 0ull;
 #pragma unroll
@@ -399,8 +426,10 @@ __device__ __forceinline__ void propose_block(const int32_t* tokens, int cap, in
     }
 }
 
-// Drafter over a stream held whole in LDS (`tk[0 .. len)`): the same rule as propose_block,
-// with no global reads.  Every thread of the workgroup must call it.
+// Drafter over a stream held whole in LDS (`tk[0 .. len)`, len <= 65536): the same rule as
+// propose_block, with no global reads.  End positions fit in 16 bits here, so the key
+// (match length, end position) is packed as l << 16 | e and reduced as 32 bits with DPP.  Every
+// thread of the workgroup must call it.
 __device__ __forceinline__ void propose_lds(const int32_t* tk, int len, int nmax, int K, int32_t* drafts,
                                             int32_t* state, unsigned long long* wbest, bool gated) {
     const int tid = threadIdx.x;
@@ -412,24 +441,17 @@ __device__ __forceinline__ void propose_lds(const int32_t* tk, int len, int nmax
     int32_t suf[SV_MAX_NGRAM];
 #pragma unroll
     for (int i = 0; i < SV_MAX_NGRAM; ++i) suf[i] = (i < nmax && len - 1 - i >= 0) ? tk[len - 1 - i] : -1;
-    unsigned long long best = nmax <= 4 ? scan_best_lds<4>(tk, len, nmax, suf, tid, nthreads)
-                                         : scan_best_lds<8>(tk, len, nmax, suf, tid, nthreads);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const unsigned long long o = __shfl_xor(best, off, 64);
-        best = o > best ? o : best;
-    }
-    if ((tid & 63) == 0) wbest[tid >> 6] = best;
-    __syncthreads();
+    const unsigned long long b64 = nmax <= 4 ? scan_best_lds<4>(tk, len, nmax, suf, tid, nthreads)
+                                             : scan_best_lds<8>(tk, len, nmax, suf, tid, nthreads);
+    uint32_t best = (uint32_t)((b64 >> 32) << 16) | (uint32_t)(b64 & 0xffffu);
+    best = wave_max_u32(best);
+    uint32_t* wb = reinterpret_cast<uint32_t*>(wbest);
+    if ((tid & 63) == 0) wb[tid >> 6] = best;
+    barrier_lds();
     if (tid < kWave) {
-        unsigned long long b = tid < nthreads / kWave ? wbest[tid] : 0ull;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const unsigned long long o = __shfl_xor(b, off, 64);
-            b = o > b ? o : b;
-        }
-        const int nused = (int)(b >> 32);
-        const int e = (int)(b & 0xffffffffu);
+        const uint32_t b = wave_max_u32(tid < nthreads / kWave ? wb[tid] : 0u);
+        const int nused = (int)(b >> 16);
+        const int e = (int)(b & 0xffffu);
         if (tid < K) {
             const int p = e + 1 + tid;
             drafts[tid] = (nused > 0 && p <= len - 1) ? tk[p] : -1;

@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kTreeThreads) void tree_tail_kernel(
         if (vec) prefix_store(tokens, navail, pre, tk);
         else stage_ids(tokens, len0, tk);
     }
-    __syncthreads();
+    barrier_lds();                                     // the stream (when it fits) and the argmax are in LDS
     if (wave == 0) {
         const int j = accept_tree_wave(am, parents_in, drafts_in, K, tokens, cap, state, lane, in_lds ? tk : nullptr,
                                        &sc);
@@ -285,7 +285,9 @@ __global__ __launch_bounds__(kTreeThreads) void tree_tail_kernel(
             gated_s = gated;
         }
     }
-    __syncthreads();
+    // the LDS drafter reads only LDS; the global-memory one reads the stream and state just written
+    if (in_lds) barrier_lds();
+    else __syncthreads();
     int len = new_len;
     const int32_t* st = tk;
     if (!in_lds) {                                     // long or corrupt stream: global memory
