@@ -486,13 +486,15 @@ int specverify_stack(const int8_t* wg, const uint16_t* sg, const int8_t* wu, con
  * and the head matmul kernel family (0 = automatic, 1 = one pass per 16-row item, 2 = the
  * chunked ring kernel where the shape allows it, S <= 16, 3 = automatic except that a
  * 17-row window uses two 16-row tiles instead of one tile plus the 17th row's dot
- * products).  Waves that do not divide a chunked shape make specverify_stack fail with
- * SV_ERR_SHAPE.  The override belongs to the calling thread: it affects only calls made from
- * that thread (including its *_workspace_bytes answers, so query them after changing it),
- * and other threads keep the automatic choice.  (0, 0, 0, 0) restores it.
+ * products), and the split of specverify_stack's down projection (0 or 1 = unsplit, the
+ * automatic choice; 2 .. 8 = its hidden axis split that many ways across workgroups where a
+ * held-row shape for the slices exists, else unsplit).  Waves that do not divide a chunked shape make specverify_stack
+ * fail with SV_ERR_SHAPE.  The override belongs to the calling thread: it affects only calls
+ * made from that thread (including its *_workspace_bytes answers, so query them after
+ * changing it), and other threads keep the automatic choice.  (0, 0, 0, 0, 0) restores it.
  */
 void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups, int32_t depth,
-                           int32_t head_kernel);
+                           int32_t head_kernel, int32_t split);
 
 /*
  * Timing hook for the dominant kernel.  The next int8 or int4 matmul that this thread

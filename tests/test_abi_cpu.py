@@ -107,6 +107,13 @@ def test_whole_stack_argument_errors(lib):
     f = lib.specverify_stack
     ws = lib.specverify_stack_forward_workspace_bytes(4096, 12288, 9)
     assert ws == 2 * 9 * 12288 + 4 * 9 * 256          # m [S][F] fp16 + sum-of-squares partials [S][H/16]
+    # a down projection split 8 ways (a tuning choice) adds fp32 slice sums [8][S][H] and one
+    # counter per 16-row tile
+    try:
+        lib.specverify_set_tuning(0, 0, 0, 0, 8)
+        assert lib.specverify_stack_forward_workspace_bytes(4096, 12288, 9) == ws + 4 * 8 * 9 * 4096 + 4 * 256
+    finally:
+        lib.specverify_set_tuning(0, 0, 0, 0, 0)
     assert lib.specverify_stack_forward_workspace_bytes(4096, 12288, 17) == 0
     assert lib.specverify_stack_forward_workspace_bytes(4000, 12288, 9) == 0
     B, C, D = P(0x20000), P(0x40000), P(0x60000)

@@ -114,18 +114,71 @@ def _check_block(x, layer, xl0, nrm, m_gpu, ss, eps=1e-6):
     _check_f16(nrm, out / np.sqrt(np.mean(out * out, axis=1, keepdims=True) + eps), slack=1e-5)
 
 
+SPLITS = {(512, 1024, 9, 3): 2, (1024, 1536, 16, 2): 3, (512, 2048, 5, 2): 4, (4096, 12288, 9, 1): 8,
+          (2560, 1536, 9, 2): 3, (3584, 2560, 16, 1): 5}
+
+
+@pytest.mark.parametrize("split", ["unsplit", "split"])
 @pytest.mark.parametrize("H,F,S,L", SHAPES)
-def test_stack_block_by_block_teacher_forced(H, F, S, L):
-    """Each block on its own (L = 1 per call), checked at both stages against the oracle."""
-    say(f"stack block by block H={H} F={F} S={S} L={L}")
+def test_stack_block_by_block_teacher_forced(H, F, S, L, split):
+    """Each block on its own (L = 1 per call), checked at both stages against the oracle, with
+    the down projection unsplit (the automatic choice) and with its hidden axis split across
+    workgroups (2 .. 8 slices, each shape's own count; (2048, 512, 1) has no split shape)."""
+    if split == "split" and (H, F, S, L) not in SPLITS:
+        pytest.skip("no held-row shape splits this down projection")
+    split = SPLITS[(H, F, S, L)] if split == "split" else 0
+    say(f"stack block by block H={H} F={F} S={S} L={L} split={split}")
     rng = np.random.default_rng(H + 3 * F + S + L)
     layers, mats = _stacked(rng, L, H, F)
     x = (synth.fp16_normal(rng, (S, H)).astype(np.float32) * 3).astype(np.float16)
-    for li in range(L):
-        one = [m[li:li + 1] for m in mats]
-        _, xl, nrm, m_gpu, ss = _run(one, x, 1, want_ws=True)
-        _check_block(x, layers[li], xl[0], nrm, m_gpu, ss)
-        x = xl[0]
+    sv.set_tuning(0, 0, 0, 0, split)
+    try:
+        base = (2 * S * F + 255) // 256 * 256 + (4 * S * (H // 16) + 255) // 256 * 256
+        assert (sv.stack_forward_workspace_bytes(H, F, S) > base) == (split > 1), "split not applied"
+        for li in range(L):
+            one = [m[li:li + 1] for m in mats]
+            _, xl, nrm, m_gpu, ss = _run(one, x, 1, want_ws=True)
+            _check_block(x, layers[li], xl[0], nrm, m_gpu, ss)
+            x = xl[0]
+    finally:
+        sv.set_tuning(0, 0, 0, 0, 0)
+
+
+@pytest.mark.parametrize("ks", [2, 3, 4, 6, 8])
+def test_stack_down_split_counts(ks):
+    """The dense-stack block shape (4096 -> 12288 -> 4096, S = 9) with its down projection
+    split 2 .. 8 ways where a shape exists (3, 4, 6, 8; 2 falls back to unsplit): two blocks,
+    each teacher-forced against the oracle; the second block's norm comes from the fold's
+    sum-of-squares partials, and the tile counters the first launch left must be zero again."""
+    H, F, S, L = 4096, 12288, 9, 2
+    say(f"stack down split ks={ks}")
+    rng = np.random.default_rng(77 + ks)
+    layers, mats = _stacked(rng, L, H, F)
+    x = (synth.fp16_normal(rng, (S, H)).astype(np.float32) * 3).astype(np.float16)
+    sv.set_tuning(0, 0, 0, 0, ks)
+    try:
+        _, xl, nrm = _run(mats, x, L)
+        # the counters after a call: zero (the workspace's last 256-byte-aligned part when split)
+        ws = sv.workspace(sv.stack_forward_workspace_bytes(H, F, S), dev())
+        ws.fill_(0x5A)
+        sv.stack(*[to_dev(m) for m in mats], to_dev(x), to_dev(np.zeros((S, H), np.float16)), ws, 1e-6,
+                 x_layers=to_dev(np.zeros((L, S, H), np.float16)))
+        torch.cuda.synchronize()
+        al = lambda b: (b + 255) // 256 * 256
+        base = al(2 * S * F) + al(4 * S * (H // 16))
+        tiles = H // 16
+        if ws.numel() > base:
+            cnt = ws.cpu().numpy()[-al(4 * tiles):][:4 * tiles].view(np.uint32)
+            assert (cnt == 0).all(), "tile counters not left at zero"
+        prev = x
+        for li in range(L):
+            _, xl1, nrm1, m_gpu, ss = _run([m[li:li + 1] for m in mats], prev, 1, want_ws=True)
+            assert np.array_equal(xl1[0], xl[li]), f"block {li}: multi-block output differs"
+            _check_block(prev, layers[li], xl1[0], nrm1, m_gpu, ss)
+            prev = xl[li]
+        assert np.array_equal(nrm, nrm1)
+    finally:
+        sv.set_tuning(0, 0, 0, 0, 0)
 
 
 @pytest.mark.parametrize("H,F,S,L", [sh for sh in SHAPES if sh[3] > 1])

@@ -109,14 +109,16 @@ int specverify_profile_next_matmul(hipEvent_t before, hipEvent_t after) {
     return SV_OK;
 }
 
-void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups, int32_t depth, int32_t head_kernel) {
+void specverify_set_tuning(int32_t waves_per_group, int32_t max_groups, int32_t depth, int32_t head_kernel,
+                           int32_t split) {
     if (waves_per_group != 0 && waves_per_group != 4 && waves_per_group != 8 && waves_per_group != 16)
         waves_per_group = 0;
     if (max_groups < 0 || max_groups > sv::kGridMax) max_groups = 0;
     if (depth < 0 || depth > 4) depth = 0;
     if (head_kernel < 0 || head_kernel > 3) head_kernel = 0;
+    if (split < 0 || split > 8) split = 0;
     sv::set_tuning(waves_per_group, max_groups, head_kernel == 3 ? 1 : 0);
-    sv::set_chunk_tuning(waves_per_group, depth, max_groups, head_kernel);
+    sv::set_chunk_tuning(waves_per_group, depth, max_groups, head_kernel, split);
 }
 
 int specverify_propose(const int32_t* tokens, int32_t cap, int32_t* state, int32_t ngram_max, int32_t K,
@@ -766,7 +768,9 @@ int specverify_linear_residual_rmsnorm_q8b32(const int8_t* w, const uint16_t* sc
 namespace {
 
 // Workspace of specverify_stack: m = silu(g) * u [S][F] fp16, then the sum-of-squares
-// partials [S][H/16] fp32, each part 256-byte aligned.
+// partials [S][H/16] fp32, then (when the down projection splits its hidden axis ks ways) its
+// fp32 slice sums [ks][S][H] and one arrival counter per 16-row tile; each part 256-byte
+// aligned.
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 size_t stack_m_bytes(int S, int F) { return align256((size_t)2 * S * F); }
 size_t stack_ss_bytes(int S, int H) { return align256((size_t)4 * S * (H / 16)); }
@@ -781,7 +785,7 @@ bool stack_shape_ok(int H, int F) {
 
 size_t specverify_stack_forward_workspace_bytes(int32_t H, int32_t F, int32_t S) {
     if (S < 1 || S > 16 || !stack_shape_ok(H, F)) return 0;
-    return stack_m_bytes(S, F) + stack_ss_bytes(S, H);
+    return stack_m_bytes(S, F) + stack_ss_bytes(S, H) + sv::chunked_split_bytes(H, F, S);
 }
 
 int specverify_stack(const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su,
@@ -815,11 +819,19 @@ int specverify_stack(const int8_t* wg, const uint16_t* sg, const int8_t* wu, con
 
     sv::ChunkCfg cg, cd;
     sv::chunked_config(F, H, sv::EPI_GATEUP, cg);
-    sv::chunked_config(H, F, sv::EPI_STORE, cd);
+    sv::chunked_config(H, F, sv::EPI_STORE, cd, S);
     uint16_t* m = static_cast<uint16_t*>(workspace);
     float* ss = reinterpret_cast<float*>(static_cast<char*>(workspace) + stack_m_bytes(S, F));
+    float* kpart = nullptr;
+    uint32_t* counters = nullptr;
+    if (cd.ks > 1) {
+        char* split = static_cast<char*>(workspace) + stack_m_bytes(S, F) + stack_ss_bytes(S, H);
+        kpart = reinterpret_cast<float*>(split);
+        counters = reinterpret_cast<uint32_t*>(split + align256((size_t)4 * cd.ks * S * H));
+    }
 
-    hipError_t e = sv::launch_row_ss(x, S, H, ss, stream);
+    // the first pass also clears the tile counters (each down launch leaves them at zero)
+    hipError_t e = sv::launch_row_ss(x, S, H, ss, counters, counters ? cd.items : 0, stream);
     if (e != hipSuccess) return hip_fail(e, "row sum-of-squares launch");
     const uint16_t* cur = x;
     for (int l = 0; l < L; ++l) {
@@ -845,6 +857,9 @@ int specverify_stack(const int8_t* wg, const uint16_t* sg, const int8_t* wu, con
         d.y = out;
         d.residual = cur;
         d.ss_out = ss;
+        d.kslices = cd.ks;
+        d.kpart = kpart;
+        d.counters = counters;
         e = launch_chunked_matmul(sv::EPI_STORE, cd, d, stream);
         if (e != hipSuccess) return hip_fail(e, "stack down launch");
         cur = out;

@@ -165,6 +165,14 @@ struct ChunkArgs {
     uint16_t* y;               // EPI_STORE / EPI_GATEUP: [S][V] fp16
     const uint16_t* residual;  // EPI_STORE: [S][V] fp16 or null
     float* ss_out;             // EPI_STORE: [S][nitems] sum of squares of each stored 16-column tile, or null
+    // EPI_STORE with the hidden axis split across workgroups (kslices > 1): workgroup b works on
+    // slice b / (grid / kslices) of the hidden axis, writes its fp32 tile sums to kpart
+    // [kslices][S][V], and the last of a tile's kslices workgroups to finish (counted in
+    // counters[tile], which must be zero at launch and is left zero) adds them in slice order
+    // and runs the epilogue.
+    int kslices;
+    float* kpart;
+    uint32_t* counters;
 };
 struct ChunkCfg {
     int nw;       // waves per workgroup (4 .. 16)
@@ -173,16 +181,27 @@ struct ChunkCfg {
     int depth;    // load units in flight per wave
     int grid;     // workgroups
     int items;    // tiles (16 rows; gate/up: 8 row pairs)
+    int ks;       // EPI_STORE: slices of the hidden axis across workgroups (1: none); nkc and hold
+                  // then describe one slice
 };
-void set_chunk_tuning(int waves, int depth, int max_groups, int head_kernel);
+// split = 0 or 1: a store projection's hidden axis is not split (the automatic choice); k > 1:
+// split k ways when a held-row shape exists for that k (else unsplit).
+void set_chunk_tuning(int waves, int depth, int max_groups, int head_kernel, int split);
+// Bytes of the split partial sums and tile counters a store projection of this shape needs
+// (0 when its configuration does not split).
+size_t chunked_split_bytes(int rows, int H, int S);
 // Whether the head matmul of this shape runs on the chunked ring kernel (when it applies).
 bool head_use_chunked(int V, int H);
-// False when H is not a whole number of 4-block segments for 4, 8 or 16 waves.
-bool chunked_config(int rows, int H, int epi, ChunkCfg& c);
+// False when H is not a whole number of 4-block segments for 4, 8 or 16 waves.  S > 0 lets a
+// store projection split its hidden axis across workgroups when the calling thread's tuning
+// asks for it (the split's workspace depends on S).
+bool chunked_config(int rows, int H, int epi, ChunkCfg& c, int S = 0);
 hipError_t launch_chunked(int epi, const ChunkCfg& c, const ChunkArgs& a, hipStream_t stream,
                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
-// ss[s][t] = sum of squares of the 16 fp16 values of x[s][16t .. 16t+15]
-hipError_t launch_row_ss(const uint16_t* x, int S, int H, float* ss, hipStream_t stream);
+// ss[s][t] = sum of squares of the 16 fp16 values of x[s][16t .. 16t+15]; also zeroes
+// zero[0 .. nzero) when zero is given.
+hipError_t launch_row_ss(const uint16_t* x, int S, int H, float* ss, uint32_t* zero, int nzero,
+                         hipStream_t stream);
 // out = fp16(x * inv[s]), inv from the ss partials as the chunked gate/up prologue computes it
 hipError_t launch_apply_norm(const uint16_t* x, const float* ss, int S, int H, float eps, uint16_t* out,
                              hipStream_t stream);

@@ -94,7 +94,7 @@ def load():
         "specverify_stack_forward_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
         "specverify_stack": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _I, ctypes.c_float, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
-        "specverify_set_tuning": (None, [_I, _I, _I, _I]),
+        "specverify_set_tuning": (None, [_I, _I, _I, _I, _I]),
         "specverify_profile_next_matmul": (_I, [_P, _P]),
         "specverify_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "specverify_last_error": (ctypes.c_char_p, []),
@@ -150,8 +150,9 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
 
 
-def set_tuning(waves_per_group: int = 0, max_groups: int = 0, depth: int = 0, head_kernel: int = 0) -> None:
-    load().specverify_set_tuning(int(waves_per_group), int(max_groups), int(depth), int(head_kernel))
+def set_tuning(waves_per_group: int = 0, max_groups: int = 0, depth: int = 0, head_kernel: int = 0,
+               split: int = 0) -> None:
+    load().specverify_set_tuning(int(waves_per_group), int(max_groups), int(depth), int(head_kernel), int(split))
 
 
 def profile_next_matmul(before, after, stream=None) -> None:
