@@ -961,6 +961,9 @@ int resident_groups(int epi, const GemmCfg& c) {
 
 }  // namespace
 
+int tuning_waves() { return g_nw_override; }
+int tuning_groups() { return g_grid_override; }
+
 void set_tuning(int waves_per_group, int max_groups, int no_extra_row) {
     g_nw_override = waves_per_group;
     g_grid_override = max_groups;

@@ -44,6 +44,9 @@ GemmCfg gemm_config(int rows, int H, int S, int epi);
 // Workgroups of the split-combine pass (also the number of argmax partials it writes).
 int combine_groups(int V);
 void set_tuning(int waves_per_group, int max_groups, int no_extra_row);
+// The calling thread's overrides (0 = automatic): waves per workgroup, workgroups per launch.
+int tuning_waves();
+int tuning_groups();
 
 struct GemmArgs {
     const int8_t* w0;

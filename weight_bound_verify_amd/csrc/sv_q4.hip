@@ -225,7 +225,7 @@ Q4Fn pick_q4(int nbw, int nw) {
     if (nbw == NBW && nw == NW) return q4b32_head<NBW, NW>;
     SV_Q4(8, 1) SV_Q4(8, 2) SV_Q4(8, 4) SV_Q4(8, 5) SV_Q4(8, 6) SV_Q4(8, 8) SV_Q4(8, 10) SV_Q4(8, 12)
     SV_Q4(8, 14) SV_Q4(8, 16)
-    SV_Q4(16, 5) SV_Q4(16, 6) SV_Q4(16, 8) SV_Q4(16, 10) SV_Q4(16, 12)   // 14, 16 waves spill at 16 blocks
+    SV_Q4(16, 4) SV_Q4(16, 5) SV_Q4(16, 6) SV_Q4(16, 8) SV_Q4(16, 10) SV_Q4(16, 12)   // 14, 16 spill
 #undef SV_Q4
     return nullptr;
 }
@@ -263,12 +263,14 @@ bool q4_config(int V, int H, Q4Cfg& c) {
     for (int nbw : {8, 16}) {
         const int nw = nb / nbw;
         if (nb % nbw || nw < 1 || nw > 16) continue;
+        if (tuning_waves() && nw != tuning_waves()) continue;     // the calling thread's override
         Q4Fn fn = pick_q4(nbw, nw);
         if (!fn) continue;
         c.nbw = nbw;
         c.nw = nw;
         const int items = (V + kTileRows - 1) / kTileRows;
         int cap = q4_resident(fn, nw);
+        if (tuning_groups() > 0) cap = tuning_groups();
         if (cap > kGridMax) cap = kGridMax;
         const int per = (items + cap - 1) / cap;
         c.grid = (items + per - 1) / per;
