@@ -459,6 +459,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=50, help="isolated head launches timed for the roofline")
     ap.add_argument("--calib-copy", action="store_true", help="run a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--down-split", type=int, default=0,
+                    help="dense stack: split the down projection's hidden axis this many ways (2..8; 0 = unsplit)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -471,6 +473,8 @@ def main():
     from weight_bound_verify_amd import specverify as sv
     from weight_bound_verify_amd import synth
 
+    if args.down_split:
+        sv.set_tuning(0, 0, 0, 0, args.down_split)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.calib_copy:
@@ -765,6 +769,8 @@ def main():
         out["c_v"] = cv
     if tree:
         out["config"]["tree"] = {"branches": tree[0], "depth": tree[1], "nodes": K}
+    if wl["layers"] and args.down_split:
+        out["config"]["down_split"] = args.down_split
     if temp:
         out["config"]["temperature"] = temp
         out["config"]["seed"] = SAMPLE_SEED
