@@ -33,6 +33,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -117,12 +118,16 @@ def kernel_fmt(workload):
 
 
 def kernel_source_hash(fmt="q8"):
-    """Hash of the sources the timed kernel of this format is built from."""
+    """Hash of the code (comments and whitespace removed) of the sources the timed kernel of
+    this format is built from: an edit of the code changes it, a comment edit does not."""
     h = hashlib.sha256()
     src = {"q4": "sv_q4.hip", "stack": "sv_chunked.hip"}.get(fmt, "sv_gemm.hip")
     for name in (src, "sv_device.h"):
-        with open(os.path.join(ROOT, "weight_bound_verify_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "weight_bound_verify_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

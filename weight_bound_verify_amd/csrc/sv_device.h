@@ -16,7 +16,9 @@ constexpr int kWave = 64;
 constexpr int kBlock = 32;       // quantization block length (hidden axis)
 constexpr int kTileRows = 16;    // vocab rows per MFMA tile (N of the 16x16x32 MFMA)
 
-// Four int8 codes packed in a dword -> four exact fp16 values.
+// Four int8 codes packed in a dword -> four exact fp16 values, by the exponent-bias ("magic
+// number") integer-to-float conversion (2^23 for fp32; here 2^10, the fp16 form that weight-only
+// quantized GEMMs use to expand int8 and int4 codes).
 // Each byte is biased to u = q + 128 (xor 0x80), placed under the fp16 exponent of 1024
 // (bit pattern 0x64uu = 1024 + u, exact since the ulp at 1024 is 1), and 1152 = 1024 + 128
 // is subtracted; the result q is an integer in [-128, 127], exact in fp16.
