@@ -302,7 +302,13 @@ struct FastRegs {
 // HL > 0 (MT = 1): the window rows of each wave's last HL blocks sit in LDS instead of
 // registers (one 16-byte LDS read per block per lane), freeing 4 registers per block for shapes
 // that would otherwise spill.
-template <int MT, int NBW, int NW, int EPI, int XR = 0, int HL = 0>
+//
+// ROLL = 1: one register set instead of two.  Each 128-byte segment of the next item is loaded
+// into the registers of the same segment of the current item as soon as those have been
+// written to the LDS exchange, and the next item's scales after the current item's last block,
+// so one item's loads are in flight during the math as with two sets, in about half the
+// registers.
+template <int MT, int NBW, int NW, int EPI, int XR = 0, int HL = 0, int ROLL = 0>
 __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
     constexpr int NSEG = NBW / 4;
     constexpr int HR = NBW - HL;                      // blocks whose window rows stay in registers
@@ -355,16 +361,17 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
     // loads: row half h feeds tile rows 8h .. 8h+7; lane l reads the tile row 8h + l/8, bytes
     // 16*(l%8) .. +15 of each 128-byte segment of the wave's range
     const int lrow = lane >> 3, lchunk = lane & 7;
-    auto load = [&](FastRegs<NBW>& r, int item) {
+    // segment t of an item's rows (both row halves)
+    auto load_seg = [&](FastRegs<NBW>& r, int item, int t) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int8_t* w = tile_up<EPI>(8 * h) ? a.w1 : a.w0;
             const int row = min(tile_row<EPI>(item, 8 * h + lrow), a.V - 1);      // tail rows: masked later
             const int8_t* p = w + (size_t)row * a.H + (size_t)bw0 * kBlock + 16 * lchunk;
-#pragma unroll
-            for (int t = 0; t < NSEG; ++t)
-                r.w[t][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 128 * t));
+            r.w[t][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 128 * t));
         }
+    };
+    auto load_sc = [&](FastRegs<NBW>& r, int item) {
         const uint16_t* s = tile_up<EPI>(n) ? a.s1 : a.s0;
         const int srow = min(tile_row<EPI>(item, n), a.V - 1);
         const uint16_t* sp = s + (size_t)srow * a.nb + bw0;
@@ -384,8 +391,14 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
             }
         }
     };
+    auto load = [&](FastRegs<NBW>& r, int item) {
+#pragma unroll
+        for (int t = 0; t < NSEG; ++t) load_seg(r, item, t);
+        load_sc(r, item);
+    };
 
-    auto process = [&](const FastRegs<NBW>& cur, int it, int buf) {
+    // nxt: the item whose loads replace cur's registers as they free up (ROLL only)
+    auto process = [&](FastRegs<NBW>& cur, int it, int buf, int nxt) {
         red_.ahead(a, it + gridDim.x, wave, lane);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         f32x4 acc[MT];
@@ -410,6 +423,7 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
                 const int row = 8 * h + lrow;
                 *reinterpret_cast<u32x4*>(&xch[wave][t & 1][row * 128 + 16 * (lchunk ^ (row & 7))]) = cur.w[t][h];
             }
+            if constexpr (ROLL) load_seg(cur, nxt, t);
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
                 const int i = 4 * t + bb;
@@ -452,6 +466,7 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[mt][r] = __builtin_fmaf(scprev, dprev[mt][r], acc[mt][r]);
         }
+        if constexpr (ROLL) load_sc(cur, nxt);
         if constexpr (XR > 0) {
             // the MFMA already summed the k groups: lanes n of group 0 hand the wave's partial
             // to LDS; the item's barrier in red_.run orders it before the readers
@@ -477,18 +492,24 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
 
     const int step = gridDim.x;
     const int last = a.nitems - 1;
-    FastRegs<NBW> ra, rb;
     int it = blockIdx.x;
-    load(ra, it);
-    while (true) {
-        if (it >= a.nitems) break;
-        load(rb, min(it + step, last));
-        process(ra, it, 0);
-        it += step;
-        if (it >= a.nitems) break;
-        load(ra, min(it + step, last));
-        process(rb, it, 1);
-        it += step;
+    if constexpr (ROLL) {
+        FastRegs<NBW> r;
+        load(r, min(it, last));
+        for (int k = 0; it < a.nitems; ++k, it += step) process(r, it, k & 1, min(it + step, last));
+    } else {
+        FastRegs<NBW> ra, rb;
+        load(ra, it);
+        while (true) {
+            if (it >= a.nitems) break;
+            load(rb, min(it + step, last));
+            process(ra, it, 0, 0);
+            it += step;
+            if (it >= a.nitems) break;
+            load(ra, min(it + step, last));
+            process(rb, it, 1, 0);
+            it += step;
+        }
     }
     if constexpr (EPI == EPI_HEAD || EPI == EPI_SAMPLE)
         if (a.ksplit == 1 && wave == 0) red_.finish(a, lane);
@@ -827,7 +848,7 @@ constexpr Shape kFast[] = {
     // S = 17: the one-tile kernel plus the 17th row's dot products (the shapes that compile
     // without spills; 20 blocks x 8 waves does not); 8 x 8 before 4 x 16 as for S <= 16
     {1, 8, 8, kH, 1}, {1, 4, 16, kH, 1}, {1, 16, 8, kH, 1}, {1, 16, 5, kH, 1}, {1, 8, 4, kH, 1}, {1, 4, 4, kH, 1},
-    {1, 20, 8, kH, 1},              // window rows of 8 of the 20 blocks held in LDS
+    {1, 20, 8, kH, 1},              // window rows of 8 of the 20 blocks in LDS, one rolling register set
 };
 // generic kernel
 constexpr Shape kGeneric[] = {
@@ -845,7 +866,9 @@ KernelFn pick_fast(const GemmCfg& c) {
 #define SV_XR(NBW, NW, XR) \
     if (c.mt == 1 && c.xr == XR && c.nbw == NBW && c.nw == NW) return q8b32_fast<1, NBW, NW, EPI, XR>;
             SV_XR(4, 16, 1) SV_XR(8, 8, 1) SV_XR(16, 8, 1) SV_XR(16, 5, 1) SV_XR(8, 4, 1) SV_XR(4, 4, 1)
-            if (c.mt == 1 && c.xr == 1 && c.nbw == 20 && c.nw == 8) return q8b32_fast<1, 20, 8, EPI, 1, 12>;
+            // one rolling register set: window rows of 8 of the 20 blocks in LDS (12 with two
+            // sets); measured 198 against 239 us at 248320 x 5120, S = 17
+            if (c.mt == 1 && c.xr == 1 && c.nbw == 20 && c.nw == 8) return q8b32_fast<1, 20, 8, EPI, 1, 8, 1>;
 #undef SV_XR
             return nullptr;
         }
@@ -853,6 +876,10 @@ KernelFn pick_fast(const GemmCfg& c) {
     if (c.xr) return nullptr;
 #define SV_SHAPE(MT, NBW, NW) \
     if (c.mt == MT && c.nbw == NBW && c.nw == NW) return q8b32_fast<MT, NBW, NW, EPI>;
+    // the argmax head at 8 x 10 (H = 2560) with one rolling register set: 63.2 against 64.4 us
+    // at 151936 x 2560; at the other shapes two sets measured even or faster
+    if constexpr (EPI == EPI_HEAD)
+        if (c.mt == 1 && c.nbw == 8 && c.nw == 10) return q8b32_fast<1, 8, 10, EPI, 0, 0, 1>;
     SV_SHAPE(1, 8, 8) SV_SHAPE(1, 8, 10) SV_SHAPE(1, 16, 8) SV_SHAPE(1, 16, 5) SV_SHAPE(1, 16, 4)
     SV_SHAPE(1, 8, 4) SV_SHAPE(1, 4, 4) SV_SHAPE(1, 8, 2) SV_SHAPE(1, 4, 16) SV_SHAPE(1, 20, 8)
     if constexpr (EPI == EPI_HEAD || EPI == EPI_STORE) { SV_SHAPE(1, 8, 16) }
