@@ -79,7 +79,7 @@ struct Q4Regs {
     uint32_t sc[NBW / 2];                          // fp16 scales of the lane's row, in pairs
 };
 
-template <int NBW, int NW>
+template <int NBW, int NW, int ROLL = 0>
 __global__ __launch_bounds__(NW * 64) void q4b32_head(Q4Args a) {
     constexpr int NSEG = NBW / 8;
     static_assert(NBW % 8 == 0, "whole 128-byte segments");
@@ -116,15 +116,15 @@ __global__ __launch_bounds__(NW * 64) void q4b32_head(Q4Args a) {
     for (int j = 0; j < RPW; ++j) { best_v[j] = -INFINITY; best_i[j] = INT_MAX; }
 
     const int lrow = lane >> 3, lchunk = lane & 7;
-    auto load = [&](Q4Regs<NBW>& r, int item) {
+    auto load_seg = [&](Q4Regs<NBW>& r, int item, int t) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int row = min(item * kTileRows + 8 * h + lrow, a.V - 1);       // tail rows: masked later
             const uint8_t* p = a.w + (size_t)row * row_bytes + (size_t)bw0 * 16 + 16 * lchunk;
-#pragma unroll
-            for (int t = 0; t < NSEG; ++t)
-                r.w[t][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 128 * t));
+            r.w[t][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 128 * t));
         }
+    };
+    auto load_sc = [&](Q4Regs<NBW>& r, int item) {
         const int srow = min(item * kTileRows + n, a.V - 1);
         const uint16_t* sp = a.s + (size_t)srow * a.nb + bw0;
 #pragma unroll
@@ -134,8 +134,14 @@ __global__ __launch_bounds__(NW * 64) void q4b32_head(Q4Args a) {
             for (int e = 0; e < 4; ++e) r.sc[4 * v + e] = q[e];
         }
     };
+    auto load = [&](Q4Regs<NBW>& r, int item) {
+#pragma unroll
+        for (int t = 0; t < NSEG; ++t) load_seg(r, item, t);
+        load_sc(r, item);
+    };
 
-    auto process = [&](const Q4Regs<NBW>& cur, int it, int buf) {
+    // nxt: with ROLL, the item whose loads replace cur's registers as they free up
+    auto process = [&](Q4Regs<NBW>& cur, int it, int buf, int nxt) {
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         f32x4 acc = zero;
         f32x4 dprev = zero;
@@ -147,6 +153,7 @@ __global__ __launch_bounds__(NW * 64) void q4b32_head(Q4Args a) {
                 const int row = 8 * h + lrow;
                 *reinterpret_cast<u32x4*>(&xch[wave][t & 1][row * 128 + 16 * (lchunk ^ (row & 7))]) = cur.w[t][h];
             }
+            if constexpr (ROLL) load_seg(cur, nxt, t);
 #pragma unroll
             for (int bb = 0; bb < 8; ++bb) {                     // 8 int4 blocks per segment
                 const int i = 8 * t + bb;
@@ -163,6 +170,7 @@ __global__ __launch_bounds__(NW * 64) void q4b32_head(Q4Args a) {
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(scprev, dprev[r], acc[r]);
+        if constexpr (ROLL) load_sc(cur, nxt);
         red[buf][wave][lane] = acc;
         lds_barrier_q4();
         const int v = it * kTileRows + n;
@@ -184,24 +192,31 @@ __global__ __launch_bounds__(NW * 64) void q4b32_head(Q4Args a) {
 
     const int step = gridDim.x;
     const int last = a.nitems - 1;
-    // three register sets: two items' loads stay in flight while one is processed
-    Q4Regs<NBW> ra, rb, rc;
     int it = blockIdx.x, k = 0;
-    load(ra, it);
-    load(rb, min(it + step, last));
-    while (true) {
-        if (it >= a.nitems) break;
-        load(rc, min(it + 2 * step, last));
-        process(ra, it, k++ & 1);
-        it += step;
-        if (it >= a.nitems) break;
-        load(ra, min(it + 2 * step, last));
-        process(rb, it, k++ & 1);
-        it += step;
-        if (it >= a.nitems) break;
-        load(rb, min(it + 2 * step, last));
-        process(rc, it, k++ & 1);
-        it += step;
+    if constexpr (ROLL) {
+        // one register set refilled segment by segment: one item's loads in flight
+        Q4Regs<NBW> r;
+        load(r, min(it, last));
+        for (; it < a.nitems; it += step) process(r, it, k++ & 1, min(it + step, last));
+    } else {
+        // three register sets: two items' loads stay in flight while one is processed
+        Q4Regs<NBW> ra, rb, rc;
+        load(ra, it);
+        load(rb, min(it + step, last));
+        while (true) {
+            if (it >= a.nitems) break;
+            load(rc, min(it + 2 * step, last));
+            process(ra, it, k++ & 1, 0);
+            it += step;
+            if (it >= a.nitems) break;
+            load(ra, min(it + 2 * step, last));
+            process(rb, it, k++ & 1, 0);
+            it += step;
+            if (it >= a.nitems) break;
+            load(rb, min(it + 2 * step, last));
+            process(rc, it, k++ & 1, 0);
+            it += step;
+        }
     }
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
@@ -221,8 +236,11 @@ typedef void (*Q4Fn)(Q4Args);
 
 // (blocks per wave, waves) -> kernel
 Q4Fn pick_q4(int nbw, int nw) {
+// 8-block waves in workgroups of up to 8 waves keep one rolling register set: 80 registers,
+// so three 8-wave workgroups fit on a compute unit instead of two (measured at 248320 x 2048:
+// 55.0 against 57.8 us with three sets); wider workgroups keep the three sets.
 #define SV_Q4(NBW, NW) \
-    if (nbw == NBW && nw == NW) return q4b32_head<NBW, NW>;
+    if (nbw == NBW && nw == NW) return q4b32_head<NBW, NW, (NBW == 8 && NW <= 8) ? 1 : 0>;
     SV_Q4(8, 1) SV_Q4(8, 2) SV_Q4(8, 4) SV_Q4(8, 5) SV_Q4(8, 6) SV_Q4(8, 8) SV_Q4(8, 10) SV_Q4(8, 12)
     SV_Q4(8, 14) SV_Q4(8, 16)
     SV_Q4(16, 4) SV_Q4(16, 5) SV_Q4(16, 6) SV_Q4(16, 8) SV_Q4(16, 10) SV_Q4(16, 12)   // 14, 16 spill
