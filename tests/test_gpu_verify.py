@@ -17,7 +17,9 @@ pytestmark = pytest.mark.gpu
     (333, 2048, 33), (100, 96, 64), (8192, 512, 9), (4099, 320, 5), (70000, 64, 3), (777, 5120, 2),
     # 17 rows: one MFMA tile plus the 17th row's dot products (H = 512, 1024, 2048, 2560, 4096)
     (3001, 512, 17), (1000, 1024, 17), (5003, 2048, 17), (2000, 2560, 17), (1500, 4096, 17),
-    (2500, 5120, 17),                 # 8 of each wave's 20 blocks of window rows held in LDS
+    # one rolling register set, each with a ragged last tile: the argmax head at H = 2560, and
+    # the 17-row head at H = 5120 (8 of each wave's 20 blocks of window rows held in LDS)
+    (4099, 2560, 9), (2500, 5120, 17),
 ])
 def test_verify_matches_oracle(V, H, S):
     say(f"verify V={V} H={H} S={S}")
