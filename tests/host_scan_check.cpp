@@ -4,9 +4,15 @@
 // four past len - 1).  Built with AddressSanitizer, so any read below or past that array (the
 // kind of read that faulted the tree drafter's LDS scan on the GPU) stops the run.
 //
+// It also runs the global-memory drafter's chunked scan (chunk_window, chunk_key) at several
+// chunk sizes: each chunk is staged into a heap array of exactly kHalo + chunk ids, whose
+// slots outside the staged window hold the suffix's own ids, so a read of an unstaged slot
+// would show as a spurious match.
+//
 // stdin:  cases, then per case: len nmax nthreads, then len ids
 // stdout: per case: l e (best of scan_best_lds; 0 0 when nothing matched), then the four best
-//         keys of scan_top_lds merged over the threads, as l e pairs (0 0 past the last)
+//         keys of scan_top_lds merged over the threads, as l e pairs (0 0 past the last), then
+//         the best key of the chunked scan for each chunk size of kChunks, as l e pairs
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
@@ -14,6 +20,30 @@
 #include <vector>
 
 #include "../weight_bound_verify_amd/csrc/sv_tail.h"
+
+static const int kChunks[] = {1, 2, 3, 5, 8, 17, 64, 8192};
+
+// propose_block's scan, chunk by chunk, thread by simulated thread
+static unsigned long long chunked_best(const std::vector<int32_t>& ids, int len, int nmax, const int32_t* suf,
+                                       int chunk, int nthreads) {
+    unsigned long long best = 0;
+    const size_t n = (size_t)sv::kHalo + (size_t)chunk;
+    for (int base = 0; base < len - 1; base += chunk) {
+        int32_t* tk = static_cast<int32_t*>(std::malloc(n * 4));
+        if (!tk) std::exit(3);
+        for (size_t i = 0; i < n; ++i) tk[i] = suf[i % (nmax > 0 ? nmax : 1)];
+        const sv::ChunkWindow w = sv::chunk_window(base, chunk, len);
+        if (w.hi > w.lo) std::memcpy(tk + w.dst, ids.data() + w.lo, (size_t)(w.hi - w.lo) * 4);
+        // the staged ids stay in place; poison only marks what was never staged
+        for (int t = 0; t < nthreads; ++t)
+            for (int e = base + t; e < w.end; e += nthreads) {
+                const unsigned long long k = sv::chunk_key(tk, base, e, suf, nmax);
+                best = k > best ? k : best;
+            }
+        std::free(tk);
+    }
+    return best;
+}
 
 int main() {
     int cases = 0;
@@ -51,6 +81,10 @@ int main() {
         keys.resize(sv::kMaxBranches, 0ull);
         std::printf("%llu %llu", best >> 32, best & 0xffffffffull);
         for (unsigned long long k : keys) std::printf(" %llu %llu", k >> 32, k & 0xffffffffull);
+        for (int chunk : kChunks) {
+            const unsigned long long cb = chunked_best(ids, len, nmax, suf, chunk, nthreads < 64 ? nthreads : 64);
+            std::printf(" %llu %llu", cb >> 32, cb & 0xffffffffull);
+        }
         std::printf("\n");
         std::free(tk);
     }

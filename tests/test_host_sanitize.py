@@ -5,7 +5,9 @@
    guarantee: AddressSanitizer stops any read outside it (the regression test for the read
    below the LDS array that faulted the tree drafter's scan), and the results must equal the
    oracle's ranking of end positions (oracle.tree._ranked_matches), also on streams whose ids
-   are negative or INT_MIN (ids are never range-checked).
+   are negative or INT_MIN (ids are never range-checked).  The global-memory drafter's chunk
+   and halo arithmetic (chunk_window, chunk_key) runs the same way at chunk sizes 1 .. 8192,
+   each chunk staged into an array of exactly kHalo + chunk ids.
 2. The library's host code (argument validation, launch-shape selection, workspace sizing)
    built with both sanitizers runs the C-ABI tests of test_abi_cpu.py.
 
@@ -92,6 +94,9 @@ def test_lds_scans_stay_in_bounds_and_match_the_oracle(scan_harness):
         got_best, got_top = (v[0], v[1]), [(v[2 + 2 * i], v[3 + 2 * i]) for i in range(4)]
         assert got_best == tuple(best), (len(ids), nmax, nt, got_best, best)
         assert got_top == [tuple(t) for t in top], (len(ids), nmax, nt, got_top, top)
+        # the global-memory drafter's chunked scan at chunk sizes 1, 2, 3, 5, 8, 17, 64, 8192
+        chunked = [(v[10 + 2 * i], v[11 + 2 * i]) for i in range(8)]
+        assert all(c == tuple(best) for c in chunked), (len(ids), nmax, nt, chunked, best)
 
 
 @pytest.fixture(scope="module")

@@ -352,6 +352,34 @@ __device__ __forceinline__ int accept_sample_wave(const int32_t* sample, const f
 }
 
 // n-gram prompt lookup by a whole workgroup ("Stream C - Speculative decoding", the delta:
+// One chunk of the global-memory drafter: end positions [base, end) are scanned, and stream
+// ids [lo, hi) are staged at tk[dst .. dst + hi - lo) (tk[t] holds id base - kHalo + t).
+// Every id a scan of this chunk compares, e - i for e in [base, end), i < nmax <= kHalo and
+// e - i >= 0, lies in [lo, hi), and every tk index lies in [0, kHalo + chunk).
+struct ChunkWindow {
+    int lo, hi, dst, end;
+};
+__host__ __device__ __forceinline__ ChunkWindow chunk_window(int base, int chunk, int len) {
+    ChunkWindow w;
+    w.lo = base - kHalo < 0 ? 0 : base - kHalo;
+    w.hi = base + chunk < len ? base + chunk : len;
+    w.dst = w.lo - (base - kHalo);
+    w.end = base + chunk < len - 1 ? base + chunk : len - 1;
+    return w;
+}
+
+// The (match length, end position) key of end position e against the suffix suf (nmax ids,
+// newest first), read from a chunk staged as chunk_window describes: 0 when nothing matches.
+__host__ __device__ __forceinline__ unsigned long long chunk_key(const int32_t* tk, int base, int e,
+                                                                 const int32_t* suf, int nmax) {
+    int l = 0;
+#pragma unroll
+    for (int i = 0; i < SV_MAX_NGRAM; ++i) {
+        if (l == i && i < nmax && e - i >= 0 && tk[e - i - base + kHalo] == suf[i]) l = i + 1;
+    }
+    return l > 0 ? ((unsigned long long)l << 32) | (unsigned)e : 0ull;
+}
+
 // the last m ids of the stream index their most recent continuation; "Spec-decode on GDN
 // hybrids", harness lessons: the stream ends in the pending anchor, so drafts continue past
 // it).  For every end position e <= len-2 a thread computes the match length l(e) of the
@@ -381,22 +409,13 @@ __device__ __forceinline__ void propose_block(const int32_t* tokens, int cap, in
     unsigned long long best = 0;
     for (int base = 0; base < len - 1; base += chunk) {
         barrier_lds();
-        // tk[t] holds stream id base - kHalo + t; ids before the stream start are never compared
-        const int lo = base - kHalo < 0 ? 0 : base - kHalo;
-        const int hi = base + chunk < len ? base + chunk : len;
-        stage_ids(tokens + lo, hi - lo, tk + (lo - (base - kHalo)));
+        // ids before the stream start are never staged or compared
+        const ChunkWindow w = chunk_window(base, chunk, len);
+        stage_ids(tokens + w.lo, w.hi - w.lo, tk + w.dst);
         barrier_lds();
-        const int end = min(base + chunk, len - 1);     // e in [base, end)
-        for (int e = base + tid; e < end; e += nthreads) {
-            int l = 0;
-#pragma unroll
-            for (int i = 0; i < SV_MAX_NGRAM; ++i) {
-                if (l == i && i < nmax && e - i >= 0 && tk[e - i - base + kHalo] == suf[i]) l = i + 1;
-            }
-            if (l > 0) {
-                const unsigned long long key = ((unsigned long long)l << 32) | (unsigned)e;
-                best = key > best ? key : best;
-            }
+        for (int e = base + tid; e < w.end; e += nthreads) {
+            const unsigned long long key = chunk_key(tk, base, e, suf, nmax);
+            best = key > best ? key : best;
         }
     }
 #pragma unroll
