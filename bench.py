@@ -47,7 +47,7 @@ METRIC = "verify rounds/s and achieved HBM GB/s (% of peak), int8 lm_head S=K+1"
 
 # workloads: (config id for seeds, V, H, K, drafts, context length, copy rate, layers)
 WORKLOADS = {
-    "c1": dict(cid=0, V=8192, H=512, K=8, drafts="ngram", ctx=512, copy=None, layers=0,
+    "c1": dict(cid=0, V=8192, H=512, K=8, drafts="ngram", ctx=512, copy=None, layers=0, graph=64,
                name="tiny head H=512 V=8192 K=8 S=9, n-gram drafts over a 512-id context with a planted span"),
     "c2": dict(cid=1, V=151936, H=2560, K=8, drafts="ngram", ctx=4096, copy=0.30, layers=0,
                name="Qwen3-4B-shaped head H=2560 V=151936 K=8 S=9, n-gram drafts over 4096 Zipf(1.1) ids with 30% copied spans"),
@@ -464,6 +464,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=50, help="isolated head launches timed for the roofline")
     ap.add_argument("--calib-copy", action="store_true", help="run a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--graph-rounds", type=int, default=-1,
+                    help="replay the timed rounds and the batches from one HIP graph of this many rounds "
+                         "(0 = launch every round; -1 = the workload's default: a graph only where the round "
+                         "is launch-bound)")
     ap.add_argument("--down-split", type=int, default=0,
                     help="dense stack: split the down projection's hidden axis this many ways (2..8; 0 = unsplit)")
     args = ap.parse_args()
@@ -480,6 +484,13 @@ def main():
 
     if args.down_split:
         sv.set_tuning(0, 0, 0, 0, args.down_split)
+    if args.graph_rounds < 0:
+        args.graph_rounds = WORKLOADS[args.config].get("graph", 0)
+    if args.graph_rounds > 0:
+        # whole graphs only: the timed rounds and every batch are replays of one graph
+        G = args.graph_rounds
+        args.steps = -(-args.steps // G) * G
+        args.batch_rounds = G
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.calib_copy:
@@ -643,12 +654,26 @@ def main():
     for r in range(args.warmup):
         round_(r)
     torch.cuda.synchronize()
+    graph = None
+    if args.graph_rounds > 0:
+        # G rounds captured once (nothing runs during capture; the round state lives on the
+        # device, so every replay advances it by G rounds).  Round i of the graph uses hidden
+        # set, forced drafts and weight copy number i, as eager round i would.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.graph_rounds):
+                round_(i)
+        torch.cuda.synchronize()
     st0 = state.cpu().numpy().copy()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
-    for r in range(args.steps):
-        round_(args.warmup + r)
+    if graph is not None:
+        for _ in range(args.steps // args.graph_rounds):
+            graph.replay()
+    else:
+        for r in range(args.steps):
+            round_(args.warmup + r)
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
@@ -666,8 +691,12 @@ def main():
 
     # batches of rounds (median, IQR), rotated weights and one copy; c_v(S)
     base = args.warmup + args.steps
-    batches = _batch_stats(time_batches(lambda i: round_(base + i), args.batches, args.batch_rounds),
-                           args.batch_rounds)
+    if graph is not None:
+        replay = lambda i: graph.replay() if i % args.graph_rounds == 0 else None
+        batches = _batch_stats(time_batches(replay, args.batches, args.batch_rounds), args.batch_rounds)
+    else:
+        batches = _batch_stats(time_batches(lambda i: round_(base + i), args.batches, args.batch_rounds),
+                               args.batch_rounds)
     single = None
     if copies > 1:
         single = _batch_stats(time_batches(lambda i: round_(base + i, single=True), args.batches, args.batch_rounds),
@@ -776,6 +805,8 @@ def main():
         out["config"]["tree"] = {"branches": tree[0], "depth": tree[1], "nodes": K}
     if wl["layers"] and args.down_split:
         out["config"]["down_split"] = args.down_split
+    if args.graph_rounds > 0:
+        out["config"]["graph_rounds"] = args.graph_rounds
     if temp:
         out["config"]["temperature"] = temp
         out["config"]["seed"] = SAMPLE_SEED
