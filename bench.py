@@ -698,7 +698,15 @@ def main():
         batches = _batch_stats(time_batches(lambda i: round_(base + i), args.batches, args.batch_rounds),
                                args.batch_rounds)
     single = None
-    if copies > 1:
+    if copies > 1 and graph is not None:
+        # the same rounds on one weight copy, from a graph of their own
+        graph1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph1):
+            for i in range(args.graph_rounds):
+                round_(i, single=True)
+        replay1 = lambda i: graph1.replay() if i % args.graph_rounds == 0 else None
+        single = _batch_stats(time_batches(replay1, args.batches, args.batch_rounds), args.batch_rounds)
+    elif copies > 1:
         single = _batch_stats(time_batches(lambda i: round_(base + i, single=True), args.batches, args.batch_rounds),
                               args.batch_rounds)
     cv = None
