@@ -79,6 +79,8 @@ struct Q4Regs {
     uint32_t sc[NBW / 2];                          // fp16 scales of the lane's row, in pairs
 };
 
+// ROLL = 0: three fixed register sets (two items' loads in flight while one is converted);
+// ROLL = k > 0: k sets refilled segment by segment as the LDS exchange frees them.
 template <int NBW, int NW, int ROLL = 0>
 __global__ __launch_bounds__(NW * 64) void q4b32_head(Q4Args a) {
     constexpr int NSEG = NBW / 8;
@@ -194,10 +196,18 @@ __global__ __launch_bounds__(NW * 64) void q4b32_head(Q4Args a) {
     const int last = a.nitems - 1;
     int it = blockIdx.x, k = 0;
     if constexpr (ROLL) {
-        // one register set refilled segment by segment: one item's loads in flight
-        Q4Regs<NBW> r;
-        load(r, min(it, last));
-        for (; it < a.nitems; it += step) process(r, it, k++ & 1, min(it + step, last));
+        // ROLL register sets refilled segment by segment: set j holds items j, j + ROLL, ...,
+        // so ROLL items' loads are in flight
+        Q4Regs<NBW> rs[ROLL];
+#pragma unroll
+        for (int j = 0; j < ROLL; ++j) load(rs[j], min(it + j * step, last));
+        while (it < a.nitems) {
+#pragma unroll
+            for (int j = 0; j < ROLL; ++j) {
+                if (it < a.nitems) process(rs[j], it, k++ & 1, min(it + ROLL * step, last));
+                it += step;
+            }
+        }
     } else {
         // three register sets: two items' loads stay in flight while one is processed
         Q4Regs<NBW> ra, rb, rc;
@@ -238,9 +248,12 @@ typedef void (*Q4Fn)(Q4Args);
 Q4Fn pick_q4(int nbw, int nw) {
 // 8-block waves in workgroups of up to 8 waves keep one rolling register set: 80 registers,
 // so three 8-wave workgroups fit on a compute unit instead of two (measured at 248320 x 2048:
-// 55.0 against 57.8 us with three sets); wider workgroups keep the three sets.
+// 55.0 against 57.8 us with three fixed sets); wider workgroups keep the three sets.  More
+// rolling sets keep more items in flight but fewer waves: 2 sets measured even, 3 and 4 sets
+// 1.5% and 4.5% slower.
+constexpr int kQ4Sets = 1;
 #define SV_Q4(NBW, NW) \
-    if (nbw == NBW && nw == NW) return q4b32_head<NBW, NW, (NBW == 8 && NW <= 8) ? 1 : 0>;
+    if (nbw == NBW && nw == NW) return q4b32_head<NBW, NW, (NBW == 8 && NW <= 8) ? kQ4Sets : 0>;
     SV_Q4(8, 1) SV_Q4(8, 2) SV_Q4(8, 4) SV_Q4(8, 5) SV_Q4(8, 6) SV_Q4(8, 8) SV_Q4(8, 10) SV_Q4(8, 12)
     SV_Q4(8, 14) SV_Q4(8, 16)
     SV_Q4(16, 4) SV_Q4(16, 5) SV_Q4(16, 6) SV_Q4(16, 8) SV_Q4(16, 10) SV_Q4(16, 12)   // 14, 16 spill
