@@ -30,6 +30,7 @@ Host-only helpers for the profile summaries (no GPU needed):
 from __future__ import annotations
 
 import argparse
+import functools
 import hashlib
 import json
 import os
@@ -205,11 +206,17 @@ def summarize_counters(workload, kernel_sub, pdir, commands):
     print(json.dumps(rec, indent=1))
 
 
+def _streams(wl, synth):
+    """The workload's seeded streams; a nonzero --seed moves every stream to another base (the
+    config ids stay below 2^16 apart, so no two (seed, config) pairs share a base)."""
+    return synth.streams(wl["cid"], synth.SEED_BASE + (wl["seed"] << 16))
+
+
 def build_inputs(wl, args, torch, sv, synth):
     dev = torch.device("cuda:0")
     V, H, K = wl["V"], wl["H"], wl["K"]
     S = K + 1
-    st = synth.streams(wl["cid"])
+    st = _streams(wl, synth)
     t0 = time.time()
     if wl.get("fmt") == "q4":
         q, s = synth.quantized_head_q4(st.weights, V, H)
@@ -300,15 +307,15 @@ class _OracleRound:
             self.r += 1
             return
         if wl.get("tree"):
-            parents, drafts, _, _ = oracle.propose_tree(self.tokens, 3, K, *wl["tree"])
+            parents, drafts, _, _ = oracle.propose_tree(self.tokens, wl["ngram"], K, *wl["tree"])
         else:
-            drafts, _, _ = oracle.propose_scan(self.tokens, 3, K)
+            drafts, _, _ = oracle.propose_scan(self.tokens, wl["ngram"], K)
         L = self.logits(self.window(drafts))
         a = oracle.argmax_lowest(L)
         if wl["drafts"] == "forced":
             drafts, _ = self.synth.forced_drafts(self.rng, a, K, wl["V"])
         if wl.get("temp"):
-            app = oracle.sampling_verify(L, drafts, wl["temp"], SAMPLE_SEED, len(self.tokens))["appended"]
+            app = oracle.sampling_verify(L, drafts, wl["temp"], wl["sample_seed"], len(self.tokens))["appended"]
         elif wl.get("tree"):
             _, app, _ = oracle.tree_accept(a, parents, drafts)
         else:
@@ -396,7 +403,7 @@ def _cpu_baseline_stack(wl, inp, cores, budget=8.0):
             if sum(tb) > budget:
                 break
         t1 = time.perf_counter()
-        drafts, _, _ = oracle.propose_scan(list(inp["ctx"]), 3, K)
+        drafts, _, _ = oracle.propose_scan(list(inp["ctx"]), wl["ngram"], K)
         Lg = oracle.head_logits(inp["q"], inp["s"], oracle.rmsnorm_fp16(x))
         oracle.accept(oracle.argmax_lowest(Lg), drafts)
         th = time.perf_counter() - t1
@@ -444,6 +451,30 @@ def _batch_stats(ms_per_batch, rounds_per_batch):
             "median_us_per_round": round(1e6 / float(med), 3)}
 
 
+def configure_workload(args):
+    """The workload of --config with the --K, --ngram and --seed overrides applied."""
+    wl = dict(WORKLOADS[args.config])
+    if not 1 <= args.ngram <= 8:
+        raise SystemExit(f"--ngram {args.ngram}: the drafter takes n-gram orders 1..8")
+    if not 0 <= args.seed < 2 ** 15:
+        raise SystemExit(f"--seed {args.seed}: use 0 .. {2 ** 15 - 1}")
+    if args.K is not None and args.K != wl["K"]:
+        # the sampling, tree, int4 and dense-stack paths take windows of at most 16 rows
+        kmax = 15 if (wl.get("tree") or wl.get("temp") or wl.get("fmt") == "q4" or wl["layers"]) else 63
+        if wl["K"] == 0 or not 1 <= args.K <= kmax:
+            raise SystemExit(f"--K {args.K}: workload {args.config} takes K in 1..{kmax}"
+                             if wl["K"] else f"--K: {args.config} is the one-row decode step (K = 0)")
+        K = args.K
+        name = re.sub(r"K=\d+ S=\d+", f"K={K} S={K + 1}", wl["name"])
+        name = re.sub(r"\d+ tree nodes \(S=\d+\)", f"{K} tree nodes (S={K + 1})", name)
+        wl["name"] = name if name != wl["name"] else f"{name}; K={K} S={K + 1}"
+        wl["K"] = K
+    wl["ngram"] = args.ngram
+    wl["seed"] = args.seed
+    wl["sample_seed"] = SAMPLE_SEED + args.seed
+    return wl
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "summarize-trace":
         # bench.py summarize-trace DB OUT TITLE COMMAND [NOTE]
@@ -468,6 +499,11 @@ def main():
                     help="replay the timed rounds and the batches from one HIP graph of this many rounds "
                          "(0 = launch every round; -1 = the workload's default: a graph only where the round "
                          "is launch-bound)")
+    ap.add_argument("--K", type=int, default=None,
+                    help="drafts per round (S = K+1 window rows; default: the workload's K)")
+    ap.add_argument("--ngram", type=int, default=3, help="largest n-gram order of the drafter (1..8)")
+    ap.add_argument("--seed", type=int, default=0,
+                    help="input seed: 0 = the workload's own streams, others move every seeded input")
     ap.add_argument("--down-split", type=int, default=0,
                     help="dense stack: split the down projection's hidden axis this many ways (2..8; 0 = unsplit)")
     args = ap.parse_args()
@@ -504,7 +540,7 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "launches": 3}))
         return
 
-    wl = WORKLOADS[args.config]
+    wl = configure_workload(args)
     V, H, K = wl["V"], wl["H"], wl["K"]
     S = K + 1
     if not args.batch_rounds:
@@ -531,7 +567,7 @@ def main():
     if wl.get("model") == "table":
         # token-indexed stand-in model: hidden row of a window position = table[token]
         gen = torch.Generator(device=dev)
-        gen.manual_seed(20261202 + wl["cid"])
+        gen.manual_seed(20261202 + wl["cid"] + (wl["seed"] << 16))
         table = torch.randn((V, H), generator=gen, device=dev, dtype=torch.float32).half()
         window = torch.empty((S, H), dtype=torch.float16, device=dev)
         h_last = torch.empty((1, H), dtype=torch.float16, device=dev)
@@ -543,7 +579,7 @@ def main():
         window = torch.empty((S, H), dtype=torch.float16, device=dev)
         h_last = rows[len(inp["ctx"]) - 1:len(inp["ctx"])].clone()
     else:
-        h_last = torch.from_numpy(synth.fp16_normal(synth.streams(wl["cid"]).h_last, (1, H))).to(dev)
+        h_last = torch.from_numpy(synth.fp16_normal(_streams(wl, synth).h_last, (1, H))).to(dev)
 
     def gather_script(stream=None):
         sv.gather_positions(state, cap, rows, window, stream=stream)
@@ -551,16 +587,18 @@ def main():
     # anchor bootstrap: S = 1 verify of the last context row, then accept with K = 0 commits a0
     a0 = torch.empty(1, dtype=torch.int32, device=dev)
     head_verify = sv.verify_q4 if wl.get("fmt") == "q4" else sv.verify
-    head_round = sv.round_q4 if wl.get("fmt") == "q4" else sv.round
+    ngram = wl["ngram"]
+    sample_seed = wl["sample_seed"]
+    head_round = functools.partial(sv.round_q4 if wl.get("fmt") == "q4" else sv.round, ngram_max=ngram)
     if temp:
         # sampling: the anchor is a draw from the last context row, a one-row sampling round
         lse0, zd0 = (torch.empty(1, dtype=torch.float32, device=dev) for _ in range(2))
-        sv.verify_sample(wq[0], ws[0], h_last, None, temp, SAMPLE_SEED, state, a0, lse0, zd0,
+        sv.verify_sample(wq[0], ws[0], h_last, None, temp, sample_seed, state, a0, lse0, zd0,
                          sv.workspace(sv.sample_workspace_bytes(V, H, 1), dev))
-        sv.accept_sample(a0, lse0, zd0, None, V, SAMPLE_SEED, tokens, state)
+        sv.accept_sample(a0, lse0, zd0, None, V, sample_seed, tokens, state)
 
         def head_round(w_, s_, x_, d_in_, tokens_, state_, drafts_, argmax_, work_, stream=None):
-            sv.round_sample(w_, s_, x_, d_in_, temp, SAMPLE_SEED, tokens_, state_, drafts_, work_, 3, argmax_,
+            sv.round_sample(w_, s_, x_, d_in_, temp, sample_seed, tokens_, state_, drafts_, work_, ngram, argmax_,
                             stream=stream)
     else:
         head_verify(wq[0], ws[0], h_last, a0, work1)
@@ -569,7 +607,7 @@ def main():
     forced = None
     if wl["drafts"] == "forced":
         # drafts that match the first j ~ U{0..K} greedy ids of each hidden set (setup, untimed)
-        rng_d = np.random.default_rng(synth.streams(wl["cid"]).drafts)
+        rng_d = np.random.default_rng(_streams(wl, synth).drafts)
         fd = np.empty((R_SETS, K), dtype=np.int32)
         gwork = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev)
         for r in range(R_SETS):
@@ -593,13 +631,13 @@ def main():
     tree = wl.get("tree")
     if tree:
         parents = torch.empty(K, dtype=torch.int32, device=dev)
-        sv.propose_tree(tokens, state, parents, drafts, 3, tree[0], tree[1])
+        sv.propose_tree(tokens, state, parents, drafts, ngram, tree[0], tree[1])
 
         def head_round(w_, s_, x_, d_in_, tokens_, state_, drafts_, argmax_, work_, stream=None):
-            sv.round_tree(w_, s_, x_, parents, d_in_, tokens_, state_, parents, drafts_, argmax_, work_, 3,
+            sv.round_tree(w_, s_, x_, parents, d_in_, tokens_, state_, parents, drafts_, argmax_, work_, ngram,
                           tree[0], tree[1], stream=stream)
     elif not decode:
-        sv.propose(tokens, state, drafts, 3)
+        sv.propose(tokens, state, drafts, ngram)
 
     def round_(r, single=False):
         c = 0 if single else r % copies
@@ -610,7 +648,7 @@ def main():
             return
         if table is not None:
             # gather the window [a0, drafts] from the stand-in model, verify, accept, draft
-            sv.generate(wq[c], ws[c], table, tokens, state, drafts, window, argmax, work, 1)
+            sv.generate(wq[c], ws[c], table, tokens, state, drafts, window, argmax, work, 1, ngram)
             return
         if rows is not None:
             gather_script()
@@ -748,7 +786,7 @@ def main():
         elif decode:
             head_verify(wq[c], ws[c], x[:1], a0, work1, stream=stream)
         elif table is not None:
-            sv.generate(wq[c], ws[c], table, tokens, state, drafts, window, argmax, work, 1, stream=stream)
+            sv.generate(wq[c], ws[c], table, tokens, state, drafts, window, argmax, work, 1, ngram, stream=stream)
         elif rows is not None:
             gather_script(stream)
             head_round(wq[c], ws[c], window, drafts, tokens, state, drafts, argmax, work, stream=stream)
@@ -780,12 +818,13 @@ def main():
         "dtype": "i4xf16->f32" if wl.get("fmt") == "q4" else "i8xf16->f32",
         "data": "synthetic",
         "config": {"workload": wl["name"], "V": V, "H": H, "S": S, "K": K, "layers": wl["layers"],
-                   "drafts": wl["drafts"], "weight_copies": copies, "hidden_sets": R_SETS},
+                   "drafts": wl["drafts"], "ngram_max": ngram, "seed": wl["seed"], "weight_copies": copies,
+                   "hidden_sets": R_SETS},
         "achieved_GBps": round(gbps, 1),
         "pct_of_peak_hbm": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "bytes_per_round": round_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": load_traffic(args.config),
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": load_traffic(args.config) if wl["K"] == WORKLOADS[args.config]["K"] else None,
                      "kernel": (f"q8b32 gate/up projection of the dense stack with the RMSNorm in its prologue "
                                 f"and the SiLU-mul epilogue ({wl['layers']} launches per round, block 0 timed)"
                                 if wl["layers"] else
@@ -817,7 +856,7 @@ def main():
         out["config"]["graph_rounds"] = args.graph_rounds
     if temp:
         out["config"]["temperature"] = temp
-        out["config"]["seed"] = SAMPLE_SEED
+        out["config"]["sample_seed"] = sample_seed
     if inp["copy_frac"] is not None:
         out["config"]["context_copy_fraction"] = round(inp["copy_frac"], 3)
     if table is not None or rows is not None:

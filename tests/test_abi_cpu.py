@@ -283,6 +283,45 @@ def test_bench_refuses_more_than_one_gpu():
     assert res.returncode == 2 and "one GPU" in res.stderr and res.stdout == ""
 
 
+def test_bench_workload_overrides():
+    """--K, --ngram and --seed: the workload's K and name follow an override; the decode step
+    and the 16-row window limit of the sampling, tree, int4 and stack paths refuse one; a
+    nonzero seed moves every seeded stream while seed 0 keeps the workload's own."""
+    import importlib.util
+    import types
+    import numpy as np
+    from weight_bound_verify_amd import synth
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    args = lambda config, K=None, ngram=3, seed=0: types.SimpleNamespace(config=config, K=K, ngram=ngram, seed=seed)
+
+    wl = bench.configure_workload(args("c3", K=16, ngram=2))
+    assert wl["K"] == 16 and wl["ngram"] == 2 and "K=16 S=17" in wl["name"] and "K=8" not in wl["name"]
+    assert bench.WORKLOADS["c3"]["K"] == 8                         # the table itself is untouched
+    wl = bench.configure_workload(args("c3tree", K=12))
+    assert "12 tree nodes (S=13)" in wl["name"]
+    for bad in (args("c4s1", K=2), args("c3samp", K=16), args("c3tree", K=16), args("c3q4", K=16),
+                args("c5", K=16), args("c3", K=64),
+                args("c3", K=0), args("c3", ngram=0), args("c3", ngram=9), args("c3", seed=-1)):
+        with pytest.raises(SystemExit):
+            bench.configure_workload(bad)
+
+    def first_words(wl):
+        return words(bench._streams(wl, synth))
+
+    def words(st):
+        return [np.random.default_rng(getattr(st, f)).integers(0, 2 ** 32, 2).tolist()
+                for f in ("weights", "h_last", "hidden", "context", "drafts")]
+    same = first_words(bench.configure_workload(args("c3")))
+    assert same == words(synth.streams(2))
+    moved = first_words(bench.configure_workload(args("c3", seed=1)))
+    assert all(a != b for a, b in zip(same, moved))
+    other = first_words(bench.configure_workload(args("c2", seed=1)))       # config 1, seed 1
+    assert all(a != b for a, b in zip(moved, other))
+
+
 def test_round_noalloc_refuses_scratch_beyond_its_static_array(lib):
     """A split hidden axis over a large vocabulary needs more than the 2 MiB library-held
     scratch: refused on the host (SV_ERR_SHAPE) before any HIP call, with the sizes in the
