@@ -454,6 +454,8 @@ def _batch_stats(ms_per_batch, rounds_per_batch):
 def configure_workload(args):
     """The workload of --config with the --K, --ngram and --seed overrides applied."""
     wl = dict(WORKLOADS[args.config])
+    if getattr(args, "logits", False) and (wl.get("temp") or wl.get("model") or wl["K"] == 0):
+        raise SystemExit(f"--logits: workload {args.config} has no round call that writes logits")
     if not 1 <= args.ngram <= 8:
         raise SystemExit(f"--ngram {args.ngram}: the drafter takes n-gram orders 1..8")
     if not 0 <= args.seed < 2 ** 15:
@@ -504,6 +506,9 @@ def main():
     ap.add_argument("--ngram", type=int, default=3, help="largest n-gram order of the drafter (1..8)")
     ap.add_argument("--seed", type=int, default=0,
                     help="input seed: 0 = the workload's own streams, others move every seeded input")
+    ap.add_argument("--logits", action="store_true",
+                    help="every round also writes the full fp32 logits [S][V] (greedy workloads that verify "
+                         "through a round call: not the sampling, generation or decode workloads)")
     ap.add_argument("--down-split", type=int, default=0,
                     help="dense stack: split the down projection's hidden axis this many ways (2..8; 0 = unsplit)")
     args = ap.parse_args()
@@ -589,7 +594,10 @@ def main():
     head_verify = sv.verify_q4 if wl.get("fmt") == "q4" else sv.verify
     ngram = wl["ngram"]
     sample_seed = wl["sample_seed"]
-    head_round = functools.partial(sv.round_q4 if wl.get("fmt") == "q4" else sv.round, ngram_max=ngram)
+    # --logits: every timed round also writes the window's full fp32 logits [S][V]
+    logits_buf = torch.empty((S, V), dtype=torch.float32, device=dev) if args.logits else None
+    head_round = functools.partial(sv.round_q4 if wl.get("fmt") == "q4" else sv.round, ngram_max=ngram,
+                                   logits=logits_buf)
     if temp:
         # sampling: the anchor is a draw from the last context row, a one-row sampling round
         lse0, zd0 = (torch.empty(1, dtype=torch.float32, device=dev) for _ in range(2))
@@ -635,7 +643,7 @@ def main():
 
         def head_round(w_, s_, x_, d_in_, tokens_, state_, drafts_, argmax_, work_, stream=None):
             sv.round_tree(w_, s_, x_, parents, d_in_, tokens_, state_, parents, drafts_, argmax_, work_, ngram,
-                          tree[0], tree[1], stream=stream)
+                          tree[0], tree[1], logits=logits_buf, stream=stream)
     elif not decode:
         sv.propose(tokens, state, drafts, ngram)
 
@@ -850,6 +858,9 @@ def main():
         out["c_v"] = cv
     if tree:
         out["config"]["tree"] = {"branches": tree[0], "depth": tree[1], "nodes": K}
+    if args.logits:
+        out["config"]["logits"] = "fp32 [S][V] written every round"
+        out["bytes_per_round_with_logits"] = round_bytes + 4 * S * V
     if wl["layers"] and args.down_split:
         out["config"]["down_split"] = args.down_split
     if args.graph_rounds > 0:

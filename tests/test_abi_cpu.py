@@ -284,9 +284,10 @@ def test_bench_refuses_more_than_one_gpu():
 
 
 def test_bench_workload_overrides():
-    """--K, --ngram and --seed: the workload's K and name follow an override; the decode step
-    and the 16-row window limit of the sampling, tree, int4 and stack paths refuse one; a
-    nonzero seed moves every seeded stream while seed 0 keeps the workload's own."""
+    """--K, --ngram, --seed and --logits: the workload's K and name follow an override; the
+    decode step and the 16-row window limit of the sampling, tree, int4 and stack paths refuse
+    one; a nonzero seed moves every seeded stream while seed 0 keeps the workload's own;
+    --logits is refused where no round call writes logits."""
     import importlib.util
     import types
     import numpy as np
@@ -295,16 +296,20 @@ def test_bench_workload_overrides():
     spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(root, "bench.py"))
     bench = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(bench)
-    args = lambda config, K=None, ngram=3, seed=0: types.SimpleNamespace(config=config, K=K, ngram=ngram, seed=seed)
+    args = lambda config, K=None, ngram=3, seed=0, logits=False: types.SimpleNamespace(
+        config=config, K=K, ngram=ngram, seed=seed, logits=logits)
 
     wl = bench.configure_workload(args("c3", K=16, ngram=2))
     assert wl["K"] == 16 and wl["ngram"] == 2 and "K=16 S=17" in wl["name"] and "K=8" not in wl["name"]
     assert bench.WORKLOADS["c3"]["K"] == 8                         # the table itself is untouched
+    for cfg in ("c1", "c2", "c3", "c3q4", "c3tree", "c4s17", "c5"):
+        bench.configure_workload(args(cfg, logits=True))           # these write logits when asked
     wl = bench.configure_workload(args("c3tree", K=12))
     assert "12 tree nodes (S=13)" in wl["name"]
     for bad in (args("c4s1", K=2), args("c3samp", K=16), args("c3tree", K=16), args("c3q4", K=16),
                 args("c5", K=16), args("c3", K=64),
-                args("c3", K=0), args("c3", ngram=0), args("c3", ngram=9), args("c3", seed=-1)):
+                args("c3", K=0), args("c3", ngram=0), args("c3", ngram=9), args("c3", seed=-1),
+                args("c3samp", logits=True), args("c3gen", logits=True), args("c4s1", logits=True)):
         with pytest.raises(SystemExit):
             bench.configure_workload(bad)
 
