@@ -452,7 +452,8 @@ def _batch_stats(ms_per_batch, rounds_per_batch):
 
 
 def configure_workload(args):
-    """The workload of --config with the --K, --ngram and --seed overrides applied."""
+    """The workload of --config with the --K, --ngram and --seed overrides applied (and --logits
+    checked against it); raises SystemExit on a value the workload cannot take."""
     wl = dict(WORKLOADS[args.config])
     if getattr(args, "logits", False) and (wl.get("temp") or wl.get("model") or wl["K"] == 0):
         raise SystemExit(f"--logits: workload {args.config} has no round call that writes logits")
@@ -517,6 +518,7 @@ def main():
         print("bench.py measures one GPU: the library has no multi-GPU path (the vocab-sharded head "
               "and the tensor-parallel stack are a design, not code); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    wl = configure_workload(args)          # argument errors before anything touches the GPU
 
     import torch
 
@@ -545,7 +547,6 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "launches": 3}))
         return
 
-    wl = configure_workload(args)
     V, H, K = wl["V"], wl["H"], wl["K"]
     S = K + 1
     if not args.batch_rounds:
