@@ -8,12 +8,15 @@ several hidden-axis splits), the int4 head's supported widths, and vocabularies 
 16-row tile is ragged.  Each case meets the fixed-shape tests' bar: logits within 1e-3 of the
 oracle's (relative, with the row RMS as floor), argmax equal except below a 1e-3 top-2 gap.  A
 fused-round sweep draws (V, H, K, n-gram order, context length) and checks the committed ids
-and next drafts of three rounds exactly against oracle.accept and oracle.propose_scan."""
+and next drafts of three rounds exactly against oracle.accept and oracle.propose_scan; a
+tree-round sweep does the same for tree verify (K nodes, B branches, depth D) against
+oracle.tree."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
+from oracle import tree as tr
 from weight_bound_verify_amd import specverify as sv
 from weight_bound_verify_amd import synth
 
@@ -118,4 +121,59 @@ def test_round_random_shape(V, H, K, n, ctx_len):
         assert m == len(stream) and tokens[:m].cpu().tolist() == stream, r
         d = drafts.cpu().tolist()
         assert d == list(oracle.propose_scan(stream, n, K)[0]), r
+    assert int(state[sv.STATE_FLAGS]) == 0
+
+
+def _tree_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        H = int(32 * rng.integers(1, 129))
+        V = int(rng.choice([int(rng.integers(2, 40)), int(rng.integers(40, min(20000, ELEMS // H) + 1))]))
+        K = int(rng.integers(1, 16))
+        out.append((V, H, K, int(rng.integers(1, 5)), int(rng.integers(1, K + 1)), int(rng.integers(1, 9)),
+                    int(rng.integers(1, 3000))))
+    return out
+
+
+@pytest.mark.parametrize("V,H,K,B,D,n,ctx_len", _tree_cases(20261206, 10))
+def test_round_tree_random_shape(V, H, K, B, D, n, ctx_len):
+    """Three fused tree rounds (K nodes from the B best matches D deep, n-gram order n): the
+    argmax rows against the oracle's logits (near-tie rule), then the walk, the committed stream
+    and the next tree exactly against oracle.tree applied to the GPU's argmax rows.  Small
+    vocabularies make accepted paths common."""
+    say(f"round_tree random V={V} H={H} K={K} B={B} D={D} n={n} ctx={ctx_len}")
+    S = K + 1
+    rng = np.random.default_rng(V + H + K + B + D + n + ctx_len)
+    q, s = synth.quantized_head(np.random.SeedSequence(V + 5 * H), V, H)
+    ctx = synth.zipf_context_with_copies(rng, ctx_len, V, 0.3)[0]
+    hidden = synth.fp16_normal(rng, (3, S, H))
+    cap = ctx_len + 3 * S + 8
+    buf = np.zeros(cap, dtype=np.int32)
+    buf[:ctx_len] = ctx
+    tokens = to_dev(buf)
+    state = sv.new_state(dev())
+    state[sv.STATE_LEN] = ctx_len
+    parents = torch.empty(K, dtype=torch.int32, device=dev())
+    drafts = torch.empty(K, dtype=torch.int32, device=dev())
+    argmax = torch.empty(S, dtype=torch.int32, device=dev())
+    work = sv.workspace(sv.verify_workspace_bytes(V, H, S), dev())
+    wq, ws = to_dev(q), to_dev(s)
+    sv.propose_tree(tokens, state, parents, drafts, n, B, D)
+    torch.cuda.synchronize()
+    stream = [int(t) for t in ctx]
+    p0, d0, _, _ = tr.propose_tree(stream, n, K, B, D)
+    assert parents.cpu().tolist() == list(p0) and drafts.cpu().tolist() == list(d0)
+    for r in range(3):
+        sv.round_tree(wq, ws, to_dev(hidden[r]), parents, drafts, tokens, state, parents, drafts, argmax, work,
+                      n, B, D)
+        torch.cuda.synchronize()
+        a_gpu = argmax.cpu().numpy()
+        check_argmax(a_gpu, oracle.head_logits(q, s, hidden[r]))
+        j, app, _ = tr.tree_accept(a_gpu, p0, d0)
+        stream += app
+        m = int(state[sv.STATE_LEN])
+        assert m == len(stream) and tokens[:m].cpu().tolist() == stream and int(state[sv.STATE_J]) == j, r
+        p0, d0, _, _ = tr.propose_tree(stream, n, K, B, D)
+        assert parents.cpu().tolist() == list(p0) and drafts.cpu().tolist() == list(d0), r
     assert int(state[sv.STATE_FLAGS]) == 0
