@@ -10,7 +10,7 @@ oracle's (relative, with the row RMS as floor), argmax equal except below a 1e-3
 fused-round sweep draws (V, H, K, n-gram order, context length) and checks the committed ids
 and next drafts of three rounds exactly against oracle.accept and oracle.propose_scan; a
 tree-round sweep does the same for tree verify (K nodes, B branches, depth D) against
-oracle.tree."""
+oracle.tree, and a dense-stack sweep checks random block shapes block by block."""
 import numpy as np
 import pytest
 import torch
@@ -177,3 +177,36 @@ def test_round_tree_random_shape(V, H, K, B, D, n, ctx_len):
         p0, d0, _, _ = tr.propose_tree(stream, n, K, B, D)
         assert parents.cpu().tolist() == list(p0) and drafts.cpu().tolist() == list(d0), r
     assert int(state[sv.STATE_FLAGS]) == 0
+
+
+def _stack_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        H = int(512 * rng.integers(1, 9))
+        F = int(512 * rng.integers(1, 13))
+        if H * F > 8 * 1024 * 1024:
+            continue
+        out.append((H, F, int(rng.integers(1, 17)), int(rng.integers(1, 4))))
+    return out
+
+
+@pytest.mark.parametrize("H,F,S,L", _stack_cases(20261207, 10))
+def test_stack_random_shape(H, F, S, L):
+    """The dense stack at random block shapes (hidden and inner sizes multiples of 512, S = 1..16,
+    1..3 blocks): every block of the multi-block call equals a single-block call on its input,
+    and each single-block call meets the teacher-forced oracle bounds of the fixed-shape stack
+    tests at both stages."""
+    from test_gpu_stack_fused import _check_block, _run, _stacked
+    say(f"stack random H={H} F={F} S={S} L={L}")
+    rng = np.random.default_rng(H + 7 * F + S + L)
+    layers, mats = _stacked(rng, L, H, F)
+    x = (synth.fp16_normal(rng, (S, H)).astype(np.float32) * 3).astype(np.float16)
+    _, xl, nrm = _run(mats, x, L)
+    prev = x
+    for li in range(L):
+        _, xl1, nrm1, m_gpu, ss = _run([m[li:li + 1] for m in mats], prev, 1, want_ws=True)
+        assert np.array_equal(xl1[0], xl[li]), f"block {li}: differs from a single-block call"
+        _check_block(prev, layers[li], xl1[0], nrm1, m_gpu, ss)
+        prev = xl[li]
+    assert np.array_equal(nrm, nrm1)
