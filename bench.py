@@ -850,6 +850,9 @@ def main():
                         pct_of_peak_hbm=round(100.0 * round_bytes * batches["median_rounds_per_s"] / 1e9
                                               / PEAK_HBM_GBPS, 2)),
         "accept_hist": hist,
+        # the share of rounds that accepted at least one draft (the zero-accept rounds are what
+        # the hit-rate gate counts)
+        "draft_hit_rate": round(1.0 - hist[0] / max(1, sum(hist)), 4) if not decode else None,
         "tokens_per_round": round((args.steps + sum_j) / args.steps, 3),
     }
     if single is not None:
