@@ -30,7 +30,8 @@ def _state_tokens(ctx, cap):
 
 
 @pytest.mark.parametrize("V,H,K,alias", [(30000, 2048, 8, True), (30000, 2048, 8, False), (5000, 512, 16, True),
-                                         (777, 8192, 4, True), (3000, 16384, 8, False), (20000, 1024, 3, True)])
+                                         (777, 8192, 4, True), (3000, 16384, 8, False), (20000, 1024, 3, True),
+                                         (30000, 2048, 40, True), (6000, 512, 63, False)])
 def test_round_equals_separate_calls(V, H, K, alias):
     """Every round: the fused round equals the three separate entry points bit for bit, its
     argmax equals the oracle's (near-tie rule), the ids it commits equal oracle.accept on the

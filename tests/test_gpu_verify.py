@@ -20,6 +20,9 @@ pytestmark = pytest.mark.gpu
     # one rolling register set, each with a ragged last tile: the argmax head at H = 2560, and
     # the 17-row head at H = 5120 (8 of each wave's 20 blocks of window rows held in LDS)
     (4099, 2560, 9), (2500, 5120, 17),
+    # more than 32 rows in two passes of the two-tile kernel (rows 0 .. 31, then the rest), each
+    # writing whole dot products, at the hidden sizes a two-tile shape covers unsplit
+    (5000, 512, 40), (3001, 1024, 64), (2000, 1280, 33), (4099, 2048, 48),
 ])
 def test_verify_matches_oracle(V, H, S):
     say(f"verify V={V} H={H} S={S}")
@@ -194,10 +197,11 @@ def test_verify_17_rows_both_kernels_agree(H):
     check_argmax(a2, L)
 
 
-@pytest.mark.parametrize("V,H,S", [(20000, 2048, 9), (900, 16384, 40)])
+@pytest.mark.parametrize("V,H,S", [(20000, 2048, 9), (900, 16384, 40), (20000, 2048, 40)])
 def test_timing_hook_brackets_exactly_one_matmul(V, H, S):
     """specverify_profile_next_matmul attaches the caller's events to the next matmul's dispatch
-    (through the combine pass when the hidden axis is split, the second shape): both events
+    (through the combine pass when the hidden axis is split, the second shape; across both
+    passes of a window of more than 32 rows, the third): both events
     complete with a positive duration, the results are those of an untimed call, and the hook
     is consumed, so the next call runs untimed."""
     q, s = head(23, V, H)

@@ -75,6 +75,24 @@ hipError_t launch_matmul(int epi, const sv::GemmCfg& cfg, const sv::GemmArgs& a,
     return sv::launch_q8b32(epi, cfg, a, stream, combine, before, after);
 }
 
+// The argmax head's matmul under its launch plan: one launch, or two passes over rows 0 .. 31
+// and 32 .. S-1 (the hook's events then bracket both).
+hipError_t launch_head_matmul(const sv::GemmCfg& cfg, int passes, const sv::GemmArgs& a, hipStream_t stream) {
+    if (passes == 1) return launch_matmul(sv::EPI_HEAD, cfg, a, stream);
+    hipEvent_t before = g_prof_before, after = g_prof_after;
+    g_prof_before = g_prof_after = nullptr;
+    sv::GemmArgs lo = a, hi = a;
+    lo.S = 32;
+    hi.S = a.S - 32;
+    hi.x = a.x + (size_t)32 * a.H;
+    hi.part_val = a.part_val + (size_t)32 * sv::kGridMax;
+    hi.part_idx = a.part_idx + (size_t)32 * sv::kGridMax;
+    if (a.logits) hi.logits = a.logits + (size_t)32 * a.V;
+    hipError_t e = sv::launch_q8b32(sv::EPI_HEAD, cfg, lo, stream, true, before, nullptr);
+    if (e != hipSuccess) return e;
+    return sv::launch_q8b32(sv::EPI_HEAD, cfg, hi, stream, true, nullptr, after);
+}
+
 // A chunked matmul (head or stack projection), timed by the pending hook's events if one is set.
 hipError_t launch_chunked_matmul(int epi, const sv::ChunkCfg& cfg, const sv::ChunkArgs& a, hipStream_t stream) {
     hipEvent_t before = g_prof_before, after = g_prof_after;
@@ -163,7 +181,8 @@ int launch_head(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, 
                                   state, ngram_max, round ? drafts_out : nullptr, stream);
         return e == hipSuccess ? SV_OK : hip_fail(e, "argmax/round tail launch");
     }
-    const sv::GemmCfg cfg = sv::gemm_config(V, H, S, sv::EPI_HEAD);
+    int passes = 1;
+    const sv::GemmCfg cfg = sv::head_config(V, H, S, passes);
     sv::GemmArgs a{};
     a.w0 = wq;
     a.s0 = wscale;
@@ -178,7 +197,7 @@ int launch_head(const int8_t* wq, const uint16_t* wscale, int32_t V, int32_t H, 
     a.part_idx = part_idx;
     a.logits = logits;
     if (cfg.ksplit > 1) a.kpart0 = reinterpret_cast<float*>(ws + sv::head_partials_bytes(S));
-    hipError_t e = launch_matmul(sv::EPI_HEAD, cfg, a, stream);
+    hipError_t e = launch_head_matmul(cfg, passes, a, stream);
     if (e != hipSuccess) return hip_fail(e, "verify matmul launch");
     const int nparts = cfg.ksplit > 1 ? sv::combine_groups(V) : cfg.grid;
     e = sv::launch_round_tail(a.part_val, a.part_idx, nparts, S, argmax, round ? drafts_in : nullptr, tokens, cap,

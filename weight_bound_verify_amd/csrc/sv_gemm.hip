@@ -1035,8 +1035,27 @@ int combine_groups(int V) {
     return g < 256 ? g : 256;
 }
 
+// More than 32 window rows: the four-tile shapes cover the hidden axis only by splitting it
+// across workgroups (their window rows and cross-wave sums outgrow the registers and LDS of
+// one workgroup), and a split head writes and re-reads 4 x ks x S x V bytes of fp32 partial
+// sums.  Two passes of an unsplit two-tile shape read the weights twice instead and keep every
+// dot product whole (measured at 248320 x 2048: 187 us for both passes against 236-283 us
+// split at S = 33 .. 64).
+GemmCfg head_config(int V, int H, int S, int& passes) {
+    passes = 1;
+    if (S > 32) {
+        const GemmCfg c = gemm_config(V, H, 32, EPI_HEAD);
+        if (c.fast && c.ksplit == 1) {
+            passes = 2;
+            return c;
+        }
+    }
+    return gemm_config(V, H, S, EPI_HEAD);
+}
+
 size_t head_workspace_bytes(int V, int H, int S) {
-    const GemmCfg c = gemm_config(V, H, S, EPI_HEAD);
+    int passes = 1;
+    const GemmCfg c = head_config(V, H, S, passes);
     size_t b = head_partials_bytes(S);
     if (c.ksplit > 1) b += (size_t)4 * c.ksplit * S * V;
     return b;

@@ -41,6 +41,10 @@ struct GemmCfg {
 
 // epi = the epilogue kind (Epi); the stack epilogues take S <= 16.
 GemmCfg gemm_config(int rows, int H, int S, int epi);
+// Launch plan of the argmax head: passes = 2 runs a window of more than 32 rows as two passes
+// of the returned two-tile configuration (rows 0 .. 31, then 32 .. S-1), each writing complete
+// argmax partials for its own rows; passes = 1 is one launch of the returned configuration.
+GemmCfg head_config(int V, int H, int S, int& passes);
 // Workgroups of the split-combine pass (also the number of argmax partials it writes).
 int combine_groups(int V);
 void set_tuning(int waves_per_group, int max_groups, int no_extra_row);
