@@ -1,6 +1,7 @@
 """A window row whose logits are all NaN (e.g. an fp16 activation that overflowed upstream)
-has no argmax: verify reports -1 for it, and every accept step refuses to commit -1 (sticky
-argmax flag, no token, no round recorded).  Rows past the first rejected draft do not matter."""
+has no argmax: verify reports -1 for it (the int8 and int4 heads), and every accept step refuses
+to commit -1 (sticky argmax flag, no token, no round recorded), the fused sampling round
+included.  Rows past the first rejected draft do not matter."""
 import numpy as np
 import pytest
 import torch
@@ -99,3 +100,41 @@ def test_standalone_accepts_refuse_a_missing_id():
         stv = st.cpu().numpy()
         assert stv[sv.STATE_FLAGS] == sv.FLAG_ARGMAX and stv[sv.STATE_LEN] == 10 and stv[sv.STATE_ROUNDS] == 0
         assert np.array_equal(t.cpu().numpy(), buf)
+
+
+def test_verify_q4_nan_row_has_no_argmax():
+    """The int4 head: the NaN row reports -1, the other rows match the oracle."""
+    V, H = 3001, 1024
+    rng = np.random.default_rng(11)
+    p, s = synth.quantized_head_q4(np.random.SeedSequence(11), V, H)
+    hidden = synth.fp16_normal(rng, (6, H))
+    hidden[2] = NAN16
+    am = torch.full((6,), 7, dtype=torch.int32, device=dev())
+    sv.verify_q4(to_dev(p), to_dev(s), to_dev(hidden), am, sv.workspace(sv.verify_workspace_bytes(V, H, 6), dev()))
+    torch.cuda.synchronize()
+    a = am.cpu().numpy()
+    assert a[2] == -1
+    ok = [0, 1, 3, 4, 5]
+    check_argmax(a[ok], oracle.head_logits_q4b32(p, s, hidden[ok]))
+
+
+def test_round_sample_nan_first_row_commits_nothing():
+    """Sampling verify with window row 0 all NaN: its keep test cannot pass and its draw is
+    missing, so the fused round commits nothing, records no round and sets the flag."""
+    V, H, K = 4000, 512, 4
+    S = K + 1
+    rng = np.random.default_rng(12)
+    q, s = synth.quantized_head(np.random.SeedSequence(12), V, H)
+    hidden = synth.fp16_normal(rng, (S, H))
+    hidden[0] = NAN16
+    buf = np.zeros(400, np.int32)
+    buf[:300] = rng.integers(0, V, size=300)
+    tokens, st = to_dev(buf), _state(300)
+    d_in = to_dev(rng.integers(0, V, size=K).astype(np.int32))
+    d_out = torch.empty(K, dtype=torch.int32, device=dev())
+    work = sv.workspace(sv.sample_workspace_bytes(V, H, S), dev())
+    sv.round_sample(to_dev(q), to_dev(s), to_dev(hidden), d_in, 0.7, 2026, tokens, st, d_out, work)
+    torch.cuda.synchronize()
+    stv = st.cpu().numpy()
+    assert stv[sv.STATE_FLAGS] == sv.FLAG_ARGMAX and stv[sv.STATE_LEN] == 300 and stv[sv.STATE_ROUNDS] == 0
+    assert np.array_equal(tokens.cpu().numpy(), buf)
