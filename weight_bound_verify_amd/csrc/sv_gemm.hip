@@ -1,5 +1,6 @@
 // q8b32 skinny matmul for gfx950: int8 rows with per-block-32 fp16 scales against S <= 64
-// fp16 activation rows, fp32 accumulation, one pass over the weights.
+// fp16 activation rows, fp32 accumulation, one pass over the weights (two for an argmax head
+// of more than 32 window rows, where head_config runs the two-tile kernel twice).
 //
 // Contraction (pages: "Riding Apple's pipelined GPU engine", quantization on the GPU
 // delegate -- linear per-block-32 int8; "Stream C - Speculative decoding", C1 substrate map
