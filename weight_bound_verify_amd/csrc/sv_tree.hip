@@ -28,6 +28,7 @@ namespace {
 
 constexpr int kTreeThreads = 1024;
 constexpr int kTreeIds = 32768;                      // stream ids held in LDS (128 KB)
+constexpr int kTreeHead = 8192;                      // stream ids loaded before the length is known
 
 // Walk down the tree by one wave (lane i holds node i+1).  `am` holds the argmax of every
 // window row.  Appends the path's tokens and the final argmax to `tokens` (and `mirror` when
@@ -254,12 +255,15 @@ __global__ __launch_bounds__(kTreeThreads) void tree_tail_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int K = S - 1;
-    // every independent load first: the stream's first min(cap, kTreeIds) ids (whatever its
-    // length), the state and the partials; the stream goes to LDS once the partials are reduced
-    IdPrefix<kTreeIds / (4 * kTreeThreads)> pre;
+    // every independent load first: the stream's first min(cap, kTreeHead) ids (whatever its
+    // length), the state and the partials; the rest of the stream is loaded once its length is
+    // known, only up to it, and the stream goes to LDS once the partials are reduced
+    IdPrefix<kTreeHead / (4 * kTreeThreads)> pre;
+    IdPrefix<(kTreeIds - kTreeHead) / (4 * kTreeThreads)> pre2;
     const int navail = cap < kTreeIds ? cap : kTreeIds;
+    const int nhead = navail < kTreeHead ? navail : kTreeHead;
     const bool vec = (reinterpret_cast<uintptr_t>(tokens) & 15) == 0;
-    if (vec) prefix_load(tokens, navail, pre);
+    if (vec) prefix_load(tokens, nhead, pre);
     const int len0 = state[SV_STATE_LEN];
     StateCache sc{0, 0};
     if (wave == 0) sc = state_cache_load(state, lane);
@@ -268,9 +272,18 @@ __global__ __launch_bounds__(kTreeThreads) void tree_tail_kernel(
         const int bi = argmax_id(reduce_argmax_row(pv, pi, nparts, s, lane));
         if (lane == 0) { argmax[s] = bi; am[s] = bi; }
     }
+    // the stream beyond its first kTreeHead ids, up to its length
+    const int nrest = in_lds && len0 > kTreeHead ? len0 : kTreeHead;
+    if (vec) prefix_load_from(tokens, kTreeHead, nrest, pre2);
     if (in_lds) {
-        if (vec) prefix_store(tokens, navail, pre, tk);
-        else stage_ids(tokens, len0, tk);
+        if (vec) {
+            prefix_store(tokens, nhead < len0 ? nhead : len0, pre, tk);
+            prefix_store_from(tokens, kTreeHead, nrest, pre2, tk);
+            for (int i = ((len0 >> 2) << 2) + threadIdx.x; i < len0; i += kTreeThreads)    // the ragged end
+                if (i >= kTreeHead) tk[i] = tokens[i];
+        } else {
+            stage_ids(tokens, len0, tk);
+        }
     }
     barrier_lds();                                     // the stream (when it fits) and the argmax are in LDS
     if (wave == 0) {
