@@ -44,6 +44,35 @@ def test_propose_tree_matches_oracle(n, vocab, nmax, K, B, D):
         assert st[sv.STATE_NVALID] == real and st[sv.STATE_NUSED] == used
 
 
+@pytest.mark.parametrize("filler", [(1 << 27) - 3001, (1 << 27) + 5])
+def test_propose_tree_long_stream_equals_its_live_part(filler):
+    """A stream of 2^27 ids or more (the drafter's 64-bit key merge; shorter streams pack the
+    (length, end) keys into 32 bits) and one just below: `filler` copies of an id the rest never
+    uses, then a 3000-id Zipf context.  No n-gram that reaches into the filler matches the
+    suffix, and match lengths and their order do not depend on where the context starts, so the
+    tree equals the oracle's tree over the context alone."""
+    V, nmax, K, B, D = 64, 3, 15, 4, 6
+    ctx = synth.zipf_context_with_copies(np.random.default_rng(filler & 0xffff), 3000, V, 0.3)[0].astype(np.int32)
+    say(f"propose_tree over {filler} filler ids + 3000")
+    n = filler + ctx.size
+    toks = np.full(n + 8, V + 1, dtype=np.int32)
+    toks[filler:n] = ctx
+    tokens = to_dev(toks)
+    del toks
+    state = _state(n)
+    parents = torch.full((K,), -9, dtype=torch.int32, device=dev())
+    drafts = torch.full((K,), -9, dtype=torch.int32, device=dev())
+    sv.propose_tree(tokens, state, parents, drafts, nmax, B, D)
+    torch.cuda.synchronize()
+    p_ref, d_ref, used, real = tr.propose_tree(list(ctx), nmax, K, B, D)
+    assert real > 0
+    assert parents.cpu().tolist() == p_ref and drafts.cpu().tolist() == d_ref
+    st = state.cpu().numpy()
+    assert st[sv.STATE_NVALID] == real and st[sv.STATE_NUSED] == used
+    del tokens
+    torch.cuda.empty_cache()
+
+
 def test_propose_tree_one_branch_is_the_linear_drafter():
     rng = np.random.default_rng(3)
     for case in range(20):
