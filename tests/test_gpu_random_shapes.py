@@ -7,15 +7,18 @@ size that is a multiple of 32 up to 8192 for the int8 head (fast and generic ker
 several hidden-axis splits), the int4 head's supported widths, and vocabularies whose last
 16-row tile is ragged.  Each case meets the fixed-shape tests' bar: logits within 1e-3 of the
 oracle's (relative, with the row RMS as floor), argmax equal except below a 1e-3 top-2 gap.  A
-fused-round sweep draws (V, H, K, n-gram order, context length) and checks the committed ids
-and next drafts of three rounds exactly against oracle.accept and oracle.propose_scan; a
-tree-round sweep does the same for tree verify (K nodes, B branches, depth D) against
-oracle.tree, and a dense-stack sweep checks random block shapes block by block."""
+sampling-verify sweep draws (V, H, S, T) and checks draws and log-sum-exp as the fixed-shape
+sampling tests do.  A fused-round sweep draws (V, H, K, n-gram order, context length) and
+checks the committed ids and next drafts of three rounds exactly against oracle.accept and
+oracle.propose_scan; a tree-round sweep does the same for tree verify (K nodes, B branches,
+depth D) against oracle.tree, and a dense-stack sweep checks random block shapes block by
+block."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
+from oracle import sampling as smp
 from oracle import tree as tr
 from weight_bound_verify_amd import specverify as sv
 from weight_bound_verify_amd import synth
@@ -72,6 +75,36 @@ def test_verify_q4_random_shape(V, H, S):
     L = oracle.head_logits_q4b32(p, s, hidden)
     check_logits(lg.cpu().numpy().astype(np.float64), L)
     check_argmax(am.cpu().numpy(), L)
+
+
+def _sample_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        H = int(32 * rng.integers(1, 257))
+        V = int(rng.integers(2, min(20000, ELEMS // H) + 1))
+        out.append((V, H, int(rng.integers(1, 17)), round(float(rng.uniform(0.3, 1.5)), 3)))
+    return out
+
+
+@pytest.mark.parametrize("V,H,S,T", _sample_cases(20261208, 12))
+def test_verify_sample_random_shape(V, H, S, T):
+    """Sampling verify (its own epilogue and launch shapes) at random shapes, on the rule of the
+    fixed-shape sampling tests: logits, log-sum-exp and draft logits within tolerance, every
+    draw the oracle's unless its two best residual keys are within the keys' tolerance."""
+    from test_gpu_sample import _key_tol, _setup, check_draws, gpu_verify_sample
+    say(f"verify_sample random V={V} H={H} S={S} T={T}")
+    seed, P0 = (V * 104729 + H + S) | (1 << 41), 77 + H
+    q, s, hidden, L, drafts = _setup(V, H, S, V + H, P0)
+    sample, lse, zd, lg = gpu_verify_sample(q, s, hidden, drafts, T, seed, P0)
+    check_logits(lg, L)
+    _, lse_o = smp.probabilities(L, T)
+    ltol = _key_tol(L, T)
+    assert np.all(np.abs(lse - lse_o) <= ltol), (lse, lse_o)
+    for r, d in enumerate(drafts):
+        if 0 <= d < V:
+            assert abs(zd[r] - L[r, d] / T) <= ltol[r]
+    check_draws(sample, L, drafts, T, seed, P0)
 
 
 def _round_cases(seed, n):
