@@ -101,6 +101,31 @@ def test_verify_launch_shapes_agree(nw, grid):
     check_argmax(a, L)
 
 
+@pytest.mark.parametrize("V,S,groups", [(70001, 9, 0), (70031, 17, 0), (70031, 1, 64), (70001, 16, 333),
+                                        (65573, 9, 104), (65573, 9, 100)])
+def test_verify_per_die_item_ranges(V, S, groups):
+    """Heads over 2 KB rows with at least 8 items per workgroup take their items in one
+    contiguous range per die: item counts that 8 divides and that it does not (4376, 4377, 4099),
+    a last tile of one row, the 17-row window, and grids capped at 64, 104 and 333 workgroups
+    (8, 13 and 40 per die).  A cap of 100 leaves a grid of 100, which cannot be rounded up to a
+    multiple of 8 within the cap, so that launch keeps the interleaved order.  Every logit
+    (pre-filled with NaN) and every argmax row against the oracle."""
+    H = 2048
+    say(f"per-die item ranges V={V} S={S} groups={groups}")
+    q, s = head(V + S, V, H)
+    hidden = synth.fp16_normal(np.random.default_rng(V + S + groups), (S, H))
+    try:
+        sv.set_tuning(0, groups)
+        a, lg = gpu_verify(q, s, hidden)
+        a2, _ = gpu_verify(q, s, hidden, want_logits=False)
+    finally:
+        sv.set_tuning(0, 0)
+    L = oracle.head_logits(q, s, hidden)
+    check_logits(lg, L)
+    check_argmax(a, L)
+    assert np.array_equal(a, a2)
+
+
 def test_verify_split_hidden_axis_path():
     # S = 40 (three M tiles of 16) with H = 16384: the hidden axis is split across workgroups
     V, H, S = 900, 16384, 40

@@ -48,6 +48,25 @@ thread_local int g_nw_override = 0;       // tuning overrides of the calling thr
 thread_local int g_grid_override = 0;     // 0 = choose
 thread_local int g_no_xr = 0;            // 1: a 17-row window uses the two-tile kernels (tuning experiments)
 
+constexpr int kXcds = 8;         // accelerator dies; workgroup b of a launch runs on die b % kXcds
+
+// The items a workgroup of a persistent grid takes: first, first + step, ... below lim.  By
+// default workgroup b takes b, b + grid, ...  With `xcd` the items split into kXcds contiguous
+// ranges, one per die, and the workgroups of a die stride through its range (taken only when
+// every workgroup then has an item: at least kXcds workgroups and kXcds items per workgroup).
+struct ItemRange {
+    int first, step, lim;
+};
+__device__ __forceinline__ ItemRange item_range(int nitems, bool xcd) {
+    const int b = blockIdx.x, grid = gridDim.x;
+    if (xcd && grid >= kXcds && nitems >= kXcds * grid) {
+        const int x = b % kXcds;
+        return {(int)((long long)nitems * x / kXcds) + b / kXcds, (grid - x + kXcds - 1) / kXcds,
+                (int)((long long)nitems * (x + 1) / kXcds)};
+    }
+    return {b, grid, nitems};
+}
+
 // Workgroup barrier that orders LDS only, so prefetched global loads stay in flight.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -111,8 +130,8 @@ struct Reducer {
     }
 
     // Per-round inputs of the sampling epilogue (every wave: the start position; wave 0: the
-    // drafts it leaves out), then the first item's noise.
-    __device__ __forceinline__ void setup(const GemmArgs& a, int wave, int lane) {
+    // drafts it leaves out), then the noise of the workgroup's first item.
+    __device__ __forceinline__ void setup(const GemmArgs& a, int wave, int lane, int first) {
         if constexpr (EPI == EPI_SAMPLE) {
             const int g = lane >> 4;
             p0 = (uint32_t)a.state[SV_STATE_LEN];
@@ -123,7 +142,7 @@ struct Reducer {
                     excl[r] = s < a.S - 1 ? a.drafts[s] : -1;
                 }
             }
-            if (wave == (NW > 1 ? 1 : 0)) make_noise(a, blockIdx.x, 0, lane);
+            if (wave == (NW > 1 ? 1 : 0)) make_noise(a, first, 0, lane);
         }
     }
 
@@ -357,7 +376,10 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
     Reducer<MT, NW, EPI> red_{red};
     red_.init();
     red_.noise = noise;
-    red_.setup(a, wave, lane);
+    // per-die item ranges for the argmax head only (the other epilogues keep b, b + grid, ...)
+    ItemRange ir{(int)blockIdx.x, (int)gridDim.x, a.nitems};
+    if constexpr (EPI == EPI_HEAD) ir = item_range(a.nitems, a.xcd != 0);
+    red_.setup(a, wave, lane, ir.first);
 
     // loads: row half h feeds tile rows 8h .. 8h+7; lane l reads the tile row 8h + l/8, bytes
     // 16*(l%8) .. +15 of each 128-byte segment of the wave's range
@@ -400,7 +422,7 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
 
     // nxt: the item whose loads replace cur's registers as they free up (ROLL only)
     auto process = [&](FastRegs<NBW>& cur, int it, int buf, int nxt) {
-        red_.ahead(a, it + gridDim.x, wave, lane);
+        red_.ahead(a, it + ir.step, wave, lane);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         f32x4 acc[MT];
 #pragma unroll
@@ -491,22 +513,22 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
         }
     };
 
-    const int step = gridDim.x;
-    const int last = a.nitems - 1;
-    int it = blockIdx.x;
+    const int step = ir.step, lim = ir.lim;
+    const int last = lim - 1;
+    int it = ir.first;
     if constexpr (ROLL) {
         FastRegs<NBW> r;
         load(r, min(it, last));
-        for (int k = 0; it < a.nitems; ++k, it += step) process(r, it, k & 1, min(it + step, last));
+        for (int k = 0; it < lim; ++k, it += step) process(r, it, k & 1, min(it + step, last));
     } else {
         FastRegs<NBW> ra, rb;
         load(ra, it);
         while (true) {
-            if (it >= a.nitems) break;
+            if (it >= lim) break;
             load(rb, min(it + step, last));
             process(ra, it, 0, 0);
             it += step;
-            if (it >= a.nitems) break;
+            if (it >= lim) break;
             load(ra, min(it + step, last));
             process(rb, it, 1, 0);
             it += step;
@@ -571,7 +593,7 @@ __global__ __launch_bounds__(NW * 64) void q8b32_generic(GemmArgs a) {
     Reducer<MT, NW, EPI> red_{red};
     red_.init();
     red_.noise = noise;
-    red_.setup(a, wave, lane);
+    red_.setup(a, wave, lane, blockIdx.x);                // items blockIdx.x, + grid, ...
 
     const int8_t* w = tile_up<EPI>(n) ? a.w1 : a.w0;
     const uint16_t* sc = tile_up<EPI>(n) ? a.s1 : a.s0;
@@ -1028,6 +1050,23 @@ GemmCfg gemm_config(int rows, int H, int S, int epi) {
     // divide), so no single workgroup runs an extra item after the others have finished.
     const int per = (items + cap - 1) / cap;
     c.grid = items > 0 ? (items + per - 1) / per : 1;
+    // One contiguous range of items per die for the one-tile fast argmax head over rows of at
+    // most 2 KB, the grid rounded up to a multiple of kXcds within the resident cap.  Measured,
+    // head alone, alternating builds on one device each: 248320 x 2048 at S = 9 82.2-83.0
+    // against 85.3-86.3 us (80.2-80.6 against 80.9-81.8 us on another device) and at S = 17
+    // 81.7-83.1 against 84.3-85.0 us; the fused round at that shape 86.1-86.5 against
+    // 87.2-87.4 us.  At H = 2560 and 5120 it measured 0.5% slower and at 4096 even, and the
+    // sampling head (4 x 16 shape, one workgroup per compute unit) and the int4 head gained
+    // nothing, so those keep the interleaved order (the kernels read xcd for EPI_HEAD only: the
+    // sampling kernel built with the runtime choice ran 3% slower even in the interleaved order).
+    c.xcd = 0;
+    if (c.fast && c.mt == 1 && c.ksplit == 1 && epi == EPI_HEAD && H <= 2048) {
+        const int g8 = (c.grid + kXcds - 1) / kXcds * kXcds;
+        if (c.grid >= kXcds && g8 <= cap && items >= kXcds * g8) {
+            c.grid = g8;
+            c.xcd = 1;
+        }
+    }
     return c;
 }
 
@@ -1080,7 +1119,9 @@ hipError_t launch_q8b32(int epi, const GemmCfg& cfg, const GemmArgs& a, hipStrea
     KernelFn fn = kernel_for(epi, cfg);
     if (!fn) return hipErrorInvalidConfiguration;
     const bool split = cfg.ksplit > 1 && combine;
-    launch_timed(fn, dim3(cfg.grid, cfg.ksplit), dim3(cfg.nw * 64), stream, start, split ? nullptr : stop, a);
+    GemmArgs ka = a;
+    ka.xcd = cfg.xcd;
+    launch_timed(fn, dim3(cfg.grid, cfg.ksplit), dim3(cfg.nw * 64), stream, start, split ? nullptr : stop, ka);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !split) return e;
     const int cg = combine_groups(a.V);

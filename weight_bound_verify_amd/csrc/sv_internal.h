@@ -37,6 +37,8 @@ struct GemmCfg {
     int fast;     // 1: 128-byte-segment loads with an LDS exchange; 0: generic loads
     int xr;       // head, mt = 1: window rows beyond the 16-row tile handled by dot products
                   // from LDS (1 for a 17-row window), 0 otherwise
+    int xcd;      // 1: items in one contiguous range per die (item_range in sv_gemm.hip), grid a
+                  // multiple of 8
 };
 
 // epi = the epilogue kind (Epi); the stack epilogues take S <= 16.
@@ -73,6 +75,8 @@ struct GemmArgs {
     const int32_t* drafts;     // [S-1] or null (S = 1)
     float inv_temp;
     uint32_t key0, key1;       // Philox key = the 64-bit seed
+    int xcd;                   // item order of the argmax head (GemmCfg::xcd), set by the launcher;
+                               // it fills the padding before the next pointer
     float* part_m;             // [S][kGridMax]
     float* part_l;
     float* zd;                 // [S]
