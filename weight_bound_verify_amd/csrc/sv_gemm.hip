@@ -376,9 +376,10 @@ __global__ __launch_bounds__(NW * 64) void q8b32_fast(GemmArgs a) {
     Reducer<MT, NW, EPI> red_{red};
     red_.init();
     red_.noise = noise;
-    // per-die item ranges for the argmax head only (the other epilogues keep b, b + grid, ...)
+    // per-die item ranges for the argmax head only, and not for its shapes that hold window rows
+    // in LDS (H = 5120, never given xcd); the others keep b, b + grid, ...
     ItemRange ir{(int)blockIdx.x, (int)gridDim.x, a.nitems};
-    if constexpr (EPI == EPI_HEAD) ir = item_range(a.nitems, a.xcd != 0);
+    if constexpr (EPI == EPI_HEAD && HL == 0) ir = item_range(a.nitems, a.xcd != 0);
     red_.setup(a, wave, lane, ir.first);
 
     // loads: row half h feeds tile rows 8h .. 8h+7; lane l reads the tile row 8h + l/8, bytes
