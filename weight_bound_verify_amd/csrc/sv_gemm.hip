@@ -54,6 +54,8 @@ constexpr int kXcds = 8;         // accelerator dies; workgroup b of a launch ru
 // default workgroup b takes b, b + grid, ...  With `xcd` the items split into kXcds contiguous
 // ranges, one per die, and the workgroups of a die stride through its range (taken only when
 // every workgroup then has an item: at least kXcds workgroups and kXcds items per workgroup).
+// Either order covers every item exactly once, so results never depend on where the hardware
+// actually places the workgroups; only the speed does.
 struct ItemRange {
     int first, step, lim;
 };
