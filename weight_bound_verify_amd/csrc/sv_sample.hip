@@ -83,9 +83,17 @@ __global__ __launch_bounds__(kTailThreads) void sample_tail_kernel(
     const bool vec = round && (reinterpret_cast<uintptr_t>(tokens) & 15) == 0;
     if (vec) prefix_load(tokens, navail, pre);
     StateCache sc{0, 0};
+    int d0 = -1;                                       // wave 0: the round's drafts and their scaled logits
+    float zd0 = 0.f;
     if (round) {
         len0 = state[SV_STATE_LEN];
-        if (wave == 0) sc = state_cache_load(state, lane);
+        if (wave == 0) {
+            sc = state_cache_load(state, lane);
+            if (lane < K) {
+                d0 = drafts_in[lane];
+                zd0 = zd[lane];
+            }
+        }
         in_lds = len0 >= 0 && len0 + K + 1 <= cap && len0 + K + 1 <= kTailIds;
     }
     for (int s = wave; s < S; s += kTailThreads / kWave) {
@@ -106,16 +114,14 @@ __global__ __launch_bounds__(kTailThreads) void sample_tail_kernel(
     }
     if (!in_lds) {                                     // long or corrupt stream: the global-memory path
         __syncthreads();
-        if (wave == 0) accept_sample_wave(draw_s, lse_s, zd, drafts_in, K, V, key0, key1, tokens, cap, state, lane,
-                                          nullptr);
+        if (wave == 0) accept_sample_regs(draw_s, lse_s, d0, zd0, K, V, key0, key1, tokens, cap, state, lane, nullptr);
         __syncthreads();
         propose_block(tokens, cap, state, nmax, K, drafts_out, tk, kTailIds - kHalo, wbest);
         return;
     }
     barrier_lds();                                     // the stream and the draws are in LDS
     if (wave == 0) {
-        const int j = accept_sample_wave(draw_s, lse_s, zd, drafts_in, K, V, key0, key1, tokens, cap, state, lane, tk,
-                                         &sc);
+        const int j = accept_sample_regs(draw_s, lse_s, d0, zd0, K, V, key0, key1, tokens, cap, state, lane, tk, &sc);
         // the gate word after this round: recomputed from the cache as the accept recorded it
         const int zero_run = j == 0 ? state_word(sc, SV_STATE_ZERO_RUN) + 1 : 0;
         const int gate_after = state_word(sc, SV_STATE_GATE_AFTER);

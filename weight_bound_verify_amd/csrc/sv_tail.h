@@ -308,24 +308,22 @@ __device__ __forceinline__ void accept_wave(const int32_t* argmax, const int32_t
 // draw (its residual draw, or the bonus draw when j = K) are appended, so len advances by
 // 1 + j.  `mirror` (may be null) receives the same ids at the same positions.  A call that
 // could overflow `cap` writes no token and sets the sticky capacity flag.  Returns j, or -1.
-__device__ __forceinline__ int accept_sample_wave(const int32_t* sample, const float* lse, const float* zd,
-                                                  const int32_t* drafts, int K, int V, uint32_t key0,
-                                                  uint32_t key1, int32_t* tokens, int cap, int32_t* state,
-                                                  int lane, int32_t* mirror, const StateCache* cache = nullptr) {
+// The lane's draft `d` and its scaled logit `zdl` come in registers (lanes >= K: ignored).
+__device__ __forceinline__ int accept_sample_regs(const int32_t* sample, const float* lse, int d, float zdl, int K,
+                                                  int V, uint32_t key0, uint32_t key1, int32_t* tokens, int cap,
+                                                  int32_t* state, int lane, int32_t* mirror,
+                                                  const StateCache* cache = nullptr) {
     const int len = cache ? state_word(*cache, SV_STATE_LEN) : state[SV_STATE_LEN];
     if (len + K + 1 > cap || len < 0) {
         if (lane == 0) state[SV_STATE_FLAGS] |= SV_FLAG_CAPACITY;
         return -1;
     }
-    int d = -1;
+    if (lane >= K) d = -1;
     bool keep = false;
-    if (lane < K) {
-        d = drafts[lane];
-        if (d >= 0 && d < V) {
-            const Philox4 rnd = philox4x32_10(0u, (uint32_t)len, (uint32_t)(lane >> 2), 1u, key0, key1);
-            const float u = uniform01(philox_word(rnd, lane & 3));
-            keep = u < __expf(zd[lane] - lse[lane]);
-        }
+    if (lane < K && d >= 0 && d < V) {
+        const Philox4 rnd = philox4x32_10(0u, (uint32_t)len, (uint32_t)(lane >> 2), 1u, key0, key1);
+        const float u = uniform01(philox_word(rnd, lane & 3));
+        keep = u < __expf(zdl - lse[lane]);
     }
     const unsigned long long kept = __ballot(keep);
     const int j = __builtin_ctzll(~kept);                // <= K: bit K is never set
@@ -349,6 +347,20 @@ __device__ __forceinline__ int accept_sample_wave(const int32_t* sample, const f
         if (K > 0) record_round(state, j);        // K = 0 is the anchor bootstrap, not a round
     }
     return j;
+}
+
+// The same accept with the drafts and their scaled logits read from `drafts` / `zd`.
+__device__ __forceinline__ int accept_sample_wave(const int32_t* sample, const float* lse, const float* zd,
+                                                  const int32_t* drafts, int K, int V, uint32_t key0,
+                                                  uint32_t key1, int32_t* tokens, int cap, int32_t* state,
+                                                  int lane, int32_t* mirror) {
+    int d = -1;
+    float zdl = 0.f;
+    if (lane < K) {
+        d = drafts[lane];
+        zdl = zd[lane];
+    }
+    return accept_sample_regs(sample, lse, d, zdl, K, V, key0, key1, tokens, cap, state, lane, mirror);
 }
 
 // n-gram prompt lookup by a whole workgroup ("Stream C - Speculative decoding", the delta:

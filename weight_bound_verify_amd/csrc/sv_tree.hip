@@ -30,20 +30,19 @@ constexpr int kTreeThreads = 1024;
 constexpr int kTreeIds = 32768;                      // stream ids held in LDS (128 KB)
 constexpr int kTreeHead = 8192;                      // stream ids loaded before the length is known
 
-// Walk down the tree by one wave (lane i holds node i+1).  `am` holds the argmax of every
-// window row.  Appends the path's tokens and the final argmax to `tokens` (and `mirror` when
-// not null), advances len, records the round.  Returns j, or -1 when `cap` would overflow
-// (nothing written, capacity flag set).
-__device__ __forceinline__ int accept_tree_wave(const int32_t* am, const int32_t* parents, const int32_t* drafts,
-                                                int K, int32_t* tokens, int cap, int32_t* state, int lane,
-                                                int32_t* mirror, const StateCache* cache = nullptr) {
+// Walk down the tree by one wave, the tree in registers: lane i < K holds node i+1 (its parent
+// `par`, its token `tok`; -1 on the other lanes).  `am` holds the argmax of every window row.
+// Appends the path's tokens and the final argmax to `tokens` (and `mirror` when not null),
+// advances len, records the round.  Returns j, or -1 when `cap` would overflow (nothing
+// written, capacity flag set).
+__device__ __forceinline__ int accept_tree_regs(const int32_t* am, int par, int tok, int K, int32_t* tokens, int cap,
+                                                int32_t* state, int lane, int32_t* mirror,
+                                                const StateCache* cache = nullptr) {
     const int len = cache ? state_word(*cache, SV_STATE_LEN) : state[SV_STATE_LEN];
     if (len + K + 1 > cap || len < 0) {
         if (lane == 0) state[SV_STATE_FLAGS] |= SV_FLAG_CAPACITY;
         return -1;
     }
-    int par = -1, tok = -1;
-    if (lane < K) { par = parents[lane]; tok = drafts[lane]; }
     int c = 0, j = 0, pos = -1;
     for (int step = 0; step < K; ++step) {             // a path has at most K nodes
         const int a = am[c];
@@ -72,6 +71,15 @@ __device__ __forceinline__ int accept_tree_wave(const int32_t* am, const int32_t
     }
     if (cache) record_round_cached(*cache, state, j, lane);
     return j;
+}
+
+// The same walk with the tree read from `parents` / `drafts` (K entries each).
+__device__ __forceinline__ int accept_tree_wave(const int32_t* am, const int32_t* parents, const int32_t* drafts,
+                                                int K, int32_t* tokens, int cap, int32_t* state, int lane,
+                                                int32_t* mirror) {
+    int par = -1, tok = -1;
+    if (lane < K) { par = parents[lane]; tok = drafts[lane]; }
+    return accept_tree_regs(am, par, tok, K, tokens, cap, state, lane, mirror);
 }
 
 // The same over a stream in global memory, one end position per thread and step.
@@ -306,7 +314,11 @@ __global__ __launch_bounds__(kTreeThreads) void tree_tail_kernel(
     if (vec) prefix_load(tokens, nhead, pre);
     const int len0 = state[SV_STATE_LEN];
     StateCache sc{0, 0};
-    if (wave == 0) sc = state_cache_load(state, lane);
+    int par0 = -1, tok0 = -1;                          // wave 0: the tree of this round (node lane + 1)
+    if (wave == 0) {
+        sc = state_cache_load(state, lane);
+        if (lane < K) { par0 = parents_in[lane]; tok0 = drafts_in[lane]; }
+    }
     const bool in_lds = len0 >= 0 && len0 + K + 1 <= cap && len0 + K + 1 <= kTreeIds;
     for (int s = wave; s < S; s += kTreeThreads / kWave) {
         const int bi = argmax_id(reduce_argmax_row(pv, pi, nparts, s, lane));
@@ -327,8 +339,7 @@ __global__ __launch_bounds__(kTreeThreads) void tree_tail_kernel(
     }
     barrier_lds();                                     // the stream (when it fits) and the argmax are in LDS
     if (wave == 0) {
-        const int j = accept_tree_wave(am, parents_in, drafts_in, K, tokens, cap, state, lane, in_lds ? tk : nullptr,
-                                       &sc);
+        const int j = accept_tree_regs(am, par0, tok0, K, tokens, cap, state, lane, in_lds ? tk : nullptr, &sc);
         // the gate word after this round, as the walk recorded it (no round recorded when j < 0)
         const int zero_run = j == 0 ? state_word(sc, SV_STATE_ZERO_RUN) + 1 : 0;
         const int gate_after = state_word(sc, SV_STATE_GATE_AFTER);
