@@ -1058,10 +1058,11 @@ GemmCfg gemm_config(int rows, int H, int S, int epi) {
     // head alone, alternating builds on one device each: 248320 x 2048 at S = 9 82.2-83.0
     // against 85.3-86.3 us (80.2-80.6 against 80.9-81.8 us on another device) and at S = 17
     // 81.7-83.1 against 84.3-85.0 us; the fused round at that shape 86.1-86.5 against
-    // 87.2-87.4 us.  At H = 2560 and 5120 it measured 0.5% slower and at 4096 even, and the
-    // sampling head (4 x 16 shape, one workgroup per compute unit) and the int4 head gained
-    // nothing, so those keep the interleaved order (the kernels read xcd for EPI_HEAD only: the
-    // sampling kernel built with the runtime choice ran 3% slower even in the interleaved order).
+    // 87.2-87.4 us.  At H = 2560 and 5120 it measured 0.5% slower and at 4096 even, the int4
+    // head gained nothing, and the sampling head (4 x 16 shape, one workgroup per compute unit)
+    // ran 4% slower with it (c3samp rounds), so those keep the interleaved order.  The kernels
+    // read xcd for EPI_HEAD only: the sampling kernel built with the runtime choice ran 3% slower
+    // even in the interleaved order.
     c.xcd = 0;
     if (c.fast && c.mt == 1 && c.ksplit == 1 && epi == EPI_HEAD && H <= 2048) {
         const int g8 = (c.grid + kXcds - 1) / kXcds * kXcds;
