@@ -7,7 +7,8 @@ size that is a multiple of 32 up to 8192 for the int8 head (fast and generic ker
 several hidden-axis splits), the int4 head's supported widths, and vocabularies whose last
 16-row tile is ragged.  Each case meets the fixed-shape tests' bar: logits within 1e-3 of the
 oracle's (relative, with the row RMS as floor), argmax equal except below a 1e-3 top-2 gap.  A
-sampling-verify sweep draws (V, H, S, T) and checks draws and log-sum-exp as the fixed-shape
+large-vocabulary sweep (65536 .. 300000 rows, H <= 2048, S = 1 .. 17) reaches the heads that take
+their items in one contiguous range per die.  A sampling-verify sweep draws (V, H, S, T) and checks draws and log-sum-exp as the fixed-shape
 sampling tests do.  A fused-round sweep draws (V, H, K, n-gram order, context length) and
 checks the committed ids and next drafts of three rounds exactly against oracle.accept and
 oracle.propose_scan; a tree-round sweep does the same for tree verify (K nodes, B branches,
@@ -58,6 +59,32 @@ def test_verify_random_shape(V, H, S):
     check_logits(lg, L)
     check_argmax(a, L)
     # the timed path (no logits written) takes the same decisions
+    a2, _ = gpu_verify(q, s, hidden, want_logits=False)
+    assert np.array_equal(a, a2)
+
+
+def _large_vocab_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        H = int(32 * rng.integers(1, 65))
+        out.append((int(rng.integers(65536, min(300000, 200_000_000 // H) + 1)), H, int(rng.integers(1, 18))))
+    return out
+
+
+@pytest.mark.parametrize("V,H,S", _large_vocab_cases(20261209, 8))
+def test_verify_large_vocab_random_shape(V, H, S):
+    """Vocabularies of 65536 rows or more at hidden sizes up to 2048, where the one-tile argmax
+    head takes its items in one contiguous range per die whenever every workgroup gets at
+    least 8 items: every logit and argmax row against the oracle, and the timed path (no
+    logits) agrees."""
+    say(f"verify large vocab V={V} H={H} S={S}")
+    q, s = synth.quantized_head(np.random.SeedSequence(V * 3 + H + S), V, H)
+    hidden = synth.fp16_normal(np.random.default_rng(V + H + S), (S, H))
+    a, lg = gpu_verify(q, s, hidden)
+    L = oracle.head_logits(q, s, hidden)
+    check_logits(lg, L)
+    check_argmax(a, L)
     a2, _ = gpu_verify(q, s, hidden, want_logits=False)
     assert np.array_equal(a, a2)
 
