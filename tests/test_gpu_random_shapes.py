@@ -8,8 +8,9 @@ several hidden-axis splits), the int4 head's supported widths, and vocabularies 
 16-row tile is ragged.  Each case meets the fixed-shape tests' bar: logits within 1e-3 of the
 oracle's (relative, with the row RMS as floor), argmax equal except below a 1e-3 top-2 gap.  A
 large-vocabulary sweep (65536 .. 300000 rows, H <= 2048, S = 1 .. 17) reaches the heads that take
-their items in one contiguous range per die.  A sampling-verify sweep draws (V, H, S, T) and checks draws and log-sum-exp as the fixed-shape
-sampling tests do.  A fused-round sweep draws (V, H, K, n-gram order, context length) and
+their items in one contiguous range per die.  A sampling-verify sweep draws (V, H, S, T) and
+checks draws and log-sum-exp as the fixed-shape sampling tests do.  A fused-round sweep draws
+(V, H, K, n-gram order, context length) and
 checks the committed ids and next drafts of three rounds exactly against oracle.accept and
 oracle.propose_scan; a tree-round sweep does the same for tree verify (K nodes, B branches,
 depth D) against oracle.tree, and a dense-stack sweep checks random block shapes block by
