@@ -10,11 +10,10 @@ oracle's (relative, with the row RMS as floor), argmax equal except below a 1e-3
 large-vocabulary sweep (65536 .. 300000 rows, H <= 2048, S = 1 .. 17) reaches the heads that take
 their items in one contiguous range per die.  A sampling-verify sweep draws (V, H, S, T) and
 checks draws and log-sum-exp as the fixed-shape sampling tests do.  A fused-round sweep draws
-(V, H, K, n-gram order, context length) and
-checks the committed ids and next drafts of three rounds exactly against oracle.accept and
-oracle.propose_scan; a tree-round sweep does the same for tree verify (K nodes, B branches,
-depth D) against oracle.tree, and a dense-stack sweep checks random block shapes block by
-block."""
+(V, H, K, n-gram order, context length) and checks the committed ids and next drafts of three
+rounds exactly against oracle.accept and oracle.propose_scan; a tree-round sweep does the same
+for tree verify (K nodes, B branches, depth D) against oracle.tree, and a dense-stack sweep
+checks random block shapes block by block."""
 import numpy as np
 import pytest
 import torch
